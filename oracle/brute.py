@@ -1,0 +1,129 @@
+"""Pure-Python brute-force twins of the oracle, for tiny inputs.
+
+TEST INFRASTRUCTURE ONLY (same rule as mdc_oracle: only tests/, smoke() and
+the cpu_baseline leg of bench.py may use it).  Written as independent
+formulations of the same definitions, so that a mistake in one does not hide
+in the other:
+
+  * dispatch: sorted() of (local expert, src, token, k) tuples instead of a
+    stable bucket pass; counts by dictionary; prefix sums by running total;
+  * fp32 arithmetic: Python floats (binary64) rounded to binary32 through
+    struct after every operation.  A product or sum of two binary32 values
+    computed in binary64 and then rounded to binary32 equals the correctly
+    rounded binary32 result (binary64 carries more than 2*24+2 bits);
+  * bf16 rounding: exact rational comparison of the two neighbouring bf16
+    values (fractions.Fraction), ties to the even significand.
+"""
+from __future__ import annotations
+
+import math
+import struct
+from fractions import Fraction
+
+
+def f32(v: float) -> float:
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+def bits_to_float_bf16(b: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", (b & 0xFFFF) << 16))[0]
+
+
+def _bf16_value(b: int) -> Fraction:
+    return Fraction(bits_to_float_bf16(b))
+
+
+def bf16_round(v: float) -> int:
+    """Nearest bf16 to a binary32 value v, ties to even significand, by exact comparison."""
+    if math.isnan(v):
+        return 0x7FC0 | (0x8000 if math.copysign(1.0, v) < 0 else 0)
+    if v == 0.0:
+        return 0x8000 if math.copysign(1.0, v) < 0 else 0x0000
+    sign = 0x8000 if v < 0 else 0
+    mag = abs(v)
+    # candidates: largest bf16 <= mag (by truncating the binary32 pattern) and the next one up
+    u = struct.unpack("<I", struct.pack("<f", mag))[0]
+    lo = u >> 16
+    hi = lo + 1
+    fv = Fraction(mag)
+    dlo = fv - _bf16_value(lo)
+    if hi >= 0x7F80:          # next one up is inf: compare against the overflow threshold
+        dhi = Fraction(2) ** 128 - fv
+    else:
+        dhi = _bf16_value(hi) - fv
+    if dlo < dhi:
+        pick = lo
+    elif dhi < dlo:
+        pick = hi
+    else:
+        pick = lo if lo % 2 == 0 else hi
+    return sign | pick
+
+
+def dispatch(ids, mask, d, experts, capacity, x=None):
+    """Brute-force dispatch: returns (rows list of (s,t,k), counts dict, epRecvCounts list, expertTokenNums list, expand rows)."""
+    W = len(ids)
+    BS = len(ids[0])
+    K = len(ids[0][0])
+    L = experts // W
+    tuples = []
+    for s in range(W):
+        for t in range(BS):
+            if mask is not None and not mask[s][t]:
+                continue
+            for k in range(K):
+                e = int(ids[s][t][k])
+                if e < 0 or e >= experts:
+                    continue
+                if e // L != d:
+                    continue
+                tuples.append((e - d * L, s, t, k))
+    tuples = sorted(tuples)
+    cnt = {}
+    for le, s, _, _ in tuples:
+        cnt[(le, s)] = cnt.get((le, s), 0) + 1
+    ep = []
+    run = 0
+    for le in range(L):
+        for s in range(W):
+            run += cnt.get((le, s), 0)
+            ep.append(run)
+    etn = [sum(cnt.get((le, s), 0) for s in range(W)) for le in range(L)]
+    rows = [(s, t, k) for (_, s, t, k) in tuples][:capacity]
+    expand = None
+    if x is not None:
+        expand = [list(x[s][t]) for (s, t, k) in rows]
+    return rows, cnt, ep, etn, expand
+
+
+def combine(segments, r, ids_r, mask_r, scales_r, shared_r, hidden):
+    """segments: list of (y rows [list of bf16 ints], triplets [list of (s,t,k)]); returns list of bf16 rows."""
+    BS = len(ids_r)
+    K = len(ids_r[0])
+    found = {}
+    for j, (yrows, trip) in enumerate(segments):
+        for row, (s, t, k) in enumerate(trip):
+            if s == r:
+                found[(t, k)] = yrows[row]
+    out = []
+    for t in range(BS):
+        acc = [0.0] * hidden
+        for k in range(K):
+            y = found.get((t, k))
+            if y is None:
+                continue
+            sc = f32(float(scales_r[t][k]))
+            for h in range(hidden):
+                a = f32(sc * bits_to_float_bf16(int(y[h])))
+                if shared_r is not None:
+                    b = f32(sc * bits_to_float_bf16(int(shared_r[t][h])))
+                    acc[h] = f32(acc[h] + f32(a + b))
+                else:
+                    acc[h] = f32(acc[h] + a)
+        out.append([bf16_round(v) for v in acc])
+    return out
+
+
+def int_matmul(a, b_t):
+    """Exact integer a[m][k] . b_t[n][k]^T with Python ints."""
+    return [[sum(int(x) * int(y) for x, y in zip(row, col)) for col in b_t] for row in a]

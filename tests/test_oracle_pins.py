@@ -1,0 +1,369 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test checks the oracle against brute force on tiny inputs, a textbook
+routine the method reduces to, an invariant, a closed form, or a value that
+follows from the pages' own worked samples (tests/golden/).
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import brute as B
+from oracle import mdc_oracle as O
+from workloads import gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _tiny_world(seed, W, BS, E, K, mask_kind="none", dup=False, invalid=False):
+    g = np.random.default_rng(seed)
+    if dup:
+        ids = g.integers(0, E, size=(W, BS, K)).astype(np.int32)
+    else:
+        ids = np.stack([np.stack([g.permutation(E)[:K] for _ in range(BS)]) for _ in range(W)]).astype(np.int32)
+    if invalid:
+        bad = g.random((W, BS, K)) < 0.2
+        ids[bad] = g.choice([-1, E, E + 3, -7], size=int(bad.sum()))
+    if mask_kind == "none":
+        mask = None
+    elif mask_kind == "all":
+        mask = np.ones((W, BS), np.uint8)
+    elif mask_kind == "off":
+        mask = np.zeros((W, BS), np.uint8)
+    elif mask_kind == "alt":
+        mask = (np.arange(BS)[None, :] % 2 == 0).repeat(W, 0).astype(np.uint8)
+    else:
+        mask = (g.random((W, BS)) < 0.6).astype(np.uint8)
+    x = gen.bf16_from_f32(g.standard_normal((W, BS, 4), dtype=np.float32))
+    return ids, mask, x
+
+
+def _tiny_cases():
+    cases = []
+    seed = 0
+    for W in (1, 2, 3):
+        for E in sorted({e for e in range(W, 9) if e % W == 0}):
+            for K in (1, 2, 3):
+                if K > E:
+                    continue
+                for BS in (1, 3, 6):
+                    for mk in ("none", "all", "off", "alt", "rand"):
+                        seed += 1
+                        cases.append((seed, W, BS, E, K, mk, seed % 3 == 0, seed % 5 == 0))
+    return cases
+
+
+@pytest.mark.parametrize("case", _tiny_cases()[::3])
+def test_dispatch_matches_brute_force(case):
+    seed, W, BS, E, K, mk, dup, invalid = case
+    ids, mask, x = _tiny_world(seed, W, BS, E, K, mk, dup and E >= K, invalid)
+    for cap in (10 ** 6, 5, 1):
+        for d in range(W):
+            o = O.dispatch(x, ids, mask, d, E, cap)
+            rows, cnt, ep, etn, ex = B.dispatch(ids.tolist(), None if mask is None else mask.tolist(), d, E, cap, x.tolist())
+            assert [tuple(r) for r in o.assist_info.tolist()] == rows
+            assert o.ep_recv_counts.tolist() == ep
+            assert o.expert_token_nums.tolist() == etn
+            assert o.expert_token_nums.dtype == np.int64
+            assert o.ep_recv_counts.dtype == np.int32
+            assert o.expand_x.tolist() == (ex if ex else [])
+
+
+def test_single_rank_dispatch_is_stable_counting_sort():
+    """W = 1, L = E: the expert-major layout is a stable sort of the flattened ids."""
+    g = np.random.default_rng(7)
+    for trial in range(20):
+        BS, E, K = int(g.integers(1, 40)), int(g.integers(1, 20)), int(g.integers(1, 5))
+        ids = g.integers(0, E, size=(1, BS, K)).astype(np.int32)
+        o = O.dispatch(None, ids, None, 0, E, 10 ** 9)
+        order = np.argsort(ids.ravel(), kind="stable")
+        want = np.stack([np.zeros_like(order), order // K, order % K], axis=1)
+        assert np.array_equal(o.assist_info, want)
+        assert np.array_equal(o.expert_token_nums, np.bincount(ids.ravel(), minlength=E))
+        assert np.array_equal(o.ep_recv_counts, np.cumsum(np.bincount(ids.ravel(), minlength=E)))
+
+
+def _check_invariants(ids, mask, E, x):
+    W, BS, K = ids.shape
+    L = E // W
+    active = np.ones((W, BS), bool) if mask is None else mask.astype(bool)
+    valid = (ids >= 0) & (ids < E) & active[:, :, None]
+    covered = []
+    for d in range(W):
+        o = O.dispatch(x, ids, mask, d, E, 10 ** 9)
+        # I1: per share, the per-expert counts add up to the last inclusive count
+        assert o.expert_token_nums.sum() == o.ep_recv_counts[-1] == o.total
+        # I2: within each local expert block, triplets strictly increase in (s, t, k)
+        starts = np.concatenate([[0], np.cumsum(o.expert_token_nums)])
+        for le in range(L):
+            blk = [tuple(v) for v in o.assist_info[starts[le]:starts[le + 1]].tolist()]
+            assert blk == sorted(blk) and len(set(blk)) == len(blk)
+            for s, t, k in blk:       # I4/I5: each row's route maps to this (d, le)
+                assert ids[s, t, k] == d * L + le and valid[s, t, k]
+        # I4: counts equal a histogram of active local ids per source
+        for s in range(W):
+            loc = ids[s][valid[s]]
+            loc = loc[(loc // L) == d] - d * L
+            assert np.array_equal(o.counts[:, s], np.bincount(loc, minlength=L))
+        # I6: rows are bitwise copies
+        for row, (s, t, k) in enumerate(o.assist_info.tolist()):
+            assert np.array_equal(o.expand_x[row], x[s, t])
+        covered += [tuple(v) for v in o.assist_info.tolist()]
+    # I1 (world) + I7: every active valid route appears exactly once over all shares
+    assert len(covered) == len(set(covered)) == int(valid.sum())
+    assert set(covered) == {tuple(v) for v in np.argwhere(valid).tolist()}
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_dispatch_invariants(seed):
+    g = np.random.default_rng(100 + seed)
+    W = int(g.choice([1, 2, 4, 8]))
+    L = int(g.integers(1, 6))
+    E, K, BS = W * L, int(g.integers(1, min(4, W * L) + 1)), int(g.integers(1, 50))
+    ids, mask, x = _tiny_world(seed, W, BS, E, K, ["none", "rand"][seed % 2], seed % 3 == 0, seed % 4 == 1)
+    _check_invariants(ids, mask, E, x)
+
+
+def test_cv4_a2_sample_routing_closed_form():
+    """Expert ids = slot index: everything lands on rank 0 and fills A exactly."""
+    gold = json.load(open(os.path.join(GOLDEN, "cv4_a2_sample_routing.json")))
+    W, BS, K, E = gold["world"], gold["bs"], gold["topk"], gold["experts"]
+    ids = np.tile(np.arange(K, dtype=np.int32), (W, BS, 1))
+    o = O.dispatch(None, ids, None, 0, E, gold["capacity"])
+    assert o.total == gold["rank0"]["total"] == o.assist_info.shape[0] == gold["capacity"]
+    assert o.expert_token_nums.tolist() == gold["rank0"]["expert_token_nums"]
+    assert o.ep_recv_counts[:W].tolist() == gold["rank0"]["ep_recv_counts_first_block"]
+    assert o.ep_recv_counts[-1] == gold["rank0"]["ep_recv_counts_last"]
+    for d in range(1, W):
+        assert O.dispatch(None, ids, None, d, E, gold["capacity"]).total == gold["other_ranks_total"]
+    # one slot below the bound drops exactly the last row
+    o2 = O.dispatch(None, ids, None, 0, E, gold["capacity"] - 1)
+    assert o2.assist_info.shape[0] == gold["capacity"] - 1 and o2.total == gold["capacity"]
+
+
+def test_tagged_rows_bf16_values():
+    gold = json.load(open(os.path.join(GOLDEN, "tl_tagged_rows.json")))
+    for v, bits in gold["tag_bf16"].items():
+        assert int(O.f32_to_bf16_rne(np.array([float(v)], np.float32))[0]) == bits
+        assert B.bf16_round(float(v)) == bits
+
+
+def test_tagged_world_route_total():
+    """The TileLang example's shape: identical routing on every rank, K distinct experts."""
+    gold = json.load(open(os.path.join(GOLDEN, "tl_tagged_rows.json")))
+    W, BS, K, L = gold["world"], gold["bs"], gold["topk"], gold["local_experts"]
+    E = W * L
+    g = np.random.default_rng(1)
+    one = np.stack([g.permutation(E)[:K] for _ in range(BS)]).astype(np.int32)
+    ids = np.broadcast_to(one, (W, BS, K)).copy()
+    tot = sum(O.dispatch(None, ids, None, d, E, gold["window_rows_per_rank"]).total for d in range(W))
+    assert tot == gold["world_routes"] == W * BS * K
+
+
+# ----------------------------------------------------------------------------- bf16
+
+
+def _edge_f32():
+    specials = [0.0, -0.0, 1.0, -1.0, np.inf, -np.inf, 3.4028235e38, -3.4028235e38,
+                1e-45, -1e-45, 1.1754944e-38, 1.0 + 2 ** -8, 1.0 + 2 ** -9, 1.0 + 3 * 2 ** -9,
+                1.0 + 2 ** -9 + 2 ** -20, 255.5, 256.5, 3.3961776e38, 3.3961778e38]
+    u = np.array([0x3F808000, 0x3F818000, 0x3F80FFFF, 0x3F817FFF, 0x7F7FFFFF, 0x7F7F8000, 0x7F7F7FFF,
+                  0x00008000, 0x00018000, 0x80008000, 0x007FFFFF], dtype=np.uint32)
+    return np.concatenate([np.array(specials, np.float32), u.view(np.float32)])
+
+
+def test_bf16_rne_matches_torch_cast():
+    g = np.random.default_rng(3)
+    bits = g.integers(0, 2 ** 32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    vals = np.concatenate([bits.view(np.float32), _edge_f32()])
+    vals = vals[~np.isnan(vals)]
+    want = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.f32_to_bf16_rne(vals), want)
+
+
+def test_bf16_rne_matches_exact_rational_rounding():
+    g = np.random.default_rng(4)
+    vals = np.concatenate([g.standard_normal(3000).astype(np.float32) * np.float32(10.0) ** g.integers(-30, 30, 3000).astype(np.float32),
+                           _edge_f32()])
+    vals = vals[np.isfinite(vals)]
+    got = O.f32_to_bf16_rne(vals)
+    for v, b in zip(vals.tolist(), got.tolist()):
+        assert B.bf16_round(v) == b, v
+
+
+def test_bf16_nan_is_quiet():
+    v = np.array([np.nan, -np.nan], np.float32)
+    out = O.f32_to_bf16_rne(v)
+    assert all((int(b) & 0x7FFF) == 0x7FC0 for b in out)
+
+
+def test_bf16_to_f32_exact():
+    bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    f = O.bf16_to_f32(bits)
+    want = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float32).numpy()
+    fin = ~np.isnan(want)
+    assert np.array_equal(f[fin], want[fin]) and np.isnan(f[~fin]).all()
+
+
+# ----------------------------------------------------------------------------- combine
+
+
+def _world_segments(ids, mask, x, E, cap, expert=O.expert_identity):
+    W = ids.shape[0]
+    L = E // W
+    segs = [O.dispatch(x, ids, mask, d, E, cap) for d in range(W)]
+    ys = [expert(s.expand_x, s.assist_info, ids, L) for s in segs]
+    return segs, ys
+
+
+@pytest.mark.parametrize("case", _tiny_cases()[1::9])
+def test_combine_matches_brute_force(case):
+    seed, W, BS, E, K, mk, dup, invalid = case
+    ids, mask, x = _tiny_world(seed, W, BS, E, K, mk, dup and E >= K, invalid)
+    g = np.random.default_rng(seed)
+    H = x.shape[-1]
+    for shared_on in (False, True):
+        segs, ys = _world_segments(ids, mask, x, E, 10 ** 6, O.expert_pow2)
+        for r in range(W):
+            sc = g.standard_normal((BS, K)).astype(np.float32)
+            sh = gen.bf16_from_f32(g.standard_normal((BS, H), dtype=np.float32)) if shared_on else None
+            m = None if mask is None else mask[r]
+            got = O.combine(ys, [s.assist_info for s in segs], r, ids[r], m, sc, sh, H)
+            bseg = [(y.tolist(), [tuple(v) for v in s.assist_info.tolist()]) for y, s in zip(ys, segs)]
+            want = B.combine(bseg, r, ids[r].tolist(), None if m is None else m.tolist(), sc.tolist(),
+                             None if sh is None else sh.tolist(), H)
+            assert got.tolist() == want
+
+
+def test_identity_round_trip_returns_x():
+    """Dispatch -> identity expert -> combine with unit-sum scales returns x (compared by value)."""
+    w = gen.workload("tiny")
+    wi = gen.world_inputs(w)
+    for variant in range(3):
+        ww = gen.workload("tiny", world=2, experts=8, bs=24, index=50 + variant) if variant else w
+        wi = gen.world_inputs(ww)
+        segs, ys = _world_segments(wi.ids, wi.mask, wi.x, ww.experts, ww.capacity)
+        for r in range(ww.world):
+            out = O.combine(ys, [s.assist_info for s in segs], r, wi.ids[r], None, wi.scales[r], None, ww.hidden)
+            assert np.array_equal(O.bf16_to_f32(out), O.bf16_to_f32(wi.x[r]))
+
+
+def test_pow2_expert_closed_form():
+    """Power-of-two scales and tags: every step is exact, so out = x * sum_k s_k 2^c_k exactly."""
+    g = np.random.default_rng(11)
+    W, BS, E, K, H = 2, 12, 8, 3, 16
+    ids = np.stack([np.stack([g.permutation(E)[:K] for _ in range(BS)]) for _ in range(W)]).astype(np.int32)
+    # x with few significant bits so that the exact sum stays representable in bf16
+    x = gen.bf16_from_f32(g.integers(-8, 9, size=(W, BS, H)).astype(np.float32))
+    segs, ys = _world_segments(ids, None, x, E, 10 ** 6, O.expert_pow2)
+    for r in range(W):
+        sc = (2.0 ** -g.integers(0, 3, size=(BS, K))).astype(np.float32)
+        out = O.bf16_to_f32(O.combine(ys, [s.assist_info for s in segs], r, ids[r], None, sc, None, H))
+        coef = np.array([[sum(float(sc[t, k]) * 2.0 ** O.pow2_exponent(int(ids[r, t, k])) for k in range(K))]
+                         for t in range(BS)])
+        want = O.bf16_to_f32(x[r]).astype(np.float64) * coef
+        assert np.array_equal(out.astype(np.float64), want)
+
+
+def test_combine_shared_term_weighted_per_k():
+    """Shared row weighted by each present route's scale: with y = 0, out = bf16(sum_k s_k * sh)."""
+    W, BS, E, K, H = 1, 4, 4, 2, 8
+    ids = np.array([[[0, 1], [2, 3], [1, 2], [3, 0]]], np.int32)
+    x = np.zeros((1, BS, H), np.uint16)
+    sh = gen.bf16_from_f32(np.full((BS, H), 3.0, np.float32))
+    sc = np.array([[0.5, 0.25], [1.0, 2.0], [0.75, 0.0], [-1.0, 0.5]], np.float32)
+    mask = np.array([[1, 1, 0, 1]], np.uint8)
+    segs, ys = _world_segments(ids, mask, x, E, 100)
+    out = O.bf16_to_f32(O.combine(ys, [s.assist_info for s in segs], 0, ids[0], mask[0], sc, sh, H))
+    assert np.array_equal(out[:, 0], np.array([2.25, 9.0, 0.0, -1.5], np.float32))
+
+
+def test_combine_inactive_and_overflow_routes_drop():
+    g = np.random.default_rng(5)
+    W, BS, E, K, H = 2, 10, 4, 2, 8
+    ids = np.stack([np.stack([g.permutation(E)[:K] for _ in range(BS)]) for _ in range(W)]).astype(np.int32)
+    x = gen.bf16_from_f32(g.standard_normal((W, BS, H), dtype=np.float32))
+    mask = (g.random((W, BS)) < 0.5).astype(np.uint8)
+    cap = 6
+    segs, ys = _world_segments(ids, mask, x, E, cap)
+    kept = {tuple(v) for s in segs for v in s.assist_info.tolist()}
+    sc = np.ones((BS, K), np.float32)
+    for r in range(W):
+        out = O.bf16_to_f32(O.combine(ys, [s.assist_info for s in segs], r, ids[r], mask[r], sc, None, H))
+        for t in range(BS):
+            n = sum((r, t, k) in kept for k in range(K))
+            if not mask[r, t]:
+                assert n == 0 and not out[t].any()
+            want = O.bf16_to_f32(O.f32_to_bf16_rne(O.bf16_to_f32(x[r, t]) * np.float32(n)))
+            assert np.array_equal(out[t], want)
+
+
+# ----------------------------------------------------------------------------- FFN
+
+
+def test_int_gemm_exact_against_python_ints():
+    g = np.random.default_rng(9)
+    a = g.integers(-127, 128, size=(5, 33), dtype=np.int8)
+    b = g.integers(-127, 128, size=(7, 33), dtype=np.int8)
+    want = B.int_matmul(a.tolist(), b.tolist())
+    got = a.astype(np.float64) @ b.astype(np.float64).T
+    assert got.astype(np.int64).tolist() == want
+
+
+def test_quant_rows_properties():
+    g = np.random.default_rng(10)
+    v = g.standard_normal((50, 64)).astype(np.float32)
+    v[3] = 0.0
+    q, s = O.quant_rows(v)
+    assert q.dtype == np.int8 and np.abs(q.astype(int)).max() <= 127
+    assert s[3] == 0 and not q[3].any()
+    for i in range(50):
+        if i == 3:
+            continue
+        j = int(np.argmax(np.abs(v[i])))
+        assert abs(int(q[i, j])) == 127 and np.sign(q[i, j]) == np.sign(v[i, j])
+        assert np.max(np.abs(q[i] * s[i] - v[i])) <= s[i] * 0.5000001
+
+
+def test_ffn_permutation_weights_closed_form():
+    """Permutation weights: GMM1 picks known columns, so the result has a closed form.
+
+    w1[le] rows n < N/2 select input column p[n] times 1, rows n >= N/2 select
+    column p2[n - N/2] times 1; GMM2 selects g column p3[h].  Integer inputs in
+    [-127, 127] with a 127 present quantise exactly (scale 1).  This pins the
+    orientation of both weights, the per-channel scale index and which half
+    goes through silu.
+    """
+    g = np.random.default_rng(12)
+    H, N = 16, 16
+    half = N // 2
+    Lx = 2
+    R = 6
+    x_int = g.integers(-127, 128, size=(R, H)).astype(np.float32)
+    x_int[:, 0] = 127.0
+    xb = gen.bf16_from_f32(x_int)         # integers up to 127 are exact in bf16
+    row_expert = np.array([0, 1, 0, 1, 1, 0])
+    w1 = np.zeros((Lx, N, H), np.int8)
+    w2 = np.zeros((Lx, H, half), np.int8)
+    perm1 = [g.permutation(H) for _ in range(Lx)]
+    perm2 = [g.permutation(half) for _ in range(Lx)]
+    for le in range(Lx):
+        for n in range(N):
+            w1[le, n, perm1[le][n % H]] = 1
+        for h in range(H):
+            w2[le, h, perm2[le][h % half]] = 1
+    s1 = g.uniform(1e-3, 1e-2, size=(Lx, N)).astype(np.float32)
+    s2 = np.ones((Lx, H), np.float32)
+    y = O.bf16_to_f32(O.ffn(xb, row_expert, w1, s1, w2, s2)).astype(np.float64)
+    for i in range(R):
+        le = row_expert[i]
+        h = np.array([x_int[i, perm1[le][n % H]] * float(s1[le, n]) for n in range(N)])
+        gg = h[:half] / (1 + np.exp(-h[:half])) * h[half:]
+        want = np.array([gg[perm2[le][hh % half]] for hh in range(H)])
+        # second quantisation: error at most half a step of amax/127, then bf16 rounding
+        step = np.max(np.abs(gg)) / 127
+        assert np.all(np.abs(y[i] - want) <= 0.5 * step + np.abs(want) * 2 ** -8 + 1e-12)
