@@ -1,0 +1,218 @@
+"""Python binding of libmdc (MoE dispatch/combine for MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libmdc.so, declared in include/mdc.h.  torch tensors are passed as device
+pointers; torch provides device memory and streams.  The functions carry the
+names of the C entry points.  Importing this package fails loudly when
+libmdc.so has not been built (python -m combine_route_histogram_amd.build).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmdc.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libmdc.so not found at {LIB_PATH}; build it with "
+        "`python -m combine_route_histogram_amd.build` (hipcc, gfx950)")
+
+# torch provides device memory and streams.  Its wheel carries its own HIP
+# runtime (same SONAME, libamdhip64.so.7): loading torch first makes libmdc
+# bind to that runtime, so torch's streams and pointers are valid in libmdc.
+import torch  # noqa: E402,F401
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+MDC_OK = 0
+MDC_ERR_NULLPTR = 1
+MDC_ERR_INVALID = 2
+MDC_ERR_WORKSPACE = 3
+MDC_ERR_HIP = 4
+MDC_MAX_TOPK = 16
+MDC_MAX_LOCAL_EXPERTS = 2048
+MDC_MAX_COMBINE_WORLD = 64
+
+EXPORTS = (
+    "mdc_status_string", "mdc_abi_version",
+    "mdc_dispatch_workspace_size", "mdc_dispatch_layout", "mdc_dispatch_gather", "mdc_dispatch",
+    "mdc_combine_workspace_size", "mdc_combine",
+)
+
+
+class mdc_shape(ctypes.Structure):
+    _fields_ = [("world", ctypes.c_int32), ("rank", ctypes.c_int32), ("bs", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("topk", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("capacity", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_SZ = ctypes.c_size_t
+_SHP = ctypes.POINTER(mdc_shape)
+
+_lib.mdc_status_string.restype = ctypes.c_char_p
+_lib.mdc_status_string.argtypes = [ctypes.c_int]
+_lib.mdc_abi_version.restype = ctypes.c_int32
+_lib.mdc_abi_version.argtypes = []
+_lib.mdc_dispatch_workspace_size.restype = ctypes.c_int
+_lib.mdc_dispatch_workspace_size.argtypes = [_SHP, ctypes.POINTER(_SZ)]
+_lib.mdc_dispatch_layout.restype = ctypes.c_int
+_lib.mdc_dispatch_layout.argtypes = [_SHP, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.mdc_dispatch_gather.restype = ctypes.c_int
+_lib.mdc_dispatch_gather.argtypes = [_SHP, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.mdc_dispatch.restype = ctypes.c_int
+_lib.mdc_dispatch.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.mdc_combine_workspace_size.restype = ctypes.c_int
+_lib.mdc_combine_workspace_size.argtypes = [_SHP, ctypes.POINTER(_SZ)]
+_lib.mdc_combine.restype = ctypes.c_int
+_lib.mdc_combine.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+
+
+class MdcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {mdc_status_string(status)}")
+
+
+def mdc_status_string(status: int) -> str:
+    return _lib.mdc_status_string(int(status)).decode()
+
+
+def mdc_abi_version() -> int:
+    return int(_lib.mdc_abi_version())
+
+
+@dataclass
+class Shape:
+    world: int
+    rank: int
+    bs: int
+    hidden: int
+    topk: int
+    num_experts: int
+    capacity: int
+
+    @property
+    def local_experts(self) -> int:
+        return self.num_experts // self.world
+
+    def c(self) -> mdc_shape:
+        return mdc_shape(self.world, self.rank, self.bs, self.hidden, self.topk, self.num_experts, self.capacity)
+
+    def with_rank(self, rank: int) -> "Shape":
+        return Shape(self.world, rank, self.bs, self.hidden, self.topk, self.num_experts, self.capacity)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("mdc: tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _nbytes(t) -> int:
+    if t is None:
+        return 0
+    return t.numel() * t.element_size()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != MDC_OK:
+        raise MdcError(status, where)
+
+
+def mdc_dispatch_workspace_size(shape: Shape) -> int:
+    out = _SZ(0)
+    sh = shape.c()
+    _check(_lib.mdc_dispatch_workspace_size(ctypes.byref(sh), ctypes.byref(out)), "mdc_dispatch_workspace_size")
+    return int(out.value)
+
+
+def mdc_combine_workspace_size(shape: Shape) -> int:
+    out = _SZ(0)
+    sh = shape.c()
+    _check(_lib.mdc_combine_workspace_size(ctypes.byref(sh), ctypes.byref(out)), "mdc_combine_workspace_size")
+    return int(out.value)
+
+
+def mdc_dispatch_layout(shape: Shape, expert_ids, x_active_mask, ep_recv_counts, expert_token_nums,
+                        workspace, stream=None, check: bool = True) -> int:
+    sh = shape.c()
+    st = _lib.mdc_dispatch_layout(ctypes.byref(sh), _ptr(expert_ids), _ptr(x_active_mask), _ptr(ep_recv_counts),
+                                  _ptr(expert_token_nums), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    if check:
+        _check(st, "mdc_dispatch_layout")
+    return st
+
+
+def mdc_dispatch_gather(shape: Shape, x, expand_x, assist_info, expanded_row_idx, workspace,
+                        stream=None, check: bool = True) -> int:
+    sh = shape.c()
+    st = _lib.mdc_dispatch_gather(ctypes.byref(sh), _ptr(x), _ptr(expand_x), _ptr(assist_info),
+                                  _ptr(expanded_row_idx), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    if check:
+        _check(st, "mdc_dispatch_gather")
+    return st
+
+
+def mdc_dispatch(shape: Shape, x, expert_ids, x_active_mask, expand_x, assist_info, ep_recv_counts,
+                 expert_token_nums, expanded_row_idx, workspace, stream=None, check: bool = True) -> int:
+    sh = shape.c()
+    st = _lib.mdc_dispatch(ctypes.byref(sh), _ptr(x), _ptr(expert_ids), _ptr(x_active_mask), _ptr(expand_x),
+                           _ptr(assist_info), _ptr(ep_recv_counts), _ptr(expert_token_nums),
+                           _ptr(expanded_row_idx), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    if check:
+        _check(st, "mdc_dispatch")
+    return st
+
+
+def _table(items: Sequence) -> ctypes.Array:
+    arr = (ctypes.c_void_p * max(1, len(items)))()
+    for i, t in enumerate(items):
+        arr[i] = _ptr(t)
+    return arr
+
+
+def mdc_combine(shape: Shape, expand_x: Sequence, assist_info: Sequence, ep_recv_counts: Sequence,
+                expanded_row_idx, expert_ids, expert_scales, x_active_mask, shared_expert_x, x_out,
+                workspace=None, stream=None, check: bool = True) -> int:
+    sh = shape.c()
+    ty, ta, tc = _table(expand_x), _table(assist_info), _table(ep_recv_counts)
+    st = _lib.mdc_combine(ctypes.byref(sh), ctypes.cast(ty, _P), ctypes.cast(ta, _P), ctypes.cast(tc, _P),
+                          _ptr(expanded_row_idx), _ptr(expert_ids), _ptr(expert_scales), _ptr(x_active_mask),
+                          _ptr(shared_expert_x), _ptr(x_out), _ptr(workspace), _nbytes(workspace),
+                          _stream(stream))
+    if check:
+        _check(st, "mdc_combine")
+    return st
+
+
+def alloc_dispatch_outputs(shape: Shape, device="cuda"):
+    """Device buffers for one destination rank's dispatch outputs (plumbing for callers)."""
+    import torch
+    L, W, A = shape.local_experts, shape.world, shape.capacity
+    return {
+        "expand_x": torch.empty((A, shape.hidden), dtype=torch.bfloat16, device=device),
+        "assist_info": torch.empty((A, 3), dtype=torch.int32, device=device),
+        "ep_recv_counts": torch.empty((L * W,), dtype=torch.int32, device=device),
+        "expert_token_nums": torch.empty((L,), dtype=torch.int64, device=device),
+        "workspace": torch.empty((mdc_dispatch_workspace_size(shape),), dtype=torch.uint8, device=device),
+    }

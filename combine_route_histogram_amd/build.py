@@ -1,0 +1,49 @@
+"""Build libmdc.so (HIP, gfx950) in-tree: python -m combine_route_histogram_amd.build"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "mdc.hip")
+INC = os.path.join(ROOT, "include")
+OUT = os.path.join(PKG, "libmdc.so")
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # fp32 products and sums of the combine are rounded one by one (no FMA contraction)
+    "-ffp-contract=off",
+    # never emit packed fp32 arithmetic
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    return "hipcc"
+
+
+def build(verbose: bool = False) -> str:
+    tmp = OUT + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INC, SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libmdc.so")
+    os.replace(tmp, OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,212 @@
+/*
+ * mdc.h -- C ABI of the MoE dispatch/combine library (libmdc.so) for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The library implements one GPU's share of expert-parallel MoE dispatch and
+ * combine.  The W ranks of the expert-parallel group are *virtual*: their
+ * buffers live on the same GPU, so the cross-rank AllToAllV becomes a local
+ * permutation.
+ *
+ * Sources (cited by page title and section):
+ *   [TL]  "dispatch_combine_shmem.py" (TileLang-Ascend example): moe_dispatch_kernel
+ *         (send loop "AlltoAllDispatch", "SetStatus", "GetCumSum", local data copy,
+ *         "UpdateTokenNumsOut") and moe_combine_kernel (weighted sum).
+ *   [CV4] "aclnnMoeDistributeCombineV4": Function (formula), Function Prototype
+ *         (two-phase API and parameter table), Return Value, Constraints
+ *         (shape-variable table, API matching constraints, determinism).
+ *   [PTO] "PTO MegaMoE Dispatch + Combine Fusion Example": FrontReorder Stage,
+ *         Dispatch Stage, GMM1 / SwiGLU / GMM2 Stages, Combine / Unpermute Stages,
+ *         Memory Layout and HCCL Window.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is a device pointer owned by the caller; the
+ *     library never allocates, frees or synchronises.  Work is enqueued on
+ *     `stream` (a hipStream_t; NULL = the default stream) and the call returns
+ *     at once.  Inputs must stay alive and unmodified until the enqueued work
+ *     has run.
+ *   - bf16 tensors are arrays of 16-bit bf16 bit patterns; bf16 row tensors
+ *     (x, expand_x, shared_expert_x, x_out) must be 16-byte aligned.
+ *   - Expert e lives on rank e / L as local expert e % L, L = E / W
+ *     ([TL] send loop; [CV4] shape-variable table, localExpertNum).
+ *   - A route is (s, t, k): source rank s, token t, top-k slot k.
+ *   - Argument errors are reported synchronously by the return value, before
+ *     anything is enqueued (codes mirror [CV4] Return Value: null tensor,
+ *     unsupported type/shape, value out of range).  Conditions found in the
+ *     data (ids outside [0, E), too many rows for the capacity) are not
+ *     errors: see each call.
+ *   - Results are bitwise deterministic: no floating-point atomics, fixed
+ *     summation order ([CV4] Constraints, deterministic computation).
+ *   - Calls that share a workspace must not overlap (use one stream or order
+ *     them); otherwise the library keeps no state and is reentrant.
+ */
+#ifndef MDC_H
+#define MDC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MDC_ABI_VERSION 1
+#define MDC_MAX_TOPK 16        /* 0 < K <= 16 ([CV4] shape-variable table) */
+#define MDC_MAX_LOCAL_EXPERTS 2048
+#define MDC_MAX_COMBINE_WORLD 64 /* W limit of mdc_combine (pointer tables travel by value) */
+
+typedef enum {
+    MDC_OK = 0,
+    MDC_ERR_NULLPTR = 1,    /* a required pointer is NULL (cf. ACLNN_ERR_PARAM_NULLPTR) */
+    MDC_ERR_INVALID = 2,    /* shape, alignment or value outside the supported range
+                               (cf. ACLNN_ERR_PARAM_INVALID / ACLNN_ERR_INNER_TILING_ERROR) */
+    MDC_ERR_WORKSPACE = 3,  /* workspace smaller than the size query returned */
+    MDC_ERR_HIP = 4         /* a HIP kernel launch failed */
+} mdc_status;
+
+/* Problem shape.  `rank` is the destination rank for dispatch and the source
+ * rank whose tokens are combined for combine. */
+typedef struct {
+    int32_t world;        /* W >= 1 virtual EP ranks */
+    int32_t rank;         /* 0 <= rank < W */
+    int32_t bs;           /* BS >= 0 tokens per rank */
+    int32_t hidden;       /* H > 0, multiple of 8 (one 16-byte vector = 8 bf16) */
+    int32_t topk;         /* K, 1..MDC_MAX_TOPK */
+    int32_t num_experts;  /* E > 0, multiple of W; L = E / W <= MDC_MAX_LOCAL_EXPERTS */
+    int64_t capacity;     /* A >= 0: rows of expand_x / assist_info per rank.
+                             [CV4] shape-variable table asks A >= BS*W*min(L, K). */
+} mdc_shape;
+
+const char* mdc_status_string(mdc_status status);
+int32_t mdc_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Dispatch ([TL] moe_dispatch_kernel; [PTO] FrontReorder + Dispatch stages)
+ *
+ * For destination rank d = shape->rank, over all W virtual source ranks:
+ *   - a route (s, t, k) is sent iff token t of rank s is active and
+ *     e = expert_ids[s][t][k] satisfies d*L <= e < (d+1)*L.  Ids outside
+ *     [0, E) are dropped (never sent anywhere).
+ *   - the received rows are laid out expert-major in the stable order
+ *     (local expert le, source s, token t, slot k): row = base(le, s) +
+ *     number of earlier routes (t', k') < (t, k) of source s with the same
+ *     expert ([TL] send loop: rank-within-expert counts earlier equal ids;
+ *     local data copy walks status rows le*W + src; [PTO] Dispatch Stage:
+ *     a local expert's rows ordered by source rank).
+ *
+ * Outputs
+ *   ep_recv_counts    [L*W] int32, inclusive prefix of the per-(le, s) counts
+ *                     in (le-major, s-minor) order; the last entry is the total
+ *                     R of received routes ([TL] GetCumSum / local data copy:
+ *                     receive count = begin + count).
+ *   expert_token_nums [L] int64, routes received per local expert
+ *                     ([TL] UpdateTokenNumsOut).
+ *   expand_x          [A][H] bf16: row i = x[s][t] of the route at row i,
+ *                     copied bitwise ([TL] send loop row put).
+ *   assist_info       [A][3] int32: row i = (s, t, k) ([TL] triplet written
+ *                     after the row; [CV4] assistInfoForCombine).
+ *   expanded_row_idx  [W][BS][K] int32, the inverse route index ([PTO]
+ *                     Memory Layout: expandedRowIdx, route -> expert-major
+ *                     row): for every route sent to d the entry is its row, or
+ *                     -1 if that row is >= A.  Entries of routes not sent to d
+ *                     are left untouched, so the W dispatches of one step fill
+ *                     disjoint parts of one shared table.
+ *   Only rows [0, min(R, A)) of expand_x / assist_info are written; rows with
+ *   index >= A are dropped while the counts still include them, so overflow
+ *   shows as ep_recv_counts[L*W-1] > A.  Rows past the total are untouched.
+ *
+ * Inputs
+ *   x                 [W][BS][H] bf16, the virtual source ranks' tokens.
+ *   expert_ids        [W][BS][K] int32.
+ *   x_active_mask     [W][BS] uint8 (nonzero = active) or NULL (all active);
+ *                     any order of active/inactive tokens is accepted.
+ *
+ * The call is split in two stages that may be enqueued separately (same
+ * stream, same workspace, in this order); mdc_dispatch enqueues both.
+ *   mdc_dispatch_layout  histogram + scan: writes ep_recv_counts,
+ *                        expert_token_nums and the per-route ranks into ws.
+ *   mdc_dispatch_gather  rows, triplets and the inverse index, from ws.
+ * ------------------------------------------------------------------------ */
+mdc_status mdc_dispatch_workspace_size(const mdc_shape* shape, size_t* bytes);
+
+mdc_status mdc_dispatch_layout(const mdc_shape* shape,
+                               const int32_t* expert_ids,
+                               const uint8_t* x_active_mask,
+                               int32_t* ep_recv_counts,
+                               int64_t* expert_token_nums,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+mdc_status mdc_dispatch_gather(const mdc_shape* shape,
+                               const void* x,
+                               void* expand_x,
+                               int32_t* assist_info,
+                               int32_t* expanded_row_idx,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+mdc_status mdc_dispatch(const mdc_shape* shape,
+                        const void* x,
+                        const int32_t* expert_ids,
+                        const uint8_t* x_active_mask,
+                        void* expand_x,
+                        int32_t* assist_info,
+                        int32_t* ep_recv_counts,
+                        int64_t* expert_token_nums,
+                        int32_t* expanded_row_idx,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* ------------------------------------------------------------------------
+ * Combine ([CV4] Function formula without TP; [TL] moe_combine_kernel;
+ * [PTO] Combine / Unpermute stages)
+ *
+ * For source rank r = shape->rank and every token t:
+ *     xOut[t] = bf16_rne( sum over k = 0..K-1 ascending, route present, of
+ *                         ( s[t][k]*y[t][k] + s[t][k]*sharedX[t] ) )
+ * with an fp32 accumulator starting at +0.0 and every product and sum
+ * rounded to fp32 separately (no fused multiply-add), then rounded to bf16
+ * nearest-even ([TL] combine: fp32 accumulate, CAST_RINT).  The shared term
+ * is weighted per present route, as the [CV4] formula reads; it is omitted
+ * when shared_expert_x is NULL.  y[t][k] is row expanded_row_idx[t][k] of
+ * destination j = e / L (e = expert_ids[t][k]), i.e. expand_x[j]: data
+ * returns along the dispatch path ([CV4] Function note and API matching
+ * constraints).  A route is present iff the token is active, 0 <= e < E,
+ * the row index is < min(ep_recv_counts[j][L*W-1], A) and assist_info[j] at
+ * that row holds (r, t, k); otherwise it contributes nothing.  An inactive
+ * token therefore gives a +0.0 row.
+ *
+ * Inputs
+ *   expand_x          host array of W device pointers: rank j's expert
+ *                     outputs, [A][H] bf16 (the expand_x layout of dispatch j).
+ *   assist_info       host array of W device pointers: rank j's [A][3] int32.
+ *   ep_recv_counts    host array of W device pointers: rank j's [L*W] int32.
+ *   expanded_row_idx  [BS][K] int32, rank r's slice of the table the W
+ *                     dispatches filled.
+ *   expert_ids        [BS][K] int32 of rank r.
+ *   expert_scales     [BS][K] fp32 of rank r.
+ *   x_active_mask     [BS] uint8 of rank r, or NULL (all active).
+ *   shared_expert_x   [BS][H] bf16, or NULL.
+ * Output
+ *   x_out             [BS][H] bf16.
+ * W must be <= MDC_MAX_COMBINE_WORLD.
+ * ------------------------------------------------------------------------ */
+mdc_status mdc_combine_workspace_size(const mdc_shape* shape, size_t* bytes);
+
+mdc_status mdc_combine(const mdc_shape* shape,
+                       const void* const* expand_x,
+                       const int32_t* const* assist_info,
+                       const int32_t* const* ep_recv_counts,
+                       const int32_t* expanded_row_idx,
+                       const int32_t* expert_ids,
+                       const float* expert_scales,
+                       const uint8_t* x_active_mask,
+                       const void* shared_expert_x,
+                       void* x_out,
+                       void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MDC_H */

@@ -1,0 +1,189 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Dispatch is compared bit-exactly (every integer output and every copied bf16
+row); combine within 1 bf16 ulp of the oracle (the contract), and bit-exactly
+as well (the kernels round every fp32 product and sum in the oracle's order).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mdc_oracle as O
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import combine_route_histogram_amd as mdc  # noqa: E402
+from tests import gpu_harness as G  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _shape(w: gen.Workload, capacity=None):
+    return mdc.Shape(w.world, 0, w.bs, w.hidden, w.topk, w.experts, w.capacity if capacity is None else capacity)
+
+
+def _end_to_end(w: gen.Workload, expert="identity", capacity=None, ranks=None, split=False):
+    say(f"case {w.name} W={w.world} BS={w.bs} H={w.hidden} E={w.experts} K={w.topk} routing={w.routing} "
+        f"inactive={w.inactive_frac} shared={w.shared} expert={expert} cap={capacity}")
+    wi = gen.world_inputs(w)
+    cap = w.capacity if capacity is None else capacity
+    gw = G.dispatch_world(_shape(w, cap), wi.x, wi.ids, wi.mask, split=split)
+    segs, oys = G.oracle_segments(wi.x, wi.ids, wi.mask, w.experts, cap, expert)
+    G.check_dispatch(gw, wi.x, wi.ids, wi.mask, w.experts, cap, refs=segs)
+    say("  dispatch bit-exact on every rank")
+    ys = G.apply_expert(gw, expert, w.experts)
+    for r in (range(w.world) if ranks is None else ranks):
+        sh = None if wi.shared is None else wi.shared[r]
+        m = None if wi.mask is None else wi.mask[r]
+        got = G.bits(G.run_combine(gw, ys, r, wi.scales[r], sh))
+        want = O.combine(oys, [s.assist_info for s in segs], r, wi.ids[r], m, wi.scales[r], sh, w.hidden)
+        assert G.ulp_diff(got, want) <= 1, f"combine r={r} beyond 1 ulp"
+        assert np.array_equal(got, want), f"combine r={r} not bit-exact ({int((got != want).sum())} differ)"
+    say("  combine bit-exact")
+    return gw, wi
+
+
+def test_tiny_identity():
+    _end_to_end(gen.workload("tiny"))
+
+
+def test_tiny_split_stages():
+    _end_to_end(gen.workload("tiny"), split=True)
+
+
+def test_decode_shared():
+    _end_to_end(gen.workload("decode"), expert="pow2")
+
+
+def test_share_full_size():
+    """One GPU's real share (8 x 2048 x 7168, 128 experts, topK 8, shared expert), every rank."""
+    _end_to_end(gen.workload("share"))
+
+
+def test_skewed_full_size():
+    """Zipf(1.2) routing with 10% inactive tokens at the full share shape, power-of-two expert."""
+    _end_to_end(gen.workload("skewed"), expert="pow2", ranks=[0, 3, 7])
+
+
+@pytest.mark.parametrize("variant", [
+    dict(world=3, bs=101, hidden=136, experts=9, topk=3),           # ragged chunks and column tile
+    dict(world=2, bs=300, hidden=2056, experts=6, topk=5, inactive_frac=0.3),
+    dict(world=1, bs=257, hidden=8, experts=2048, topk=16),          # max K, max L, H = one vector
+    dict(world=4, bs=64, hidden=64, experts=4, topk=1),              # K = 1, L = 1
+    dict(world=5, bs=33, hidden=4104, experts=40, topk=8, shared=True),
+    dict(world=8, bs=17, hidden=7168, experts=256, topk=9, shared=True),
+])
+def test_ragged_shapes(variant):
+    w = gen.workload("tiny", index=60 + len(str(variant)), **variant)
+    _end_to_end(w, expert="pow2")
+
+
+def test_capacity_overflow_drops_rows():
+    w = gen.workload("tiny", world=2, bs=64, hidden=64, experts=4, topk=2, index=70)
+    _end_to_end(w, capacity=37)
+
+
+def test_zero_capacity():
+    w = gen.workload("tiny", world=2, bs=16, hidden=64, experts=4, topk=2, index=71)
+    _end_to_end(w, capacity=0)
+
+
+def test_all_to_first_experts_fills_capacity():
+    """The A2 sample routing: every route lands on rank 0 and A is filled exactly."""
+    w = gen.workload("tiny", world=8, bs=32, hidden=256, experts=256, topk=8, routing="first_k",
+                     shared=True, index=72)
+    gw, wi = _end_to_end(w, ranks=[0, 5])
+    assert int(gw.outs[0]["ep_recv_counts"][-1].item()) == w.capacity == 2048
+    for d in range(1, 8):
+        assert int(gw.outs[d]["ep_recv_counts"][-1].item()) == 0
+
+
+def test_round_robin_routing():
+    w = gen.workload("tiny", world=4, bs=100, hidden=128, experts=16, topk=4, routing="round_robin", index=73)
+    _end_to_end(w)
+
+
+def test_all_inactive():
+    w = gen.workload("tiny", world=2, bs=40, hidden=64, experts=8, topk=2, inactive_frac=1.0, index=74,
+                     shared=True)
+    gw, wi = _end_to_end(w)
+    for o in gw.outs:
+        assert int(o["ep_recv_counts"][-1].item()) == 0
+
+
+def test_empty_batch():
+    w = gen.workload("tiny", world=2, bs=0, hidden=64, experts=8, topk=2, index=75)
+    sh = _shape(w)
+    ids = np.zeros((2, 0, 2), np.int32)
+    gw = G.dispatch_world(sh, np.zeros((2, 0, 64), np.uint16), ids, None)
+    for o in gw.outs:
+        assert not o["ep_recv_counts"].any() and not o["expert_token_nums"].any()
+
+
+def test_invalid_and_duplicate_ids():
+    g = np.random.default_rng(5)
+    W, BS, K, E, H = 2, 50, 4, 8, 64
+    ids = g.integers(-3, E + 3, size=(W, BS, K)).astype(np.int32)   # duplicates and out-of-range ids
+    x = gen.bf16_from_f32(g.standard_normal((W, BS, H), dtype=np.float32))
+    sh = mdc.Shape(W, 0, BS, H, K, E, W * BS * K)
+    gw = G.dispatch_world(sh, x, ids, None)
+    G.check_dispatch(gw, x, ids, None, E, W * BS * K)
+    ys = G.apply_expert(gw, "identity", E)
+    segs, oys = G.oracle_segments(x, ids, None, E, W * BS * K, "identity")
+    sc = g.standard_normal((BS, K)).astype(np.float32)
+    for r in range(W):
+        got = G.bits(G.run_combine(gw, ys, r, sc, None))
+        want = O.combine(oys, [s.assist_info for s in segs], r, ids[r], None, sc, None, H)
+        assert np.array_equal(got, want)
+
+
+def test_identity_round_trip_returns_x():
+    """dispatch -> identity -> combine with unit-sum scales and no shared expert returns x by value."""
+    w = gen.workload("share", bs=512, shared=False, index=76)
+    wi = gen.world_inputs(w)
+    gw = G.dispatch_world(_shape(w), wi.x, wi.ids, None)
+    ys = G.apply_expert(gw, "identity", w.experts)
+    for r in (0, 6):
+        got = G.bits(G.run_combine(gw, ys, r, wi.scales[r], None))
+        assert np.array_equal(O.bf16_to_f32(got), O.bf16_to_f32(wi.x[r]))
+
+
+def test_deterministic_repeat():
+    w = gen.workload("decode")
+    wi = gen.world_inputs(w)
+    a = G.dispatch_world(_shape(w), wi.x, wi.ids, wi.mask)
+    b = G.dispatch_world(_shape(w), wi.x, wi.ids, wi.mask)
+    for oa, ob in zip(a.outs, b.outs):
+        n = int(oa["ep_recv_counts"][-1].item())
+        assert torch.equal(oa["assist_info"][:n], ob["assist_info"][:n])
+        assert torch.equal(oa["expand_x"][:n].view(torch.int16), ob["expand_x"][:n].view(torch.int16))
+    ya = G.apply_expert(a, "identity", w.experts)
+    ca = G.run_combine(a, ya, 0, wi.scales[0], wi.shared[0])
+    cb = G.run_combine(a, ya, 0, wi.scales[0], wi.shared[0])
+    assert torch.equal(ca.view(torch.int16), cb.view(torch.int16))
+
+
+def test_combine_stale_row_index_is_rejected():
+    """Garbage in the inverse index (a dispatch that never ran) is caught by the triplet check."""
+    w = gen.workload("tiny", world=2, bs=32, hidden=64, experts=4, topk=2, index=77)
+    wi = gen.world_inputs(w)
+    gw = G.dispatch_world(_shape(w), wi.x, wi.ids, None)
+    ys = G.apply_expert(gw, "identity", w.experts)
+    gw.row_idx[0].fill_(0)          # every entry of rank 0 now points at row 0 of its destination
+    got = G.bits(G.run_combine(gw, ys, 0, wi.scales[0], None))
+    segs, oys = G.oracle_segments(wi.x, wi.ids, None, w.experts, w.capacity, "identity")
+    # only a route whose true row is 0 survives: give the oracle just row 0 of each segment
+    first = [s.assist_info[:1] if s.assist_info.shape[0] and s.assist_info[0, 0] == 0 else s.assist_info[:0]
+             for s in segs]
+    want = O.combine(oys, first, 0, wi.ids[0], None, wi.scales[0], None, w.hidden)
+    assert np.array_equal(got, want)
