@@ -177,13 +177,12 @@ def expert_pow2(expand_x: np.ndarray, assist: np.ndarray, ids: np.ndarray, L: in
     Makes a row landing on the wrong expert, or a swapped k, visible in the
     combined output.
     """
-    out = np.empty_like(expand_x)
-    for row in range(expand_x.shape[0]):
-        s, t, k = (int(v) for v in assist[row])
-        e = int(ids[s][t][k])
-        f = bf16_to_f32(expand_x[row]).astype(np.float64) * (2.0 ** pow2_exponent(e))
-        out[row] = f32_to_bf16_rne(f.astype(np.float32))
-    return out
+    if expand_x.shape[0] == 0:
+        return expand_x.copy()
+    e = ids[assist[:, 0], assist[:, 1], assist[:, 2]].astype(np.int64)
+    f = 2.0 ** np.array([pow2_exponent(int(v)) for v in e], dtype=np.float64)
+    prod = bf16_to_f32(expand_x).astype(np.float64) * f[:, None]
+    return f32_to_bf16_rne(prod.astype(np.float32))
 
 
 # ----------------------------------------------------------------------------
