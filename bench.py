@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark: MoE dispatch + combine, one GPU's share, on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input that is
+already resident in HBM:
+    mdc_dispatch_layout + mdc_dispatch_gather for destination rank 0 (reading
+    the tokens of all 8 virtual source ranks), then mdc_combine for source
+    rank 0 (reading the expert outputs of all 8 virtual destination ranks).
+The expert between them is the identity (the combine reads the dispatched
+rows), as in the workload definition.  Expert outputs of ranks 1..7 are
+produced by their own dispatch calls before the timed region.
+
+Several copies of every input buffer are rotated (--batches) so that no step
+finds its inputs in the 256 MB Infinity Cache left there by the previous step.
+
+Output: one JSON line with the metric, the roofline of the dominant kernel
+(achieved algorithmic GB/s measured with HIP events on the launch stream
+against the 8 TB/s HBM peak), per-kernel times and the CPU oracle's rate on
+the same workload (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of peak) on 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+
+DESCR = {
+    "share": "one GPU's share: 8 virtual source ranks x 2048 tokens, H=7168 bf16, 128 experts (16 local), "
+             "top-8 uniform distinct routes, fp32 softmax scales, shared expert, identity expert",
+    "skewed": "share shapes with Zipf(1.2) routes and 10% inactive tokens",
+    "decode": "8 virtual ranks x 32 tokens, H=7168, 256 experts (32 local), top-8, shared expert",
+    "tiny": "1 virtual rank, 8 experts, 16 tokens, H=128, top-2",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="share", choices=sorted(DESCR))
+    ap.add_argument("--batches", type=int, default=2, help="rotated copies of every input buffer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run three 256 MiB device copies (counter calibration)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, ids, mask, d=0, r=0):
+    """What the method must move for one step (dispatch share d, combine share r)."""
+    import numpy as np
+    W, BS, K = ids.shape
+    L = w.experts // W
+    H2 = 2 * w.hidden
+    act = np.ones((W, BS), bool) if mask is None else mask.astype(bool)
+    valid = (ids >= 0) & (ids < w.experts) & act[:, :, None]
+    local = valid & ((ids // L) == d)
+    R = int(local.sum())                      # routed rows written on rank d
+    U = int(local.any(axis=2).sum())          # distinct source tokens read
+    present = int(valid[r].sum())             # routes of rank r combined
+    tok_any = int(valid[r].any(axis=1).sum())
+    layout = ids.size * 4 + (0 if mask is None else mask.size) + L * W * 4 + L * 8
+    gather = U * H2 + R * (H2 + 12 + 4) + ids.size * 4
+    combine = (present * H2 + BS * K * 12 + (0 if mask is None else BS)
+               + (tok_any * H2 if w.shared else 0) + BS * H2)
+    return {"R": R, "U": U, "present": present, "layout": layout, "gather": gather, "combine": combine}
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None.
+
+    The summary records the sha256 of the kernel source it was measured on;
+    once the source differs the figure no longer describes these kernels.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.json")
+    src = os.path.join(ROOT, "combine_route_histogram_amd", "csrc", "mdc.hip")
+    try:
+        prof = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if prof.get("source_sha256") != sha:
+        return None
+    for name, rec in prof.get("kernels", {}).items():
+        if name.startswith(kernel):
+            return int(round(rec["traffic_bytes"]))
+    return None
+
+
+def cpu_baseline(wi, w, budget_s):
+    """Time the oracle (as it stands) on dispatch share 0 + combine share 0 of the same workload."""
+    from oracle import mdc_oracle as O
+    segs = [O.dispatch(wi.x, wi.ids, wi.mask, d, w.experts, w.capacity) for d in range(w.world)]
+    rates = []
+    t_end = time.perf_counter() + budget_s
+    reps = 0
+    out = None
+    while reps < 1 or (time.perf_counter() < t_end and reps < 20):
+        t0 = time.perf_counter()
+        s0 = O.dispatch(wi.x, wi.ids, wi.mask, 0, w.experts, w.capacity)
+        ys = [s0.expand_x] + [s.expand_x for s in segs[1:]]
+        out = O.combine(ys, [s0.assist_info] + [s.assist_info for s in segs[1:]], 0, wi.ids[0],
+                        None if wi.mask is None else wi.mask[0], wi.scales[0],
+                        None if wi.shared is None else wi.shared[0], w.hidden)
+        rates.append(w.bs / (time.perf_counter() - t0))
+        reps += 1
+    return {"value": statistics.median(rates), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the full timed step (dispatch share 0 + combine share 0 of the {w.name} workload), "
+                      f"{reps} repetitions, median; numpy elementwise work on one thread"}, segs, out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the expert-parallel "
+              "ranks are virtual buffers on that GPU. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import combine_route_histogram_amd as mdc
+    from workloads import gen
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = gen.workload(args.workload)
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    wi = gen.world_inputs(w)
+    W, BS, K, H = w.world, w.bs, w.topk, w.hidden
+    shape = mdc.Shape(W, 0, BS, H, K, w.experts, w.capacity)
+    stream = torch.cuda.current_stream()
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # ---- one set of device buffers per batch copy --------------------------------------------
+    batches = []
+    for b in range(args.batches):
+        x = bf16(wi.x)
+        ids = torch.from_numpy(wi.ids).to(dev)
+        mask = None if wi.mask is None else torch.from_numpy(wi.mask).to(dev)
+        scales0 = torch.from_numpy(wi.scales[0]).to(dev)
+        shared0 = None if wi.shared is None else bf16(wi.shared[0])
+        row_idx = torch.full((W, BS, K), -1, dtype=torch.int32, device=dev)
+        outs = [mdc.alloc_dispatch_outputs(shape.with_rank(d), dev) for d in range(W)]
+        for d in range(1, W):     # expert outputs of the other ranks (identity expert), untimed
+            o = outs[d]
+            mdc.mdc_dispatch(shape.with_rank(d), x, ids, mask, o["expand_x"], o["assist_info"],
+                             o["ep_recv_counts"], o["expert_token_nums"], row_idx, o["workspace"])
+        x_out = torch.empty((BS, H), dtype=torch.bfloat16, device=dev)
+        batches.append(dict(x=x, ids=ids, mask=mask, scales0=scales0, shared0=shared0, row_idx=row_idx,
+                            outs=outs, x_out=x_out, ids0=ids[0].contiguous(), mask0=None if mask is None
+                            else mask[0].contiguous(), row0=row_idx[0]))
+    torch.cuda.synchronize()
+
+    # Arguments are marshalled once per batch so the host loop stays ahead of the GPU.
+    for bt in batches:
+        o0 = bt["outs"][0]
+        bt["layout"] = mdc.prepare_dispatch_layout(shape, bt["ids"], bt["mask"], o0["workspace"], stream)
+        bt["gather"] = mdc.prepare_dispatch_gather(shape, bt["x"], o0["expand_x"], o0["assist_info"],
+                                                   o0["ep_recv_counts"], o0["expert_token_nums"], bt["row_idx"],
+                                                   o0["workspace"], stream)
+        bt["combine"] = mdc.prepare_combine(shape, [o["expand_x"] for o in bt["outs"]],
+                                            [o["assist_info"] for o in bt["outs"]],
+                                            [o["ep_recv_counts"] for o in bt["outs"]], bt["row0"], bt["ids0"],
+                                            bt["scales0"], bt["mask0"], bt["shared0"], bt["x_out"],
+                                            stream=stream)
+
+    def step(bt, ev=None):
+        if ev is None:
+            bt["layout"]()
+            bt["gather"]()
+            bt["combine"]()
+            return
+        ev[0].record(stream)
+        bt["layout"]()
+        ev[1].record(stream)
+        bt["gather"]()
+        ev[2].record(stream)
+        bt["combine"]()
+        ev[3].record(stream)
+
+    if args.calibrate_copy:
+        # plain copy kernel of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(batches[i % args.batches])
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(batches[i % args.batches], evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    t_layout = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]     # us
+    t_gather = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
+    t_comb = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
+    t_step_ev = [e[0].elapsed_time(e[3]) * 1e3 for e in evs]
+    ms_per_step = elapsed * 1e3 / args.steps
+    by = algorithmic_bytes(w, wi.ids, wi.mask)
+    step_bytes = by["layout"] + by["gather"] + by["combine"]
+    mean = statistics.fmean
+    gb_gather = by["gather"] / (mean(t_gather) * 1e-6) / 1e9
+    gb_comb = by["combine"] / (mean(t_comb) * 1e-6) / 1e9
+    gb_step = step_bytes / (ms_per_step * 1e-3) / 1e9
+    if mean(t_gather) >= mean(t_comb):
+        dom = ("k_dispatch_gather", gb_gather, by["gather"], mean(t_gather))
+    else:
+        dom = ("k_combine", gb_comb, by["combine"], mean(t_comb))
+
+    result = {
+        "metric": METRIC,
+        "value": round(BS / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {DESCR[w.name]}", "world": W, "bs": BS, "hidden": H,
+                   "experts": w.experts, "topk": K, "capacity": w.capacity, "batches": args.batches,
+                   "rows_received": by["R"], "source_rows_read": by["U"]},
+        "hbm_gbps": round(gb_step, 1),
+        "hbm_frac_of_peak": round(gb_step / HBM_PEAK_GBPS, 4),
+        "step_bytes": step_bytes,
+        "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(dom[1], 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(dom[1] / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(w.name, dom[0]),
+                     "bytes_per_launch": dom[2], "avg_launch_us": round(dom[3], 3)},
+        "kernels_us": {"dispatch_layout": round(mean(t_layout), 3), "dispatch_gather": round(mean(t_gather), 3),
+                       "combine": round(mean(t_comb), 3), "step_events": round(mean(t_step_ev), 3),
+                       "gather_gbps": round(gb_gather, 1), "combine_gbps": round(gb_comb, 1),
+                       "gather_median": round(statistics.median(t_gather), 3),
+                       "combine_median": round(statistics.median(t_comb), 3)},
+    }
+
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cb, segs, ref_out = cpu_baseline(wi, w, args.cpu_seconds)
+        cb["cores"] = 1
+        result["cpu_baseline"] = cb
+        # the GPU's last step on batch 0 equals the oracle's step (same inputs)
+        got = batches[0]["x_out"].view(torch.int16).cpu().numpy().view(np.uint16)
+        result["parity_vs_oracle"] = bool(np.array_equal(got, ref_out))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -61,9 +61,9 @@ _lib.mdc_abi_version.argtypes = []
 _lib.mdc_dispatch_workspace_size.restype = ctypes.c_int
 _lib.mdc_dispatch_workspace_size.argtypes = [_SHP, ctypes.POINTER(_SZ)]
 _lib.mdc_dispatch_layout.restype = ctypes.c_int
-_lib.mdc_dispatch_layout.argtypes = [_SHP, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.mdc_dispatch_layout.argtypes = [_SHP, _P, _P, _P, _SZ, _P]
 _lib.mdc_dispatch_gather.restype = ctypes.c_int
-_lib.mdc_dispatch_gather.argtypes = [_SHP, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.mdc_dispatch_gather.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.mdc_dispatch.restype = ctypes.c_int
 _lib.mdc_dispatch.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.mdc_combine_workspace_size.restype = ctypes.c_int
@@ -153,21 +153,21 @@ def mdc_combine_workspace_size(shape: Shape) -> int:
     return int(out.value)
 
 
-def mdc_dispatch_layout(shape: Shape, expert_ids, x_active_mask, ep_recv_counts, expert_token_nums,
-                        workspace, stream=None, check: bool = True) -> int:
+def mdc_dispatch_layout(shape: Shape, expert_ids, x_active_mask, workspace, stream=None, check: bool = True) -> int:
     sh = shape.c()
-    st = _lib.mdc_dispatch_layout(ctypes.byref(sh), _ptr(expert_ids), _ptr(x_active_mask), _ptr(ep_recv_counts),
-                                  _ptr(expert_token_nums), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    st = _lib.mdc_dispatch_layout(ctypes.byref(sh), _ptr(expert_ids), _ptr(x_active_mask), _ptr(workspace),
+                                  _nbytes(workspace), _stream(stream))
     if check:
         _check(st, "mdc_dispatch_layout")
     return st
 
 
-def mdc_dispatch_gather(shape: Shape, x, expand_x, assist_info, expanded_row_idx, workspace,
-                        stream=None, check: bool = True) -> int:
+def mdc_dispatch_gather(shape: Shape, x, expand_x, assist_info, ep_recv_counts, expert_token_nums,
+                        expanded_row_idx, workspace, stream=None, check: bool = True) -> int:
     sh = shape.c()
     st = _lib.mdc_dispatch_gather(ctypes.byref(sh), _ptr(x), _ptr(expand_x), _ptr(assist_info),
-                                  _ptr(expanded_row_idx), _ptr(workspace), _nbytes(workspace), _stream(stream))
+                                  _ptr(ep_recv_counts), _ptr(expert_token_nums), _ptr(expanded_row_idx),
+                                  _ptr(workspace), _nbytes(workspace), _stream(stream))
     if check:
         _check(st, "mdc_dispatch_gather")
     return st
@@ -203,6 +203,50 @@ def mdc_combine(shape: Shape, expand_x: Sequence, assist_info: Sequence, ep_recv
     if check:
         _check(st, "mdc_combine")
     return st
+
+
+class Prepared:
+    """A C entry point with its arguments marshalled once, for repeated launches.
+
+    Calling it enqueues the same work again on the stream captured at
+    preparation; the referenced tensors must stay alive.
+    """
+    __slots__ = ("_fn", "_args", "_name", "_keep")
+
+    def __init__(self, fn, args, name, keep):
+        self._fn, self._args, self._name, self._keep = fn, args, name, keep
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != MDC_OK:
+            raise MdcError(st, self._name)
+
+
+def prepare_dispatch_layout(shape: Shape, expert_ids, x_active_mask, workspace, stream=None) -> Prepared:
+    sh = shape.c()
+    args = (ctypes.byref(sh), _ptr(expert_ids), _ptr(x_active_mask), _ptr(workspace), _nbytes(workspace),
+            _stream(stream))
+    return Prepared(_lib.mdc_dispatch_layout, args, "mdc_dispatch_layout", (sh,))
+
+
+def prepare_dispatch_gather(shape: Shape, x, expand_x, assist_info, ep_recv_counts, expert_token_nums,
+                            expanded_row_idx, workspace, stream=None) -> Prepared:
+    sh = shape.c()
+    args = (ctypes.byref(sh), _ptr(x), _ptr(expand_x), _ptr(assist_info), _ptr(ep_recv_counts),
+            _ptr(expert_token_nums), _ptr(expanded_row_idx), _ptr(workspace), _nbytes(workspace),
+            _stream(stream))
+    return Prepared(_lib.mdc_dispatch_gather, args, "mdc_dispatch_gather", (sh,))
+
+
+def prepare_combine(shape: Shape, expand_x: Sequence, assist_info: Sequence, ep_recv_counts: Sequence,
+                    expanded_row_idx, expert_ids, expert_scales, x_active_mask, shared_expert_x, x_out,
+                    workspace=None, stream=None) -> Prepared:
+    sh = shape.c()
+    ty, ta, tc = _table(expand_x), _table(assist_info), _table(ep_recv_counts)
+    args = (ctypes.byref(sh), ctypes.cast(ty, _P), ctypes.cast(ta, _P), ctypes.cast(tc, _P),
+            _ptr(expanded_row_idx), _ptr(expert_ids), _ptr(expert_scales), _ptr(x_active_mask),
+            _ptr(shared_expert_x), _ptr(x_out), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    return Prepared(_lib.mdc_combine, args, "mdc_combine", (sh, ty, ta, tc))
 
 
 def alloc_dispatch_outputs(shape: Shape, device="cuda"):

@@ -1,19 +1,19 @@
 // libmdc: MoE dispatch/combine hot path for AMD Instinct MI355X (gfx950).
 //
 // Kernels (one GPU's share; the W expert-parallel ranks are virtual buffers):
-//   k_route_rank     per chunk of one source's routes: local-route filter,
-//                    wavefront-ballot multi-split rank within (source, local
-//                    expert), per-chunk histogram.
-//   k_route_scan     one workgroup: exclusive scan of the chunk histograms in
-//                    (local expert, source, chunk) order -> chunk bases,
-//                    epRecvCounts (inclusive), expertTokenNums.
-//   k_dispatch_gather one workgroup per source token: reads the token's row
-//                    once into registers and writes it to each of its rows on
-//                    this rank (fan-out), with the (src, token, k) triplets and
-//                    the route -> row inverse index.
-//   k_combine        one workgroup per token of the combining rank: reads the
-//                    token's K expert rows (plus the shared-expert row),
-//                    accumulates in fp32 in ascending k, rounds to bf16 RNE.
+//   k_route_rank      per group of one source's routes: local-route filter,
+//                     wavefront-ballot multi-split rank within (source, local
+//                     expert), group histogram.  (mdc_dispatch_layout)
+//   k_dispatch_gather one wavefront per (source token, column tile): scans the
+//                     group histograms in-wavefront to place the token's
+//                     routes, reads its row tile once and writes it to each of
+//                     its rows on this rank, with the (src, token, k) triplets,
+//                     the route -> row inverse index, epRecvCounts and
+//                     expertTokenNums.  (mdc_dispatch_gather)
+//   k_combine         one wavefront per (token, column tile) of the combining
+//                     rank: reads the token's present expert rows (and the
+//                     shared-expert row), accumulates in fp32 in ascending k,
+//                     rounds to bf16 nearest-even.  (mdc_combine)
 //
 // Sources: "dispatch_combine_shmem.py" (TileLang-Ascend example),
 // moe_dispatch_kernel / moe_combine_kernel; "aclnnMoeDistributeCombineV4",
@@ -34,82 +34,51 @@ namespace {
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kRankThreads = 256;     // routes per k_route_rank workgroup (4 wavefronts)
-constexpr int kScanThreads = 1024;
-constexpr int kScanItems = 8;         // chunk counters per scan thread per tile
-constexpr int kRowVec = 2;            // 16-byte vectors per lane per row tile
-constexpr int kTileVec = 64 * kRowVec;  // 16-byte vectors per wavefront row tile
-constexpr int kMaxWaves = 16;
+// Build-time tile shapes (16-byte vectors per lane per row tile).
+#ifndef MDC_GATHER_VEC
+#define MDC_GATHER_VEC 8
+#endif
+#ifndef MDC_COMBINE_VEC
+#define MDC_COMBINE_VEC 1
+#endif
+// Cache policy per kernel (1 = non-temporal).  Measured on MI355X over whole
+// dispatch+combine steps: non-temporal row loads and stores in both kernels
+// give the shortest step (the two kernels share the Infinity Cache, so each
+// one's policy also moves the other's time).
+#ifndef MDC_GATHER_NT_LOADS
+#define MDC_GATHER_NT_LOADS 1
+#endif
+#ifndef MDC_GATHER_NT_STORES
+#define MDC_GATHER_NT_STORES 1
+#endif
+#ifndef MDC_COMBINE_NT_LOADS
+#define MDC_COMBINE_NT_LOADS 1
+#endif
+#ifndef MDC_COMBINE_NT_STORES
+#define MDC_COMBINE_NT_STORES 1
+#endif
+constexpr int kGroupRoutes = 4096;     // routes of one source ranked by one k_route_rank workgroup
+constexpr int kGatherVec = MDC_GATHER_VEC;
+constexpr int kCombineVec = MDC_COMBINE_VEC;
+
+template <bool NT>
+__device__ __forceinline__ void store_v4(v4u* p, v4u v) {
+  if (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
 
-// ---------------------------------------------------------------------------
-// a1 + a3 (local part): filter, per-chunk histogram, rank within chunk.
-//
-// A chunk is CT = floor(256 / K) consecutive tokens of one source rank, so a
-// chunk never splits a token's K routes and holds at most 256 routes, one per
-// thread.  Thread i handles flattened route f = t*K + k of the chunk.  Its key
-// is the local expert le = e - d*L when the route is sent to rank d, or L
-// otherwise.  Ranks within a wavefront come from a ballot per key bit (a
-// multi-split): the lanes holding the same key form a mask, and the rank is
-// the number of such lanes below.  Wavefront counts are prefixed in LDS over
-// the four wavefronts, which keeps the (t, k) order: rank = number of earlier
-// routes of this source and chunk with the same expert ([TL] send loop,
-// rank-within-expert counts earlier equal ids).
-//
-// P[f] = le | (rank_in_chunk << 16) for a route sent to d, else -1.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kRankThreads) void k_route_rank(
-    const int32_t* __restrict__ ids, const uint8_t* __restrict__ mask,
-    int32_t* __restrict__ P, int32_t* __restrict__ chunk_cnt,
-    int BS, int K, int E, int L, int d, int CT, int nC) {
-  extern __shared__ int32_t wave_cnt[];  // [4][L]
-  const int s = blockIdx.y;
-  const int c = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int t0 = c * CT;
-  const int nt = min(CT, BS - t0);
-  const int nroutes = nt * K;
-  const int64_t f = ((int64_t)s * BS + t0) * K + tid;
-
-  int key = L;
-  if (tid < nroutes) {
-    const int t = t0 + tid / K;
-    const int e = ids[f];
-    const bool active = (mask == nullptr) || (mask[(int64_t)s * BS + t] != 0);
-    const int q = e - d * L;
-    if (active && e >= 0 && e < E && q >= 0 && q < L) key = q;
-  }
-  for (int i = tid; i < 4 * L; i += kRankThreads) wave_cnt[i] = 0;
-
-  uint64_t same = __ballot(1);
-  const int nbits = 32 - __clz(L);
-  for (int b = 0; b < nbits; ++b) {
-    const int bit = (key >> b) & 1;
-    const uint64_t bal = __ballot(bit);
-    same &= bit ? bal : ~bal;
-  }
-  const int rank_in_wave = __popcll(same & lanes_below(lane));
-  __syncthreads();
-  if (key < L && rank_in_wave == 0) wave_cnt[wv * L + key] = __popcll(same);
-  __syncthreads();
-  for (int le = tid; le < L; le += kRankThreads) {
-    int run = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int v = wave_cnt[w * L + le];
-      wave_cnt[w * L + le] = run;
-      run += v;
-    }
-    chunk_cnt[((int64_t)s * nC + c) * L + le] = run;
-  }
-  __syncthreads();
-  if (tid < nroutes) {
-    P[f] = (key < L) ? (key | ((wave_cnt[wv * L + key] + rank_in_wave) << 16)) : -1;
-  }
+// Loads through addresses rebuilt from integers (readlane / shuffles) would be
+// compiled as flat accesses; these keep them in the global address space.
+typedef const v4u __attribute__((address_space(1))) g_v4u;
+typedef const int32_t __attribute__((address_space(1))) g_i32;
+template <bool NT>
+__device__ __forceinline__ v4u load_v4(uint64_t addr) {
+  if (NT) return __builtin_nontemporal_load(reinterpret_cast<g_v4u*>(addr));
+  return *reinterpret_cast<g_v4u*>(addr);
 }
+__device__ __forceinline__ int32_t load_i32(uint64_t addr) { return *reinterpret_cast<g_i32*>(addr); }
 
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 #pragma unroll
@@ -120,122 +89,239 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
-// ---------------------------------------------------------------------------
-// a2: scan.  Items are the chunk counters in (le, s, c) order, so the
-// exclusive prefix of item (le, s, c) is the first row of that chunk's routes
-// to le.  The inclusive prefix at the last chunk of (le, s) is
-// epRecvCounts[le*W + s] ([TL] GetCumSum and local data copy: receive count
-// = begin + count); expertTokenNums[le] is the difference of consecutive
-// inclusive prefixes at the end of each le block ([TL] UpdateTokenNumsOut).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kScanThreads) void k_route_scan(
-    const int32_t* __restrict__ chunk_cnt, int32_t* __restrict__ chunk_base,
-    int32_t* __restrict__ ep_recv, int64_t* __restrict__ expert_nums,
-    int W, int L, int nC) {
-  extern __shared__ int32_t le_end[];  // [L]
-  __shared__ int32_t wave_tot[kScanThreads / 64];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int64_t per_le = (int64_t)W * nC;
-  const int64_t N = per_le * L;
+__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
+  const unsigned lo = (unsigned)__shfl((int)(unsigned)v, src, 64);
+  const unsigned hi = (unsigned)__shfl((int)(unsigned)(v >> 32), src, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
 
-  for (int i = tid; i < L; i += kScanThreads) le_end[i] = 0;
-  if (nC == 0) {
-    for (int64_t i = tid; i < (int64_t)L * W; i += kScanThreads) ep_recv[i] = 0;
-  }
-  __syncthreads();
-
-  int carry = 0;
-  for (int64_t tile = 0; tile < N; tile += (int64_t)kScanThreads * kScanItems) {
-    int vals[kScanItems];
-    int sum = 0;
-#pragma unroll
-    for (int j = 0; j < kScanItems; ++j) {
-      const int64_t q = tile + (int64_t)tid * kScanItems + j;
-      int v = 0;
-      if (q < N) {
-        const int le = (int)(q / per_le);
-        const int64_t rem = q - (int64_t)le * per_le;
-        const int s = (int)(rem / nC);
-        const int c = (int)(rem - (int64_t)s * nC);
-        v = chunk_cnt[((int64_t)s * nC + c) * L + le];
-      }
-      vals[j] = v;
-      sum += v;
-    }
-    const int incl = wave_inclusive_scan(sum, lane);
-    if (lane == 63) wave_tot[wv] = incl;
-    __syncthreads();
-    int wave_off = 0;
-    int tile_tot = 0;
-#pragma unroll
-    for (int w = 0; w < kScanThreads / 64; ++w) {
-      const int x = wave_tot[w];
-      wave_off += (w < wv) ? x : 0;
-      tile_tot += x;
-    }
-    int run = carry + wave_off + incl - sum;
-#pragma unroll
-    for (int j = 0; j < kScanItems; ++j) {
-      const int64_t q = tile + (int64_t)tid * kScanItems + j;
-      if (q < N) {
-        const int le = (int)(q / per_le);
-        const int64_t rem = q - (int64_t)le * per_le;
-        const int s = (int)(rem / nC);
-        const int c = (int)(rem - (int64_t)s * nC);
-        chunk_base[((int64_t)s * nC + c) * L + le] = run;
-        if (c == nC - 1) {
-          ep_recv[(int64_t)le * W + s] = run + vals[j];
-          if (s == W - 1) le_end[le] = run + vals[j];
-        }
-      }
-      run += vals[j];
-    }
-    carry += tile_tot;
-    __syncthreads();
-  }
-  for (int le = tid; le < L; le += kScanThreads) {
-    expert_nums[le] = (int64_t)le_end[le] - (le > 0 ? le_end[le - 1] : 0);
-  }
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int k) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)v, k);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(v >> 32), k);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // ---------------------------------------------------------------------------
-// a3 (global rows) + a4 + a5: one workgroup per source token g = s*BS + t.
-// Lanes 0..K-1 turn the token's ranks into rows (chunk base + rank in chunk),
-// rows at or beyond the capacity are dropped.  Wavefront 0 writes the
-// triplets and the inverse index.  Each wavefront then copies its column
-// tiles of x[s][t]: one read, one non-temporal write per destination row
-// ([TL] send loop row put and local data copy; [PTO] Dispatch Stage pull).
+// a1 + a3 (ranks): route filter, histogram and stable rank within a group.
+//
+// A group is TPG = floor(4096 / K) consecutive tokens of one source rank; one
+// workgroup walks its routes in flattened (t, k) order, one route per thread
+// per step.  A route's key is its local expert le = e - d*L when it is sent
+// to rank d (active token, 0 <= e < E, e / L == d), else L.  Inside a
+// wavefront, one ballot per key bit isolates the lanes holding the same key
+// (a multi-split); the rank is the count of those lanes below.  Wavefront
+// counts are prefixed in LDS in wavefront order on top of the counts carried
+// from earlier steps, so rank = number of earlier routes of this source and
+// group with the same expert ([TL] send loop: rank-within-expert counts the
+// earlier equal ids).
+//
+// P[f] = le | (rank << 16) for a route sent to d, else -1.
+// cnt[(le*W + s)*G + g] = routes of group g of source s sent to local expert le.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_dispatch_gather(
-    const v4u* __restrict__ x, const int32_t* __restrict__ P,
-    const int32_t* __restrict__ chunk_base, v4u* __restrict__ expand_x,
-    int32_t* __restrict__ assist, int32_t* __restrict__ row_idx,
-    int BS, int K, int L, int CT, int nC, int64_t A, int nvec) {
-  const int64_t g = blockIdx.x;
-  const int s = (int)(g / BS);
-  const int t = (int)(g - (int64_t)s * BS);
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+__global__ __launch_bounds__(1024) void k_route_rank(
+    const int32_t* __restrict__ ids, const uint8_t* __restrict__ mask,
+    int32_t* __restrict__ P, int32_t* __restrict__ cnt,
+    int BS, int K, int E, int L, int d, int W, int TPG, int G) {
+  extern __shared__ int32_t sm[];  // carry[L], wave_cnt[nw][L]
   const int nw = blockDim.x >> 6;
+  int32_t* carry = sm;
+  int32_t* wave_cnt = sm + L;
+  const int s = blockIdx.y;
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int t_begin = g * TPG;
+  const int t_end = min(BS, t_begin + TPG);
+  const int n_routes = (t_end - t_begin) * K;
+  const int64_t f_base = ((int64_t)s * BS + t_begin) * K;
+  const int nbits = 32 - __clz(L);
 
-  // A route is ours when its packed entry holds a local expert < L; the row
-  // is kept only inside [0, A), so a stale workspace can never address
-  // memory outside the outputs.
-  bool mine = false;
-  int row = -1;
-  if (lane < K) {
-    const int p = P[g * K + lane];
-    if (p >= 0 && (p & 0xFFFF) < L) {
-      mine = true;
-      const int le = p & 0xFFFF;
-      const int rk = p >> 16;
-      const int64_t r = (int64_t)chunk_base[((int64_t)s * nC + t / CT) * L + le] + rk;
-      row = (r >= 0 && r < A) ? (int)r : -1;
+  // Every key of the group is computed up front so that the id loads of all
+  // steps are in flight together (a group holds at most kGroupRoutes routes).
+  constexpr int kMaxSteps = kGroupRoutes / 256;
+  int keys[kMaxSteps];
+#pragma unroll
+  for (int i = 0; i < kMaxSteps; ++i) {
+    const int f = i * (int)blockDim.x + tid;
+    int key = L;
+    if (f < n_routes) {
+      const int t = t_begin + f / K;
+      const int e = ids[f_base + f];
+      const bool active = (mask == nullptr) || (mask[(int64_t)s * BS + t] != 0);
+      const int q = e - d * L;
+      if (active && e >= 0 && e < E && q >= 0 && q < L) key = q;
+    }
+    keys[i] = key;
+  }
+  for (int i = tid; i < L; i += blockDim.x) carry[i] = 0;
+#pragma unroll
+  for (int step = 0; step < kMaxSteps; ++step) {
+    const int f0 = step * (int)blockDim.x;
+    if (f0 >= n_routes) break;
+    for (int i = tid; i < nw * L; i += blockDim.x) wave_cnt[i] = 0;
+    const int f = f0 + tid;
+    const int key = keys[step];
+    uint64_t same = __ballot(1);
+    for (int b = 0; b < nbits; ++b) {
+      const int bit = (key >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      same &= bit ? bal : ~bal;
+    }
+    const int rank_in_wave = __popcll(same & lanes_below(lane));
+    __syncthreads();
+    if (key < L && rank_in_wave == 0) wave_cnt[wv * L + key] = __popcll(same);
+    __syncthreads();
+    for (int le = tid; le < L; le += blockDim.x) {
+      int run = carry[le];
+      for (int w = 0; w < nw; ++w) {
+        const int v = wave_cnt[w * L + le];
+        wave_cnt[w * L + le] = run;
+        run += v;
+      }
+      carry[le] = run;
+    }
+    __syncthreads();
+    if (f < n_routes) {
+      P[f_base + f] = (key < L) ? (key | ((wave_cnt[wv * L + key] + rank_in_wave) << 16)) : -1;
+    }
+    __syncthreads();
+  }
+  for (int le = tid; le < L; le += blockDim.x) cnt[((int64_t)le * W + s) * G + g] = carry[le];
+}
+
+// ---------------------------------------------------------------------------
+// a2 inside one wavefront: exclusive scan of the group counters in
+// (le, s, g) order, kScanIPL consecutive counters per lane per chunk.  The
+// exclusive prefix at (le, s, g) is the first row of that group's routes to
+// le; the inclusive prefix at the last group of (le, s) is
+// epRecvCounts[le*W + s] ([TL] GetCumSum and local data copy: receive count
+// = begin + count).  Returns the exclusive prefix at q (lanes with q < 0 get
+// 0).  With `writer`, also stores epRecvCounts.  `first` holds this lane's
+// counters of chunk 0, loaded early by the caller.
+// ---------------------------------------------------------------------------
+constexpr int kScanIPL = 8;
+constexpr int kScanChunk = 64 * kScanIPL;
+
+__device__ __forceinline__ void load_counters(const int32_t* __restrict__ cnt, int n, int c0, int lane,
+                                              int (&v)[kScanIPL]) {
+  const int i0 = c0 + lane * kScanIPL;
+#pragma unroll
+  for (int j = 0; j < kScanIPL; ++j) v[j] = (i0 + j < n) ? cnt[i0 + j] : 0;
+}
+
+__device__ int scan_lookup(const int32_t* __restrict__ cnt, int n, const int (&first)[kScanIPL], int q, int G,
+                           bool writer, int32_t* __restrict__ ep_recv, int lane) {
+  int carry = 0;
+  int found = 0;
+  for (int c0 = 0; c0 < n; c0 += kScanChunk) {
+    int v[kScanIPL];
+    if (c0 == 0) {
+#pragma unroll
+      for (int j = 0; j < kScanIPL; ++j) v[j] = first[j];
+    } else {
+      load_counters(cnt, n, c0, lane, v);
+    }
+    int ex[kScanIPL];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < kScanIPL; ++j) {
+      ex[j] = sum;
+      sum += v[j];
+    }
+    const int incl = wave_inclusive_scan(sum, lane);
+    const int lane_base = carry + incl - sum;
+    const int i0 = c0 + lane * kScanIPL;
+    if (writer) {
+#pragma unroll
+      for (int j = 0; j < kScanIPL; ++j) {
+        const int i = i0 + j;
+        if (i < n && (i % G) == G - 1) ep_recv[i / G] = lane_base + ex[j] + v[j];
+      }
+    }
+    const int rel = q - c0;
+    const bool in = (q >= 0) && (rel >= 0) && (rel < kScanChunk);
+    const int owner = in ? (rel / kScanIPL) : lane;
+    const int slot = rel & (kScanIPL - 1);
+    // the owner's prefix before its slot: lane_base + ex[slot]; fetch lane_base
+    // and the owner's counters up to the slot through cross-lane reads
+    const int ob = __shfl(lane_base, owner, 64);
+    int part = 0;
+#pragma unroll
+    for (int j = 0; j < kScanIPL; ++j) {
+      const int vj = __shfl(v[j], owner, 64);
+      part += (j < slot) ? vj : 0;
+    }
+    if (in) found = ob + part;
+    carry += __builtin_amdgcn_readlane(incl, 63);
+  }
+  return found;
+}
+
+// ---------------------------------------------------------------------------
+// a2 + a3 (rows) + a4 + a5: one wavefront per (source token, column tile).
+// Lanes 0..K-1 read the token's ranks; if any route is sent to this rank the
+// wavefront loads its column tile of x[s][t] once, turns ranks into rows
+// (group base from the in-wavefront scan + rank), and writes the tile to each
+// of the token's rows with non-temporal stores ([TL] send loop row put and
+// local data copy; [PTO] Dispatch Stage: destination rows grouped by local
+// expert then source).  Rows at or beyond the capacity A are dropped.  Tile 0
+// writes the (s, t, k) triplets and the inverse index; the wavefront of token
+// 0, tile 0 also writes epRecvCounts and expertTokenNums
+// ([TL] UpdateTokenNumsOut: per-local-expert counts).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_dispatch_gather(
+    const v4u* __restrict__ x, const int32_t* __restrict__ P, const int32_t* __restrict__ cnt,
+    v4u* __restrict__ expand_x, int32_t* __restrict__ assist, int32_t* __restrict__ ep_recv,
+    int64_t* __restrict__ expert_nums, int32_t* __restrict__ row_idx,
+    int BS, int K, int L, int W, int TPG, int G, int64_t A, int nvec, int ntiles, int vpl) {
+  const unsigned item = blockIdx.x;
+  const unsigned gu = item / (unsigned)ntiles;
+  const int tile = (int)(item - gu * (unsigned)ntiles);
+  const int s = (int)(gu / (unsigned)BS);
+  const int t = (int)(gu - (unsigned)s * (unsigned)BS);
+  const int64_t g = gu;
+  const int lane = threadIdx.x;
+  const bool writer = (g == 0) && (tile == 0);
+
+  const int n_cnt = L * W * G;
+  int cnt0[kScanIPL];
+  load_counters(cnt, n_cnt, 0, lane, cnt0);
+  const int p = (lane < K) ? P[g * K + lane] : -1;
+  const bool mine = (p >= 0) && ((p & 0xFFFF) < L);
+  const uint64_t has = __ballot(mine);
+  if (has == 0 && !writer) return;
+
+  // Column tile of the source row: issued before the scan so the loads overlap it.
+  const int base = tile * 64 * vpl + lane;
+  const v4u* src = x + g * nvec;
+  v4u v[kGatherVec];
+  if (has != 0) {
+#pragma unroll
+    for (int u = 0; u < kGatherVec; ++u) {
+      const int idx = base + u * 64;
+      if (u < vpl && idx < nvec) v[u] = MDC_GATHER_NT_LOADS ? __builtin_nontemporal_load(src + idx) : src[idx];
     }
   }
-  if (wv == 0 && mine) {
+
+  const int le = p & 0xFFFF;
+  const int q = mine ? ((le * W + s) * G + t / TPG) : -1;
+  const int first = scan_lookup(cnt, n_cnt, cnt0, q, G, writer, ep_recv, lane);
+  if (writer) {
+    for (int e = lane; e < L; e += 64) {
+      int64_t sum = 0;
+      for (int i = 0; i < W * G; ++i) sum += cnt[(int64_t)e * W * G + i];
+      expert_nums[e] = sum;
+    }
+  }
+  if (has == 0) return;
+
+  int row = -1;
+  if (mine) {
+    const int64_t r = (int64_t)first + (p >> 16);
+    row = (r >= 0 && r < A) ? (int)r : -1;
+  }
+  if (tile == 0 && mine) {
     row_idx[g * K + lane] = row;
     if (row >= 0) {
       int32_t* a = assist + (int64_t)row * 3;
@@ -244,35 +330,29 @@ __global__ __launch_bounds__(1024) void k_dispatch_gather(
       a[2] = lane;
     }
   }
-  const uint64_t has = __ballot(row >= 0);
-  if (has == 0) return;
-
-  const v4u* src = x + g * nvec;
-  for (int tile = wv; tile * kTileVec < nvec; tile += nw) {
-    const int base = tile * kTileVec + lane;
-    v4u v[kRowVec];
+  uint64_t rem = __ballot(row >= 0);
+  while (rem) {
+    const int k = __ffsll((unsigned long long)rem) - 1;
+    rem &= rem - 1;
+    const int rk = __builtin_amdgcn_readlane(row, k);
+    v4u* dst = expand_x + (int64_t)rk * nvec;
 #pragma unroll
-    for (int u = 0; u < kRowVec; ++u) {
+    for (int u = 0; u < kGatherVec; ++u) {
       const int idx = base + u * 64;
-      if (idx < nvec) v[u] = src[idx];
-    }
-    uint64_t rem = has;
-    while (rem) {
-      const int k = __ffsll((unsigned long long)rem) - 1;
-      rem &= rem - 1;
-      const int rk = __builtin_amdgcn_readlane(row, k);
-      v4u* dst = expand_x + (int64_t)rk * nvec;
-#pragma unroll
-      for (int u = 0; u < kRowVec; ++u) {
-        const int idx = base + u * 64;
-        if (idx < nvec) __builtin_nontemporal_store(v[u], dst + idx);
-      }
+      if (u < vpl && idx < nvec) store_v4<MDC_GATHER_NT_STORES != 0>(dst + idx, v[u]);
     }
   }
 }
 
+// Empty batch: every count is zero.
+__global__ __launch_bounds__(64) void k_zero_counts(int32_t* __restrict__ ep_recv, int64_t* __restrict__ expert_nums,
+                                                    int L, int W) {
+  for (int i = threadIdx.x; i < L * W; i += 64) ep_recv[i] = 0;
+  for (int i = threadIdx.x; i < L; i += 64) expert_nums[i] = 0;
+}
+
 // ---------------------------------------------------------------------------
-// a6: combine.  One workgroup per token t of rank r.
+// a6: combine.  One wavefront per (token t of rank r, column tile).
 // ---------------------------------------------------------------------------
 struct CombineTables {
   const v4u* y[MDC_MAX_COMBINE_WORLD];
@@ -291,117 +371,138 @@ __device__ __forceinline__ unsigned bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int k) {
-  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)v, k);
-  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(v >> 32), k);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-template <int KMAX, bool SHARED>
-__global__ __launch_bounds__(1024) void k_combine(
+// Route (r, t, k) is present when the token is active, 0 <= e < E, and row
+// idx[t][k] of destination j = e / L is below min(count_j, A) and holds the
+// triplet (r, t, k).  The prologue is two load levels: (ids, row index,
+// scale, mask, pointer tables) then (count_j, triplet); every address is
+// kept inside its buffer so the loads can be issued without branches.
+template <int KMAX, int V, bool SHARED>
+__global__ __launch_bounds__(64) void k_combine(
     CombineTables tabs, const int32_t* __restrict__ row_idx, const int32_t* __restrict__ ids,
     const float* __restrict__ scales, const uint8_t* __restrict__ mask,
     const v4u* __restrict__ shared, v4u* __restrict__ out,
-    int r, int W, int K, int E, int L, int64_t A, int nvec) {
-  const int t = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
+    int r, int W, int K, int E, int L, int64_t A, int nvec, int ntiles) {
+  const unsigned item = blockIdx.x;
+  const int t = (int)(item / (unsigned)ntiles);
+  const int tile = (int)(item - (unsigned)t * (unsigned)ntiles);
+  const int lane = threadIdx.x;
+  const int kk = lane < K ? lane : 0;
+  const int64_t rt = (int64_t)t * K + kk;
 
-  // Lane k < K resolves route (r, t, k): destination j = e / L, row from the
-  // inverse index, checked against that destination's count and triplet.
+  const int e = ids[rt];
+  const int row = row_idx[rt];
+  const float sc = scales[rt];
+  const bool act = (mask == nullptr) || (mask[t] != 0);
+  const int tl = lane < W ? lane : 0;
+  const uint64_t yb = (uint64_t)tabs.y[tl];
+  const uint64_t ab = (uint64_t)tabs.assist[tl];
+  const uint64_t cb = (uint64_t)tabs.counts[tl];
+
+  const bool valid = (lane < K) && act && e >= 0 && e < E && A > 0;
+  const int j = valid ? e / L : 0;
+  const bool inrange = row >= 0 && row < A;
+  const int64_t rowc = inrange ? row : 0;
+  const uint64_t yj = shfl64(yb, j);
+  const uint64_t aj = shfl64(ab, j);
+  const uint64_t cj = shfl64(cb, j);
+
   bool ok = false;
-  uint64_t yrow = 0;
-  float sc = 0.f;
-  if (lane < K && (mask == nullptr || mask[t] != 0)) {
-    const int e = ids[(int64_t)t * K + lane];
-    if (e >= 0 && e < E) {
-      const int j = e / L;
-      const int row = row_idx[(int64_t)t * K + lane];
-      const int64_t total = tabs.counts[j][(int64_t)L * W - 1];
-      const int64_t lim = total < A ? total : A;
-      if (row >= 0 && row < lim) {
-        const int32_t* a = tabs.assist[j] + (int64_t)row * 3;
-        if (a[0] == r && a[1] == t && a[2] == lane) {
-          ok = true;
-          yrow = (uint64_t)(tabs.y[j] + (int64_t)row * nvec);
-          sc = scales[(int64_t)t * K + lane];
-        }
-      }
-    }
+  if (A > 0) {
+    const int32_t total = load_i32(cj + ((uint64_t)L * W - 1) * 4);
+    const uint64_t a = aj + (uint64_t)rowc * 12;
+    const int a0 = load_i32(a), a1 = load_i32(a + 4), a2 = load_i32(a + 8);
+    ok = valid && inrange && row < total && a0 == r && a1 == t && a2 == lane;
   }
   const uint64_t has = __ballot(ok);
   const int np = __popcll(has);
+  const int base = tile * 64 * V + lane;
+  v4u* orow = out + (int64_t)t * nvec;
 
-  // Present routes in ascending k, as wavefront-uniform pointers and scales.
-  const v4u* yp[KMAX];
+  if (np == 0) {
+    const v4u z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+      const int idx = base + u * 64;
+      if (idx < nvec) store_v4<MDC_COMBINE_NT_STORES != 0>(orow + idx, z);
+    }
+    return;
+  }
+
+  // Present routes in ascending k as wavefront-uniform row addresses and scales;
+  // slots past the last present route repeat the first one (loaded, never summed).
+  const uint64_t yrow = yj + (uint64_t)rowc * (uint64_t)nvec * sizeof(v4u);
+  uint64_t yp[KMAX];
   float sk[KMAX];
   uint64_t rem = has;
 #pragma unroll
   for (int i = 0; i < KMAX; ++i) {
-    const int k = rem ? (__ffsll((unsigned long long)rem) - 1) : 0;
-    yp[i] = (const v4u*)readlane64(yrow, k);
+    const int k = rem ? (__ffsll((unsigned long long)rem) - 1) : (__ffsll((unsigned long long)has) - 1);
+    yp[i] = readlane64(yrow, k);
     sk[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), k));
     rem &= rem - 1;
   }
 
-  const v4u* shrow = SHARED ? shared + (int64_t)t * nvec : nullptr;
-  v4u* orow = out + (int64_t)t * nvec;
-  for (int tile = wv; tile * kTileVec < nvec; tile += nw) {
-    const int base = tile * kTileVec + lane;
-    v4u yv[KMAX][kRowVec];
-    v4u shv[kRowVec];
+  v4u yv[KMAX][V];
+  v4u shv[V];
+  const uint64_t srow = (uint64_t)(shared + (int64_t)t * nvec);
+  const bool full = (tile + 1) * 64 * V <= nvec;
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i)
+#pragma unroll
+      for (int u = 0; u < V; ++u) yv[i][u] = load_v4<MDC_COMBINE_NT_LOADS != 0>(yp[i] + (uint64_t)(base + u * 64) * sizeof(v4u));
+    if (SHARED) {
+#pragma unroll
+      for (int u = 0; u < V; ++u) shv[u] = load_v4<MDC_COMBINE_NT_LOADS != 0>(srow + (uint64_t)(base + u * 64) * sizeof(v4u));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i)
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+        const int idx = base + u * 64;
+        yv[i][u] = (idx < nvec) ? load_v4<MDC_COMBINE_NT_LOADS != 0>(yp[i] + (uint64_t)idx * sizeof(v4u)) : v4u{0u, 0u, 0u, 0u};
+      }
+    if (SHARED) {
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+        const int idx = base + u * 64;
+        shv[u] = (idx < nvec) ? load_v4<MDC_COMBINE_NT_LOADS != 0>(srow + (uint64_t)idx * sizeof(v4u)) : v4u{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const int idx = base + u * 64;
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
       if (i < np) {
+        const float s_ = sk[i];
 #pragma unroll
-        for (int u = 0; u < kRowVec; ++u) {
-          const int idx = base + u * 64;
-          if (idx < nvec) yv[i][u] = yp[i][idx];
-        }
-      }
-    }
-    if (SHARED && np > 0) {
-#pragma unroll
-      for (int u = 0; u < kRowVec; ++u) {
-        const int idx = base + u * 64;
-        if (idx < nvec) shv[u] = shrow[idx];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kRowVec; ++u) {
-      const int idx = base + u * 64;
-      if (idx >= nvec) continue;
-      float acc[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll
-      for (int i = 0; i < KMAX; ++i) {
-        if (i < np) {
-          const float s_ = sk[i];
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const unsigned yw = yv[i][u][w];
-            const float a0 = s_ * bf16_lo(yw);
-            const float a1 = s_ * bf16_hi(yw);
-            if (SHARED) {
-              const unsigned sw = shv[u][w];
-              const float b0 = s_ * bf16_lo(sw);
-              const float b1 = s_ * bf16_hi(sw);
-              acc[2 * w] = acc[2 * w] + (a0 + b0);
-              acc[2 * w + 1] = acc[2 * w + 1] + (a1 + b1);
-            } else {
-              acc[2 * w] = acc[2 * w] + a0;
-              acc[2 * w + 1] = acc[2 * w + 1] + a1;
-            }
+        for (int w = 0; w < 4; ++w) {
+          const unsigned yw = yv[i][u][w];
+          const float a0 = s_ * bf16_lo(yw);
+          const float a1 = s_ * bf16_hi(yw);
+          if (SHARED) {
+            const unsigned sw = shv[u][w];
+            const float b0 = s_ * bf16_lo(sw);
+            const float b1 = s_ * bf16_hi(sw);
+            acc[2 * w] = acc[2 * w] + (a0 + b0);
+            acc[2 * w + 1] = acc[2 * w + 1] + (a1 + b1);
+          } else {
+            acc[2 * w] = acc[2 * w] + a0;
+            acc[2 * w + 1] = acc[2 * w + 1] + a1;
           }
         }
       }
-      v4u o;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) o[w] = bf16_rne(acc[2 * w]) | (bf16_rne(acc[2 * w + 1]) << 16);
-      __builtin_nontemporal_store(o, orow + idx);
     }
+    v4u o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o[w] = bf16_rne(acc[2 * w]) | (bf16_rne(acc[2 * w + 1]) << 16);
+    if (idx < nvec) store_v4<MDC_COMBINE_NT_STORES != 0>(orow + idx, o);
   }
 }
 
@@ -425,9 +526,9 @@ mdc_status check_shape(const mdc_shape* sh) {
 }
 
 struct DispatchPlan {
-  int W, d, BS, H, K, E, L, CT, nC, nvec;
+  int W, d, BS, H, K, E, L, TPG, G, nvec, rank_threads;
   int64_t A;
-  size_t off_p, off_cnt, off_base, bytes;
+  size_t off_p, off_cnt, bytes;
 };
 
 DispatchPlan make_plan(const mdc_shape* sh) {
@@ -440,51 +541,49 @@ DispatchPlan make_plan(const mdc_shape* sh) {
   p.E = sh->num_experts;
   p.L = p.E / p.W;
   p.A = sh->capacity;
-  p.CT = kRankThreads / p.K;
-  p.nC = (p.BS + p.CT - 1) / p.CT;
+  p.TPG = kGroupRoutes / p.K;
+  p.G = (p.BS + p.TPG - 1) / p.TPG;
   p.nvec = p.H / 8;
+  // wave_cnt[nw][L] + carry[L] must fit in LDS: 16 wavefronts up to L = 512, 4 beyond
+  p.rank_threads = p.L <= 512 ? 1024 : 256;
   const size_t routes = (size_t)p.W * p.BS * p.K;
-  const size_t chunks = (size_t)p.W * p.nC * p.L;
+  const size_t counters = (size_t)p.L * p.W * p.G;
   p.off_p = 0;
   p.off_cnt = round_up(routes * 4, 256);
-  p.off_base = p.off_cnt + round_up(chunks * 4, 256);
-  p.bytes = p.off_base + round_up(chunks * 4, 256);
+  p.bytes = p.off_cnt + round_up(counters * 4, 256);
   if (p.bytes == 0) p.bytes = 256;
   return p;
 }
 
-int row_waves(int nvec) {
-  int tiles = (nvec + kTileVec - 1) / kTileVec;
-  return tiles < kMaxWaves ? tiles : kMaxWaves;
-}
-
 mdc_status launched() { return hipGetLastError() == hipSuccess ? MDC_OK : MDC_ERR_HIP; }
 
-mdc_status layout_impl(const DispatchPlan& p, const int32_t* ids, const uint8_t* mask,
-                       int32_t* ep_recv, int64_t* expert_nums, char* ws, hipStream_t st) {
+mdc_status layout_impl(const DispatchPlan& p, const int32_t* ids, const uint8_t* mask, char* ws, hipStream_t st) {
   int32_t* P = reinterpret_cast<int32_t*>(ws + p.off_p);
   int32_t* cnt = reinterpret_cast<int32_t*>(ws + p.off_cnt);
-  int32_t* base = reinterpret_cast<int32_t*>(ws + p.off_base);
+  if (p.G == 0) return MDC_OK;
   (void)hipGetLastError();
-  if (p.nC > 0) {
-    hipLaunchKernelGGL(k_route_rank, dim3(p.nC, p.W), dim3(kRankThreads), 4 * p.L * sizeof(int32_t), st,
-                       ids, mask, P, cnt, p.BS, p.K, p.E, p.L, p.d, p.CT, p.nC);
-  }
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kScanThreads), p.L * sizeof(int32_t), st,
-                     cnt, base, ep_recv, expert_nums, p.W, p.L, p.nC);
+  const size_t lds = (size_t)(p.rank_threads / 64 + 1) * p.L * sizeof(int32_t);
+  hipLaunchKernelGGL(k_route_rank, dim3(p.G, p.W), dim3(p.rank_threads), lds, st,
+                     ids, mask, P, cnt, p.BS, p.K, p.E, p.L, p.d, p.W, p.TPG, p.G);
   return launched();
 }
 
-mdc_status gather_impl(const DispatchPlan& p, const void* x, void* expand_x, int32_t* assist,
-                       int32_t* row_idx, char* ws, hipStream_t st) {
+mdc_status gather_impl(const DispatchPlan& p, const void* x, void* expand_x, int32_t* assist, int32_t* ep_recv,
+                       int64_t* expert_nums, int32_t* row_idx, char* ws, hipStream_t st) {
   const int32_t* P = reinterpret_cast<const int32_t*>(ws + p.off_p);
-  const int32_t* base = reinterpret_cast<const int32_t*>(ws + p.off_base);
-  const int64_t tokens = (int64_t)p.W * p.BS;
-  if (tokens == 0) return MDC_OK;
+  const int32_t* cnt = reinterpret_cast<const int32_t*>(ws + p.off_cnt);
   (void)hipGetLastError();
-  hipLaunchKernelGGL(k_dispatch_gather, dim3((unsigned)tokens), dim3(64 * row_waves(p.nvec)), 0, st,
-                     static_cast<const v4u*>(x), P, base, static_cast<v4u*>(expand_x), assist, row_idx,
-                     p.BS, p.K, p.L, p.CT, p.nC, p.A, p.nvec);
+  const int64_t tokens = (int64_t)p.W * p.BS;
+  if (tokens == 0) {
+    // nothing routed: zero the counts with one wavefront of the gather kernel's writer path
+    hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(64), 0, st, ep_recv, expert_nums, p.L, p.W);
+    return launched();
+  }
+  const int ntiles = (p.nvec + 64 * kGatherVec - 1) / (64 * kGatherVec);
+  const int vpl = (p.nvec + 64 * ntiles - 1) / (64 * ntiles);
+  hipLaunchKernelGGL(k_dispatch_gather, dim3((unsigned)(tokens * ntiles)), dim3(64), 0, st,
+                     static_cast<const v4u*>(x), P, cnt, static_cast<v4u*>(expand_x), assist, ep_recv,
+                     expert_nums, row_idx, p.BS, p.K, p.L, p.W, p.TPG, p.G, p.A, p.nvec, ntiles, vpl);
   return launched();
 }
 
@@ -513,33 +612,30 @@ mdc_status mdc_dispatch_workspace_size(const mdc_shape* shape, size_t* bytes) {
   return MDC_OK;
 }
 
-mdc_status mdc_dispatch_layout(const mdc_shape* shape, const int32_t* expert_ids,
-                               const uint8_t* x_active_mask, int32_t* ep_recv_counts,
-                               int64_t* expert_token_nums, void* workspace, size_t workspace_bytes,
-                               void* stream) {
-  mdc_status st = check_shape(shape);
-  if (st != MDC_OK) return st;
-  const DispatchPlan p = make_plan(shape);
-  if (ep_recv_counts == nullptr || expert_token_nums == nullptr || workspace == nullptr) return MDC_ERR_NULLPTR;
-  if (p.BS > 0 && expert_ids == nullptr) return MDC_ERR_NULLPTR;
-  if (workspace_bytes < p.bytes) return MDC_ERR_WORKSPACE;
-  return layout_impl(p, expert_ids, x_active_mask, ep_recv_counts, expert_token_nums,
-                     static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
-}
-
-mdc_status mdc_dispatch_gather(const mdc_shape* shape, const void* x, void* expand_x, int32_t* assist_info,
-                               int32_t* expanded_row_idx, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+mdc_status mdc_dispatch_layout(const mdc_shape* shape, const int32_t* expert_ids, const uint8_t* x_active_mask,
+                               void* workspace, size_t workspace_bytes, void* stream) {
   mdc_status st = check_shape(shape);
   if (st != MDC_OK) return st;
   const DispatchPlan p = make_plan(shape);
   if (workspace == nullptr) return MDC_ERR_NULLPTR;
+  if (p.BS > 0 && expert_ids == nullptr) return MDC_ERR_NULLPTR;
+  if (workspace_bytes < p.bytes) return MDC_ERR_WORKSPACE;
+  return layout_impl(p, expert_ids, x_active_mask, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+mdc_status mdc_dispatch_gather(const mdc_shape* shape, const void* x, void* expand_x, int32_t* assist_info,
+                               int32_t* ep_recv_counts, int64_t* expert_token_nums, int32_t* expanded_row_idx,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  mdc_status st = check_shape(shape);
+  if (st != MDC_OK) return st;
+  const DispatchPlan p = make_plan(shape);
+  if (workspace == nullptr || ep_recv_counts == nullptr || expert_token_nums == nullptr) return MDC_ERR_NULLPTR;
   if (p.BS > 0 && (x == nullptr || expanded_row_idx == nullptr)) return MDC_ERR_NULLPTR;
   if (p.BS > 0 && p.A > 0 && (expand_x == nullptr || assist_info == nullptr)) return MDC_ERR_NULLPTR;
   if (!aligned16(x) || !aligned16(expand_x)) return MDC_ERR_INVALID;
   if (workspace_bytes < p.bytes) return MDC_ERR_WORKSPACE;
-  return gather_impl(p, x, expand_x, assist_info, expanded_row_idx, static_cast<char*>(workspace),
-                     static_cast<hipStream_t>(stream));
+  return gather_impl(p, x, expand_x, assist_info, ep_recv_counts, expert_token_nums, expanded_row_idx,
+                     static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 mdc_status mdc_dispatch(const mdc_shape* shape, const void* x, const int32_t* expert_ids,
@@ -556,9 +652,9 @@ mdc_status mdc_dispatch(const mdc_shape* shape, const void* x, const int32_t* ex
   if (workspace_bytes < p.bytes) return MDC_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = layout_impl(p, expert_ids, x_active_mask, ep_recv_counts, expert_token_nums, ws, s);
+  st = layout_impl(p, expert_ids, x_active_mask, ws, s);
   if (st != MDC_OK) return st;
-  return gather_impl(p, x, expand_x, assist_info, expanded_row_idx, ws, s);
+  return gather_impl(p, x, expand_x, assist_info, ep_recv_counts, expert_token_nums, expanded_row_idx, ws, s);
 }
 
 mdc_status mdc_combine_workspace_size(const mdc_shape* shape, size_t* bytes) {
@@ -600,25 +696,30 @@ mdc_status mdc_combine(const mdc_shape* shape, const void* const* expand_x, cons
   const int E = shape->num_experts;
   const int L = E / W;
   const int nvec = shape->hidden / 8;
-  const dim3 grid(BS), block(64 * row_waves(nvec));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const v4u* sh = static_cast<const v4u*>(shared_expert_x);
   v4u* out = static_cast<v4u*>(x_out);
+  const int r = shape->rank;
+  const int64_t A = shape->capacity;
   (void)hipGetLastError();
   if (K <= 8) {
+    const int ntiles = (nvec + 64 * kCombineVec - 1) / (64 * kCombineVec);
+    const dim3 grid((unsigned)((int64_t)BS * ntiles)), block(64);
     if (sh)
-      hipLaunchKernelGGL((k_combine<8, true>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
-                         expert_scales, x_active_mask, sh, out, shape->rank, W, K, E, L, shape->capacity, nvec);
+      hipLaunchKernelGGL((k_combine<8, kCombineVec, true>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
+                         expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles);
     else
-      hipLaunchKernelGGL((k_combine<8, false>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
-                         expert_scales, x_active_mask, sh, out, shape->rank, W, K, E, L, shape->capacity, nvec);
+      hipLaunchKernelGGL((k_combine<8, kCombineVec, false>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
+                         expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles);
   } else {
+    const int ntiles = (nvec + 63) / 64;
+    const dim3 grid((unsigned)((int64_t)BS * ntiles)), block(64);
     if (sh)
-      hipLaunchKernelGGL((k_combine<16, true>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
-                         expert_scales, x_active_mask, sh, out, shape->rank, W, K, E, L, shape->capacity, nvec);
+      hipLaunchKernelGGL((k_combine<16, 1, true>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
+                         expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles);
     else
-      hipLaunchKernelGGL((k_combine<16, false>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
-                         expert_scales, x_active_mask, sh, out, shape->rank, W, K, E, L, shape->capacity, nvec);
+      hipLaunchKernelGGL((k_combine<16, 1, false>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
+                         expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles);
   }
   return launched();
 }

@@ -122,17 +122,17 @@ int32_t mdc_abi_version(void);
  *
  * The call is split in two stages that may be enqueued separately (same
  * stream, same workspace, in this order); mdc_dispatch enqueues both.
- *   mdc_dispatch_layout  histogram + scan: writes ep_recv_counts,
- *                        expert_token_nums and the per-route ranks into ws.
- *   mdc_dispatch_gather  rows, triplets and the inverse index, from ws.
+ *   mdc_dispatch_layout  route filter, histogram and stable ranks
+ *                        ([PTO] FrontReorder Stage); writes only the workspace.
+ *   mdc_dispatch_gather  scan, rows, triplets, inverse index, epRecvCounts and
+ *                        expertTokenNums ([PTO] Dispatch Stage), from the
+ *                        workspace the layout stage filled.
  * ------------------------------------------------------------------------ */
 mdc_status mdc_dispatch_workspace_size(const mdc_shape* shape, size_t* bytes);
 
 mdc_status mdc_dispatch_layout(const mdc_shape* shape,
                                const int32_t* expert_ids,
                                const uint8_t* x_active_mask,
-                               int32_t* ep_recv_counts,
-                               int64_t* expert_token_nums,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
 
@@ -140,6 +140,8 @@ mdc_status mdc_dispatch_gather(const mdc_shape* shape,
                                const void* x,
                                void* expand_x,
                                int32_t* assist_info,
+                               int32_t* ep_recv_counts,
+                               int64_t* expert_token_nums,
                                int32_t* expanded_row_idx,
                                void* workspace, size_t workspace_bytes,
                                void* stream);

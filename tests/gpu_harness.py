@@ -49,8 +49,9 @@ def dispatch_world(shape: mdc.Shape, x: np.ndarray, ids: np.ndarray, mask: Optio
         sh = shape.with_rank(d)
         o = mdc.alloc_dispatch_outputs(sh, DEV)
         if split:
-            mdc.mdc_dispatch_layout(sh, idd, md, o["ep_recv_counts"], o["expert_token_nums"], o["workspace"])
-            mdc.mdc_dispatch_gather(sh, xd, o["expand_x"], o["assist_info"], row_idx, o["workspace"])
+            mdc.mdc_dispatch_layout(sh, idd, md, o["workspace"])
+            mdc.mdc_dispatch_gather(sh, xd, o["expand_x"], o["assist_info"], o["ep_recv_counts"],
+                                    o["expert_token_nums"], row_idx, o["workspace"])
         else:
             mdc.mdc_dispatch(sh, xd, idd, md, o["expand_x"], o["assist_info"], o["ep_recv_counts"],
                              o["expert_token_nums"], row_idx, o["workspace"])

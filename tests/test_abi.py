@@ -79,9 +79,7 @@ def test_null_shape_and_pointers():
         (fake, fake, None, fake, fake, fake, fake, None, fake),
         (fake, fake, None, fake, fake, fake, fake, fake, None),
     ]:
-        st = mdc.mdc_dispatch(SHARE, *args[:8], args[8], check=False) if False else \
-            lib.mdc_dispatch(ctypes.byref(sh), *[ctypes.c_void_p(a) for a in args[:8]],
-                             ctypes.c_void_p(args[8]), ctypes.c_size_t(ws), None)
+        st = lib.mdc_dispatch(ctypes.byref(sh), *[ctypes.c_void_p(a) for a in args], ctypes.c_size_t(ws), None)
         assert st == mdc.MDC_ERR_NULLPTR
 
 
@@ -91,11 +89,9 @@ def test_small_workspace_rejected():
     lib = ctypes.CDLL(mdc.LIB_PATH)
     sh = SHARE.c()
     st = lib.mdc_dispatch_layout(ctypes.byref(sh), ctypes.c_void_p(fake), None, ctypes.c_void_p(fake),
-                                 ctypes.c_void_p(fake), ctypes.c_void_p(fake), ctypes.c_size_t(ws - 1), None)
-    assert st == mdc.MDC_ERR_WORKSPACE
-    st = lib.mdc_dispatch_gather(ctypes.byref(sh), ctypes.c_void_p(fake), ctypes.c_void_p(fake),
-                                 ctypes.c_void_p(fake), ctypes.c_void_p(fake), ctypes.c_void_p(fake),
                                  ctypes.c_size_t(ws - 1), None)
+    assert st == mdc.MDC_ERR_WORKSPACE
+    st = lib.mdc_dispatch_gather(ctypes.byref(sh), *[ctypes.c_void_p(fake)] * 7, ctypes.c_size_t(ws - 1), None)
     assert st == mdc.MDC_ERR_WORKSPACE
 
 
@@ -104,8 +100,7 @@ def test_misaligned_rows_rejected():
     ws = mdc.mdc_dispatch_workspace_size(SHARE)
     lib = ctypes.CDLL(mdc.LIB_PATH)
     sh = SHARE.c()
-    st = lib.mdc_dispatch_gather(ctypes.byref(sh), ctypes.c_void_p(fake + 2), ctypes.c_void_p(fake),
-                                 ctypes.c_void_p(fake), ctypes.c_void_p(fake), ctypes.c_void_p(fake),
+    st = lib.mdc_dispatch_gather(ctypes.byref(sh), ctypes.c_void_p(fake + 2), *[ctypes.c_void_p(fake)] * 6,
                                  ctypes.c_size_t(ws), None)
     assert st == mdc.MDC_ERR_INVALID
 
