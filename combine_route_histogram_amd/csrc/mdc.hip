@@ -45,6 +45,13 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 // dispatch+combine steps: non-temporal row loads and stores in both kernels
 // give the shortest step (the two kernels share the Infinity Cache, so each
 // one's policy also moves the other's time).
+// Wavefronts per workgroup (each wavefront handles its own row tile).
+#ifndef MDC_GATHER_WAVES
+#define MDC_GATHER_WAVES 1
+#endif
+#ifndef MDC_COMBINE_WAVES
+#define MDC_COMBINE_WAVES 1
+#endif
 #ifndef MDC_GATHER_NT_LOADS
 #define MDC_GATHER_NT_LOADS 1
 #endif
@@ -57,8 +64,27 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 #ifndef MDC_COMBINE_NT_STORES
 #define MDC_COMBINE_NT_STORES 1
 #endif
-constexpr int kGroupRoutes = 4096;     // routes of one source ranked by one k_route_rank workgroup
+#ifndef MDC_GROUP_ROUTES
+#define MDC_GROUP_ROUTES 2048
+#endif
+#ifndef MDC_SCAN_IPL
+#define MDC_SCAN_IPL 16
+#endif
+constexpr int kGroupRoutes = MDC_GROUP_ROUTES;  // routes of one source ranked by one k_route_rank workgroup
+constexpr int kScanIPL = MDC_SCAN_IPL;           // group counters per lane per scan chunk
+constexpr int kScanChunk = 64 * kScanIPL;
+
+// Group counters are scanned in chunks of kScanChunk, lane l taking the
+// kScanIPL consecutive counters l*kScanIPL.. of a chunk.  They are stored
+// transposed inside each chunk (counter j of lane l at j*64 + l) so that the
+// j-th load of all 64 lanes reads 64 consecutive words.
+__host__ __device__ __forceinline__ int counter_slot(int i) {
+  const int c0 = i - i % kScanChunk;
+  const int r = i - c0;
+  return c0 + (r % kScanIPL) * 64 + r / kScanIPL;
+}
 constexpr int kGatherVec = MDC_GATHER_VEC;
+static_assert(kGatherVec >= 1 && kGatherVec <= 8, "gather tiles hold 1..8 vectors per lane");
 constexpr int kCombineVec = MDC_COMBINE_VEC;
 
 template <bool NT>
@@ -80,12 +106,17 @@ __device__ __forceinline__ v4u load_v4(uint64_t addr) {
 }
 __device__ __forceinline__ int32_t load_i32(uint64_t addr) { return *reinterpret_cast<g_i32*>(addr); }
 
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
+// Inclusive prefix sum over the 64 lanes with DPP lane moves: shifts by
+// 1, 2, 4, 8 inside each row of 16 lanes, then row_bcast:15 adds the total of
+// rows 0 / 2 to rows 1 / 3 and row_bcast:31 adds the total of rows 0-1 to
+// rows 2-3.  Lanes without a source read 0.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31 into rows 2, 3
   return v;
 }
 
@@ -187,7 +218,7 @@ __global__ __launch_bounds__(1024) void k_route_rank(
     }
     __syncthreads();
   }
-  for (int le = tid; le < L; le += blockDim.x) cnt[((int64_t)le * W + s) * G + g] = carry[le];
+  for (int le = tid; le < L; le += blockDim.x) cnt[counter_slot((le * W + s) * G + g)] = carry[le];
 }
 
 // ---------------------------------------------------------------------------
@@ -200,18 +231,23 @@ __global__ __launch_bounds__(1024) void k_route_rank(
 // 0).  With `writer`, also stores epRecvCounts.  `first` holds this lane's
 // counters of chunk 0, loaded early by the caller.
 // ---------------------------------------------------------------------------
-constexpr int kScanIPL = 8;
-constexpr int kScanChunk = 64 * kScanIPL;
 
 __device__ __forceinline__ void load_counters(const int32_t* __restrict__ cnt, int n, int c0, int lane,
                                               int (&v)[kScanIPL]) {
   const int i0 = c0 + lane * kScanIPL;
 #pragma unroll
-  for (int j = 0; j < kScanIPL; ++j) v[j] = (i0 + j < n) ? cnt[i0 + j] : 0;
+  for (int j = 0; j < kScanIPL; ++j) v[j] = (i0 + j < n) ? cnt[c0 + j * 64 + lane] : 0;
+}
+
+// Orders this wavefront's LDS accesses: the LDS work issued so far completes
+// before anything after it is issued.
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
+  __builtin_amdgcn_wave_barrier();
 }
 
 __device__ int scan_lookup(const int32_t* __restrict__ cnt, int n, const int (&first)[kScanIPL], int q, int G,
-                           bool writer, int32_t* __restrict__ ep_recv, int lane) {
+                           bool writer, int32_t* __restrict__ ep_recv, int lane, int32_t* __restrict__ pref) {
   int carry = 0;
   int found = 0;
   for (int c0 = 0; c0 < n; c0 += kScanChunk) {
@@ -229,9 +265,11 @@ __device__ int scan_lookup(const int32_t* __restrict__ cnt, int n, const int (&f
       ex[j] = sum;
       sum += v[j];
     }
-    const int incl = wave_inclusive_scan(sum, lane);
+    const int incl = wave_inclusive_scan(sum);
     const int lane_base = carry + incl - sum;
     const int i0 = c0 + lane * kScanIPL;
+#pragma unroll
+    for (int j = 0; j < kScanIPL; ++j) pref[lane * kScanIPL + j] = lane_base + ex[j];
     if (writer) {
 #pragma unroll
       for (int j = 0; j < kScanIPL; ++j) {
@@ -239,21 +277,11 @@ __device__ int scan_lookup(const int32_t* __restrict__ cnt, int n, const int (&f
         if (i < n && (i % G) == G - 1) ep_recv[i / G] = lane_base + ex[j] + v[j];
       }
     }
+    lds_wave_sync();
     const int rel = q - c0;
-    const bool in = (q >= 0) && (rel >= 0) && (rel < kScanChunk);
-    const int owner = in ? (rel / kScanIPL) : lane;
-    const int slot = rel & (kScanIPL - 1);
-    // the owner's prefix before its slot: lane_base + ex[slot]; fetch lane_base
-    // and the owner's counters up to the slot through cross-lane reads
-    const int ob = __shfl(lane_base, owner, 64);
-    int part = 0;
-#pragma unroll
-    for (int j = 0; j < kScanIPL; ++j) {
-      const int vj = __shfl(v[j], owner, 64);
-      part += (j < slot) ? vj : 0;
-    }
-    if (in) found = ob + part;
+    if (q >= 0 && rel >= 0 && rel < kScanChunk) found = pref[rel];
     carry += __builtin_amdgcn_readlane(incl, 63);
+    lds_wave_sync();
   }
   return found;
 }
@@ -270,20 +298,22 @@ __device__ int scan_lookup(const int32_t* __restrict__ cnt, int n, const int (&f
 // 0, tile 0 also writes epRecvCounts and expertTokenNums
 // ([TL] UpdateTokenNumsOut: per-local-expert counts).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_dispatch_gather(
+template <int VPL>
+__global__ __launch_bounds__(64 * MDC_GATHER_WAVES) void k_dispatch_gather(
     const v4u* __restrict__ x, const int32_t* __restrict__ P, const int32_t* __restrict__ cnt,
     v4u* __restrict__ expand_x, int32_t* __restrict__ assist, int32_t* __restrict__ ep_recv,
     int64_t* __restrict__ expert_nums, int32_t* __restrict__ row_idx,
-    int BS, int K, int L, int W, int TPG, int G, int64_t A, int nvec, int ntiles, int vpl) {
-  const unsigned item = blockIdx.x;
+    int BS, int K, int L, int W, int TPG, int G, int64_t A, int nvec, int ntiles, unsigned n_items) {
+  const unsigned item = blockIdx.x * MDC_GATHER_WAVES + (threadIdx.x >> 6);
+  if (item >= n_items) return;
   const unsigned gu = item / (unsigned)ntiles;
   const int tile = (int)(item - gu * (unsigned)ntiles);
   const int s = (int)(gu / (unsigned)BS);
   const int t = (int)(gu - (unsigned)s * (unsigned)BS);
   const int64_t g = gu;
-  const int lane = threadIdx.x;
-  const bool writer = (g == 0) && (tile == 0);
+  const int lane = threadIdx.x & 63;
 
+  const bool writer = (g == 0) && (tile == 0);
   const int n_cnt = L * W * G;
   int cnt0[kScanIPL];
   load_counters(cnt, n_cnt, 0, lane, cnt0);
@@ -293,24 +323,31 @@ __global__ __launch_bounds__(64) void k_dispatch_gather(
   if (has == 0 && !writer) return;
 
   // Column tile of the source row: issued before the scan so the loads overlap it.
-  const int base = tile * 64 * vpl + lane;
-  const v4u* src = x + g * nvec;
-  v4u v[kGatherVec];
+  const int base = tile * 64 * VPL + lane;
+  const bool full = (tile + 1) * 64 * VPL <= nvec;
+  const uint64_t src = (uint64_t)(x + g * nvec);
+  v4u v[VPL];
   if (has != 0) {
+    if (full) {
 #pragma unroll
-    for (int u = 0; u < kGatherVec; ++u) {
-      const int idx = base + u * 64;
-      if (u < vpl && idx < nvec) v[u] = MDC_GATHER_NT_LOADS ? __builtin_nontemporal_load(src + idx) : src[idx];
+      for (int u = 0; u < VPL; ++u) v[u] = load_v4<MDC_GATHER_NT_LOADS != 0>(src + (uint64_t)(base + u * 64) * 16);
+    } else {
+#pragma unroll
+      for (int u = 0; u < VPL; ++u) {
+        const int idx = base + u * 64;
+        v[u] = idx < nvec ? load_v4<MDC_GATHER_NT_LOADS != 0>(src + (uint64_t)idx * 16) : v4u{0u, 0u, 0u, 0u};
+      }
     }
   }
 
   const int le = p & 0xFFFF;
   const int q = mine ? ((le * W + s) * G + t / TPG) : -1;
-  const int first = scan_lookup(cnt, n_cnt, cnt0, q, G, writer, ep_recv, lane);
+  __shared__ int32_t pref_all[MDC_GATHER_WAVES][kScanChunk];
+  const int first = scan_lookup(cnt, n_cnt, cnt0, q, G, writer, ep_recv, lane, pref_all[threadIdx.x >> 6]);
   if (writer) {
     for (int e = lane; e < L; e += 64) {
       int64_t sum = 0;
-      for (int i = 0; i < W * G; ++i) sum += cnt[(int64_t)e * W * G + i];
+      for (int i = 0; i < W * G; ++i) sum += cnt[counter_slot(e * W * G + i)];
       expert_nums[e] = sum;
     }
   }
@@ -336,10 +373,15 @@ __global__ __launch_bounds__(64) void k_dispatch_gather(
     rem &= rem - 1;
     const int rk = __builtin_amdgcn_readlane(row, k);
     v4u* dst = expand_x + (int64_t)rk * nvec;
+    if (full) {
 #pragma unroll
-    for (int u = 0; u < kGatherVec; ++u) {
-      const int idx = base + u * 64;
-      if (u < vpl && idx < nvec) store_v4<MDC_GATHER_NT_STORES != 0>(dst + idx, v[u]);
+      for (int u = 0; u < VPL; ++u) store_v4<MDC_GATHER_NT_STORES != 0>(dst + base + u * 64, v[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < VPL; ++u) {
+        const int idx = base + u * 64;
+        if (idx < nvec) store_v4<MDC_GATHER_NT_STORES != 0>(dst + idx, v[u]);
+      }
     }
   }
 }
@@ -377,15 +419,16 @@ __device__ __forceinline__ unsigned bf16_rne(float f) {
 // scale, mask, pointer tables) then (count_j, triplet); every address is
 // kept inside its buffer so the loads can be issued without branches.
 template <int KMAX, int V, bool SHARED>
-__global__ __launch_bounds__(64) void k_combine(
+__global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
     CombineTables tabs, const int32_t* __restrict__ row_idx, const int32_t* __restrict__ ids,
     const float* __restrict__ scales, const uint8_t* __restrict__ mask,
     const v4u* __restrict__ shared, v4u* __restrict__ out,
-    int r, int W, int K, int E, int L, int64_t A, int nvec, int ntiles) {
-  const unsigned item = blockIdx.x;
+    int r, int W, int K, int E, int L, int64_t A, int nvec, int ntiles, unsigned n_items) {
+  const unsigned item = blockIdx.x * MDC_COMBINE_WAVES + (threadIdx.x >> 6);
+  if (item >= n_items) return;
   const int t = (int)(item / (unsigned)ntiles);
   const int tile = (int)(item - (unsigned)t * (unsigned)ntiles);
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int kk = lane < K ? lane : 0;
   const int64_t rt = (int64_t)t * K + kk;
 
@@ -547,7 +590,7 @@ DispatchPlan make_plan(const mdc_shape* sh) {
   // wave_cnt[nw][L] + carry[L] must fit in LDS: 16 wavefronts up to L = 512, 4 beyond
   p.rank_threads = p.L <= 512 ? 1024 : 256;
   const size_t routes = (size_t)p.W * p.BS * p.K;
-  const size_t counters = (size_t)p.L * p.W * p.G;
+  const size_t counters = round_up((size_t)p.L * p.W * p.G, kScanChunk);
   p.off_p = 0;
   p.off_cnt = round_up(routes * 4, 256);
   p.bytes = p.off_cnt + round_up(counters * 4, 256);
@@ -581,9 +624,23 @@ mdc_status gather_impl(const DispatchPlan& p, const void* x, void* expand_x, int
   }
   const int ntiles = (p.nvec + 64 * kGatherVec - 1) / (64 * kGatherVec);
   const int vpl = (p.nvec + 64 * ntiles - 1) / (64 * ntiles);
-  hipLaunchKernelGGL(k_dispatch_gather, dim3((unsigned)(tokens * ntiles)), dim3(64), 0, st,
-                     static_cast<const v4u*>(x), P, cnt, static_cast<v4u*>(expand_x), assist, ep_recv,
-                     expert_nums, row_idx, p.BS, p.K, p.L, p.W, p.TPG, p.G, p.A, p.nvec, ntiles, vpl);
+  const unsigned n_items = (unsigned)(tokens * ntiles);
+  const dim3 grid((n_items + MDC_GATHER_WAVES - 1) / MDC_GATHER_WAVES), block(64 * MDC_GATHER_WAVES);
+#define MDC_LAUNCH_GATHER(V)                                                                                  \
+  hipLaunchKernelGGL(k_dispatch_gather<V>, grid, block, 0, st, static_cast<const v4u*>(x), P, cnt,            \
+                     static_cast<v4u*>(expand_x), assist, ep_recv, expert_nums, row_idx, p.BS, p.K, p.L,        \
+                     p.W, p.TPG, p.G, p.A, p.nvec, ntiles, n_items)
+  switch (vpl) {
+    case 1: MDC_LAUNCH_GATHER(1); break;
+    case 2: MDC_LAUNCH_GATHER(2); break;
+    case 3: MDC_LAUNCH_GATHER(3); break;
+    case 4: MDC_LAUNCH_GATHER(4); break;
+    case 5: MDC_LAUNCH_GATHER(5); break;
+    case 6: MDC_LAUNCH_GATHER(6); break;
+    case 7: MDC_LAUNCH_GATHER(7); break;
+    default: MDC_LAUNCH_GATHER(8); break;
+  }
+#undef MDC_LAUNCH_GATHER
   return launched();
 }
 
@@ -704,22 +761,24 @@ mdc_status mdc_combine(const mdc_shape* shape, const void* const* expand_x, cons
   (void)hipGetLastError();
   if (K <= 8) {
     const int ntiles = (nvec + 64 * kCombineVec - 1) / (64 * kCombineVec);
-    const dim3 grid((unsigned)((int64_t)BS * ntiles)), block(64);
+    const unsigned n_items = (unsigned)((int64_t)BS * ntiles);
+    const dim3 grid((n_items + MDC_COMBINE_WAVES - 1) / MDC_COMBINE_WAVES), block(64 * MDC_COMBINE_WAVES);
     if (sh)
       hipLaunchKernelGGL((k_combine<8, kCombineVec, true>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
-                         expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles);
+                         expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles, n_items);
     else
       hipLaunchKernelGGL((k_combine<8, kCombineVec, false>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
-                         expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles);
+                         expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles, n_items);
   } else {
     const int ntiles = (nvec + 63) / 64;
-    const dim3 grid((unsigned)((int64_t)BS * ntiles)), block(64);
+    const unsigned n_items = (unsigned)((int64_t)BS * ntiles);
+    const dim3 grid((n_items + MDC_COMBINE_WAVES - 1) / MDC_COMBINE_WAVES), block(64 * MDC_COMBINE_WAVES);
     if (sh)
       hipLaunchKernelGGL((k_combine<16, 1, true>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
-                         expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles);
+                         expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles, n_items);
     else
       hipLaunchKernelGGL((k_combine<16, 1, false>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
-                         expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles);
+                         expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles, n_items);
   }
   return launched();
 }
