@@ -39,7 +39,10 @@ DESCR = {
     "skewed": "share shapes with Zipf(1.2) routes and 10% inactive tokens",
     "decode": "8 virtual ranks x 32 tokens, H=7168, 256 experts (32 local), top-8, shared expert",
     "tiny": "1 virtual rank, 8 experts, 16 tokens, H=128, top-2",
+    "ffn": "share routing, then per local expert int8 GMM1 7168->4096, SwiGLU + dynamic int8 quant, "
+           "int8 GMM2 2048->7168 (mdc_ffn) on destination 0's rows, then combine",
 }
+INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA
 
 
 def parse():
@@ -98,8 +101,9 @@ def measured_traffic(workload: str, kernel: str):
     return None
 
 
-def cpu_baseline(wi, w, budget_s):
-    """Time the oracle (as it stands) on dispatch share 0 + combine share 0 of the same workload."""
+def cpu_baseline(wi, w, budget_s, fw=None):
+    """Time the oracle (as it stands) on dispatch share 0 (+ FFN) + combine share 0 of the same workload."""
+    import numpy as np
     from oracle import mdc_oracle as O
     segs = [O.dispatch(wi.x, wi.ids, wi.mask, d, w.experts, w.capacity) for d in range(w.world)]
     rates = []
@@ -109,15 +113,24 @@ def cpu_baseline(wi, w, budget_s):
     while reps < 1 or (time.perf_counter() < t_end and reps < 20):
         t0 = time.perf_counter()
         s0 = O.dispatch(wi.x, wi.ids, wi.mask, 0, w.experts, w.capacity)
-        ys = [s0.expand_x] + [s.expand_x for s in segs[1:]]
+        y0 = s0.expand_x
+        if fw is not None:
+            n = s0.assist_info.shape[0]
+            row_expert = np.repeat(np.arange(w.local_experts), s0.expert_token_nums)[:n]
+            y0 = O.ffn(s0.expand_x, row_expert, fw.w1, fw.w1_scale, fw.w2, fw.w2_scale)
+        ys = [y0] + [s.expand_x for s in segs[1:]]
         out = O.combine(ys, [s0.assist_info] + [s.assist_info for s in segs[1:]], 0, wi.ids[0],
                         None if wi.mask is None else wi.mask[0], wi.scales[0],
                         None if wi.shared is None else wi.shared[0], w.hidden)
         rates.append(w.bs / (time.perf_counter() - t0))
         reps += 1
-    return {"value": statistics.median(rates), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"the full timed step (dispatch share 0 + combine share 0 of the {w.name} workload), "
-                      f"{reps} repetitions, median; numpy elementwise work on one thread"}, segs, out
+    what = "dispatch share 0 + FFN + combine share 0" if fw is not None else "dispatch share 0 + combine share 0"
+    cores = 1
+    if fw is not None:
+        cores = os.cpu_count() or 1   # the FFN's float64 matrix products run on every host core (BLAS)
+    return {"value": statistics.median(rates), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the full timed step ({what} of the {w.name} workload), {reps} repetitions, median; "
+                      f"numpy elementwise work on one thread"}, segs, out
 
 
 def main():
@@ -161,10 +174,20 @@ def main():
             mdc.mdc_dispatch(shape.with_rank(d), x, ids, mask, o["expand_x"], o["assist_info"],
                              o["ep_recv_counts"], o["expert_token_nums"], row_idx, o["workspace"])
         x_out = torch.empty((BS, H), dtype=torch.bfloat16, device=dev)
+        if w.inter:
+            outs[0]["y"] = torch.empty_like(outs[0]["expand_x"])
         batches.append(dict(x=x, ids=ids, mask=mask, scales0=scales0, shared0=shared0, row_idx=row_idx,
                             outs=outs, x_out=x_out, ids0=ids[0].contiguous(), mask0=None if mask is None
                             else mask[0].contiguous(), row0=row_idx[0]))
     torch.cuda.synchronize()
+
+    ffn_w = None
+    if w.inter:
+        print("[bench] generating int8 expert weights", file=sys.stderr, flush=True)
+        fw = gen.ffn_weights(w, rank=0)
+        ffn_w = [torch.from_numpy(a).to(dev) for a in (fw.w1, fw.w1_scale, fw.w2, fw.w2_scale)]
+        ffn_ws = torch.empty(mdc.mdc_ffn_workspace_size(shape, w.inter), dtype=torch.uint8, device=dev)
+        del fw
 
     # Arguments are marshalled once per batch so the host loop stays ahead of the GPU.
     for bt in batches:
@@ -173,7 +196,13 @@ def main():
         bt["gather"] = mdc.prepare_dispatch_gather(shape, bt["x"], o0["expand_x"], o0["assist_info"],
                                                    o0["ep_recv_counts"], o0["expert_token_nums"], bt["row_idx"],
                                                    o0["workspace"], stream)
-        bt["combine"] = mdc.prepare_combine(shape, [o["expand_x"] for o in bt["outs"]],
+        seg0 = o0["expand_x"]
+        bt["ffn"] = None
+        if ffn_w is not None:
+            bt["ffn"] = mdc.prepare_ffn(shape, w.inter, o0["expand_x"], o0["expert_token_nums"], *ffn_w, o0["y"],
+                                        ffn_ws, stream)
+            seg0 = o0["y"]
+        bt["combine"] = mdc.prepare_combine(shape, [seg0] + [o["expand_x"] for o in bt["outs"][1:]],
                                             [o["assist_info"] for o in bt["outs"]],
                                             [o["ep_recv_counts"] for o in bt["outs"]], bt["row0"], bt["ids0"],
                                             bt["scales0"], bt["mask0"], bt["shared0"], bt["x_out"],
@@ -183,6 +212,8 @@ def main():
         if ev is None:
             bt["layout"]()
             bt["gather"]()
+            if bt["ffn"] is not None:
+                bt["ffn"]()
             bt["combine"]()
             return
         ev[0].record(stream)
@@ -190,6 +221,9 @@ def main():
         ev[1].record(stream)
         bt["gather"]()
         ev[2].record(stream)
+        if bt["ffn"] is not None:
+            bt["ffn"]()
+        ev[4].record(stream)
         bt["combine"]()
         ev[3].record(stream)
 
@@ -207,7 +241,7 @@ def main():
         step(batches[i % args.batches])
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -218,7 +252,8 @@ def main():
 
     t_layout = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]     # us
     t_gather = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
-    t_comb = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
+    t_ffn = [e[2].elapsed_time(e[4]) * 1e3 for e in evs]
+    t_comb = [e[4].elapsed_time(e[3]) * 1e3 for e in evs]
     t_step_ev = [e[0].elapsed_time(e[3]) * 1e3 for e in evs]
     ms_per_step = elapsed * 1e3 / args.steps
     by = algorithmic_bytes(w, wi.ids, wi.mask)
@@ -231,7 +266,22 @@ def main():
         dom = ("k_dispatch_gather", gb_gather, by["gather"], mean(t_gather))
     else:
         dom = ("k_combine", gb_comb, by["combine"], mean(t_comb))
+    ffn_info = None
+    if w.inter:
+        ops = 2.0 * by["R"] * (w.inter * H + H * (w.inter // 2))
+        tops = ops / (mean(t_ffn) * 1e-6) / 1e12
+        ffn_info = {"us": round(mean(t_ffn), 2), "median_us": round(statistics.median(t_ffn), 2),
+                    "int8_ops": ops, "tops": round(tops, 1), "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)}
 
+    roofline = {"bound": "hbm", "kernel": dom[0], "achieved": round(dom[1], 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(dom[1] / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(w.name, dom[0]),
+                "bytes_per_launch": dom[2], "avg_launch_us": round(dom[3], 3)}
+    if ffn_info is not None:
+        roofline = {"bound": "mfma", "kernel": "mdc_ffn (k_ffn_quant_rows + 2 x k_ffn_gemm)",
+                    "achieved": ffn_info["tops"], "peak": INT8_PEAK_TOPS, "unit": "TOP/s (int8)",
+                    "frac": ffn_info["mfma_frac"], "traffic": None, "ops_per_launch": ffn_info["int8_ops"],
+                    "avg_launch_us": ffn_info["us"]}
     result = {
         "metric": METRIC,
         "value": round(BS / (ms_per_step * 1e-3), 1),
@@ -251,25 +301,32 @@ def main():
         "hbm_gbps": round(gb_step, 1),
         "hbm_frac_of_peak": round(gb_step / HBM_PEAK_GBPS, 4),
         "step_bytes": step_bytes,
-        "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(dom[1], 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(dom[1] / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(w.name, dom[0]),
-                     "bytes_per_launch": dom[2], "avg_launch_us": round(dom[3], 3)},
+        "roofline": roofline,
         "kernels_us": {"dispatch_layout": round(mean(t_layout), 3), "dispatch_gather": round(mean(t_gather), 3),
                        "combine": round(mean(t_comb), 3), "step_events": round(mean(t_step_ev), 3),
                        "gather_gbps": round(gb_gather, 1), "combine_gbps": round(gb_comb, 1),
                        "gather_median": round(statistics.median(t_gather), 3),
                        "combine_median": round(statistics.median(t_comb), 3)},
     }
+    if ffn_info is not None:
+        result["ffn"] = ffn_info
 
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cb, segs, ref_out = cpu_baseline(wi, w, args.cpu_seconds)
-        cb["cores"] = 1
+        fw = gen.ffn_weights(w, rank=0) if w.inter else None
+        cb, segs, ref_out = cpu_baseline(wi, w, args.cpu_seconds, fw)
         result["cpu_baseline"] = cb
-        # the GPU's last step on batch 0 equals the oracle's step (same inputs)
+        # the GPU's last step on batch 0 has the oracle's inputs
         got = batches[0]["x_out"].view(torch.int16).cpu().numpy().view(np.uint16)
-        result["parity_vs_oracle"] = bool(np.array_equal(got, ref_out))
+        if fw is None:
+            result["parity_vs_oracle"] = bool(np.array_equal(got, ref_out))
+        else:
+            from oracle import mdc_oracle as O
+            a = O.bf16_to_f32(got).astype(np.float64)
+            b = O.bf16_to_f32(ref_out).astype(np.float64)
+            err = float(np.linalg.norm(a - b) / np.linalg.norm(b))
+            result["parity_vs_oracle"] = bool(err <= 2e-2)
+            result["rel_l2_vs_oracle"] = err
     print(json.dumps(result), flush=True)
 
 

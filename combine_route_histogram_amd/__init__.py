@@ -4,7 +4,7 @@ Argument marshalling only: every step of the path runs in the HIP kernels of
 libmdc.so, declared in include/mdc.h.  torch tensors are passed as device
 pointers; torch provides device memory and streams.  The functions carry the
 names of the C entry points.  Importing this package fails loudly when
-libmdc.so has not been built (python -m combine_route_histogram_amd.build).
+libmdc.so has not been built (python combine_route_histogram_amd/build.py).
 """
 from __future__ import annotations
 
@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmdc.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"libmdc.so not found at {LIB_PATH}; build it with "
-        "`python -m combine_route_histogram_amd.build` (hipcc, gfx950)")
+        "`python combine_route_histogram_amd/build.py` (hipcc, gfx950)")
 
 # torch provides device memory and streams.  Its wheel carries its own HIP
 # runtime (same SONAME, libamdhip64.so.7): loading torch first makes libmdc
@@ -41,6 +41,7 @@ EXPORTS = (
     "mdc_status_string", "mdc_abi_version",
     "mdc_dispatch_workspace_size", "mdc_dispatch_layout", "mdc_dispatch_gather", "mdc_dispatch",
     "mdc_combine_workspace_size", "mdc_combine",
+    "mdc_ffn_workspace_size", "mdc_ffn",
 )
 
 
@@ -70,6 +71,10 @@ _lib.mdc_combine_workspace_size.restype = ctypes.c_int
 _lib.mdc_combine_workspace_size.argtypes = [_SHP, ctypes.POINTER(_SZ)]
 _lib.mdc_combine.restype = ctypes.c_int
 _lib.mdc_combine.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.mdc_ffn_workspace_size.restype = ctypes.c_int
+_lib.mdc_ffn_workspace_size.argtypes = [_SHP, ctypes.c_int32, ctypes.POINTER(_SZ)]
+_lib.mdc_ffn.restype = ctypes.c_int
+_lib.mdc_ffn.argtypes = [_SHP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
 
 
 class MdcError(RuntimeError):
@@ -118,7 +123,8 @@ def _ptr(t) -> Optional[int]:
 
 
 def _nbytes(t) -> int:
-    if t is None:
+    """Size in bytes of a tensor argument; a raw integer pointer carries no size (0)."""
+    if t is None or isinstance(t, int):
         return 0
     return t.numel() * t.element_size()
 
@@ -203,6 +209,32 @@ def mdc_combine(shape: Shape, expand_x: Sequence, assist_info: Sequence, ep_recv
     if check:
         _check(st, "mdc_combine")
     return st
+
+
+def mdc_ffn_workspace_size(shape: Shape, inter_n: int) -> int:
+    out = _SZ(0)
+    sh = shape.c()
+    _check(_lib.mdc_ffn_workspace_size(ctypes.byref(sh), int(inter_n), ctypes.byref(out)), "mdc_ffn_workspace_size")
+    return int(out.value)
+
+
+def mdc_ffn(shape: Shape, inter_n: int, expand_x, expert_token_nums, w1, w1_scale, w2, w2_scale, y, workspace,
+            stream=None, check: bool = True) -> int:
+    sh = shape.c()
+    st = _lib.mdc_ffn(ctypes.byref(sh), int(inter_n), _ptr(expand_x), _ptr(expert_token_nums), _ptr(w1),
+                      _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(y), _ptr(workspace), _nbytes(workspace),
+                      _stream(stream))
+    if check:
+        _check(st, "mdc_ffn")
+    return st
+
+
+def prepare_ffn(shape: Shape, inter_n: int, expand_x, expert_token_nums, w1, w1_scale, w2, w2_scale, y,
+                workspace, stream=None) -> "Prepared":
+    sh = shape.c()
+    args = (ctypes.byref(sh), int(inter_n), _ptr(expand_x), _ptr(expert_token_nums), _ptr(w1), _ptr(w1_scale),
+            _ptr(w2), _ptr(w2_scale), _ptr(y), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    return Prepared(_lib.mdc_ffn, args, "mdc_ffn", (sh,))
 
 
 class Prepared:

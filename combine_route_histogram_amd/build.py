@@ -1,4 +1,7 @@
-"""Build libmdc.so (HIP, gfx950) in-tree: python -m combine_route_histogram_amd.build"""
+"""Build libmdc.so (HIP, gfx950) in-tree: python combine_route_histogram_amd/build.py
+
+Run it as a script (or load it by path): importing the package needs the built library.
+"""
 from __future__ import annotations
 
 import os

@@ -550,6 +550,257 @@ __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
 }
 
 // ---------------------------------------------------------------------------
+// a7: grouped int8 expert FFN ([PTO] GMM1 / SwiGLU / GMM2 stages).
+//
+// Per local expert e, on its expert-major rows of expand_x:
+//   q1, s1 = per-row int8 quantisation of x (amax / 127, round half even)
+//   h      = (q1 . W1[e]^T) * s1[row] * w1s[e][n]          (int32 MFMA accumulate)
+//   g      = silu(h[:, j]) * h[:, j + N/2],  j < N/2        (fused in GMM1's epilogue)
+//   q2, s2 = per-row int8 quantisation of g (quantised while GMM2 loads its tiles)
+//   y      = bf16((q2 . W2[e]^T) * s2[row] * w2s[e][h])
+// The GEMMs use v_mfma_i32_16x16x64_i8 on 256 x 128 output tiles (GMM1: 128
+// gate + 128 up weight rows per tile so gate and up land in the same lanes);
+// tiles are staged through LDS with a register prefetch of the next k step.
+// ---------------------------------------------------------------------------
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kFfnBM = 256;        // rows per tile
+constexpr int kFfnBN = 128;        // output columns per tile
+constexpr int kFfnBK = 64;         // k bytes per step (one MFMA k)
+constexpr int kFfnThreads = 512;   // 8 wavefronts: 4 along rows x 2 along columns
+constexpr int kLdsRow = 80;        // LDS row stride in bytes (64 + 16 pad)
+
+// Row range of m-tile `mblk`: experts' rows are contiguous (expert-major), each
+// expert split into tiles of kFfnBM rows; rows at or beyond A do not exist.
+__device__ bool ffn_tile_rows(const int64_t* __restrict__ expert_nums, int L, int64_t A, int mblk,
+                              int& e, int& row0, int& row_end) {
+  int64_t off = 0;
+  int t = 0;
+  for (int i = 0; i < L; ++i) {
+    const int64_t c = expert_nums[i];
+    const int64_t lo = off < A ? off : A;
+    const int64_t hi = (off + c) < A ? (off + c) : A;
+    const int tiles = (int)((hi - lo + kFfnBM - 1) / kFfnBM);
+    if (mblk < t + tiles) {
+      e = i;
+      row0 = (int)(lo + (int64_t)(mblk - t) * kFfnBM);
+      row_end = (int)hi;
+      return true;
+    }
+    t += tiles;
+    off += c;
+  }
+  return false;
+}
+
+__device__ __forceinline__ float ffn_silu(float a) { return a / (1.0f + __expf(-a)); }
+
+// Per-row int8 quantisation of bf16 rows (one wavefront per row), decided in
+// fp32 exactly as: amax = max|v|, inv = 127 / amax, q = clamp(rint(v * inv),
+// -127, 127), scale = amax / 127 (a zero row gives q = 0, scale = 0).  Also
+// clears the row's GMM2 amax word.
+__global__ __launch_bounds__(256) void k_ffn_quant_rows(
+    const v4u* __restrict__ x, int8_t* __restrict__ q, float* __restrict__ scale, uint32_t* __restrict__ amax2,
+    const int64_t* __restrict__ expert_nums, int L, int64_t A, int nvec) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  int64_t total = 0;
+  for (int i = 0; i < L; ++i) total += expert_nums[i];
+  if (row >= (total < A ? total : A)) return;
+  const v4u* xr = x + row * nvec;
+  float amax = 0.f;
+  for (int i = lane; i < nvec; i += 64) {
+    const v4u v = xr[i];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[w])), fabsf(bf16_hi(v[w]))));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+  uint64_t* qr = reinterpret_cast<uint64_t*>(q + row * (int64_t)nvec * 8);
+  for (int i = lane; i < nvec; i += 64) {
+    const v4u v = xr[i];
+    uint64_t packed = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = fminf(fmaxf(rintf(bf16_lo(v[w]) * inv), -127.f), 127.f);
+      const float b = fminf(fmaxf(rintf(bf16_hi(v[w]) * inv), -127.f), 127.f);
+      packed |= (uint64_t)(uint8_t)(int8_t)(int)a << (16 * w);
+      packed |= (uint64_t)(uint8_t)(int8_t)(int)b << (16 * w + 8);
+    }
+    qr[i] = packed;
+  }
+  if (lane == 0) {
+    scale[row] = amax / 127.0f;
+    amax2[row] = 0u;
+  }
+}
+
+// GLU = true: GMM1 (A = q1 int8, epilogue dequant + SwiGLU -> bf16 g, row amax).
+// GLU = false: GMM2 (A = bf16 g quantised on load with amax2, epilogue -> bf16 y).
+template <bool GLU>
+__global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(
+    const void* __restrict__ a_src, const float* __restrict__ row_scale, const uint32_t* __restrict__ amax_in,
+    const int8_t* __restrict__ w, const float* __restrict__ w_scale, uint16_t* __restrict__ out,
+    uint32_t* __restrict__ amax_out, const int64_t* __restrict__ expert_nums, int L, int64_t A,
+    int K, int Nw, int Nout) {
+  __shared__ __attribute__((aligned(16))) uint8_t As[kFfnBM * kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[(GLU ? 2 * kFfnBN : kFfnBN) * kLdsRow];
+  __shared__ int tile_info[3];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int wm = wv & 3;
+  const int wn = wv >> 2;
+  if (tid == 0) {
+    int e = 0, r0 = 0, re = 0;
+    if (!ffn_tile_rows(expert_nums, L, A, blockIdx.y, e, r0, re)) e = -1;
+    tile_info[0] = e;
+    tile_info[1] = r0;
+    tile_info[2] = re;
+  }
+  __syncthreads();
+  const int e = tile_info[0];
+  if (e < 0) return;
+  const int row0 = tile_info[1];
+  const int row_end = tile_info[2];
+  const int n0 = blockIdx.x * kFfnBN;
+
+  // Global -> register staging: thread t loads 32 k-bytes of A row t/2 and of
+  // B row t/2 (GLU: 256 B rows, gate then up) or 16 bytes of B row t/4.
+  const int a_r = tid >> 1;
+  const int a_k = (tid & 1) * 32;
+  const int64_t a_row = (int64_t)min(row0 + a_r, row_end - 1);
+  float a_inv = 0.f;
+  if (!GLU) {
+    const float am = __uint_as_float(amax_in[a_row]);
+    a_inv = am > 0.f ? 127.0f / am : 0.f;
+  }
+  int b_r, b_k;
+  int64_t b_row;
+  if (GLU) {
+    b_r = tid >> 1;
+    b_k = (tid & 1) * 32;
+    const int half = Nw / 2;
+    b_row = (int64_t)e * Nw + (b_r < kFfnBN ? n0 + b_r : half + n0 + (b_r - kFfnBN));
+  } else {
+    b_r = tid >> 2;
+    b_k = (tid & 3) * 16;
+    b_row = (int64_t)e * Nw + n0 + b_r;
+  }
+
+  v4i ra[2], rb[2];
+  auto load_tiles = [&](int k0) {
+    if (GLU) {
+      const int8_t* ap = static_cast<const int8_t*>(a_src) + a_row * K + k0 + a_k;
+      ra[0] = *reinterpret_cast<const v4i*>(ap);
+      ra[1] = *reinterpret_cast<const v4i*>(ap + 16);
+    } else {
+      // 32 bf16 of g -> 32 int8 codes, decided in fp32 like the row quantiser
+      const v4u* gp = reinterpret_cast<const v4u*>(static_cast<const uint16_t*>(a_src) + a_row * K + k0 + a_k);
+      v4u g4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g4[i] = gp[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        unsigned packed[2] = {0u, 0u};
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          const float a = fminf(fmaxf(rintf(bf16_lo(g4[i][w2]) * a_inv), -127.f), 127.f);
+          const float b = fminf(fmaxf(rintf(bf16_hi(g4[i][w2]) * a_inv), -127.f), 127.f);
+          const unsigned pair = (unsigned)(uint8_t)(int8_t)(int)a | ((unsigned)(uint8_t)(int8_t)(int)b << 8);
+          packed[w2 >> 1] |= pair << (16 * (w2 & 1));
+        }
+        reinterpret_cast<unsigned*>(ra)[2 * i] = packed[0];
+        reinterpret_cast<unsigned*>(ra)[2 * i + 1] = packed[1];
+      }
+    }
+    const int8_t* bp = w + b_row * K + k0 + b_k;
+    rb[0] = *reinterpret_cast<const v4i*>(bp);
+    if (GLU) rb[1] = *reinterpret_cast<const v4i*>(bp + 16);
+  };
+  auto store_tiles = [&]() {
+    *reinterpret_cast<v4i*>(As + a_r * kLdsRow + a_k) = ra[0];
+    *reinterpret_cast<v4i*>(As + a_r * kLdsRow + a_k + 16) = ra[1];
+    *reinterpret_cast<v4i*>(Bs + b_r * kLdsRow + b_k) = rb[0];
+    if (GLU) *reinterpret_cast<v4i*>(Bs + b_r * kLdsRow + b_k + 16) = rb[1];
+  };
+
+  constexpr int NJ = 4;  // 16-column MFMA tiles per wavefront (64 columns)
+  v4i acc[4][NJ];
+  v4i accu[4][NJ];  // GLU: up columns
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      acc[i][j] = v4i{0, 0, 0, 0};
+      accu[i][j] = v4i{0, 0, 0, 0};
+    }
+
+  const int nk = K / kFfnBK;
+  load_tiles(0);
+  const int frag_off = (lane & 15) * kLdsRow + 16 * (lane >> 4);
+  for (int ks = 0; ks < nk; ++ks) {
+    __syncthreads();
+    store_tiles();
+    __syncthreads();
+    if (ks + 1 < nk) load_tiles((ks + 1) * kFfnBK);
+    v4i af[4], bf[NJ], bu[NJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const v4i*>(As + (wm * 64 + 16 * i) * kLdsRow + frag_off);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      bf[j] = *reinterpret_cast<const v4i*>(Bs + (wn * 64 + 16 * j) * kLdsRow + frag_off);
+      if (GLU) bu[j] = *reinterpret_cast<const v4i*>(Bs + (kFfnBN + wn * 64 + 16 * j) * kLdsRow + frag_off);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        if (GLU) accu[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bu[j], accu[i][j], 0, 0, 0);
+      }
+  }
+
+  // Epilogue.  Lane l holds rows 4*(l/16) + jj of each 16 x 16 tile, column l % 16.
+  const float* wsc = w_scale + (int64_t)e * Nw;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int row = row0 + wm * 64 + 16 * i + 4 * (lane >> 4) + jj;
+      const bool live = row < row_end;
+      const int64_t rowc = live ? row : row_end - 1;
+      float rs;
+      if (GLU) rs = row_scale[rowc];
+      else rs = __uint_as_float(amax_in[rowc]) / 127.0f;
+      float rmax = 0.f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int col = n0 + wn * 64 + 16 * j + (lane & 15);
+        float v;
+        if (GLU) {
+          const float hg = (float)acc[i][j][jj] * rs * wsc[col];
+          const float hu = (float)accu[i][j][jj] * rs * wsc[Nw / 2 + col];
+          v = ffn_silu(hg) * hu;
+        } else {
+          v = (float)acc[i][j][jj] * rs * wsc[col];
+        }
+        const unsigned b = bf16_rne(v);
+        if (live) out[rowc * Nout + col] = (uint16_t)b;
+        if (GLU) rmax = fmaxf(rmax, fabsf(__uint_as_float(b << 16)));
+      }
+      if (GLU) {
+        // the 16 lanes of this row hold consecutive columns: reduce, one atomic per row
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o, 64));
+        if (live && (lane & 15) == 0) atomicMax(&amax_out[rowc], __float_as_uint(rmax));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -642,6 +893,36 @@ mdc_status gather_impl(const DispatchPlan& p, const void* x, void* expand_x, int
   }
 #undef MDC_LAUNCH_GATHER
   return launched();
+}
+
+struct FfnPlan {
+  int64_t A;
+  int H, N, L;
+  size_t off_q1, off_s1, off_g, off_amax2, bytes;
+};
+
+FfnPlan make_ffn_plan(const mdc_shape* sh, int inter_n) {
+  FfnPlan f;
+  f.A = sh->capacity;
+  f.H = sh->hidden;
+  f.N = inter_n;
+  f.L = sh->num_experts / sh->world;
+  f.off_q1 = 0;
+  f.off_s1 = round_up((size_t)f.A * f.H, 256);
+  f.off_g = f.off_s1 + round_up((size_t)f.A * 4, 256);
+  f.off_amax2 = f.off_g + round_up((size_t)f.A * (f.N / 2) * 2, 256);
+  f.bytes = f.off_amax2 + round_up((size_t)f.A * 4, 256);
+  if (f.bytes == 0) f.bytes = 256;
+  return f;
+}
+
+mdc_status check_ffn(const mdc_shape* sh, int inter_n) {
+  const mdc_status st = check_shape(sh);
+  if (st != MDC_OK) return st;
+  if (inter_n <= 0 || (inter_n % (2 * kFfnBN)) != 0) return MDC_ERR_INVALID;
+  if ((sh->hidden % kFfnBN) != 0) return MDC_ERR_INVALID;
+  if ((int64_t)(sh->capacity + kFfnBM - 1) / kFfnBM + sh->num_experts / sh->world > 65535) return MDC_ERR_INVALID;
+  return MDC_OK;
 }
 
 }  // namespace
@@ -780,6 +1061,46 @@ mdc_status mdc_combine(const mdc_shape* shape, const void* const* expand_x, cons
       hipLaunchKernelGGL((k_combine<16, 1, false>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
                          expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles, n_items);
   }
+  return launched();
+}
+
+mdc_status mdc_ffn_workspace_size(const mdc_shape* shape, int32_t inter_n, size_t* bytes) {
+  if (bytes == nullptr) return MDC_ERR_NULLPTR;
+  const mdc_status st = check_ffn(shape, inter_n);
+  if (st != MDC_OK) return st;
+  *bytes = make_ffn_plan(shape, inter_n).bytes;
+  return MDC_OK;
+}
+
+mdc_status mdc_ffn(const mdc_shape* shape, int32_t inter_n, const void* expand_x, const int64_t* expert_token_nums,
+                   const int8_t* w1, const float* w1_scale, const int8_t* w2, const float* w2_scale, void* y,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  mdc_status st = check_ffn(shape, inter_n);
+  if (st != MDC_OK) return st;
+  const FfnPlan f = make_ffn_plan(shape, inter_n);
+  if (f.A == 0) return MDC_OK;
+  if (expand_x == nullptr || expert_token_nums == nullptr || w1 == nullptr || w1_scale == nullptr ||
+      w2 == nullptr || w2_scale == nullptr || y == nullptr || workspace == nullptr)
+    return MDC_ERR_NULLPTR;
+  if (!aligned16(expand_x) || !aligned16(w1) || !aligned16(w2) || !aligned16(y)) return MDC_ERR_INVALID;
+  if (workspace_bytes < f.bytes) return MDC_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  int8_t* q1 = reinterpret_cast<int8_t*>(ws + f.off_q1);
+  float* s1 = reinterpret_cast<float*>(ws + f.off_s1);
+  uint16_t* g = reinterpret_cast<uint16_t*>(ws + f.off_g);
+  uint32_t* amax2 = reinterpret_cast<uint32_t*>(ws + f.off_amax2);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const unsigned m_tiles = (unsigned)((f.A + kFfnBM - 1) / kFfnBM + f.L);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_ffn_quant_rows, dim3((unsigned)((f.A + 3) / 4)), dim3(256), 0, s,
+                     static_cast<const v4u*>(expand_x), q1, s1, amax2, expert_token_nums, f.L, f.A, f.H / 8);
+  hipLaunchKernelGGL(k_ffn_gemm<true>, dim3(f.N / 2 / kFfnBN, m_tiles), dim3(kFfnThreads), 0, s,
+                     static_cast<const void*>(q1), s1, static_cast<const uint32_t*>(nullptr), w1, w1_scale, g, amax2,
+                     expert_token_nums, f.L, f.A, f.H, f.N, f.N / 2);
+  hipLaunchKernelGGL(k_ffn_gemm<false>, dim3(f.H / kFfnBN, m_tiles), dim3(kFfnThreads), 0, s,
+                     static_cast<const void*>(g), static_cast<const float*>(nullptr), amax2, w2, w2_scale,
+                     static_cast<uint16_t*>(y), static_cast<uint32_t*>(nullptr), expert_token_nums, f.L, f.A, f.N / 2,
+                     f.H, f.H);
   return launched();
 }
 

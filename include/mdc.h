@@ -207,6 +207,45 @@ mdc_status mdc_combine(const mdc_shape* shape,
                        void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* ------------------------------------------------------------------------
+ * Grouped int8 expert FFN ([PTO] GMM1 / SwiGLU / GMM2 stages; Specification:
+ * int8 weights with per-channel scales; Tiling Parameters: N is GMM1's output
+ * width and GMM2 consumes N/2 after SwiGLU).
+ *
+ * For every row of expand_x (rows [0, min(sum(expert_token_nums), A)), grouped
+ * by local expert in expert-major order as dispatch lays them out), with e the
+ * row's local expert:
+ *   q1, s1 = per-row int8 quantisation of x: amax = max|x|, codes
+ *            clamp(rint(x * (127 / amax)), -127, 127), s1 = amax / 127,
+ *            decided in fp32 (a zero row gives codes 0 and s1 = 0)
+ *   h      = (q1 . w1[e]^T) * s1 * w1_scale[e][n]      int32 accumulate, n < N
+ *   g      = silu(h[:, j]) * h[:, j + N/2], j < N/2, stored as bf16 (RNE)
+ *   q2, s2 = per-row int8 quantisation of g, as for x
+ *   y      = bf16_rne((q2 . w2[e]^T) * s2 * w2_scale[e][c]),  c < H
+ * silu(a) = a / (1 + exp(-a)).  Which half goes through silu, the quantiser
+ * and the intermediate precisions are this library's readings; the pages
+ * name the stages and their order.
+ *
+ * Inputs (device): expand_x [A][H] bf16, expert_token_nums [L] int64 (from
+ *   dispatch), w1 [L][N][H] int8, w1_scale [L][N] fp32, w2 [L][H][N/2] int8,
+ *   w2_scale [L][H] fp32.   Output: y [A][H] bf16 (rows past the total are
+ *   untouched).  inter_n = N must be a positive multiple of 256 and H a
+ *   multiple of 128.
+ * ------------------------------------------------------------------------ */
+mdc_status mdc_ffn_workspace_size(const mdc_shape* shape, int32_t inter_n, size_t* bytes);
+
+mdc_status mdc_ffn(const mdc_shape* shape,
+                   int32_t inter_n,
+                   const void* expand_x,
+                   const int64_t* expert_token_nums,
+                   const int8_t* w1,
+                   const float* w1_scale,
+                   const int8_t* w2,
+                   const float* w2_scale,
+                   void* y,
+                   void* workspace, size_t workspace_bytes,
+                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -105,6 +105,22 @@ def test_misaligned_rows_rejected():
     assert st == mdc.MDC_ERR_INVALID
 
 
+def test_ffn_shape_checks():
+    ok = mdc.Shape(world=8, rank=0, bs=2048, hidden=7168, topk=8, num_experts=128, capacity=131072)
+    assert mdc.mdc_ffn_workspace_size(ok, 4096) > 131072 * 7168
+    for inter in (0, 100, 4096 + 128):
+        with pytest.raises(mdc.MdcError) as ei:
+            mdc.mdc_ffn_workspace_size(ok, inter)
+        assert ei.value.status == mdc.MDC_ERR_INVALID
+    bad_h = mdc.Shape(world=8, rank=0, bs=16, hidden=7176, topk=8, num_experts=128, capacity=1024)
+    with pytest.raises(mdc.MdcError):
+        mdc.mdc_ffn_workspace_size(bad_h, 4096)
+    fake = 1 << 20
+    with pytest.raises(mdc.MdcError) as ei:
+        mdc.mdc_ffn(ok, 4096, fake, None, fake, fake, fake, fake, fake, fake)
+    assert ei.value.status == mdc.MDC_ERR_NULLPTR
+
+
 def test_combine_world_limit_and_nulls():
     big = mdc.Shape(world=65, rank=0, bs=4, hidden=64, topk=2, num_experts=65, capacity=16)
     fake = 1 << 20
