@@ -570,9 +570,23 @@ constexpr int kFfnBK = 64;         // k bytes per step (one MFMA k)
 constexpr int kFfnThreads = 512;   // 8 wavefronts: 4 along rows x 2 along columns
 constexpr int kLdsRow = 80;        // LDS row stride in bytes (64 + 16 pad)
 
-// Row range of m-tile `mblk`: experts' rows are contiguous (expert-major), each
-// expert split into tiles of kFfnBM rows; rows at or beyond A do not exist.
-__device__ bool ffn_tile_rows(const int64_t* __restrict__ expert_nums, int L, int64_t A, int mblk,
+// Number of m-tiles over all experts: each expert's rows (contiguous,
+// expert-major, clipped at A) split into tiles of kFfnBM rows.
+__device__ int ffn_total_mtiles(const int64_t* __restrict__ expert_nums, int L, int64_t A) {
+  int64_t off = 0;
+  int t = 0;
+  for (int i = 0; i < L; ++i) {
+    const int64_t c = expert_nums[i];
+    const int64_t lo = off < A ? off : A;
+    const int64_t hi = (off + c) < A ? (off + c) : A;
+    t += (int)((hi - lo + kFfnBM - 1) / kFfnBM);
+    off += c;
+  }
+  return t;
+}
+
+// Row range of m-tile `mblk`.
+__device__ void ffn_tile_rows(const int64_t* __restrict__ expert_nums, int L, int64_t A, int mblk,
                               int& e, int& row0, int& row_end) {
   int64_t off = 0;
   int t = 0;
@@ -585,216 +599,234 @@ __device__ bool ffn_tile_rows(const int64_t* __restrict__ expert_nums, int L, in
       e = i;
       row0 = (int)(lo + (int64_t)(mblk - t) * kFfnBM);
       row_end = (int)hi;
-      return true;
+      return;
     }
     t += tiles;
     off += c;
   }
-  return false;
+  e = -1;
+  row0 = row_end = 0;
 }
 
 __device__ __forceinline__ float ffn_silu(float a) { return a / (1.0f + __expf(-a)); }
 
-// Per-row int8 quantisation of bf16 rows (one wavefront per row), decided in
-// fp32 exactly as: amax = max|v|, inv = 127 / amax, q = clamp(rint(v * inv),
-// -127, 127), scale = amax / 127 (a zero row gives q = 0, scale = 0).  Also
-// clears the row's GMM2 amax word.
+// Per-row int8 quantisation of bf16 rows of `width` elements, decided in fp32
+// exactly as: amax = max|v|, inv = 127 / amax, q = clamp(rint(v * inv), -127,
+// 127), scale = amax / 127 (a zero row gives q = 0, scale = 0).  One
+// wavefront per row, rows [0, min(sum(expert_nums), A)) visited grid-stride;
+// rows of up to 64 * kQuantVec vectors stay in registers between the passes.
+constexpr int kQuantVec = 16;
 __global__ __launch_bounds__(256) void k_ffn_quant_rows(
-    const v4u* __restrict__ x, int8_t* __restrict__ q, float* __restrict__ scale, uint32_t* __restrict__ amax2,
+    const v4u* __restrict__ x, int8_t* __restrict__ q, float* __restrict__ scale,
     const int64_t* __restrict__ expert_nums, int L, int64_t A, int nvec) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * 4;
   int64_t total = 0;
   for (int i = 0; i < L; ++i) total += expert_nums[i];
-  if (row >= (total < A ? total : A)) return;
-  const v4u* xr = x + row * nvec;
-  float amax = 0.f;
-  for (int i = lane; i < nvec; i += 64) {
-    const v4u v = xr[i];
+  const int64_t rows = total < A ? total : A;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += nw) {
+    const v4u* xr = x + row * nvec;
+    uint64_t* qr = reinterpret_cast<uint64_t*>(q + row * (int64_t)nvec * 8);
+    v4u cache[kQuantVec];
+    float amax = 0.f;
+    if (nvec <= 64 * kQuantVec) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[w])), fabsf(bf16_hi(v[w]))));
-  }
+      for (int u = 0; u < kQuantVec; ++u) {
+        const int i = lane + 64 * u;
+        cache[u] = i < nvec ? xr[i] : v4u{0u, 0u, 0u, 0u};
+      }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-  const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-  uint64_t* qr = reinterpret_cast<uint64_t*>(q + row * (int64_t)nvec * 8);
-  for (int i = lane; i < nvec; i += 64) {
-    const v4u v = xr[i];
-    uint64_t packed = 0;
+      for (int u = 0; u < kQuantVec; ++u)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float a = fminf(fmaxf(rintf(bf16_lo(v[w]) * inv), -127.f), 127.f);
-      const float b = fminf(fmaxf(rintf(bf16_hi(v[w]) * inv), -127.f), 127.f);
-      packed |= (uint64_t)(uint8_t)(int8_t)(int)a << (16 * w);
-      packed |= (uint64_t)(uint8_t)(int8_t)(int)b << (16 * w + 8);
+        for (int w = 0; w < 4; ++w)
+          amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(cache[u][w])), fabsf(bf16_hi(cache[u][w]))));
+    } else {
+      for (int i = lane; i < nvec; i += 64) {
+        const v4u v = xr[i];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[w])), fabsf(bf16_hi(v[w]))));
+      }
     }
-    qr[i] = packed;
-  }
-  if (lane == 0) {
-    scale[row] = amax / 127.0f;
-    amax2[row] = 0u;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+    auto quant8 = [&](const v4u& v) {
+      uint64_t packed = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float a = fminf(fmaxf(rintf(bf16_lo(v[w]) * inv), -127.f), 127.f);
+        const float b = fminf(fmaxf(rintf(bf16_hi(v[w]) * inv), -127.f), 127.f);
+        packed |= (uint64_t)(uint8_t)(int8_t)(int)a << (16 * w);
+        packed |= (uint64_t)(uint8_t)(int8_t)(int)b << (16 * w + 8);
+      }
+      return packed;
+    };
+    if (nvec <= 64 * kQuantVec) {
+#pragma unroll
+      for (int u = 0; u < kQuantVec; ++u) {
+        const int i = lane + 64 * u;
+        if (i < nvec) qr[i] = quant8(cache[u]);
+      }
+    } else {
+      for (int i = lane; i < nvec; i += 64) qr[i] = quant8(xr[i]);
+    }
+    if (lane == 0) scale[row] = amax / 127.0f;
   }
 }
 
-// GLU = true: GMM1 (A = q1 int8, epilogue dequant + SwiGLU -> bf16 g, row amax).
-// GLU = false: GMM2 (A = bf16 g quantised on load with amax2, epilogue -> bf16 y).
+// Persistent grouped GEMM, C = A . W[e]^T with A int8 [rows][K] and W int8
+// [L][Nw][K].  GLU = true (GMM1): each output tile pairs 128 gate rows of W
+// (columns n) with the 128 up rows (columns N/2 + n); the epilogue dequantises
+// both, applies silu(gate) * up and writes bf16 g.  GLU = false (GMM2): the
+// epilogue dequantises and writes bf16 y.  Dequant: acc * row_scale[row] *
+// w_scale[e][col].
+//
+// Tiles: T = (m-tiles over all experts) x (Nout / 128).  The launch holds one
+// workgroup per resident slot; workgroup b walks tiles i*G + (b % 8)*(G/8) +
+// b / 8.  Hardware places workgroup b on XCD b % 8, so each XCD walks a
+// contiguous run of tiles; tiles are ordered in groups of 4 m-tiles x 8
+// n-tiles (m fastest), so the 32 tiles an XCD runs together share 4 A tiles
+// and 8 W tiles in its L2.
 template <bool GLU>
 __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(
-    const void* __restrict__ a_src, const float* __restrict__ row_scale, const uint32_t* __restrict__ amax_in,
+    const int8_t* __restrict__ a_src, const float* __restrict__ row_scale,
     const int8_t* __restrict__ w, const float* __restrict__ w_scale, uint16_t* __restrict__ out,
-    uint32_t* __restrict__ amax_out, const int64_t* __restrict__ expert_nums, int L, int64_t A,
-    int K, int Nw, int Nout) {
+    const int64_t* __restrict__ expert_nums, int L, int64_t A, int K, int Nw, int Nout) {
   __shared__ __attribute__((aligned(16))) uint8_t As[kFfnBM * kLdsRow];
   __shared__ __attribute__((aligned(16))) uint8_t Bs[(GLU ? 2 * kFfnBN : kFfnBN) * kLdsRow];
-  __shared__ int tile_info[3];
+  __shared__ int tile_info[4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
   const int wm = wv & 3;
   const int wn = wv >> 2;
-  if (tid == 0) {
-    int e = 0, r0 = 0, re = 0;
-    if (!ffn_tile_rows(expert_nums, L, A, blockIdx.y, e, r0, re)) e = -1;
-    tile_info[0] = e;
-    tile_info[1] = r0;
-    tile_info[2] = re;
-  }
+  const int G = gridDim.x;
+  const int nn = Nout / kFfnBN;
+  constexpr int GM = 4, GN = 8;
+  if (tid == 0) tile_info[3] = ffn_total_mtiles(expert_nums, L, A);
   __syncthreads();
-  const int e = tile_info[0];
-  if (e < 0) return;
-  const int row0 = tile_info[1];
-  const int row_end = tile_info[2];
-  const int n0 = blockIdx.x * kFfnBN;
+  const int MT = tile_info[3];
+  const int64_t T = (int64_t)MT * nn;
+  const int b = blockIdx.x;
+  const int lin = (b % 8) * (G / 8) + b / 8;   // XCD-contiguous walk (G is a multiple of 8)
 
-  // Global -> register staging: thread t loads 32 k-bytes of A row t/2 and of
-  // B row t/2 (GLU: 256 B rows, gate then up) or 16 bytes of B row t/4.
-  const int a_r = tid >> 1;
-  const int a_k = (tid & 1) * 32;
-  const int64_t a_row = (int64_t)min(row0 + a_r, row_end - 1);
-  float a_inv = 0.f;
-  if (!GLU) {
-    const float am = __uint_as_float(amax_in[a_row]);
-    a_inv = am > 0.f ? 127.0f / am : 0.f;
-  }
-  int b_r, b_k;
-  int64_t b_row;
-  if (GLU) {
-    b_r = tid >> 1;
-    b_k = (tid & 1) * 32;
-    const int half = Nw / 2;
-    b_row = (int64_t)e * Nw + (b_r < kFfnBN ? n0 + b_r : half + n0 + (b_r - kFfnBN));
-  } else {
-    b_r = tid >> 2;
-    b_k = (tid & 3) * 16;
-    b_row = (int64_t)e * Nw + n0 + b_r;
-  }
+  for (int64_t t = lin; t < T; t += G) {
+    // tile t -> (m-tile, n-tile): groups of GM m-tiles x GN n-tiles, m fastest
+    const int64_t band = (int64_t)GM * nn;
+    const int64_t mg = t / band;
+    const int64_t r = t - mg * band;
+    const int m_in_group = (int)min((int64_t)GM, (int64_t)MT - mg * GM);
+    const int64_t per_ng = (int64_t)m_in_group * GN;
+    const int64_t ng = r / per_ng;
+    const int64_t r2 = r - ng * per_ng;
+    const int n_in_group = (int)min((int64_t)GN, (int64_t)nn - ng * GN);
+    const int mt = (int)(mg * GM + r2 % m_in_group);
+    const int nt = (int)(ng * GN + (r2 / m_in_group) % n_in_group);
+    __syncthreads();
+    if (tid == 0) {
+      int e, r0, re;
+      ffn_tile_rows(expert_nums, L, A, mt, e, r0, re);
+      tile_info[0] = e;
+      tile_info[1] = r0;
+      tile_info[2] = re;
+    }
+    __syncthreads();
+    const int e = tile_info[0];
+    if (e < 0) continue;
+    const int row0 = tile_info[1];
+    const int row_end = tile_info[2];
+    const int n0 = nt * kFfnBN;
 
-  v4i ra[2], rb[2];
-  auto load_tiles = [&](int k0) {
+    // Global -> register staging: thread t loads 32 k-bytes of A row t/2 and of
+    // W row t/2 (GLU: 256 rows, gate then up) or 16 bytes of W row t/4.
+    const int a_r = tid >> 1;
+    const int a_k = (tid & 1) * 32;
+    const int64_t a_row = (int64_t)min(row0 + a_r, row_end - 1);
+    int b_r, b_k;
+    int64_t b_row;
     if (GLU) {
-      const int8_t* ap = static_cast<const int8_t*>(a_src) + a_row * K + k0 + a_k;
-      ra[0] = *reinterpret_cast<const v4i*>(ap);
-      ra[1] = *reinterpret_cast<const v4i*>(ap + 16);
+      b_r = tid >> 1;
+      b_k = (tid & 1) * 32;
+      b_row = (int64_t)e * Nw + (b_r < kFfnBN ? n0 + b_r : Nw / 2 + n0 + (b_r - kFfnBN));
     } else {
-      // 32 bf16 of g -> 32 int8 codes, decided in fp32 like the row quantiser
-      const v4u* gp = reinterpret_cast<const v4u*>(static_cast<const uint16_t*>(a_src) + a_row * K + k0 + a_k);
-      v4u g4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) g4[i] = gp[i];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        unsigned packed[2] = {0u, 0u};
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          const float a = fminf(fmaxf(rintf(bf16_lo(g4[i][w2]) * a_inv), -127.f), 127.f);
-          const float b = fminf(fmaxf(rintf(bf16_hi(g4[i][w2]) * a_inv), -127.f), 127.f);
-          const unsigned pair = (unsigned)(uint8_t)(int8_t)(int)a | ((unsigned)(uint8_t)(int8_t)(int)b << 8);
-          packed[w2 >> 1] |= pair << (16 * (w2 & 1));
-        }
-        reinterpret_cast<unsigned*>(ra)[2 * i] = packed[0];
-        reinterpret_cast<unsigned*>(ra)[2 * i + 1] = packed[1];
-      }
+      b_r = tid >> 2;
+      b_k = (tid & 3) * 16;
+      b_row = (int64_t)e * Nw + n0 + b_r;
     }
-    const int8_t* bp = w + b_row * K + k0 + b_k;
-    rb[0] = *reinterpret_cast<const v4i*>(bp);
-    if (GLU) rb[1] = *reinterpret_cast<const v4i*>(bp + 16);
-  };
-  auto store_tiles = [&]() {
-    *reinterpret_cast<v4i*>(As + a_r * kLdsRow + a_k) = ra[0];
-    *reinterpret_cast<v4i*>(As + a_r * kLdsRow + a_k + 16) = ra[1];
-    *reinterpret_cast<v4i*>(Bs + b_r * kLdsRow + b_k) = rb[0];
-    if (GLU) *reinterpret_cast<v4i*>(Bs + b_r * kLdsRow + b_k + 16) = rb[1];
-  };
+    const int8_t* ap = a_src + a_row * K + a_k;
+    const int8_t* bp = w + b_row * K + b_k;
+    v4i ra[2], rb[2];
+    auto load_tiles = [&](int k0) {
+      ra[0] = *reinterpret_cast<const v4i*>(ap + k0);
+      ra[1] = *reinterpret_cast<const v4i*>(ap + k0 + 16);
+      rb[0] = *reinterpret_cast<const v4i*>(bp + k0);
+      if (GLU) rb[1] = *reinterpret_cast<const v4i*>(bp + k0 + 16);
+    };
+    auto store_tiles = [&]() {
+      *reinterpret_cast<v4i*>(As + a_r * kLdsRow + a_k) = ra[0];
+      *reinterpret_cast<v4i*>(As + a_r * kLdsRow + a_k + 16) = ra[1];
+      *reinterpret_cast<v4i*>(Bs + b_r * kLdsRow + b_k) = rb[0];
+      if (GLU) *reinterpret_cast<v4i*>(Bs + b_r * kLdsRow + b_k + 16) = rb[1];
+    };
 
-  constexpr int NJ = 4;  // 16-column MFMA tiles per wavefront (64 columns)
-  v4i acc[4][NJ];
-  v4i accu[4][NJ];  // GLU: up columns
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      acc[i][j] = v4i{0, 0, 0, 0};
-      accu[i][j] = v4i{0, 0, 0, 0};
-    }
-
-  const int nk = K / kFfnBK;
-  load_tiles(0);
-  const int frag_off = (lane & 15) * kLdsRow + 16 * (lane >> 4);
-  for (int ks = 0; ks < nk; ++ks) {
-    __syncthreads();
-    store_tiles();
-    __syncthreads();
-    if (ks + 1 < nk) load_tiles((ks + 1) * kFfnBK);
-    v4i af[4], bf[NJ], bu[NJ];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const v4i*>(As + (wm * 64 + 16 * i) * kLdsRow + frag_off);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      bf[j] = *reinterpret_cast<const v4i*>(Bs + (wn * 64 + 16 * j) * kLdsRow + frag_off);
-      if (GLU) bu[j] = *reinterpret_cast<const v4i*>(Bs + (kFfnBN + wn * 64 + 16 * j) * kLdsRow + frag_off);
-    }
+    constexpr int NJ = 4;  // 16-column MFMA tiles per wavefront (64 columns)
+    v4i acc[4][NJ];
+    v4i accu[4][NJ];  // GLU: up columns
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-        if (GLU) accu[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bu[j], accu[i][j], 0, 0, 0);
+        acc[i][j] = v4i{0, 0, 0, 0};
+        accu[i][j] = v4i{0, 0, 0, 0};
       }
-  }
 
-  // Epilogue.  Lane l holds rows 4*(l/16) + jj of each 16 x 16 tile, column l % 16.
-  const float* wsc = w_scale + (int64_t)e * Nw;
+    const int nk = K / kFfnBK;
+    load_tiles(0);
+    const int frag_off = (lane & 15) * kLdsRow + 16 * (lane >> 4);
+    for (int ks = 0; ks < nk; ++ks) {
+      __syncthreads();
+      store_tiles();
+      __syncthreads();
+      if (ks + 1 < nk) load_tiles((ks + 1) * kFfnBK);
+      v4i af[4], bf[NJ], bu[NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int row = row0 + wm * 64 + 16 * i + 4 * (lane >> 4) + jj;
-      const bool live = row < row_end;
-      const int64_t rowc = live ? row : row_end - 1;
-      float rs;
-      if (GLU) rs = row_scale[rowc];
-      else rs = __uint_as_float(amax_in[rowc]) / 127.0f;
-      float rmax = 0.f;
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const v4i*>(As + (wm * 64 + 16 * i) * kLdsRow + frag_off);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int col = n0 + wn * 64 + 16 * j + (lane & 15);
-        float v;
-        if (GLU) {
-          const float hg = (float)acc[i][j][jj] * rs * wsc[col];
-          const float hu = (float)accu[i][j][jj] * rs * wsc[Nw / 2 + col];
-          v = ffn_silu(hg) * hu;
-        } else {
-          v = (float)acc[i][j][jj] * rs * wsc[col];
-        }
-        const unsigned b = bf16_rne(v);
-        if (live) out[rowc * Nout + col] = (uint16_t)b;
-        if (GLU) rmax = fmaxf(rmax, fabsf(__uint_as_float(b << 16)));
+        bf[j] = *reinterpret_cast<const v4i*>(Bs + (wn * 64 + 16 * j) * kLdsRow + frag_off);
+        if (GLU) bu[j] = *reinterpret_cast<const v4i*>(Bs + (kFfnBN + wn * 64 + 16 * j) * kLdsRow + frag_off);
       }
-      if (GLU) {
-        // the 16 lanes of this row hold consecutive columns: reduce, one atomic per row
 #pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o, 64));
-        if (live && (lane & 15) == 0) atomicMax(&amax_out[rowc], __float_as_uint(rmax));
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+          if (GLU) accu[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bu[j], accu[i][j], 0, 0, 0);
+        }
+    }
+
+    // Epilogue.  Lane l holds rows 4*(l/16) + jj of each 16 x 16 tile, column l % 16.
+    const float* wsc = w_scale + (int64_t)e * Nw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int row = row0 + wm * 64 + 16 * i + 4 * (lane >> 4) + jj;
+        if (row >= row_end) continue;
+        const float rs = row_scale[row];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int col = n0 + wn * 64 + 16 * j + (lane & 15);
+          float v;
+          if (GLU) {
+            const float hg = (float)acc[i][j][jj] * rs * wsc[col];
+            const float hu = (float)accu[i][j][jj] * rs * wsc[Nw / 2 + col];
+            v = ffn_silu(hg) * hu;
+          } else {
+            v = (float)acc[i][j][jj] * rs * wsc[col];
+          }
+          out[(int64_t)row * Nout + col] = (uint16_t)bf16_rne(v);
+        }
       }
     }
   }
@@ -898,7 +930,7 @@ mdc_status gather_impl(const DispatchPlan& p, const void* x, void* expand_x, int
 struct FfnPlan {
   int64_t A;
   int H, N, L;
-  size_t off_q1, off_s1, off_g, off_amax2, bytes;
+  size_t off_q1, off_s1, off_g, off_q2, off_s2, bytes;
 };
 
 FfnPlan make_ffn_plan(const mdc_shape* sh, int inter_n) {
@@ -910,8 +942,9 @@ FfnPlan make_ffn_plan(const mdc_shape* sh, int inter_n) {
   f.off_q1 = 0;
   f.off_s1 = round_up((size_t)f.A * f.H, 256);
   f.off_g = f.off_s1 + round_up((size_t)f.A * 4, 256);
-  f.off_amax2 = f.off_g + round_up((size_t)f.A * (f.N / 2) * 2, 256);
-  f.bytes = f.off_amax2 + round_up((size_t)f.A * 4, 256);
+  f.off_q2 = f.off_g + round_up((size_t)f.A * (f.N / 2) * 2, 256);
+  f.off_s2 = f.off_q2 + round_up((size_t)f.A * (f.N / 2), 256);
+  f.bytes = f.off_s2 + round_up((size_t)f.A * 4, 256);
   if (f.bytes == 0) f.bytes = 256;
   return f;
 }
@@ -921,7 +954,6 @@ mdc_status check_ffn(const mdc_shape* sh, int inter_n) {
   if (st != MDC_OK) return st;
   if (inter_n <= 0 || (inter_n % (2 * kFfnBN)) != 0) return MDC_ERR_INVALID;
   if ((sh->hidden % kFfnBN) != 0) return MDC_ERR_INVALID;
-  if ((int64_t)(sh->capacity + kFfnBM - 1) / kFfnBM + sh->num_experts / sh->world > 65535) return MDC_ERR_INVALID;
   return MDC_OK;
 }
 
@@ -1088,19 +1120,24 @@ mdc_status mdc_ffn(const mdc_shape* shape, int32_t inter_n, const void* expand_x
   int8_t* q1 = reinterpret_cast<int8_t*>(ws + f.off_q1);
   float* s1 = reinterpret_cast<float*>(ws + f.off_s1);
   uint16_t* g = reinterpret_cast<uint16_t*>(ws + f.off_g);
-  uint32_t* amax2 = reinterpret_cast<uint32_t*>(ws + f.off_amax2);
+  int8_t* q2 = reinterpret_cast<int8_t*>(ws + f.off_q2);
+  float* s2 = reinterpret_cast<float*>(ws + f.off_s2);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const unsigned m_tiles = (unsigned)((f.A + kFfnBM - 1) / kFfnBM + f.L);
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const unsigned quant_wgs = (unsigned)(cus * 8);
+  // one 8-wavefront workgroup per CU (both GEMMs need more than 128 VGPRs)
+  const unsigned g1 = (unsigned)(((cus + 7) / 8) * 8);
+  const unsigned g2 = g1;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(k_ffn_quant_rows, dim3((unsigned)((f.A + 3) / 4)), dim3(256), 0, s,
-                     static_cast<const v4u*>(expand_x), q1, s1, amax2, expert_token_nums, f.L, f.A, f.H / 8);
-  hipLaunchKernelGGL(k_ffn_gemm<true>, dim3(f.N / 2 / kFfnBN, m_tiles), dim3(kFfnThreads), 0, s,
-                     static_cast<const void*>(q1), s1, static_cast<const uint32_t*>(nullptr), w1, w1_scale, g, amax2,
+  hipLaunchKernelGGL(k_ffn_quant_rows, dim3(quant_wgs), dim3(256), 0, s, static_cast<const v4u*>(expand_x), q1, s1,
+                     expert_token_nums, f.L, f.A, f.H / 8);
+  hipLaunchKernelGGL(k_ffn_gemm<true>, dim3(g1), dim3(kFfnThreads), 0, s, q1, s1, w1, w1_scale, g,
                      expert_token_nums, f.L, f.A, f.H, f.N, f.N / 2);
-  hipLaunchKernelGGL(k_ffn_gemm<false>, dim3(f.H / kFfnBN, m_tiles), dim3(kFfnThreads), 0, s,
-                     static_cast<const void*>(g), static_cast<const float*>(nullptr), amax2, w2, w2_scale,
-                     static_cast<uint16_t*>(y), static_cast<uint32_t*>(nullptr), expert_token_nums, f.L, f.A, f.N / 2,
-                     f.H, f.H);
+  hipLaunchKernelGGL(k_ffn_quant_rows, dim3(quant_wgs), dim3(256), 0, s, reinterpret_cast<const v4u*>(g), q2, s2,
+                     expert_token_nums, f.L, f.A, f.N / 2 / 8);
+  hipLaunchKernelGGL(k_ffn_gemm<false>, dim3(g2), dim3(kFfnThreads), 0, s, q2, s2, w2, w2_scale,
+                     static_cast<uint16_t*>(y), expert_token_nums, f.L, f.A, f.N / 2, f.H, f.H);
   return launched();
 }
 
