@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="share", choices=sorted(DESCR))
     ap.add_argument("--batches", type=int, default=2, help="rotated copies of every input buffer")
-    ap.add_argument("--event-every", type=int, default=4,
+    ap.add_argument("--event-every", type=int, default=10,
                     help="record the per-kernel HIP events on every n-th timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget")
