@@ -69,9 +69,11 @@ def dispatch(ids, mask, d, experts, capacity, x=None):
     tuples = []
     for s in range(W):
         for t in range(BS):
-            if mask is not None and not mask[s][t]:
-                continue
             for k in range(K):
+                if mask is not None:
+                    m = mask[s][t]
+                    if not (m[k] if isinstance(m, (list, tuple)) else m):
+                        continue
                 e = int(ids[s][t][k])
                 if e < 0 or e >= experts:
                     continue
@@ -96,8 +98,12 @@ def dispatch(ids, mask, d, experts, capacity, x=None):
     return rows, cnt, ep, etn, expand
 
 
-def combine(segments, r, ids_r, mask_r, scales_r, shared_r, hidden):
-    """segments: list of (y rows [list of bf16 ints], triplets [list of (s,t,k)]); returns list of bf16 rows."""
+def combine(segments, r, ids_r, mask_r, scales_r, shared_r, hidden, experts=None, zero=0, copy=0, ori=None):
+    """segments: list of (y rows [list of bf16 ints], triplets [list of (s,t,k)]); returns list of bf16 rows.
+
+    Special experts: id in [experts, experts+zero) -> output row of zeros;
+    [experts+zero, experts+zero+copy) -> the token's own row ori[t].
+    """
     BS = len(ids_r)
     K = len(ids_r[0])
     found = {}
@@ -109,7 +115,17 @@ def combine(segments, r, ids_r, mask_r, scales_r, shared_r, hidden):
     for t in range(BS):
         acc = [0.0] * hidden
         for k in range(K):
+            if mask_r is not None:
+                m = mask_r[t]
+                if not (m[k] if isinstance(m, (list, tuple)) else m):
+                    continue
             y = found.get((t, k))
+            if y is None and experts is not None:
+                e = int(ids_r[t][k])
+                if experts <= e < experts + zero:
+                    y = [0] * hidden
+                elif experts + zero <= e < experts + zero + copy:
+                    y = list(ori[t])
             if y is None:
                 continue
             sc = f32(float(scales_r[t][k]))

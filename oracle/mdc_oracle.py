@@ -29,7 +29,13 @@ notes):
   * expertTokenNums are per-local-expert counts, int64 ([TL] UpdateTokenNumsOut);
   * assistInfo rows are (src, token, k) int32 triplets ([TL] send loop);
   * a 1D mask in any order is accepted; inactive tokens send nothing and
-    combine to +0.0 (the empty sum of the [CV4] formula);
+    combine to +0.0 (the empty sum of the [CV4] formula); a 2D mask [BS][K]
+    switches single routes off ([CV4] A3 notes: a token whose K entries are all
+    false does not take part);
+  * zero experts (ids in [E, E+Z)) and copy experts (ids in [E+Z, E+Z+C)) are
+    never dispatched; in combine such a route is present with output 0 (zero)
+    or the token's own unprocessed row oriX[t] (copy) ([CV4] parameter notes on
+    zeroExpertNum, copyExpertNum and oriXOptional);
   * ids outside [0, E) are dropped;
   * rows whose index would reach the capacity A are not written; counts still
     include them, so overflow is visible from epRecvCounts;
@@ -93,22 +99,31 @@ class DispatchResult:
     expanded_row_idx: dict        # (src, token, k) -> row, for written rows
 
 
+def route_active(mask: Optional[np.ndarray], t: int, k: int) -> bool:
+    """Mask of one rank: None (all active), 1D [BS] per token, or 2D [BS][K] per route."""
+    if mask is None:
+        return True
+    if mask.ndim == 1:
+        return bool(mask[t])
+    return bool(mask[t][k])
+
+
 def local_routes(ids: np.ndarray, mask: Optional[np.ndarray], d: int, experts: int):
     """Active routes whose expert lives on rank d, as (le, s, t, k), enumerated in (s, t, k) order.
 
     Routing rule: expert e goes to rank e // L as local expert e % L
-    ([TL] send loop).  Inactive tokens send nothing ([CV4] xActiveMask:
-    whether the token takes part in communication).  Ids outside [0, E) are
-    dropped.
+    ([TL] send loop).  Inactive tokens or routes send nothing ([CV4]
+    xActiveMask: whether the token takes part in communication; 2D per
+    route).  Ids outside [0, E) are not dispatched.
     """
     W, BS, K = ids.shape
     L = experts // W
     out = []
     for s in range(W):
         for t in range(BS):
-            if mask is not None and not mask[s][t]:
-                continue
             for k in range(K):
+                if mask is not None and not route_active(mask[s], t, k):
+                    continue
                 e = int(ids[s][t][k])
                 if 0 <= e < experts and e // L == d:
                     out.append((e % L, s, t, k))
@@ -192,15 +207,19 @@ def expert_pow2(expand_x: np.ndarray, assist: np.ndarray, ids: np.ndarray, L: in
 
 def combine(segments_y: Sequence[np.ndarray], segments_assist: Sequence[np.ndarray], r: int,
             ids_r: np.ndarray, mask_r: Optional[np.ndarray], scales_r: np.ndarray,
-            shared_r: Optional[np.ndarray], hidden: int) -> np.ndarray:
+            shared_r: Optional[np.ndarray], hidden: int, experts: Optional[int] = None,
+            zero_experts: int = 0, copy_experts: int = 0, ori_r: Optional[np.ndarray] = None) -> np.ndarray:
     """Combine for source rank r: xOut[t] = sum_k ( s[t,k]*y[t,k] + s[t,k]*sharedX[t] ).
 
     segments_y[j] / segments_assist[j] are destination rank j's expert outputs
     and (src, token, k) triplets (valid rows only).  The expert output of route
     (r, t, k) is the row of some segment whose triplet is (r, t, k): data is
     returned along the dispatch path ([CV4] Function note; [TL] combine sends
-    each row back to slot token*K + k of its source).  A route with no such row
-    (inactive, dropped id, past capacity) contributes nothing.
+    each row back to slot token*K + k of its source).  A route whose id is a
+    zero expert (E <= e < E+Z) has output 0; a copy expert (E+Z <= e < E+Z+C)
+    has output oriX[t] ([CV4] zeroExpertNum / copyExpertNum / oriXOptional).
+    Any other route with no such row (inactive, dropped id, past capacity)
+    contributes nothing; a masked-off route contributes nothing.
 
     Arithmetic ([TL] combine weighted sum; [CV4] formula): fp32 accumulator
     from +0.0, k ascending, a = s*y and b = s*sharedX each rounded to fp32,
@@ -213,16 +232,27 @@ def combine(segments_y: Sequence[np.ndarray], segments_assist: Sequence[np.ndarr
             s, t, k = (int(v) for v in assist[row])
             if s == r:
                 where[(t, k)] = (j, row)
+    zero_row = np.zeros(hidden, dtype=np.uint16)
     out = np.zeros((BS, hidden), dtype=np.uint16)
     for t in range(BS):
         acc = np.zeros(hidden, dtype=np.float32)
         for k in range(K):
-            hit = where.get((t, k))
-            if hit is None:
+            if mask_r is not None and not route_active(mask_r, t, k):
                 continue
-            j, row = hit
+            hit = where.get((t, k))
+            if hit is not None:
+                j, row = hit
+                y = segments_y[j][row]
+            else:
+                e = int(ids_r[t][k])
+                if experts is not None and experts <= e < experts + zero_experts:
+                    y = zero_row
+                elif experts is not None and experts + zero_experts <= e < experts + zero_experts + copy_experts:
+                    y = ori_r[t]
+                else:
+                    continue
             sc = np.float32(scales_r[t][k])
-            a = sc * bf16_to_f32(segments_y[j][row])
+            a = sc * bf16_to_f32(y)
             if shared_r is not None:
                 b = sc * bf16_to_f32(shared_r[t])
                 acc = acc + (a + b)

@@ -367,3 +367,78 @@ def test_ffn_permutation_weights_closed_form():
         # second quantisation: error at most half a step of amax/127, then bf16 rounding
         step = np.max(np.abs(gg)) / 127
         assert np.all(np.abs(y[i] - want) <= 0.5 * step + np.abs(want) * 2 ** -8 + 1e-12)
+
+
+# ----------------------------------------------------------------------------- 2D mask, zero / copy experts
+
+
+def _mask2d(g, W, BS, K, kind):
+    if kind == "rand":
+        m = (g.random((W, BS, K)) < 0.6).astype(np.uint8)
+    elif kind == "token_off":
+        m = np.ones((W, BS, K), np.uint8)
+        m[:, ::3, :] = 0                     # whole tokens off (all K false)
+    else:
+        m = np.ones((W, BS, K), np.uint8)
+        m[:, :, 0] = 0                       # first slot off everywhere
+    return m
+
+
+@pytest.mark.parametrize("kind", ["rand", "token_off", "slot0_off"])
+@pytest.mark.parametrize("seed", range(4))
+def test_dispatch_2d_mask_matches_brute_force(kind, seed):
+    g = np.random.default_rng(300 + seed)
+    W, E, K, BS = [(1, 6, 2, 7), (2, 8, 3, 5), (3, 6, 2, 6), (2, 4, 4, 9)][seed]
+    ids = np.stack([np.stack([g.permutation(E)[:K] for _ in range(BS)]) for _ in range(W)]).astype(np.int32)
+    ids[g.random(ids.shape) < 0.15] = E + 1      # some special / invalid ids, never dispatched
+    mask = _mask2d(g, W, BS, K, kind)
+    x = gen.bf16_from_f32(g.standard_normal((W, BS, 4), dtype=np.float32))
+    for d in range(W):
+        o = O.dispatch(x, ids, mask, d, E, 10 ** 6)
+        rows, cnt, ep, etn, ex = B.dispatch(ids.tolist(), mask.tolist(), d, E, 10 ** 6, x.tolist())
+        assert [tuple(r) for r in o.assist_info.tolist()] == rows
+        assert o.ep_recv_counts.tolist() == ep
+    # I1 with a route mask: world total = active routes with a dispatchable id
+    tot = sum(O.dispatch(None, ids, mask, d, E, 10 ** 6).total for d in range(W))
+    assert tot == int(((ids >= 0) & (ids < E) & (mask != 0)).sum())
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_combine_special_experts_match_brute_force(seed):
+    g = np.random.default_rng(400 + seed)
+    W, E, Z, C, K, BS, H = 2, 4, 2, 2, 3, 6, 8
+    ids = np.stack([np.stack([g.permutation(E + Z + C + 2)[:K] for _ in range(BS)]) for _ in range(W)]).astype(np.int32)
+    x = gen.bf16_from_f32(g.standard_normal((W, BS, H), dtype=np.float32))
+    mask = _mask2d(g, W, BS, K, "rand") if seed % 2 else None
+    segs = [O.dispatch(x, ids, mask, d, E, 10 ** 6) for d in range(W)]
+    ys = [O.expert_pow2(s.expand_x, s.assist_info, ids, E // W) for s in segs]
+    for shared_on in (False, True):
+        for r in range(W):
+            sc = g.standard_normal((BS, K)).astype(np.float32)
+            sh = gen.bf16_from_f32(g.standard_normal((BS, H), dtype=np.float32)) if shared_on else None
+            m = None if mask is None else mask[r]
+            got = O.combine(ys, [s.assist_info for s in segs], r, ids[r], m, sc, sh, H, experts=E,
+                            zero_experts=Z, copy_experts=C, ori_r=x[r])
+            bseg = [(y.tolist(), [tuple(v) for v in s.assist_info.tolist()]) for y, s in zip(ys, segs)]
+            want = B.combine(bseg, r, ids[r].tolist(), None if m is None else m.tolist(), sc.tolist(),
+                             None if sh is None else sh.tolist(), H, experts=E, zero=Z, copy=C, ori=x[r].tolist())
+            assert got.tolist() == want
+
+
+def test_copy_and_zero_experts_closed_form():
+    """One copy route with scale 1 returns oriX; a zero route adds only its shared term."""
+    E, Z, C, H = 4, 1, 1, 16
+    g = np.random.default_rng(9)
+    x = gen.bf16_from_f32(g.standard_normal((1, 2, H), dtype=np.float32))
+    sh = gen.bf16_from_f32(np.full((2, H), 2.0, np.float32))
+    ids = np.array([[[E + Z, E], [E, E + 7]]], np.int32)       # token 0: copy, zero; token 1: zero, invalid
+    sc = np.array([[1.0, 0.25], [0.5, 9.0]], np.float32)
+    segs = [O.dispatch(x, ids, None, 0, E, 100)]
+    assert segs[0].total == 0
+    out = O.combine([segs[0].expand_x], [segs[0].assist_info], 0, ids[0], None, sc, None, H, experts=E,
+                    zero_experts=Z, copy_experts=C, ori_r=x[0])
+    assert np.array_equal(O.bf16_to_f32(out[0]), O.bf16_to_f32(x[0, 0]))
+    assert not O.bf16_to_f32(out[1]).any()
+    out2 = O.combine([segs[0].expand_x], [segs[0].assist_info], 0, ids[0], None, sc, sh, H, experts=E,
+                     zero_experts=Z, copy_experts=C, ori_r=x[0])
+    assert np.array_equal(O.bf16_to_f32(out2[1]), np.full(H, 1.0, np.float32))      # 0.5 * 2.0 from the zero route
