@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -48,7 +48,8 @@ EXPORTS = (
 class mdc_shape(ctypes.Structure):
     _fields_ = [("world", ctypes.c_int32), ("rank", ctypes.c_int32), ("bs", ctypes.c_int32),
                 ("hidden", ctypes.c_int32), ("topk", ctypes.c_int32), ("num_experts", ctypes.c_int32),
-                ("capacity", ctypes.c_int64)]
+                ("capacity", ctypes.c_int64), ("mask_per_route", ctypes.c_int32),
+                ("zero_experts", ctypes.c_int32), ("copy_experts", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -70,7 +71,7 @@ _lib.mdc_dispatch.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.mdc_combine_workspace_size.restype = ctypes.c_int
 _lib.mdc_combine_workspace_size.argtypes = [_SHP, ctypes.POINTER(_SZ)]
 _lib.mdc_combine.restype = ctypes.c_int
-_lib.mdc_combine.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.mdc_combine.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.mdc_ffn_workspace_size.restype = ctypes.c_int
 _lib.mdc_ffn_workspace_size.argtypes = [_SHP, ctypes.c_int32, ctypes.POINTER(_SZ)]
 _lib.mdc_ffn.restype = ctypes.c_int
@@ -100,16 +101,20 @@ class Shape:
     topk: int
     num_experts: int
     capacity: int
+    mask_per_route: int = 0
+    zero_experts: int = 0
+    copy_experts: int = 0
 
     @property
     def local_experts(self) -> int:
         return self.num_experts // self.world
 
     def c(self) -> mdc_shape:
-        return mdc_shape(self.world, self.rank, self.bs, self.hidden, self.topk, self.num_experts, self.capacity)
+        return mdc_shape(self.world, self.rank, self.bs, self.hidden, self.topk, self.num_experts, self.capacity,
+                         self.mask_per_route, self.zero_experts, self.copy_experts, 0)
 
     def with_rank(self, rank: int) -> "Shape":
-        return Shape(self.world, rank, self.bs, self.hidden, self.topk, self.num_experts, self.capacity)
+        return replace(self, rank=rank)
 
 
 def _ptr(t) -> Optional[int]:
@@ -199,12 +204,12 @@ def _table(items: Sequence) -> ctypes.Array:
 
 def mdc_combine(shape: Shape, expand_x: Sequence, assist_info: Sequence, ep_recv_counts: Sequence,
                 expanded_row_idx, expert_ids, expert_scales, x_active_mask, shared_expert_x, x_out,
-                workspace=None, stream=None, check: bool = True) -> int:
+                workspace=None, stream=None, check: bool = True, ori_x=None) -> int:
     sh = shape.c()
     ty, ta, tc = _table(expand_x), _table(assist_info), _table(ep_recv_counts)
     st = _lib.mdc_combine(ctypes.byref(sh), ctypes.cast(ty, _P), ctypes.cast(ta, _P), ctypes.cast(tc, _P),
                           _ptr(expanded_row_idx), _ptr(expert_ids), _ptr(expert_scales), _ptr(x_active_mask),
-                          _ptr(shared_expert_x), _ptr(x_out), _ptr(workspace), _nbytes(workspace),
+                          _ptr(shared_expert_x), _ptr(ori_x), _ptr(x_out), _ptr(workspace), _nbytes(workspace),
                           _stream(stream))
     if check:
         _check(st, "mdc_combine")
@@ -272,12 +277,13 @@ def prepare_dispatch_gather(shape: Shape, x, expand_x, assist_info, ep_recv_coun
 
 def prepare_combine(shape: Shape, expand_x: Sequence, assist_info: Sequence, ep_recv_counts: Sequence,
                     expanded_row_idx, expert_ids, expert_scales, x_active_mask, shared_expert_x, x_out,
-                    workspace=None, stream=None) -> Prepared:
+                    workspace=None, stream=None, ori_x=None) -> Prepared:
     sh = shape.c()
     ty, ta, tc = _table(expand_x), _table(assist_info), _table(ep_recv_counts)
     args = (ctypes.byref(sh), ctypes.cast(ty, _P), ctypes.cast(ta, _P), ctypes.cast(tc, _P),
             _ptr(expanded_row_idx), _ptr(expert_ids), _ptr(expert_scales), _ptr(x_active_mask),
-            _ptr(shared_expert_x), _ptr(x_out), _ptr(workspace), _nbytes(workspace), _stream(stream))
+            _ptr(shared_expert_x), _ptr(ori_x), _ptr(x_out), _ptr(workspace), _nbytes(workspace),
+            _stream(stream))
     return Prepared(_lib.mdc_combine, args, "mdc_combine", (sh, ty, ta, tc))
 
 

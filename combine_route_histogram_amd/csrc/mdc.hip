@@ -152,7 +152,7 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int k) {
 __global__ __launch_bounds__(1024) void k_route_rank(
     const int32_t* __restrict__ ids, const uint8_t* __restrict__ mask,
     int32_t* __restrict__ P, int32_t* __restrict__ cnt,
-    int BS, int K, int E, int L, int d, int W, int TPG, int G) {
+    int BS, int K, int E, int L, int d, int W, int TPG, int G, int mask_per_route) {
   extern __shared__ int32_t sm[];  // carry[L], wave_cnt[nw][L]
   const int nw = blockDim.x >> 6;
   int32_t* carry = sm;
@@ -179,7 +179,8 @@ __global__ __launch_bounds__(1024) void k_route_rank(
     if (f < n_routes) {
       const int t = t_begin + f / K;
       const int e = ids[f_base + f];
-      const bool active = (mask == nullptr) || (mask[(int64_t)s * BS + t] != 0);
+      const bool active = (mask == nullptr) ||
+                          (mask[mask_per_route ? f_base + f : (int64_t)s * BS + t] != 0);
       const int q = e - d * L;
       if (active && e >= 0 && e < E && q >= 0 && q < L) key = q;
     }
@@ -422,8 +423,9 @@ template <int KMAX, int V, bool SHARED>
 __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
     CombineTables tabs, const int32_t* __restrict__ row_idx, const int32_t* __restrict__ ids,
     const float* __restrict__ scales, const uint8_t* __restrict__ mask,
-    const v4u* __restrict__ shared, v4u* __restrict__ out,
-    int r, int W, int K, int E, int L, int64_t A, int nvec, int ntiles, unsigned n_items) {
+    const v4u* __restrict__ shared, const v4u* __restrict__ ori, v4u* __restrict__ out,
+    int r, int W, int K, int E, int L, int64_t A, int nvec, int ntiles, unsigned n_items,
+    int mask_per_route, int Z, int C) {
   const unsigned item = blockIdx.x * MDC_COMBINE_WAVES + (threadIdx.x >> 6);
   if (item >= n_items) return;
   const int t = (int)(item / (unsigned)ntiles);
@@ -435,7 +437,7 @@ __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
   const int e = ids[rt];
   const int row = row_idx[rt];
   const float sc = scales[rt];
-  const bool act = (mask == nullptr) || (mask[t] != 0);
+  const bool act = (mask == nullptr) || (mask[mask_per_route ? rt : (int64_t)t] != 0);
   const int tl = lane < W ? lane : 0;
   const uint64_t yb = (uint64_t)tabs.y[tl];
   const uint64_t ab = (uint64_t)tabs.assist[tl];
@@ -456,10 +458,19 @@ __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
     const int a0 = load_i32(a), a1 = load_i32(a + 4), a2 = load_i32(a + 8);
     ok = valid && inrange && row < total && a0 == r && a1 == t && a2 == lane;
   }
+  v4u* orow = out + (int64_t)t * nvec;
+  // Zero experts [E, E+Z) and copy experts [E+Z, E+Z+C) are present without a
+  // dispatched row: output 0 (read from a valid row, then replaced by zero) or
+  // the token's own row ori[t].
+  const bool special = (lane < K) && act && e >= E && e - E < Z + C;
+  const bool is_zero = special && e - E < Z;
+  uint64_t yrow = yj + (uint64_t)rowc * (uint64_t)nvec * sizeof(v4u);
+  if (special) yrow = is_zero ? (uint64_t)orow : (uint64_t)(ori + (int64_t)t * nvec);
+  ok = ok || special;
   const uint64_t has = __ballot(ok);
+  const uint64_t zero_lanes = __ballot(is_zero);
   const int np = __popcll(has);
   const int base = tile * 64 * V + lane;
-  v4u* orow = out + (int64_t)t * nvec;
 
   if (np == 0) {
     const v4u z = {0u, 0u, 0u, 0u};
@@ -473,15 +484,16 @@ __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
 
   // Present routes in ascending k as wavefront-uniform row addresses and scales;
   // slots past the last present route repeat the first one (loaded, never summed).
-  const uint64_t yrow = yj + (uint64_t)rowc * (uint64_t)nvec * sizeof(v4u);
   uint64_t yp[KMAX];
   float sk[KMAX];
+  bool zk[KMAX];
   uint64_t rem = has;
 #pragma unroll
   for (int i = 0; i < KMAX; ++i) {
     const int k = rem ? (__ffsll((unsigned long long)rem) - 1) : (__ffsll((unsigned long long)has) - 1);
     yp[i] = readlane64(yrow, k);
     sk[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), k));
+    zk[i] = (zero_lanes >> k) & 1;
     rem &= rem - 1;
   }
 
@@ -514,6 +526,11 @@ __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
       }
     }
   }
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i)
+#pragma unroll
+    for (int u = 0; u < V; ++u)
+      if (zk[i]) yv[i][u] = v4u{0u, 0u, 0u, 0u};
 #pragma unroll
   for (int u = 0; u < V; ++u) {
     const int idx = base + u * 64;
@@ -848,11 +865,15 @@ mdc_status check_shape(const mdc_shape* sh) {
   if (sh->capacity < 0 || sh->capacity > INT32_MAX) return MDC_ERR_INVALID;
   if ((int64_t)sh->world * sh->bs * sh->topk > INT32_MAX) return MDC_ERR_INVALID;
   if (sh->world > 65535) return MDC_ERR_INVALID;
+  if (sh->mask_per_route != 0 && sh->mask_per_route != 1) return MDC_ERR_INVALID;
+  if (sh->zero_experts < 0 || sh->copy_experts < 0 || sh->reserved != 0) return MDC_ERR_INVALID;
+  if ((int64_t)sh->num_experts + sh->zero_experts + sh->copy_experts > INT32_MAX) return MDC_ERR_INVALID;
+  if (sh->topk > sh->num_experts + sh->zero_experts + sh->copy_experts) return MDC_ERR_INVALID;
   return MDC_OK;
 }
 
 struct DispatchPlan {
-  int W, d, BS, H, K, E, L, TPG, G, nvec, rank_threads;
+  int W, d, BS, H, K, E, L, TPG, G, nvec, rank_threads, mask_per_route;
   int64_t A;
   size_t off_p, off_cnt, bytes;
 };
@@ -867,6 +888,7 @@ DispatchPlan make_plan(const mdc_shape* sh) {
   p.E = sh->num_experts;
   p.L = p.E / p.W;
   p.A = sh->capacity;
+  p.mask_per_route = sh->mask_per_route;
   p.TPG = kGroupRoutes / p.K;
   p.G = (p.BS + p.TPG - 1) / p.TPG;
   p.nvec = p.H / 8;
@@ -890,7 +912,7 @@ mdc_status layout_impl(const DispatchPlan& p, const int32_t* ids, const uint8_t*
   (void)hipGetLastError();
   const size_t lds = (size_t)(p.rank_threads / 64 + 1) * p.L * sizeof(int32_t);
   hipLaunchKernelGGL(k_route_rank, dim3(p.G, p.W), dim3(p.rank_threads), lds, st,
-                     ids, mask, P, cnt, p.BS, p.K, p.E, p.L, p.d, p.W, p.TPG, p.G);
+                     ids, mask, P, cnt, p.BS, p.K, p.E, p.L, p.d, p.W, p.TPG, p.G, p.mask_per_route);
   return launched();
 }
 
@@ -1038,8 +1060,8 @@ mdc_status mdc_combine_workspace_size(const mdc_shape* shape, size_t* bytes) {
 mdc_status mdc_combine(const mdc_shape* shape, const void* const* expand_x, const int32_t* const* assist_info,
                        const int32_t* const* ep_recv_counts, const int32_t* expanded_row_idx,
                        const int32_t* expert_ids, const float* expert_scales, const uint8_t* x_active_mask,
-                       const void* shared_expert_x, void* x_out, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       const void* shared_expert_x, const void* ori_x, void* x_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
   mdc_status st = check_shape(shape);
@@ -1061,7 +1083,8 @@ mdc_status mdc_combine(const mdc_shape* shape, const void* const* expand_x, cons
     tabs.assist[j] = assist_info[j];
     tabs.counts[j] = ep_recv_counts[j];
   }
-  if (!aligned16(shared_expert_x) || !aligned16(x_out)) return MDC_ERR_INVALID;
+  if (shape->copy_experts > 0 && ori_x == nullptr) return MDC_ERR_NULLPTR;
+  if (!aligned16(shared_expert_x) || !aligned16(x_out) || !aligned16(ori_x)) return MDC_ERR_INVALID;
   const int K = shape->topk;
   const int E = shape->num_experts;
   const int L = E / W;
@@ -1069,6 +1092,7 @@ mdc_status mdc_combine(const mdc_shape* shape, const void* const* expand_x, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   const v4u* sh = static_cast<const v4u*>(shared_expert_x);
   v4u* out = static_cast<v4u*>(x_out);
+  const v4u* ori = static_cast<const v4u*>(ori_x);
   const int r = shape->rank;
   const int64_t A = shape->capacity;
   (void)hipGetLastError();
@@ -1078,20 +1102,24 @@ mdc_status mdc_combine(const mdc_shape* shape, const void* const* expand_x, cons
     const dim3 grid((n_items + MDC_COMBINE_WAVES - 1) / MDC_COMBINE_WAVES), block(64 * MDC_COMBINE_WAVES);
     if (sh)
       hipLaunchKernelGGL((k_combine<8, kCombineVec, true>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
-                         expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles, n_items);
+                         expert_scales, x_active_mask, sh, ori, out, r, W, K, E, L, A, nvec, ntiles, n_items,
+                         shape->mask_per_route, shape->zero_experts, shape->copy_experts);
     else
       hipLaunchKernelGGL((k_combine<8, kCombineVec, false>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
-                         expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles, n_items);
+                         expert_scales, x_active_mask, sh, ori, out, r, W, K, E, L, A, nvec, ntiles, n_items,
+                         shape->mask_per_route, shape->zero_experts, shape->copy_experts);
   } else {
     const int ntiles = (nvec + 63) / 64;
     const unsigned n_items = (unsigned)((int64_t)BS * ntiles);
     const dim3 grid((n_items + MDC_COMBINE_WAVES - 1) / MDC_COMBINE_WAVES), block(64 * MDC_COMBINE_WAVES);
     if (sh)
       hipLaunchKernelGGL((k_combine<16, 1, true>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
-                         expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles, n_items);
+                         expert_scales, x_active_mask, sh, ori, out, r, W, K, E, L, A, nvec, ntiles, n_items,
+                         shape->mask_per_route, shape->zero_experts, shape->copy_experts);
     else
       hipLaunchKernelGGL((k_combine<16, 1, false>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
-                         expert_scales, x_active_mask, sh, out, r, W, K, E, L, A, nvec, ntiles, n_items);
+                         expert_scales, x_active_mask, sh, ori, out, r, W, K, E, L, A, nvec, ntiles, n_items,
+                         shape->mask_per_route, shape->zero_experts, shape->copy_experts);
   }
   return launched();
 }

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MDC_ABI_VERSION 1
+#define MDC_ABI_VERSION 2
 #define MDC_MAX_TOPK 16        /* 0 < K <= 16 ([CV4] shape-variable table) */
 #define MDC_MAX_LOCAL_EXPERTS 2048
 #define MDC_MAX_COMBINE_WORLD 64 /* W limit of mdc_combine (pointer tables travel by value) */
@@ -74,6 +74,16 @@ typedef struct {
     int32_t num_experts;  /* E > 0, multiple of W; L = E / W <= MDC_MAX_LOCAL_EXPERTS */
     int64_t capacity;     /* A >= 0: rows of expand_x / assist_info per rank.
                              [CV4] shape-variable table asks A >= BS*W*min(L, K). */
+    int32_t mask_per_route; /* 0: x_active_mask holds one flag per token ([.][BS]);
+                               1: one flag per route ([.][BS][K]) ([CV4] parameter
+                               notes: a 2D xActiveMask; a token whose K flags are all
+                               false takes no part) */
+    int32_t zero_experts;   /* Z >= 0: ids in [E, E+Z) are zero experts ([CV4]
+                               zeroExpertNum): never dispatched; output 0 in combine */
+    int32_t copy_experts;   /* C >= 0: ids in [E+Z, E+Z+C) are copy experts ([CV4]
+                               copyExpertNum): never dispatched; output ori_x[t] in
+                               combine.  K <= E + Z + C. */
+    int32_t reserved;       /* must be 0 */
 } mdc_shape;
 
 const char* mdc_status_string(mdc_status status);
@@ -83,9 +93,10 @@ int32_t mdc_abi_version(void);
  * Dispatch ([TL] moe_dispatch_kernel; [PTO] FrontReorder + Dispatch stages)
  *
  * For destination rank d = shape->rank, over all W virtual source ranks:
- *   - a route (s, t, k) is sent iff token t of rank s is active and
- *     e = expert_ids[s][t][k] satisfies d*L <= e < (d+1)*L.  Ids outside
- *     [0, E) are dropped (never sent anywhere).
+ *   - a route (s, t, k) is sent iff it is active (its token's flag, or its
+ *     own flag with mask_per_route) and e = expert_ids[s][t][k] satisfies
+ *     d*L <= e < (d+1)*L.  Ids outside [0, E) (zero/copy experts, invalid
+ *     ids) are never sent anywhere.
  *   - the received rows are laid out expert-major in the stable order
  *     (local expert le, source s, token t, slot k): row = base(le, s) +
  *     number of earlier routes (t', k') < (t, k) of source s with the same
@@ -117,8 +128,9 @@ int32_t mdc_abi_version(void);
  * Inputs
  *   x                 [W][BS][H] bf16, the virtual source ranks' tokens.
  *   expert_ids        [W][BS][K] int32.
- *   x_active_mask     [W][BS] uint8 (nonzero = active) or NULL (all active);
- *                     any order of active/inactive tokens is accepted.
+ *   x_active_mask     [W][BS] uint8 (nonzero = active), or [W][BS][K] with
+ *                     mask_per_route, or NULL (all active); any order of active
+ *                     and inactive entries is accepted.
  *
  * The call is split in two stages that may be enqueued separately (same
  * stream, same workspace, in this order); mdc_dispatch enqueues both.
@@ -169,13 +181,17 @@ mdc_status mdc_dispatch(const mdc_shape* shape,
  * rounded to fp32 separately (no fused multiply-add), then rounded to bf16
  * nearest-even ([TL] combine: fp32 accumulate, CAST_RINT).  The shared term
  * is weighted per present route, as the [CV4] formula reads; it is omitted
- * when shared_expert_x is NULL.  y[t][k] is row expanded_row_idx[t][k] of
- * destination j = e / L (e = expert_ids[t][k]), i.e. expand_x[j]: data
- * returns along the dispatch path ([CV4] Function note and API matching
- * constraints).  A route is present iff the token is active, 0 <= e < E,
- * the row index is < min(ep_recv_counts[j][L*W-1], A) and assist_info[j] at
- * that row holds (r, t, k); otherwise it contributes nothing.  An inactive
- * token therefore gives a +0.0 row.
+ * when shared_expert_x is NULL.  For an active route (its token's flag, or
+ * its own flag with mask_per_route) with e = expert_ids[t][k]:
+ *   - 0 <= e < E: y[t][k] is row expanded_row_idx[t][k] of destination
+ *     j = e / L, i.e. expand_x[j]: data returns along the dispatch path
+ *     ([CV4] Function note and API matching constraints).  The route is
+ *     present iff that row is < min(ep_recv_counts[j][L*W-1], A) and
+ *     assist_info[j] at that row holds (r, t, k);
+ *   - E <= e < E+Z (zero expert): present with y = 0;
+ *   - E+Z <= e < E+Z+C (copy expert): present with y = ori_x[t];
+ *   - otherwise the route contributes nothing.
+ * A token with no present route gives a +0.0 row.
  *
  * Inputs
  *   expand_x          host array of W device pointers: rank j's expert
@@ -188,6 +204,9 @@ mdc_status mdc_dispatch(const mdc_shape* shape,
  *   expert_scales     [BS][K] fp32 of rank r.
  *   x_active_mask     [BS] uint8 of rank r, or NULL (all active).
  *   shared_expert_x   [BS][H] bf16, or NULL.
+ *   ori_x             [BS][H] bf16, rank r's unprocessed tokens ([CV4]
+ *                     oriXOptional); required when copy_experts > 0, else
+ *                     may be NULL.
  * Output
  *   x_out             [BS][H] bf16.
  * W must be <= MDC_MAX_COMBINE_WORLD.
@@ -203,6 +222,7 @@ mdc_status mdc_combine(const mdc_shape* shape,
                        const float* expert_scales,
                        const uint8_t* x_active_mask,
                        const void* shared_expert_x,
+                       const void* ori_x,
                        void* x_out,
                        void* workspace, size_t workspace_bytes,
                        void* stream);

@@ -120,15 +120,16 @@ def oracle_segments(x, ids, mask, experts, capacity, kind):
 
 
 def run_combine(gw: GpuWorld, ys: List[torch.Tensor], r: int, scales: np.ndarray,
-                shared: Optional[np.ndarray]) -> torch.Tensor:
+                shared: Optional[np.ndarray], ori: Optional[np.ndarray] = None) -> torch.Tensor:
     sh = gw.shape.with_rank(r)
     BS, K = scales.shape
     out = torch.empty((BS, sh.hidden), dtype=torch.bfloat16, device=DEV)
     sc = torch.from_numpy(np.ascontiguousarray(scales)).to(DEV)
     shd = None if shared is None else to_dev_bf16(shared)
+    orid = None if ori is None else to_dev_bf16(ori)
     m = None if gw.mask is None else gw.mask[r].contiguous()
     mdc.mdc_combine(sh, ys, [o["assist_info"] for o in gw.outs], [o["ep_recv_counts"] for o in gw.outs],
-                    gw.row_idx[r].contiguous(), gw.ids[r].contiguous(), sc, m, shd, out)
+                    gw.row_idx[r].contiguous(), gw.ids[r].contiguous(), sc, m, shd, out, ori_x=orid)
     torch.cuda.synchronize()
     return out
 

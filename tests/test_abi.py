@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert mdc.mdc_abi_version() == 1
+    assert mdc.mdc_abi_version() == 2
     for code in range(5):
         assert mdc.mdc_status_string(code).startswith("MDC_")
 

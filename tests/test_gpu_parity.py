@@ -29,12 +29,15 @@ def say(*a):
 
 
 def _shape(w: gen.Workload, capacity=None):
-    return mdc.Shape(w.world, 0, w.bs, w.hidden, w.topk, w.experts, w.capacity if capacity is None else capacity)
+    return mdc.Shape(w.world, 0, w.bs, w.hidden, w.topk, w.experts, w.capacity if capacity is None else capacity,
+                     mask_per_route=1 if w.route_mask_frac > 0 else 0, zero_experts=w.zero_experts,
+                     copy_experts=w.copy_experts)
 
 
 def _end_to_end(w: gen.Workload, expert="identity", capacity=None, ranks=None, split=False):
     say(f"case {w.name} W={w.world} BS={w.bs} H={w.hidden} E={w.experts} K={w.topk} routing={w.routing} "
-        f"inactive={w.inactive_frac} shared={w.shared} expert={expert} cap={capacity}")
+        f"inactive={w.inactive_frac} route_mask={w.route_mask_frac} Z={w.zero_experts} C={w.copy_experts} "
+        f"shared={w.shared} expert={expert} cap={capacity}")
     wi = gen.world_inputs(w)
     cap = w.capacity if capacity is None else capacity
     gw = G.dispatch_world(_shape(w, cap), wi.x, wi.ids, wi.mask, split=split)
@@ -45,8 +48,10 @@ def _end_to_end(w: gen.Workload, expert="identity", capacity=None, ranks=None, s
     for r in (range(w.world) if ranks is None else ranks):
         sh = None if wi.shared is None else wi.shared[r]
         m = None if wi.mask is None else wi.mask[r]
-        got = G.bits(G.run_combine(gw, ys, r, wi.scales[r], sh))
-        want = O.combine(oys, [s.assist_info for s in segs], r, wi.ids[r], m, wi.scales[r], sh, w.hidden)
+        ori = wi.x[r] if w.copy_experts else None
+        got = G.bits(G.run_combine(gw, ys, r, wi.scales[r], sh, ori))
+        want = O.combine(oys, [s.assist_info for s in segs], r, wi.ids[r], m, wi.scales[r], sh, w.hidden,
+                         experts=w.experts, zero_experts=w.zero_experts, copy_experts=w.copy_experts, ori_r=ori)
         assert G.ulp_diff(got, want) <= 1, f"combine r={r} beyond 1 ulp"
         assert np.array_equal(got, want), f"combine r={r} not bit-exact ({int((got != want).sum())} differ)"
     say("  combine bit-exact")
@@ -187,3 +192,25 @@ def test_combine_stale_row_index_is_rejected():
              for s in segs]
     want = O.combine(oys, first, 0, wi.ids[0], None, wi.scales[0], None, w.hidden)
     assert np.array_equal(got, want)
+
+
+def test_route_mask_2d():
+    """Route-level mask [BS][K]: single routes off, some whole tokens off."""
+    w = gen.workload("tiny", world=2, bs=100, hidden=264, experts=8, topk=3, route_mask_frac=0.3,
+                     inactive_frac=0.1, shared=True, index=90)
+    _end_to_end(w, expert="pow2")
+
+
+def test_zero_and_copy_experts():
+    """Zero experts contribute 0, copy experts the token's own row; neither is dispatched."""
+    w = gen.workload("tiny", world=2, bs=64, hidden=136, experts=8, topk=4, zero_experts=2, copy_experts=3,
+                     inactive_frac=0.2, shared=True, index=91)
+    gw, wi = _end_to_end(w, expert="pow2")
+    n_special = int(((wi.ids >= w.experts) & (wi.ids < w.experts + 5)).sum())
+    assert n_special > 0
+
+
+def test_special_experts_and_route_mask_full_size():
+    """Share shapes with 8 zero and 8 copy experts and a 2D route mask."""
+    w = gen.workload("share", zero_experts=8, copy_experts=8, route_mask_frac=0.05, index=92)
+    _end_to_end(w, ranks=[0, 4])

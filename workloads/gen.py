@@ -50,6 +50,9 @@ class Workload:
     inactive_frac: float = 0.0    # Bernoulli fraction of inactive tokens (1D mask)
     shared: bool = False          # sharedExpertX present in combine
     inter: int = 0                # FFN intermediate N (0 = no FFN weights)
+    zero_experts: int = 0         # Z: ids [E, E+Z) are zero experts (drawn like routed experts)
+    copy_experts: int = 0         # C: ids [E+Z, E+Z+C) are copy experts
+    route_mask_frac: float = 0.0  # >0: 2D mask [BS][K], each route off with this probability
 
     @property
     def local_experts(self) -> int:
@@ -95,9 +98,11 @@ def normal_bf16(g: np.random.Generator, shape) -> np.ndarray:
 def draw_routes(w: Workload, vrank: int) -> np.ndarray:
     """expertIds [BS][K] int32 for one virtual rank."""
     g = rng(w.index, vrank, "routes")
+    n_ids = w.experts + w.zero_experts + w.copy_experts
     if w.routing == "uniform":
-        # first K of a uniform random permutation = K distinct experts, uniform
-        keys = g.random((w.bs, w.experts))
+        # first K of a uniform random permutation = K distinct ids, uniform over
+        # routed and special experts
+        keys = g.random((w.bs, n_ids))
         return np.argsort(keys, axis=1, kind="stable")[:, :w.topk].astype(np.int32)
     if w.routing == "zipf":
         # successive sampling without replacement with p(e) ~ (e+1)^-s,
@@ -125,10 +130,16 @@ def draw_scales(w: Workload, vrank: int) -> np.ndarray:
 
 
 def draw_mask(w: Workload, vrank: int) -> Optional[np.ndarray]:
-    """1D xActiveMask [BS] (uint8 0/1), or None when every token is active."""
+    """xActiveMask: 2D [BS][K] per route when route_mask_frac > 0, else 1D [BS]
+    per token when inactive_frac > 0 (uint8 0/1), else None (all active)."""
+    g = rng(w.index, vrank, "mask")
+    if w.route_mask_frac > 0.0:
+        m = (g.random((w.bs, w.topk)) >= w.route_mask_frac).astype(np.uint8)
+        if w.inactive_frac > 0.0:
+            m[g.random(w.bs) < w.inactive_frac, :] = 0     # whole tokens off
+        return m
     if w.inactive_frac <= 0.0:
         return None
-    g = rng(w.index, vrank, "mask")
     return (g.random(w.bs) >= w.inactive_frac).astype(np.uint8)
 
 
