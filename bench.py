@@ -63,7 +63,10 @@ def parse():
 
 
 def algorithmic_bytes(w, ids, mask, d=0, r=0):
-    """What the method must move for one step (dispatch share d, combine share r)."""
+    """What the method must move for one step (dispatch share d, combine share r).
+
+    With the FFN workload the dispatch writes int8 rows plus a 4-byte scale.
+    """
     import numpy as np
     W, BS, K = ids.shape
     L = w.experts // W
@@ -76,7 +79,7 @@ def algorithmic_bytes(w, ids, mask, d=0, r=0):
     present = int(valid[r].sum())             # routes of rank r combined
     tok_any = int(valid[r].any(axis=1).sum())
     layout = ids.size * 4 + (0 if mask is None else mask.size) + L * W * 4 + L * 8
-    gather = U * H2 + R * (H2 + 12 + 4) + ids.size * 4
+    gather = U * H2 + R * ((w.hidden + 4 if w.inter else H2) + 12 + 4) + ids.size * 4
     combine = (present * H2 + BS * K * 12 + (0 if mask is None else BS)
                + (tok_any * H2 if w.shared else 0) + BS * H2)
     return {"R": R, "U": U, "present": present, "layout": layout, "gather": gather, "combine": combine}
@@ -179,6 +182,8 @@ def main():
         x_out = torch.empty((BS, H), dtype=torch.bfloat16, device=dev)
         if w.inter:
             outs[0]["y"] = torch.empty_like(outs[0]["expand_x"])
+            outs[0]["expand_q"] = torch.empty((w.capacity, H), dtype=torch.int8, device=dev)
+            outs[0]["dyn_scales"] = torch.empty((w.capacity,), dtype=torch.float32, device=dev)
         batches.append(dict(x=x, ids=ids, mask=mask, scales0=scales0, shared0=shared0, row_idx=row_idx,
                             outs=outs, x_out=x_out, ids0=ids[0].contiguous(), mask0=None if mask is None
                             else mask[0].contiguous(), row0=row_idx[0]))
@@ -196,14 +201,21 @@ def main():
     for bt in batches:
         o0 = bt["outs"][0]
         bt["layout"] = mdc.prepare_dispatch_layout(shape, bt["ids"], bt["mask"], o0["workspace"], stream)
-        bt["gather"] = mdc.prepare_dispatch_gather(shape, bt["x"], o0["expand_x"], o0["assist_info"],
-                                                   o0["ep_recv_counts"], o0["expert_token_nums"], bt["row_idx"],
-                                                   o0["workspace"], stream)
+        if w.inter:
+            # the FFN workload dispatches int8 rows with per-row scales and feeds them to the FFN
+            bt["gather"] = mdc.prepare_dispatch_quant_gather(shape, bt["x"], o0["expand_q"], o0["dyn_scales"],
+                                                             o0["assist_info"], o0["ep_recv_counts"],
+                                                             o0["expert_token_nums"], bt["row_idx"],
+                                                             o0["workspace"], stream)
+        else:
+            bt["gather"] = mdc.prepare_dispatch_gather(shape, bt["x"], o0["expand_x"], o0["assist_info"],
+                                                       o0["ep_recv_counts"], o0["expert_token_nums"],
+                                                       bt["row_idx"], o0["workspace"], stream)
         seg0 = o0["expand_x"]
         bt["ffn"] = None
         if ffn_w is not None:
-            bt["ffn"] = mdc.prepare_ffn(shape, w.inter, o0["expand_x"], o0["expert_token_nums"], *ffn_w, o0["y"],
-                                        ffn_ws, stream)
+            bt["ffn"] = mdc.prepare_ffn_quant_input(shape, w.inter, o0["expand_q"], o0["dyn_scales"],
+                                                    o0["expert_token_nums"], *ffn_w, o0["y"], ffn_ws, stream)
             seg0 = o0["y"]
         bt["combine"] = mdc.prepare_combine(shape, [seg0] + [o["expand_x"] for o in bt["outs"][1:]],
                                             [o["assist_info"] for o in bt["outs"]],

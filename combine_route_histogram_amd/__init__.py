@@ -41,7 +41,8 @@ EXPORTS = (
     "mdc_status_string", "mdc_abi_version",
     "mdc_dispatch_workspace_size", "mdc_dispatch_layout", "mdc_dispatch_gather", "mdc_dispatch",
     "mdc_combine_workspace_size", "mdc_combine",
-    "mdc_ffn_workspace_size", "mdc_ffn",
+    "mdc_ffn_workspace_size", "mdc_ffn", "mdc_dispatch_quant", "mdc_dispatch_quant_gather",
+    "mdc_ffn_quant_input",
 )
 
 
@@ -76,6 +77,12 @@ _lib.mdc_ffn_workspace_size.restype = ctypes.c_int
 _lib.mdc_ffn_workspace_size.argtypes = [_SHP, ctypes.c_int32, ctypes.POINTER(_SZ)]
 _lib.mdc_ffn.restype = ctypes.c_int
 _lib.mdc_ffn.argtypes = [_SHP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.mdc_dispatch_quant.restype = ctypes.c_int
+_lib.mdc_dispatch_quant.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.mdc_dispatch_quant_gather.restype = ctypes.c_int
+_lib.mdc_dispatch_quant_gather.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.mdc_ffn_quant_input.restype = ctypes.c_int
+_lib.mdc_ffn_quant_input.argtypes = [_SHP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
 
 
 class MdcError(RuntimeError):
@@ -232,6 +239,48 @@ def mdc_ffn(shape: Shape, inter_n: int, expand_x, expert_token_nums, w1, w1_scal
     if check:
         _check(st, "mdc_ffn")
     return st
+
+
+def mdc_dispatch_quant(shape: Shape, x, expert_ids, x_active_mask, expand_q, dynamic_scales, assist_info,
+                       ep_recv_counts, expert_token_nums, expanded_row_idx, workspace, stream=None,
+                       check: bool = True) -> int:
+    sh = shape.c()
+    st = _lib.mdc_dispatch_quant(ctypes.byref(sh), _ptr(x), _ptr(expert_ids), _ptr(x_active_mask), _ptr(expand_q),
+                                 _ptr(dynamic_scales), _ptr(assist_info), _ptr(ep_recv_counts),
+                                 _ptr(expert_token_nums), _ptr(expanded_row_idx), _ptr(workspace),
+                                 _nbytes(workspace), _stream(stream))
+    if check:
+        _check(st, "mdc_dispatch_quant")
+    return st
+
+
+def prepare_dispatch_quant_gather(shape: Shape, x, expand_q, dynamic_scales, assist_info, ep_recv_counts,
+                                  expert_token_nums, expanded_row_idx, workspace, stream=None) -> "Prepared":
+    sh = shape.c()
+    args = (ctypes.byref(sh), _ptr(x), _ptr(expand_q), _ptr(dynamic_scales), _ptr(assist_info),
+            _ptr(ep_recv_counts), _ptr(expert_token_nums), _ptr(expanded_row_idx), _ptr(workspace),
+            _nbytes(workspace), _stream(stream))
+    return Prepared(_lib.mdc_dispatch_quant_gather, args, "mdc_dispatch_quant_gather", (sh,))
+
+
+def mdc_ffn_quant_input(shape: Shape, inter_n: int, expand_q, dynamic_scales, expert_token_nums, w1, w1_scale, w2,
+                        w2_scale, y, workspace, stream=None, check: bool = True) -> int:
+    sh = shape.c()
+    st = _lib.mdc_ffn_quant_input(ctypes.byref(sh), int(inter_n), _ptr(expand_q), _ptr(dynamic_scales),
+                                  _ptr(expert_token_nums), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale),
+                                  _ptr(y), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    if check:
+        _check(st, "mdc_ffn_quant_input")
+    return st
+
+
+def prepare_ffn_quant_input(shape: Shape, inter_n: int, expand_q, dynamic_scales, expert_token_nums, w1, w1_scale,
+                            w2, w2_scale, y, workspace, stream=None) -> "Prepared":
+    sh = shape.c()
+    args = (ctypes.byref(sh), int(inter_n), _ptr(expand_q), _ptr(dynamic_scales), _ptr(expert_token_nums), _ptr(w1),
+            _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(y), _ptr(workspace), _nbytes(workspace),
+            _stream(stream))
+    return Prepared(_lib.mdc_ffn_quant_input, args, "mdc_ffn_quant_input", (sh,))
 
 
 def prepare_ffn(shape: Shape, inter_n: int, expand_x, expert_token_nums, w1, w1_scale, w2, w2_scale, y,

@@ -95,6 +95,17 @@ __device__ __forceinline__ void store_v4(v4u* p, v4u v) {
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
 
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 round to nearest, ties to even (the CAST_RINT of [TL] combine):
+// add 0x7FFF plus the lowest kept bit, keep the top 16 bits; NaN -> quiet NaN.
+__device__ __forceinline__ unsigned bf16_rne(float f) {
+  const unsigned u = __float_as_uint(f);
+  if (f != f) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 // Loads through addresses rebuilt from integers (readlane / shuffles) would be
 // compiled as flat accesses; these keep them in the global address space.
 typedef const v4u __attribute__((address_space(1))) g_v4u;
@@ -387,6 +398,115 @@ __global__ __launch_bounds__(64 * MDC_GATHER_WAVES) void k_dispatch_gather(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Quantised dispatch ([CV4] int8 communication quantisation; [PTO]
+// FrontReorder Stage: quantised token rows with a per-token scale): one
+// wavefront per source token with a local route reads the whole row once,
+// quantises it per row in fp32 (amax / 127, round half even, clamp +-127) and
+// writes the int8 row and its scale to each destination row.  Placement,
+// triplets, inverse index and counts are those of k_dispatch_gather.
+// Rows of up to 64 * 16 vectors (H <= 8192) are held in registers.
+// ---------------------------------------------------------------------------
+constexpr int kQuantRowVec = 16;
+
+template <int VPL>
+__global__ __launch_bounds__(64) void k_dispatch_gather_q(
+    const v4u* __restrict__ x, const int32_t* __restrict__ P, const int32_t* __restrict__ cnt,
+    int8_t* __restrict__ expand_q, float* __restrict__ dyn_scale, int32_t* __restrict__ assist,
+    int32_t* __restrict__ ep_recv, int64_t* __restrict__ expert_nums, int32_t* __restrict__ row_idx,
+    int BS, int K, int L, int W, int TPG, int G, int64_t A, int nvec) {
+  const unsigned gu = blockIdx.x;
+  const int s = (int)(gu / (unsigned)BS);
+  const int t = (int)(gu - (unsigned)s * (unsigned)BS);
+  const int64_t g = gu;
+  const int lane = threadIdx.x & 63;
+  const bool writer = (g == 0);
+  const int n_cnt = L * W * G;
+  int cnt0[kScanIPL];
+  load_counters(cnt, n_cnt, 0, lane, cnt0);
+  const int p = (lane < K) ? P[g * K + lane] : -1;
+  const bool mine = (p >= 0) && ((p & 0xFFFF) < L);
+  const uint64_t has = __ballot(mine);
+  if (has == 0 && !writer) return;
+
+  const uint64_t src = (uint64_t)(x + g * nvec);
+  v4u v[VPL];
+  if (has != 0) {
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) {
+      const int idx = lane + u * 64;
+      v[u] = idx < nvec ? load_v4<MDC_GATHER_NT_LOADS != 0>(src + (uint64_t)idx * 16) : v4u{0u, 0u, 0u, 0u};
+    }
+  }
+  const int le = p & 0xFFFF;
+  const int q = mine ? ((le * W + s) * G + t / TPG) : -1;
+  __shared__ int32_t pref_all[kScanChunk];
+  const int first = scan_lookup(cnt, n_cnt, cnt0, q, G, writer, ep_recv, lane, pref_all);
+  if (writer) {
+    for (int e = lane; e < L; e += 64) {
+      int64_t sum = 0;
+      for (int i = 0; i < W * G; ++i) sum += cnt[counter_slot(e * W * G + i)];
+      expert_nums[e] = sum;
+    }
+  }
+  if (has == 0) return;
+
+  // per-row quantisation, decided in fp32
+  float amax = 0.f;
+#pragma unroll
+  for (int u = 0; u < VPL; ++u)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[u][w])), fabsf(bf16_hi(v[u][w]))));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+  const float scale = amax / 127.0f;
+  uint64_t qv[VPL];
+#pragma unroll
+  for (int u = 0; u < VPL; ++u) {
+    uint64_t packed = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = fminf(fmaxf(rintf(bf16_lo(v[u][w]) * inv), -127.f), 127.f);
+      const float b = fminf(fmaxf(rintf(bf16_hi(v[u][w]) * inv), -127.f), 127.f);
+      packed |= (uint64_t)(uint8_t)(int8_t)(int)a << (16 * w);
+      packed |= (uint64_t)(uint8_t)(int8_t)(int)b << (16 * w + 8);
+    }
+    qv[u] = packed;
+  }
+
+  int row = -1;
+  if (mine) {
+    const int64_t r = (int64_t)first + (p >> 16);
+    row = (r >= 0 && r < A) ? (int)r : -1;
+  }
+  if (mine) {
+    row_idx[g * K + lane] = row;
+    if (row >= 0) {
+      int32_t* a = assist + (int64_t)row * 3;
+      a[0] = s;
+      a[1] = t;
+      a[2] = lane;
+      dyn_scale[row] = scale;
+    }
+  }
+  uint64_t rem = __ballot(row >= 0);
+  while (rem) {
+    const int k = __ffsll((unsigned long long)rem) - 1;
+    rem &= rem - 1;
+    const int rk = __builtin_amdgcn_readlane(row, k);
+    uint64_t* dst = reinterpret_cast<uint64_t*>(expand_q + (int64_t)rk * nvec * 8);
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) {
+      const int idx = lane + u * 64;
+      if (idx < nvec) {
+        if (MDC_GATHER_NT_STORES) __builtin_nontemporal_store(qv[u], dst + idx);
+        else dst[idx] = qv[u];
+      }
+    }
+  }
+}
+
 // Empty batch: every count is zero.
 __global__ __launch_bounds__(64) void k_zero_counts(int32_t* __restrict__ ep_recv, int64_t* __restrict__ expert_nums,
                                                     int L, int W) {
@@ -403,16 +523,6 @@ struct CombineTables {
   const int32_t* counts[MDC_MAX_COMBINE_WORLD];
 };
 
-__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// fp32 -> bf16 round to nearest, ties to even (the CAST_RINT of [TL] combine):
-// add 0x7FFF plus the lowest kept bit, keep the top 16 bits; NaN -> quiet NaN.
-__device__ __forceinline__ unsigned bf16_rne(float f) {
-  const unsigned u = __float_as_uint(f);
-  if (f != f) return ((u >> 16) & 0x8000u) | 0x7FC0u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 
 // Route (r, t, k) is present when the token is active, 0 <= e < E, and row
 // idx[t][k] of destination j = e / L is below min(count_j, A) and holds the
@@ -949,6 +1059,29 @@ mdc_status gather_impl(const DispatchPlan& p, const void* x, void* expand_x, int
   return launched();
 }
 
+mdc_status gather_q_impl(const DispatchPlan& p, const void* x, int8_t* expand_q, float* dyn_scale, int32_t* assist,
+                         int32_t* ep_recv, int64_t* expert_nums, int32_t* row_idx, char* ws, hipStream_t st) {
+  const int32_t* P = reinterpret_cast<const int32_t*>(ws + p.off_p);
+  const int32_t* cnt = reinterpret_cast<const int32_t*>(ws + p.off_cnt);
+  (void)hipGetLastError();
+  const int64_t tokens = (int64_t)p.W * p.BS;
+  if (tokens == 0) {
+    hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(64), 0, st, ep_recv, expert_nums, p.L, p.W);
+    return launched();
+  }
+  const int vpl = (p.nvec + 63) / 64;
+#define MDC_LAUNCH_GQ(V)                                                                                          \
+  hipLaunchKernelGGL(k_dispatch_gather_q<V>, dim3((unsigned)tokens), dim3(64), 0, st, static_cast<const v4u*>(x), \
+                     P, cnt, expand_q, dyn_scale, assist, ep_recv, expert_nums, row_idx, p.BS, p.K, p.L, p.W,   \
+                     p.TPG, p.G, p.A, p.nvec)
+  if (vpl <= 4) MDC_LAUNCH_GQ(4);
+  else if (vpl <= 8) MDC_LAUNCH_GQ(8);
+  else if (vpl <= 12) MDC_LAUNCH_GQ(12);
+  else MDC_LAUNCH_GQ(16);
+#undef MDC_LAUNCH_GQ
+  return launched();
+}
+
 struct FfnPlan {
   int64_t A;
   int H, N, L;
@@ -977,6 +1110,38 @@ mdc_status check_ffn(const mdc_shape* sh, int inter_n) {
   if (inter_n <= 0 || (inter_n % (2 * kFfnBN)) != 0) return MDC_ERR_INVALID;
   if ((sh->hidden % kFfnBN) != 0) return MDC_ERR_INVALID;
   return MDC_OK;
+}
+
+mdc_status ffn_impl(const FfnPlan& f, const void* expand_x, const int8_t* expand_q, const float* dyn_scale,
+                    const int64_t* expert_token_nums, const int8_t* w1, const float* w1_scale, const int8_t* w2,
+                    const float* w2_scale, void* y, char* ws, hipStream_t s) {
+  int8_t* q1 = reinterpret_cast<int8_t*>(ws + f.off_q1);
+  float* s1 = reinterpret_cast<float*>(ws + f.off_s1);
+
+  uint16_t* g = reinterpret_cast<uint16_t*>(ws + f.off_g);
+  int8_t* q2 = reinterpret_cast<int8_t*>(ws + f.off_q2);
+  float* s2 = reinterpret_cast<float*>(ws + f.off_s2);
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const unsigned quant_wgs = (unsigned)(cus * 8);
+  // one 8-wavefront workgroup per CU (both GEMMs need more than 128 VGPRs)
+  const unsigned g1 = (unsigned)(((cus + 7) / 8) * 8);
+  const unsigned g2 = g1;
+  (void)hipGetLastError();
+  if (expand_q == nullptr) {
+    hipLaunchKernelGGL(k_ffn_quant_rows, dim3(quant_wgs), dim3(256), 0, s, static_cast<const v4u*>(expand_x), q1,
+                       s1, expert_token_nums, f.L, f.A, f.H / 8);
+  } else {
+    q1 = const_cast<int8_t*>(expand_q);   // rows already quantised by mdc_dispatch_quant
+    s1 = const_cast<float*>(dyn_scale);
+  }
+  hipLaunchKernelGGL(k_ffn_gemm<true>, dim3(g1), dim3(kFfnThreads), 0, s, q1, s1, w1, w1_scale, g,
+                     expert_token_nums, f.L, f.A, f.H, f.N, f.N / 2);
+  hipLaunchKernelGGL(k_ffn_quant_rows, dim3(quant_wgs), dim3(256), 0, s, reinterpret_cast<const v4u*>(g), q2, s2,
+                     expert_token_nums, f.L, f.A, f.N / 2 / 8);
+  hipLaunchKernelGGL(k_ffn_gemm<false>, dim3(g2), dim3(kFfnThreads), 0, s, q2, s2, w2, w2_scale,
+                     static_cast<uint16_t*>(y), expert_token_nums, f.L, f.A, f.N / 2, f.H, f.H);
+  return launched();
 }
 
 }  // namespace
@@ -1047,6 +1212,46 @@ mdc_status mdc_dispatch(const mdc_shape* shape, const void* x, const int32_t* ex
   st = layout_impl(p, expert_ids, x_active_mask, ws, s);
   if (st != MDC_OK) return st;
   return gather_impl(p, x, expand_x, assist_info, ep_recv_counts, expert_token_nums, expanded_row_idx, ws, s);
+}
+
+mdc_status mdc_dispatch_quant_gather(const mdc_shape* shape, const void* x, int8_t* expand_q, float* dynamic_scales,
+                                     int32_t* assist_info, int32_t* ep_recv_counts, int64_t* expert_token_nums,
+                                     int32_t* expanded_row_idx, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  mdc_status st = check_shape(shape);
+  if (st != MDC_OK) return st;
+  const DispatchPlan p = make_plan(shape);
+  if (p.nvec > 64 * kQuantRowVec) return MDC_ERR_INVALID;
+  if (workspace == nullptr || ep_recv_counts == nullptr || expert_token_nums == nullptr) return MDC_ERR_NULLPTR;
+  if (p.BS > 0 && (x == nullptr || expanded_row_idx == nullptr)) return MDC_ERR_NULLPTR;
+  if (p.BS > 0 && p.A > 0 && (expand_q == nullptr || dynamic_scales == nullptr || assist_info == nullptr))
+    return MDC_ERR_NULLPTR;
+  if (!aligned16(x) || !aligned16(expand_q)) return MDC_ERR_INVALID;
+  if (workspace_bytes < p.bytes) return MDC_ERR_WORKSPACE;
+  return gather_q_impl(p, x, expand_q, dynamic_scales, assist_info, ep_recv_counts, expert_token_nums,
+                       expanded_row_idx, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+mdc_status mdc_dispatch_quant(const mdc_shape* shape, const void* x, const int32_t* expert_ids,
+                              const uint8_t* x_active_mask, int8_t* expand_q, float* dynamic_scales,
+                              int32_t* assist_info, int32_t* ep_recv_counts, int64_t* expert_token_nums,
+                              int32_t* expanded_row_idx, void* workspace, size_t workspace_bytes, void* stream) {
+  mdc_status st = check_shape(shape);
+  if (st != MDC_OK) return st;
+  const DispatchPlan p = make_plan(shape);
+  if (p.nvec > 64 * kQuantRowVec) return MDC_ERR_INVALID;
+  if (ep_recv_counts == nullptr || expert_token_nums == nullptr || workspace == nullptr) return MDC_ERR_NULLPTR;
+  if (p.BS > 0 && (x == nullptr || expert_ids == nullptr || expanded_row_idx == nullptr)) return MDC_ERR_NULLPTR;
+  if (p.BS > 0 && p.A > 0 && (expand_q == nullptr || dynamic_scales == nullptr || assist_info == nullptr))
+    return MDC_ERR_NULLPTR;
+  if (!aligned16(x) || !aligned16(expand_q)) return MDC_ERR_INVALID;
+  if (workspace_bytes < p.bytes) return MDC_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = layout_impl(p, expert_ids, x_active_mask, ws, s);
+  if (st != MDC_OK) return st;
+  return gather_q_impl(p, x, expand_q, dynamic_scales, assist_info, ep_recv_counts, expert_token_nums,
+                       expanded_row_idx, ws, s);
 }
 
 mdc_status mdc_combine_workspace_size(const mdc_shape* shape, size_t* bytes) {
@@ -1144,29 +1349,26 @@ mdc_status mdc_ffn(const mdc_shape* shape, int32_t inter_n, const void* expand_x
     return MDC_ERR_NULLPTR;
   if (!aligned16(expand_x) || !aligned16(w1) || !aligned16(w2) || !aligned16(y)) return MDC_ERR_INVALID;
   if (workspace_bytes < f.bytes) return MDC_ERR_WORKSPACE;
-  char* ws = static_cast<char*>(workspace);
-  int8_t* q1 = reinterpret_cast<int8_t*>(ws + f.off_q1);
-  float* s1 = reinterpret_cast<float*>(ws + f.off_s1);
-  uint16_t* g = reinterpret_cast<uint16_t*>(ws + f.off_g);
-  int8_t* q2 = reinterpret_cast<int8_t*>(ws + f.off_q2);
-  float* s2 = reinterpret_cast<float*>(ws + f.off_s2);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const unsigned quant_wgs = (unsigned)(cus * 8);
-  // one 8-wavefront workgroup per CU (both GEMMs need more than 128 VGPRs)
-  const unsigned g1 = (unsigned)(((cus + 7) / 8) * 8);
-  const unsigned g2 = g1;
-  (void)hipGetLastError();
-  hipLaunchKernelGGL(k_ffn_quant_rows, dim3(quant_wgs), dim3(256), 0, s, static_cast<const v4u*>(expand_x), q1, s1,
-                     expert_token_nums, f.L, f.A, f.H / 8);
-  hipLaunchKernelGGL(k_ffn_gemm<true>, dim3(g1), dim3(kFfnThreads), 0, s, q1, s1, w1, w1_scale, g,
-                     expert_token_nums, f.L, f.A, f.H, f.N, f.N / 2);
-  hipLaunchKernelGGL(k_ffn_quant_rows, dim3(quant_wgs), dim3(256), 0, s, reinterpret_cast<const v4u*>(g), q2, s2,
-                     expert_token_nums, f.L, f.A, f.N / 2 / 8);
-  hipLaunchKernelGGL(k_ffn_gemm<false>, dim3(g2), dim3(kFfnThreads), 0, s, q2, s2, w2, w2_scale,
-                     static_cast<uint16_t*>(y), expert_token_nums, f.L, f.A, f.N / 2, f.H, f.H);
-  return launched();
+  return ffn_impl(f, expand_x, nullptr, nullptr, expert_token_nums, w1, w1_scale, w2, w2_scale, y,
+                  static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
+
+mdc_status mdc_ffn_quant_input(const mdc_shape* shape, int32_t inter_n, const int8_t* expand_q,
+                               const float* dynamic_scales, const int64_t* expert_token_nums, const int8_t* w1,
+                               const float* w1_scale, const int8_t* w2, const float* w2_scale, void* y,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  mdc_status st = check_ffn(shape, inter_n);
+  if (st != MDC_OK) return st;
+  const FfnPlan f = make_ffn_plan(shape, inter_n);
+  if (f.A == 0) return MDC_OK;
+  if (expand_q == nullptr || dynamic_scales == nullptr || expert_token_nums == nullptr || w1 == nullptr ||
+      w1_scale == nullptr || w2 == nullptr || w2_scale == nullptr || y == nullptr || workspace == nullptr)
+    return MDC_ERR_NULLPTR;
+  if (!aligned16(expand_q) || !aligned16(w1) || !aligned16(w2) || !aligned16(y)) return MDC_ERR_INVALID;
+  if (workspace_bytes < f.bytes) return MDC_ERR_WORKSPACE;
+  return ffn_impl(f, nullptr, expand_q, dynamic_scales, expert_token_nums, w1, w1_scale, w2, w2_scale, y,
+                  static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
 
 }  // extern "C"

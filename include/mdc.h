@@ -171,6 +171,44 @@ mdc_status mdc_dispatch(const mdc_shape* shape,
                         void* stream);
 
 /* ------------------------------------------------------------------------
+ * Quantised dispatch ([CV4] parameter notes: commQuantMode 2 = int8
+ * quantisation during communication, with per-row dynamic scales; [PTO]
+ * FrontReorder Stage: quantised token rows carrying their scale).
+ *
+ * As mdc_dispatch / mdc_dispatch_gather (same placement, triplets, inverse
+ * index and counts, same workspace and layout stage), but each received row
+ * is the int8 quantisation of its source token's row, decided in fp32:
+ * amax = max|x|, codes clamp(rint(x * (127 / amax)), -127, 127), and
+ * dynamic_scales[row] = amax / 127 (a zero row gives codes 0 and scale 0).
+ *   expand_q        [A][H] int8 (16-byte aligned)
+ *   dynamic_scales  [A] fp32
+ * H <= 8192 (a whole row is held in one wavefront's registers).
+ * ------------------------------------------------------------------------ */
+mdc_status mdc_dispatch_quant_gather(const mdc_shape* shape,
+                                     const void* x,
+                                     int8_t* expand_q,
+                                     float* dynamic_scales,
+                                     int32_t* assist_info,
+                                     int32_t* ep_recv_counts,
+                                     int64_t* expert_token_nums,
+                                     int32_t* expanded_row_idx,
+                                     void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+mdc_status mdc_dispatch_quant(const mdc_shape* shape,
+                              const void* x,
+                              const int32_t* expert_ids,
+                              const uint8_t* x_active_mask,
+                              int8_t* expand_q,
+                              float* dynamic_scales,
+                              int32_t* assist_info,
+                              int32_t* ep_recv_counts,
+                              int64_t* expert_token_nums,
+                              int32_t* expanded_row_idx,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* ------------------------------------------------------------------------
  * Combine ([CV4] Function formula without TP; [TL] moe_combine_kernel;
  * [PTO] Combine / Unpermute stages)
  *
@@ -265,6 +303,22 @@ mdc_status mdc_ffn(const mdc_shape* shape,
                    void* y,
                    void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/* mdc_ffn on rows already quantised by mdc_dispatch_quant: expand_q [A][H]
+ * int8 and dynamic_scales [A] fp32 take the place of q1 and s1 (the codes
+ * equal what mdc_ffn computes from the bf16 rows, so y is the same). */
+mdc_status mdc_ffn_quant_input(const mdc_shape* shape,
+                               int32_t inter_n,
+                               const int8_t* expand_q,
+                               const float* dynamic_scales,
+                               const int64_t* expert_token_nums,
+                               const int8_t* w1,
+                               const float* w1_scale,
+                               const int8_t* w2,
+                               const float* w2_scale,
+                               void* y,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 #ifdef __cplusplus
 }

@@ -172,6 +172,21 @@ def dispatch(x: Optional[np.ndarray], ids: np.ndarray, mask: Optional[np.ndarray
     return DispatchResult(ex, assist, ep_recv_counts, expert_token_nums, counts, total, rowmap)
 
 
+def dispatch_quant(x: np.ndarray, ids: np.ndarray, mask: Optional[np.ndarray], d: int, experts: int,
+                   capacity: int):
+    """Quantised dispatch: the rows of dispatch(), each the per-row int8 quantisation of its token.
+
+    [CV4] parameter notes: commQuantMode 2 quantises communicated rows to int8
+    with a dynamic per-row scale; [PTO] FrontReorder Stage writes quantised
+    token rows.  The quantiser is quant_rows (fp32 decisions).  Returns the
+    DispatchResult and (codes [n][H] int8, scales [n] fp32).
+    """
+    res = dispatch(x, ids, mask, d, experts, capacity)
+    q, sc = quant_rows(bf16_to_f32(res.expand_x)) if res.expand_x.shape[0] else (
+        np.zeros((0, x.shape[-1]), np.int8), np.zeros(0, np.float32))
+    return res, q, sc
+
+
 # ----------------------------------------------------------------------------
 # Experts used by the tests in place of the FFN
 # ----------------------------------------------------------------------------
