@@ -685,17 +685,21 @@ __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
 //   g      = silu(h[:, j]) * h[:, j + N/2],  j < N/2        (fused in GMM1's epilogue)
 //   q2, s2 = per-row int8 quantisation of g (quantised while GMM2 loads its tiles)
 //   y      = bf16((q2 . W2[e]^T) * s2[row] * w2s[e][h])
-// The GEMMs use v_mfma_i32_16x16x64_i8 on 256 x 128 output tiles (GMM1: 128
-// gate + 128 up weight rows per tile so gate and up land in the same lanes);
-// tiles are staged through LDS with a register prefetch of the next k step.
+// The GEMMs use v_mfma_i32_32x32x32_i8 on 256-token x 256-weight-row tiles
+// (GMM1: 128 gate + 128 up weight rows per tile so gate and up land in the
+// same lanes), eight wavefronts (two per SIMD) each holding a 128 x 64 int32
+// accumulator block in AGPRs, k staged through a double-buffered LDS ring 128
+// bytes deep; the output tile leaves through LDS as whole rows.
 // ---------------------------------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kFfnBM = 256;        // rows per tile
-constexpr int kFfnBN = 128;        // output columns per tile
-constexpr int kFfnBK = 64;         // k bytes per step (one MFMA k)
-constexpr int kFfnThreads = 512;   // 8 wavefronts: 4 along rows x 2 along columns
-constexpr int kLdsRow = 80;        // LDS row stride in bytes (64 + 16 pad)
+constexpr int kFfnBM = 256;        // token rows per tile
+constexpr int kFfnBW = 256;        // weight rows per tile (GMM1: 128 gate + 128 up)
+constexpr int kFfnBK = 128;        // k bytes per LDS stage
+constexpr int kFfnThreads = 512;   // 8 wavefronts: 2 along tokens x 4 along weight rows
+constexpr int kFfnStage = (kFfnBM + kFfnBW) * kFfnBK;   // bytes of one LDS stage
+constexpr int kFfnOutAlign = 128;  // GMM output widths (N/2 and H) must be multiples of this
 
 // Number of m-tiles over all experts: each expert's rows (contiguous,
 // expert-major, clipped at A) split into tiles of kFfnBM rows.
@@ -735,7 +739,15 @@ __device__ void ffn_tile_rows(const int64_t* __restrict__ expert_nums, int L, in
   row0 = row_end = 0;
 }
 
-__device__ __forceinline__ float ffn_silu(float a) { return a / (1.0f + __expf(-a)); }
+__device__ __forceinline__ float ffn_silu(float a) { return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
+
+// Two fp32 -> two bf16 (round to nearest even, one v_cvt_pk_bf16_f32), lo in
+// the low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t ffn_pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
 
 // Per-row int8 quantisation of bf16 rows of `width` elements, decided in fp32
 // exactly as: amax = max|v|, inv = 127 / amax, q = clamp(rint(v * inv), -127,
@@ -801,41 +813,215 @@ __global__ __launch_bounds__(256) void k_ffn_quant_rows(
   }
 }
 
-// Persistent grouped GEMM, C = A . W[e]^T with A int8 [rows][K] and W int8
-// [L][Nw][K].  GLU = true (GMM1): each output tile pairs 128 gate rows of W
-// (columns n) with the 128 up rows (columns N/2 + n); the epilogue dequantises
-// both, applies silu(gate) * up and writes bf16 g.  GLU = false (GMM2): the
-// epilogue dequantises and writes bf16 y.  Dequant: acc * row_scale[row] *
-// w_scale[e][col].
+// Persistent grouped GEMM, C = A . W[e]^T with A int8 [rows][K] (token rows
+// of expert e) and W int8 [L][Nw][K].  GLU = true (GMM1): each tile pairs 128
+// gate rows of W (columns n) with the 128 up rows (columns N/2 + n); the
+// epilogue dequantises both, applies silu(gate) * up and writes bf16 g.
+// GLU = false (GMM2): the epilogue dequantises and writes bf16 y.  Dequant:
+// acc * row_scale[row] * w_scale[e][col].
 //
-// Tiles: T = (m-tiles over all experts) x (Nout / 128).  The launch holds one
-// workgroup per resident slot; workgroup b walks tiles i*G + (b % 8)*(G/8) +
-// b / 8.  Hardware places workgroup b on XCD b % 8, so each XCD walks a
-// contiguous run of tiles; tiles are ordered in groups of 4 m-tiles x 8
-// n-tiles (m fastest), so the 32 tiles an XCD runs together share 4 A tiles
-// and 8 W tiles in its L2.
+// MFMA v_mfma_i32_32x32x32_i8: lane l supplies row l % 32 and k bytes
+// 16 (l / 32) .. +16 of each 32 x 32 operand block and receives
+// C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32], r < 16.  The weight block is the
+// first operand and the token block the second, so each lane holds runs of 4
+// consecutive output columns of one token and stores each run as one 8-byte
+// word.  (This MFMA also updates its accumulator in place, which the 16 x 16
+// shapes do not get from the compiler: they copy accumulators every step.)
+//
+// LDS: two stages, each [256 token rows][128 B] + [256 weight rows][128 B],
+// filled straight from global memory by buffer_load ... lds (each lane's 16
+// bytes land at the wavefront's LDS base + 16 * lane).  The 16-byte chunk c
+// of row r sits at chunk c ^ ((r / 2) & 7) of that row, so any 16 consecutive
+// rows read at one chunk cover all 16 bank groups of 16 bytes.  Stage s + 1 is
+// in flight while stage s feeds the MFMAs: one wait and one barrier per
+// 128-byte k step.  Out-of-range rows (past the expert's rows or past Nw) read
+// as zero through the buffer descriptors' range checks and are never stored.
+//
+// Tiles: T = (m-tiles over all experts) x (output columns / tile columns).
+// The launch holds one workgroup per CU; workgroup b walks tiles
+// i*G + (b % 8)*(G/8) + b / 8.  Hardware places workgroup b on XCD b % 8, so
+// each XCD walks a contiguous run of tiles; tiles are ordered in groups of 4
+// m-tiles x 8 n-tiles (m fastest), so the tiles an XCD runs together share A
+// and W tiles in its L2.
+// The k loop of one tile (see k_ffn_gemm).  Stage ks + 1 travels global ->
+// registers during stage ks - 1 and registers -> LDS during stage ks, into the
+// buffer nobody reads in stage ks; one barrier ends each stage.  Fragments of
+// k substep q + 1 are read while the MFMAs of substep q run, and the last
+// substep's MFMAs run after the stage barrier, beside the next stage's first
+// fragment reads.  Scheduling groups (sched_group_barrier masks: 0x8 MFMA,
+// 0x100 LDS read, 0x200 LDS write, 0x20 global read) interleave the memory
+// instructions with the MFMAs.
+struct FfnStaging {
+  __amdgpu_buffer_rsrc_t ra, rw;   // token rows, weight rows (range-checked)
+  unsigned va, vw;                 // lane offsets of this thread's i = 0 rows
+  unsigned whi;                    // extra weight offset of rows i >= 2 (GMM1: gate -> up)
+  int K;
+  int lds_off;                     // this thread's LDS byte offset for i = 0
+};
+
+template <bool GLU>
+__device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const FfnStaging& st, int wt, int wn,
+                                          const int (&fr)[4]) {
+  constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;
+  // LDS row of weight block j (32 rows) within the stage's weight tile
+  auto wrow = [&](int j) {
+    if (GLU) return j == 0 ? wn * 32 : NCOLS + wn * 32;
+    return wn * 64 + 32 * j;
+  };
+  v4i sa[4], sw[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sa[i] = __builtin_amdgcn_raw_buffer_load_b128(st.ra, st.va + (unsigned)(64 * i * st.K), (unsigned)k0, 0);
+      sw[i] = __builtin_amdgcn_raw_buffer_load_b128(st.rw, st.vw + (unsigned)(64 * i * st.K) + (i >= 2 ? st.whi : 0u),
+                                                    (unsigned)k0, 0);
+    }
+  };
+  auto lwrite = [&](uint8_t* buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<v4i*>(buf + st.lds_off + 64 * i * kFfnBK) = sa[i];
+      *reinterpret_cast<v4i*>(buf + kFfnBM * kFfnBK + st.lds_off + 64 * i * kFfnBK) = sw[i];
+    }
+  };
+  auto frags = [&](const uint8_t* sb, int q, v4i (&tf)[4], v4i (&wf)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tf[i] = *reinterpret_cast<const v4i*>(sb + (wt * 128 + 32 * i) * kFfnBK + fr[q]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      wf[j] = *reinterpret_cast<const v4i*>(sb + kFfnBM * kFfnBK + wrow(j) * kFfnBK + fr[q]);
+  };
+  auto mfmas = [&](const v4i (&tf)[4], const v4i (&wf)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j], tf[i], acc[j][i], 0, 0, 0);
+  };
+  auto interleave_reads = [&]() {
+#pragma unroll
+    for (int n = 0; n < 6; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto interleave_staging = [&]() {
+#pragma unroll
+    for (int n = 0; n < 6; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  const int nk = st.K / kFfnBK;
+  v4i tf[4], wf[2], tg[4], wg[2];
+  gload(0);
+  lwrite(lds);
+  __syncthreads();
+  gload(min(1, nk - 1) * kFfnBK);
+  frags(lds, 0, tf, wf);
+  for (int ks = 0; ks < nk; ++ks) {
+    uint8_t* cur = lds + (ks & 1) * kFfnStage;
+    uint8_t* nxt = lds + ((ks + 1) & 1) * kFfnStage;
+    frags(cur, 1, tg, wg);
+    mfmas(tf, wf);
+    interleave_reads();
+    // stage ks + 1: registers -> LDS, then stage ks + 2: global -> registers
+    // (the last iterations repeat the last stage; nobody reads it)
+    lwrite(nxt);
+    gload(min(ks + 2, nk - 1) * kFfnBK);
+    frags(cur, 2, tf, wf);
+    mfmas(tg, wg);
+    interleave_staging();
+    frags(cur, 3, tg, wg);
+    mfmas(tf, wf);
+    interleave_reads();
+    __syncthreads();
+    frags(nxt, 0, tf, wf);
+    mfmas(tg, wg);
+    interleave_reads();
+  }
+}
+
+// Persistent grouped GEMM, C = A . W[e]^T with A int8 [rows][K] (token rows
+// of expert e) and W int8 [L][Nw][K].  GLU = true (GMM1): each tile pairs 128
+// gate rows of W (columns n) with the 128 up rows (columns N/2 + n); the
+// epilogue dequantises both, applies silu(gate) * up and writes bf16 g.
+// GLU = false (GMM2): the epilogue dequantises and writes bf16 y.  Dequant:
+// acc * row_scale[row] * w_scale[e][col].
+//
+// MFMA v_mfma_i32_32x32x32_i8: lane l supplies row l % 32 and k bytes
+// 16 (l / 32) .. +16 of each 32 x 32 operand block and receives
+// C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32], r < 16.  The weight block is the
+// first operand and the token block the second, so each lane holds runs of 4
+// consecutive output columns of one token.  (This MFMA also updates its
+// accumulator in place, which the 16 x 16 shapes do not get from the
+// compiler: they copy accumulators every step.)
+//
+// Wavefront wv = 2 wn + wt holds tokens 128 wt .. +128 of the tile and weight
+// rows 32 wn .. +32 (GMM1: those gate rows and the matching up rows) or
+// 64 wn .. +64 (GMM2).  Two wavefronts per SIMD keep the LDS busy while the
+// other one waits.
+//
+// LDS: two stages, each [256 token rows][128 B] + [256 weight rows][128 B].
+// The 16-byte chunk c of row r sits at chunk c ^ ((r / 2) & 7) of that row,
+// so any 16 consecutive rows read at one chunk cover all 16 bank groups.
+// Out-of-range rows (past the expert's rows or past Nw) read as zero through
+// the buffer descriptors' range checks and are never stored.
+//
+// Epilogue, per token half: the wavefronts of that half write their bf16
+// outputs into LDS rows (row pitch padded by 8 bytes so 32 rows written at
+// one column fall in distinct banks), then all wavefronts store whole rows
+// with 16-byte stores.
+//
+// Tiles: T = (m-tiles over all experts) x (output columns / tile columns).
+// The launch holds one workgroup per CU; workgroup b walks tiles
+// i*G + (b % 8)*(G/8) + b / 8.  Hardware places workgroup b on XCD b % 8, so
+// each XCD walks a contiguous run of tiles; tiles are ordered in groups of 4
+// m-tiles x 8 n-tiles (m fastest), so the tiles an XCD runs together share A
+// and W tiles in its L2.
 template <bool GLU>
 __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(
     const int8_t* __restrict__ a_src, const float* __restrict__ row_scale,
     const int8_t* __restrict__ w, const float* __restrict__ w_scale, uint16_t* __restrict__ out,
     const int64_t* __restrict__ expert_nums, int L, int64_t A, int K, int Nw, int Nout) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[kFfnBM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[(GLU ? 2 * kFfnBN : kFfnBN) * kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFfnStage];
+  __shared__ float sc_row[kFfnBM];   // row scales of the tile's token rows
+  __shared__ float sc_col[kFfnBW];   // weight-row scales (GMM1: 128 gate, then 128 up)
   __shared__ int tile_info[4];
+  constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;   // output columns per tile
+  constexpr int OU = NCOLS / 8;                      // 16-byte output units per tile row
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int wm = wv & 3;
-  const int wn = wv >> 2;
+  // wavefront-uniform values are read into scalar registers (readfirstlane)
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wt = wv & 1;    // token half of the tile
+  const int wn = wv >> 1;   // weight-row quarter of the tile
   const int G = gridDim.x;
-  const int nn = Nout / kFfnBN;
+  const int nn = (Nout + NCOLS - 1) / NCOLS;
   constexpr int GM = 4, GN = 8;
   if (tid == 0) tile_info[3] = ffn_total_mtiles(expert_nums, L, A);
   __syncthreads();
-  const int MT = tile_info[3];
+  const int MT = __builtin_amdgcn_readfirstlane(tile_info[3]);
   const int64_t T = (int64_t)MT * nn;
   const int b = blockIdx.x;
   const int lin = (b % 8) * (G / 8) + b / 8;   // XCD-contiguous walk (G is a multiple of 8)
+
+  // staging: thread t moves chunk t & 7 of rows 64 i + t / 8 (i < 4) of both
+  // tiles; in LDS that chunk sits at slot (t & 7) ^ ((row / 2) & 7), and
+  // (row / 2) & 7 = (t / 16) & 7 for every i
+  const int st_row = tid >> 3;
+  const int st_chunk = tid & 7;
+  const int st_lds = st_row * kFfnBK + ((st_chunk ^ ((tid >> 4) & 7)) << 4);
+  // fragment reads: lane l reads row l & 31, chunk 2 s + l / 32 (k substep s)
+  int fr[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) fr[q] = (lane & 31) * kFfnBK + (((2 * q + (lane >> 5)) ^ ((lane >> 1) & 7)) << 4);
 
   for (int64_t t = lin; t < T; t += G) {
     // tile t -> (m-tile, n-tile): groups of GM m-tiles x GN n-tiles, m fastest
@@ -858,101 +1044,94 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(
       tile_info[2] = re;
     }
     __syncthreads();
-    const int e = tile_info[0];
+    const int e = __builtin_amdgcn_readfirstlane(tile_info[0]);
     if (e < 0) continue;
-    const int row0 = tile_info[1];
-    const int row_end = tile_info[2];
-    const int n0 = nt * kFfnBN;
+    const int row0 = __builtin_amdgcn_readfirstlane(tile_info[1]);
+    const int row_end = __builtin_amdgcn_readfirstlane(tile_info[2]);
+    const int n0 = nt * NCOLS;
 
-    // Global -> register staging: thread t loads 32 k-bytes of A row t/2 and of
-    // W row t/2 (GLU: 256 rows, gate then up) or 16 bytes of W row t/4.
-    const int a_r = tid >> 1;
-    const int a_k = (tid & 1) * 32;
-    const int64_t a_row = (int64_t)min(row0 + a_r, row_end - 1);
-    int b_r, b_k;
-    int64_t b_row;
-    if (GLU) {
-      b_r = tid >> 1;
-      b_k = (tid & 1) * 32;
-      b_row = (int64_t)e * Nw + (b_r < kFfnBN ? n0 + b_r : Nw / 2 + n0 + (b_r - kFfnBN));
+    // buffer descriptors: token rows [row0, min(row_end, row0 + 256)) and
+    // weight rows [n0, Nw) of expert e (GMM1 up rows at Nw/2 + n0 + ...)
+    const int rows_here = min(row_end - row0, kFfnBM);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(a_src + (int64_t)row0 * K), (short)0, rows_here * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(w + ((int64_t)e * Nw + n0) * K), (short)0, (Nw - n0) * K, 0x00020000);
+    // weight rows (relative to n0): i < 2 -> rows 64 i + t / 8 (GMM1: gate),
+    // i >= 2 -> GMM1: up rows Nw/2 + 64 (i - 2) + t / 8, GMM2: rows 64 i + t / 8
+    const unsigned whi = GLU ? (unsigned)((Nw / 2 - NCOLS) * K) : 0u;
+    const unsigned v0 = (unsigned)(st_row * K + st_chunk * 16);
+    const FfnStaging st{ra, rw, v0, v0, whi, K, st_lds};
+
+    // the epilogue's scales, read from LDS after the k loop's first barrier
+    if (tid < kFfnBM) {
+      sc_row[tid] = row_scale[min(row0 + tid, row_end - 1)];
     } else {
-      b_r = tid >> 2;
-      b_k = (tid & 3) * 16;
-      b_row = (int64_t)e * Nw + n0 + b_r;
-    }
-    const int8_t* ap = a_src + a_row * K + a_k;
-    const int8_t* bp = w + b_row * K + b_k;
-    v4i ra[2], rb[2];
-    auto load_tiles = [&](int k0) {
-      ra[0] = *reinterpret_cast<const v4i*>(ap + k0);
-      ra[1] = *reinterpret_cast<const v4i*>(ap + k0 + 16);
-      rb[0] = *reinterpret_cast<const v4i*>(bp + k0);
-      if (GLU) rb[1] = *reinterpret_cast<const v4i*>(bp + k0 + 16);
-    };
-    auto store_tiles = [&]() {
-      *reinterpret_cast<v4i*>(As + a_r * kLdsRow + a_k) = ra[0];
-      *reinterpret_cast<v4i*>(As + a_r * kLdsRow + a_k + 16) = ra[1];
-      *reinterpret_cast<v4i*>(Bs + b_r * kLdsRow + b_k) = rb[0];
-      if (GLU) *reinterpret_cast<v4i*>(Bs + b_r * kLdsRow + b_k + 16) = rb[1];
-    };
-
-    constexpr int NJ = 4;  // 16-column MFMA tiles per wavefront (64 columns)
-    v4i acc[4][NJ];
-    v4i accu[4][NJ];  // GLU: up columns
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        acc[i][j] = v4i{0, 0, 0, 0};
-        accu[i][j] = v4i{0, 0, 0, 0};
-      }
-
-    const int nk = K / kFfnBK;
-    load_tiles(0);
-    const int frag_off = (lane & 15) * kLdsRow + 16 * (lane >> 4);
-    for (int ks = 0; ks < nk; ++ks) {
-      __syncthreads();
-      store_tiles();
-      __syncthreads();
-      if (ks + 1 < nk) load_tiles((ks + 1) * kFfnBK);
-      v4i af[4], bf[NJ], bu[NJ];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const v4i*>(As + (wm * 64 + 16 * i) * kLdsRow + frag_off);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        bf[j] = *reinterpret_cast<const v4i*>(Bs + (wn * 64 + 16 * j) * kLdsRow + frag_off);
-        if (GLU) bu[j] = *reinterpret_cast<const v4i*>(Bs + (kFfnBN + wn * 64 + 16 * j) * kLdsRow + frag_off);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-          if (GLU) accu[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bu[j], accu[i][j], 0, 0, 0);
-        }
+      const int c = tid - kFfnBM;
+      const int wr = GLU ? (c < NCOLS ? n0 + c : Nw / 2 + n0 + (c - NCOLS)) : min(n0 + c, Nw - 1);
+      sc_col[c] = w_scale[(int64_t)e * Nw + wr];
     }
 
-    // Epilogue.  Lane l holds rows 4*(l/16) + jj of each 16 x 16 tile, column l % 16.
-    const float* wsc = w_scale + (int64_t)e * Nw;
+    // acc[j][i]: weight block j (32 rows), token block i (32 rows)
+    v16i acc[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j][i] = v16i{};
+    ffn_kloop<GLU>(lds, acc, st, wt, wn, fr);
+
+    // Epilogue.  Lane l holds, for each (j, i) and run q < 4, token
+    // 32 i + (l & 31) of the wavefront's token half and weight rows
+    // 32 j + 8 q + 4 (l / 32) + 0..3 of its block j.  The bf16 tile goes to
+    // LDS as [256 rows][NCOLS] with 16-byte unit u of row r at unit
+    // u ^ (r % OU), then leaves as whole rows, 16 bytes per thread.
+    __syncthreads();   // every wavefront is done reading the k loop's stages
+    const int cq = 4 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const int trow = wt * 128 + 32 * i + (lane & 31);
+      const float rs = sc_row[trow];
+      uint8_t* orow = lds + trow * (NCOLS * 2);
+      auto put = [&](int c, uint32_t lo, uint32_t hi) {   // c: tile column, multiple of 4
+        const int u = (c >> 3) ^ (trow % OU);
+        *reinterpret_cast<uint2*>(orow + u * 16 + (c & 4) * 2) = uint2{lo, hi};
+      };
+      if (GLU) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int row = row0 + wm * 64 + 16 * i + 4 * (lane >> 4) + jj;
-        if (row >= row_end) continue;
-        const float rs = row_scale[row];
+        for (int q = 0; q < 4; ++q) {
+          const int c = wn * 32 + 8 * q + cq;
+          float v[4];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int col = n0 + wn * 64 + 16 * j + (lane & 15);
-          float v;
-          if (GLU) {
-            const float hg = (float)acc[i][j][jj] * rs * wsc[col];
-            const float hu = (float)accu[i][j][jj] * rs * wsc[Nw / 2 + col];
-            v = ffn_silu(hg) * hu;
-          } else {
-            v = (float)acc[i][j][jj] * rs * wsc[col];
+          for (int jj = 0; jj < 4; ++jj) {
+            const float hg = (float)acc[0][i][4 * q + jj] * rs * sc_col[c + jj];
+            const float hu = (float)acc[1][i][4 * q + jj] * rs * sc_col[NCOLS + c + jj];
+            v[jj] = ffn_silu(hg) * hu;
           }
-          out[(int64_t)row * Nout + col] = (uint16_t)bf16_rne(v);
+          put(c, ffn_pack_bf16(v[0], v[1]), ffn_pack_bf16(v[2], v[3]));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = wn * 64 + 32 * j + 8 * q + cq;
+            float v[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) v[jj] = (float)acc[j][i][4 * q + jj] * rs * sc_col[c + jj];
+            put(c, ffn_pack_bf16(v[0], v[1]), ffn_pack_bf16(v[2], v[3]));
+          }
+      }
+    }
+    __syncthreads();
+    {
+      const int u = tid % OU;
+      const int col = n0 + u * 8;
+#pragma unroll 4
+      for (int rr = tid / OU; rr < kFfnBM; rr += kFfnThreads / OU) {
+        const int row = row0 + rr;
+        if (row < row_end && col < Nout) {
+          const v4u v = *reinterpret_cast<const v4u*>(lds + rr * (NCOLS * 2) + ((u ^ (rr % OU)) * 16));
+          *reinterpret_cast<v4u*>(out + (int64_t)row * Nout + col) = v;
         }
       }
     }
@@ -1107,8 +1286,10 @@ FfnPlan make_ffn_plan(const mdc_shape* sh, int inter_n) {
 mdc_status check_ffn(const mdc_shape* sh, int inter_n) {
   const mdc_status st = check_shape(sh);
   if (st != MDC_OK) return st;
-  if (inter_n <= 0 || (inter_n % (2 * kFfnBN)) != 0) return MDC_ERR_INVALID;
-  if ((sh->hidden % kFfnBN) != 0) return MDC_ERR_INVALID;
+  if (inter_n <= 0 || (inter_n % (2 * kFfnOutAlign)) != 0) return MDC_ERR_INVALID;
+  if ((sh->hidden % kFfnOutAlign) != 0) return MDC_ERR_INVALID;
+  // one expert's weight matrix (N x H or H x N/2 bytes) is addressed with 32-bit offsets
+  if ((int64_t)inter_n * sh->hidden > INT32_MAX) return MDC_ERR_INVALID;
   return MDC_OK;
 }
 
@@ -1124,7 +1305,7 @@ mdc_status ffn_impl(const FfnPlan& f, const void* expand_x, const int8_t* expand
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const unsigned quant_wgs = (unsigned)(cus * 8);
-  // one 8-wavefront workgroup per CU (both GEMMs need more than 128 VGPRs)
+  // one workgroup per CU (128 KB of LDS each)
   const unsigned g1 = (unsigned)(((cus + 7) / 8) * 8);
   const unsigned g2 = g1;
   (void)hipGetLastError();
