@@ -701,42 +701,80 @@ constexpr int kFfnThreads = 512;   // 8 wavefronts: 2 along tokens x 4 along wei
 constexpr int kFfnStage = (kFfnBM + kFfnBW) * kFfnBK;   // bytes of one LDS stage
 constexpr int kFfnOutAlign = 128;  // GMM output widths (N/2 and H) must be multiples of this
 
-// Number of m-tiles over all experts: each expert's rows (contiguous,
-// expert-major, clipped at A) split into tiles of kFfnBM rows.
-__device__ int ffn_total_mtiles(const int64_t* __restrict__ expert_nums, int L, int64_t A) {
-  int64_t off = 0;
-  int t = 0;
-  for (int i = 0; i < L; ++i) {
-    const int64_t c = expert_nums[i];
-    const int64_t lo = off < A ? off : A;
-    const int64_t hi = (off + c) < A ? (off + c) : A;
-    t += (int)((hi - lo + kFfnBM - 1) / kFfnBM);
-    off += c;
+// Tile plan shared by both GEMMs.  Each local expert's rows (contiguous,
+// expert-major, clipped at A) split into m-tiles of kFfnBM rows.  The table
+// lists every full m-tile first (expert order), then each expert's partial
+// last m-tile by row count, largest first: the persistent GEMMs walk tiles
+// in table order, so the workgroups that run one tile more than the others
+// end on the cheapest tiles.  tiles[0].x = number of m-tiles; tiles[1 + m] =
+// {expert, first row, expert's end row, 0}.  One workgroup of 1024 threads;
+// L <= 2048 (two experts per thread).
+constexpr int kPlanThreads = 1024;
+
+// Exclusive prefix over the 2048 values held two per thread (elements 2t and
+// 2t + 1); returns the prefix of element 2t and the grand total.
+__device__ int64_t plan_scan_pair(int64_t a, int64_t b, int64_t* wsum, int64_t& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t own = a + b;
+  int64_t s = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t n = __shfl_up(s, o, 64);
+    if (lane >= o) s += n;
   }
-  return t;
+  if (lane == 63) wsum[wave] = s;
+  __syncthreads();
+  if (tid == 0) {
+    int64_t run = 0;
+    for (int w = 0; w < kPlanThreads / 64; ++w) {
+      const int64_t x = wsum[w];
+      wsum[w] = run;
+      run += x;
+    }
+    wsum[kPlanThreads / 64] = run;
+  }
+  __syncthreads();
+  const int64_t excl = wsum[wave] + s - own;
+  total = wsum[kPlanThreads / 64];
+  __syncthreads();   // wsum is reused by the next scan
+  return excl;
 }
 
-// Row range of m-tile `mblk`.
-__device__ void ffn_tile_rows(const int64_t* __restrict__ expert_nums, int L, int64_t A, int mblk,
-                              int& e, int& row0, int& row_end) {
-  int64_t off = 0;
-  int t = 0;
-  for (int i = 0; i < L; ++i) {
-    const int64_t c = expert_nums[i];
-    const int64_t lo = off < A ? off : A;
-    const int64_t hi = (off + c) < A ? (off + c) : A;
-    const int tiles = (int)((hi - lo + kFfnBM - 1) / kFfnBM);
-    if (mblk < t + tiles) {
-      e = i;
-      row0 = (int)(lo + (int64_t)(mblk - t) * kFfnBM);
-      row_end = (int)hi;
-      return;
+__global__ __launch_bounds__(kPlanThreads) void k_ffn_plan(const int64_t* __restrict__ expert_nums, int L, int64_t A,
+                                                           int4* __restrict__ tiles) {
+  __shared__ int rem_s[2 * kPlanThreads];
+  __shared__ int64_t wsum[kPlanThreads / 64 + 1];
+  const int tid = threadIdx.x;
+  const int e0 = 2 * tid, e1 = 2 * tid + 1;
+  const int64_t c0 = e0 < L ? expert_nums[e0] : 0, c1 = e1 < L ? expert_nums[e1] : 0;
+  int64_t total;
+  const int64_t x0 = plan_scan_pair(c0, c1, wsum, total);   // first row of e0 (unclipped)
+  const int64_t x1 = x0 + c0;
+  const int lo0 = (int)min(x0, A), hi0 = (int)min(x0 + c0, A);
+  const int lo1 = (int)min(x1, A), hi1 = (int)min(x1 + c1, A);
+  const int f0 = (hi0 - lo0) / kFfnBM, f1 = (hi1 - lo1) / kFfnBM;   // full m-tiles
+  const int r0 = (hi0 - lo0) % kFfnBM, r1 = (hi1 - lo1) % kFfnBM;   // rows of the partial m-tile
+  rem_s[e0] = r0;
+  rem_s[e1] = r1;
+  int64_t nfull;
+  const int fp0 = (int)plan_scan_pair(f0, f1, wsum, nfull);          // table slot of e0's first full tile
+  int64_t npart;
+  (void)plan_scan_pair(r0 > 0, r1 > 0, wsum, npart);                // also orders rem_s writes before reads
+  for (int f = 0; f < f0; ++f) tiles[1 + fp0 + f] = int4{e0, lo0 + f * kFfnBM, hi0, 0};
+  for (int f = 0; f < f1; ++f) tiles[1 + fp0 + f0 + f] = int4{e1, lo1 + f * kFfnBM, hi1, 0};
+  // partial tiles: rank by rows, descending, ties by expert
+  for (int h = 0; h < 2; ++h) {
+    const int e = h ? e1 : e0, r = h ? r1 : r0;
+    if (e >= L || r == 0) continue;
+    int rank = 0;
+    for (int o = 0; o < L; ++o) {
+      const int ro = rem_s[o];
+      rank += (ro > r) || (ro == r && o < e);
     }
-    t += tiles;
-    off += c;
+    const int lo = h ? lo1 : lo0, f = h ? f1 : f0, hi = h ? hi1 : hi0;
+    tiles[1 + (int)nfull + rank] = int4{e, lo + f * kFfnBM, hi, 0};
   }
-  e = -1;
-  row0 = row_end = 0;
+  if (tid == 0) tiles[0] = int4{(int)(nfull + npart), 0, 0, 0};
 }
 
 __device__ __forceinline__ float ffn_silu(float a) { return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
@@ -813,36 +851,6 @@ __global__ __launch_bounds__(256) void k_ffn_quant_rows(
   }
 }
 
-// Persistent grouped GEMM, C = A . W[e]^T with A int8 [rows][K] (token rows
-// of expert e) and W int8 [L][Nw][K].  GLU = true (GMM1): each tile pairs 128
-// gate rows of W (columns n) with the 128 up rows (columns N/2 + n); the
-// epilogue dequantises both, applies silu(gate) * up and writes bf16 g.
-// GLU = false (GMM2): the epilogue dequantises and writes bf16 y.  Dequant:
-// acc * row_scale[row] * w_scale[e][col].
-//
-// MFMA v_mfma_i32_32x32x32_i8: lane l supplies row l % 32 and k bytes
-// 16 (l / 32) .. +16 of each 32 x 32 operand block and receives
-// C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32], r < 16.  The weight block is the
-// first operand and the token block the second, so each lane holds runs of 4
-// consecutive output columns of one token and stores each run as one 8-byte
-// word.  (This MFMA also updates its accumulator in place, which the 16 x 16
-// shapes do not get from the compiler: they copy accumulators every step.)
-//
-// LDS: two stages, each [256 token rows][128 B] + [256 weight rows][128 B],
-// filled straight from global memory by buffer_load ... lds (each lane's 16
-// bytes land at the wavefront's LDS base + 16 * lane).  The 16-byte chunk c
-// of row r sits at chunk c ^ ((r / 2) & 7) of that row, so any 16 consecutive
-// rows read at one chunk cover all 16 bank groups of 16 bytes.  Stage s + 1 is
-// in flight while stage s feeds the MFMAs: one wait and one barrier per
-// 128-byte k step.  Out-of-range rows (past the expert's rows or past Nw) read
-// as zero through the buffer descriptors' range checks and are never stored.
-//
-// Tiles: T = (m-tiles over all experts) x (output columns / tile columns).
-// The launch holds one workgroup per CU; workgroup b walks tiles
-// i*G + (b % 8)*(G/8) + b / 8.  Hardware places workgroup b on XCD b % 8, so
-// each XCD walks a contiguous run of tiles; tiles are ordered in groups of 4
-// m-tiles x 8 n-tiles (m fastest), so the tiles an XCD runs together share A
-// and W tiles in its L2.
 // The k loop of one tile (see k_ffn_gemm).  Stage ks + 1 travels global ->
 // registers during stage ks - 1 and registers -> LDS during stage ks, into the
 // buffer nobody reads in stage ks; one barrier ends each stage.  Fragments of
@@ -859,10 +867,16 @@ struct FfnStaging {
   int lds_off;                     // this thread's LDS byte offset for i = 0
 };
 
-template <bool GLU>
+// NB = number of the wavefront's 32-row token blocks that hold valid rows:
+// blocks past them stay zero, and their fragment reads and MFMAs are not
+// issued (an expert's short last m-tile is cheap).  NB = 0 still stages and
+// joins the barriers.
+template <bool GLU, int NB>
 __device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const FfnStaging& st, int wt, int wn,
                                           const int (&fr)[4]) {
   constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;
+  constexpr int NR = NB > 0 ? NB + 2 : 0;   // fragment reads per k substep
+  constexpr int NM = 2 * NB;                // MFMAs per k substep
   // LDS row of weight block j (32 rows) within the stage's weight tile
   auto wrow = [&](int j) {
     if (GLU) return j == 0 ? wn * 32 : NCOLS + wn * 32;
@@ -885,36 +899,36 @@ __device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const
     }
   };
   auto frags = [&](const uint8_t* sb, int q, v4i (&tf)[4], v4i (&wf)[2]) {
+    if (NB == 0) return;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tf[i] = *reinterpret_cast<const v4i*>(sb + (wt * 128 + 32 * i) * kFfnBK + fr[q]);
+    for (int i = 0; i < NB; ++i) tf[i] = *reinterpret_cast<const v4i*>(sb + (wt * 128 + 32 * i) * kFfnBK + fr[q]);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       wf[j] = *reinterpret_cast<const v4i*>(sb + kFfnBM * kFfnBK + wrow(j) * kFfnBK + fr[q]);
   };
   auto mfmas = [&](const v4i (&tf)[4], const v4i (&wf)[2]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j], tf[i], acc[j][i], 0, 0, 0);
+      for (int j = 0; j < 2; ++j) acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j], tf[i], acc[j][i], 0, 0, 0);
   };
   auto interleave_reads = [&]() {
 #pragma unroll
-    for (int n = 0; n < 6; ++n) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    for (int n = 0; n < NR; ++n) {
+      if (n < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
   auto interleave_staging = [&]() {
 #pragma unroll
-    for (int n = 0; n < 6; ++n) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int n = 0; n < 8; ++n) {
+      if (n < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (n < 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      if (n < 8) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (n < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -963,10 +977,10 @@ __device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const
 // accumulator in place, which the 16 x 16 shapes do not get from the
 // compiler: they copy accumulators every step.)
 //
-// Wavefront wv = 2 wn + wt holds tokens 128 wt .. +128 of the tile and weight
+// Wavefront wv = 4 wt + wn holds tokens 128 wt .. +128 of the tile and weight
 // rows 32 wn .. +32 (GMM1: those gate rows and the matching up rows) or
-// 64 wn .. +64 (GMM2).  Two wavefronts per SIMD keep the LDS busy while the
-// other one waits.
+// 64 wn .. +64 (GMM2).  Two wavefronts per SIMD (one per token half) keep the
+// MFMAs busy while the other one waits on LDS.
 //
 // LDS: two stages, each [256 token rows][128 B] + [256 weight rows][128 B].
 // The 16-byte chunk c of row r sits at chunk c ^ ((r / 2) & 7) of that row,
@@ -979,7 +993,7 @@ __device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const
 // one column fall in distinct banks), then all wavefronts store whole rows
 // with 16-byte stores.
 //
-// Tiles: T = (m-tiles over all experts) x (output columns / tile columns).
+// Tiles: T = (m-tiles of the plan) x (output columns / tile columns).
 // The launch holds one workgroup per CU; workgroup b walks tiles
 // i*G + (b % 8)*(G/8) + b / 8.  Hardware places workgroup b on XCD b % 8, so
 // each XCD walks a contiguous run of tiles; tiles are ordered in groups of 4
@@ -989,25 +1003,23 @@ template <bool GLU>
 __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(
     const int8_t* __restrict__ a_src, const float* __restrict__ row_scale,
     const int8_t* __restrict__ w, const float* __restrict__ w_scale, uint16_t* __restrict__ out,
-    const int64_t* __restrict__ expert_nums, int L, int64_t A, int K, int Nw, int Nout) {
+    const int4* __restrict__ tiles, int K, int Nw, int Nout) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFfnStage];
   __shared__ float sc_row[kFfnBM];   // row scales of the tile's token rows
   __shared__ float sc_col[kFfnBW];   // weight-row scales (GMM1: 128 gate, then 128 up)
-  __shared__ int tile_info[4];
   constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;   // output columns per tile
   constexpr int OU = NCOLS / 8;                      // 16-byte output units per tile row
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wavefront-uniform values are read into scalar registers (readfirstlane)
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wt = wv & 1;    // token half of the tile
-  const int wn = wv >> 1;   // weight-row quarter of the tile
+  // SIMD s runs wavefronts s and s + 4: one of each token half
+  const int wt = wv >> 2;   // token half of the tile
+  const int wn = wv & 3;    // weight-row quarter of the tile
   const int G = gridDim.x;
   const int nn = (Nout + NCOLS - 1) / NCOLS;
   constexpr int GM = 4, GN = 8;
-  if (tid == 0) tile_info[3] = ffn_total_mtiles(expert_nums, L, A);
-  __syncthreads();
-  const int MT = __builtin_amdgcn_readfirstlane(tile_info[3]);
+  const int MT = tiles[0].x;
   const int64_t T = (int64_t)MT * nn;
   const int b = blockIdx.x;
   const int lin = (b % 8) * (G / 8) + b / 8;   // XCD-contiguous walk (G is a multiple of 8)
@@ -1035,19 +1047,11 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(
     const int n_in_group = (int)min((int64_t)GN, (int64_t)nn - ng * GN);
     const int mt = (int)(mg * GM + r2 % m_in_group);
     const int nt = (int)(ng * GN + (r2 / m_in_group) % n_in_group);
-    __syncthreads();
-    if (tid == 0) {
-      int e, r0, re;
-      ffn_tile_rows(expert_nums, L, A, mt, e, r0, re);
-      tile_info[0] = e;
-      tile_info[1] = r0;
-      tile_info[2] = re;
-    }
-    __syncthreads();
-    const int e = __builtin_amdgcn_readfirstlane(tile_info[0]);
-    if (e < 0) continue;
-    const int row0 = __builtin_amdgcn_readfirstlane(tile_info[1]);
-    const int row_end = __builtin_amdgcn_readfirstlane(tile_info[2]);
+    __syncthreads();   // the previous tile's epilogue is done with LDS
+    const int4 ti = tiles[1 + mt];
+    const int e = __builtin_amdgcn_readfirstlane(ti.x);
+    const int row0 = __builtin_amdgcn_readfirstlane(ti.y);
+    const int row_end = __builtin_amdgcn_readfirstlane(ti.z);
     const int n0 = nt * NCOLS;
 
     // buffer descriptors: token rows [row0, min(row_end, row0 + 256)) and
@@ -1078,7 +1082,15 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[j][i] = v16i{};
-    ffn_kloop<GLU>(lds, acc, st, wt, wn, fr);
+    // 32-row token blocks of this wavefront's half that hold valid rows
+    const int nblk = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows_here - wt * 128 + 31) / 32)));
+    switch (nblk) {
+      case 4: ffn_kloop<GLU, 4>(lds, acc, st, wt, wn, fr); break;
+      case 3: ffn_kloop<GLU, 3>(lds, acc, st, wt, wn, fr); break;
+      case 2: ffn_kloop<GLU, 2>(lds, acc, st, wt, wn, fr); break;
+      case 1: ffn_kloop<GLU, 1>(lds, acc, st, wt, wn, fr); break;
+      default: ffn_kloop<GLU, 0>(lds, acc, st, wt, wn, fr); break;
+    }
 
     // Epilogue.  Lane l holds, for each (j, i) and run q < 4, token
     // 32 i + (l & 31) of the wavefront's token half and weight rows
@@ -1264,7 +1276,7 @@ mdc_status gather_q_impl(const DispatchPlan& p, const void* x, int8_t* expand_q,
 struct FfnPlan {
   int64_t A;
   int H, N, L;
-  size_t off_q1, off_s1, off_g, off_q2, off_s2, bytes;
+  size_t off_q1, off_s1, off_g, off_q2, off_s2, off_tiles, bytes;
 };
 
 FfnPlan make_ffn_plan(const mdc_shape* sh, int inter_n) {
@@ -1278,7 +1290,9 @@ FfnPlan make_ffn_plan(const mdc_shape* sh, int inter_n) {
   f.off_g = f.off_s1 + round_up((size_t)f.A * 4, 256);
   f.off_q2 = f.off_g + round_up((size_t)f.A * (f.N / 2) * 2, 256);
   f.off_s2 = f.off_q2 + round_up((size_t)f.A * (f.N / 2), 256);
-  f.bytes = f.off_s2 + round_up((size_t)f.A * 4, 256);
+  f.off_tiles = f.off_s2 + round_up((size_t)f.A * 4, 256);
+  // m-tile table: header + at most A / kFfnBM + L tiles
+  f.bytes = f.off_tiles + round_up((size_t)(2 + f.A / kFfnBM + f.L) * sizeof(int4), 256);
   if (f.bytes == 0) f.bytes = 256;
   return f;
 }
@@ -1316,12 +1330,14 @@ mdc_status ffn_impl(const FfnPlan& f, const void* expand_x, const int8_t* expand
     q1 = const_cast<int8_t*>(expand_q);   // rows already quantised by mdc_dispatch_quant
     s1 = const_cast<float*>(dyn_scale);
   }
-  hipLaunchKernelGGL(k_ffn_gemm<true>, dim3(g1), dim3(kFfnThreads), 0, s, q1, s1, w1, w1_scale, g,
-                     expert_token_nums, f.L, f.A, f.H, f.N, f.N / 2);
+  int4* tiles = reinterpret_cast<int4*>(ws + f.off_tiles);
+  hipLaunchKernelGGL(k_ffn_plan, dim3(1), dim3(kPlanThreads), 0, s, expert_token_nums, f.L, f.A, tiles);
+  hipLaunchKernelGGL(k_ffn_gemm<true>, dim3(g1), dim3(kFfnThreads), 0, s, q1, s1, w1, w1_scale, g, tiles, f.H, f.N,
+                     f.N / 2);
   hipLaunchKernelGGL(k_ffn_quant_rows, dim3(quant_wgs), dim3(256), 0, s, reinterpret_cast<const v4u*>(g), q2, s2,
                      expert_token_nums, f.L, f.A, f.N / 2 / 8);
   hipLaunchKernelGGL(k_ffn_gemm<false>, dim3(g2), dim3(kFfnThreads), 0, s, q2, s2, w2, w2_scale,
-                     static_cast<uint16_t*>(y), expert_token_nums, f.L, f.A, f.N / 2, f.H, f.H);
+                     static_cast<uint16_t*>(y), tiles, f.N / 2, f.H, f.H);
   return launched();
 }
 
