@@ -85,18 +85,30 @@ def algorithmic_bytes(w, ids, mask, d=0, r=0):
     return {"R": R, "U": U, "present": present, "layout": layout, "gather": gather, "combine": combine}
 
 
+# sources of the dispatch/combine kernels (the ones the HBM-traffic summary measures)
+TRAFFIC_SOURCES = ("mdc_common.h", "mdc_dispatch.hip")
+
+
+def dispatch_source_sha() -> str:
+    """sha256 over the dispatch/combine kernel sources, in TRAFFIC_SOURCES order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        h.update(open(os.path.join(ROOT, "combine_route_histogram_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, or None.
 
-    The summary records the sha256 of the kernel source it was measured on;
-    once the source differs the figure no longer describes these kernels.
+    The summary records the sha256 of the kernel sources it was measured on
+    (dispatch_source_sha); once they differ the figure no longer describes
+    these kernels.
     """
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.json")
-    src = os.path.join(ROOT, "combine_route_histogram_amd", "csrc", "mdc.hip")
     try:
         prof = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = dispatch_source_sha()
     except (OSError, ValueError):
         return None
     if prof.get("source_sha256") != sha:

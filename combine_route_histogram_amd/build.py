@@ -10,7 +10,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "mdc.hip")
+# kernel sources compiled into the one library; mdc_common.h is shared by both
+SRCS = [os.path.join(PKG, "csrc", "mdc_dispatch.hip"), os.path.join(PKG, "csrc", "mdc_ffn.hip")]
 INC = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libmdc.so")
 
@@ -37,7 +38,7 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     tmp = OUT + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INC, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INC, *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -23,16 +23,9 @@
 // Built with -ffp-contract=off: the combine's products and sums are rounded
 // to fp32 one by one, in the order the combine formula lists them.
 
-#include <hip/hip_runtime.h>
-
-#include <cstdint>
-#include <cstring>
-
-#include "mdc.h"
+#include "mdc_common.h"
 
 namespace {
-
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 // Build-time tile shapes (16-byte vectors per lane per row tile).
 #ifndef MDC_GATHER_VEC
@@ -86,62 +79,6 @@ __host__ __device__ __forceinline__ int counter_slot(int i) {
 constexpr int kGatherVec = MDC_GATHER_VEC;
 static_assert(kGatherVec >= 1 && kGatherVec <= 8, "gather tiles hold 1..8 vectors per lane");
 constexpr int kCombineVec = MDC_COMBINE_VEC;
-
-template <bool NT>
-__device__ __forceinline__ void store_v4(v4u* p, v4u v) {
-  if (NT) __builtin_nontemporal_store(v, p);
-  else *p = v;
-}
-
-__device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
-
-__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// fp32 -> bf16 round to nearest, ties to even (the CAST_RINT of [TL] combine):
-// add 0x7FFF plus the lowest kept bit, keep the top 16 bits; NaN -> quiet NaN.
-__device__ __forceinline__ unsigned bf16_rne(float f) {
-  const unsigned u = __float_as_uint(f);
-  if (f != f) return ((u >> 16) & 0x8000u) | 0x7FC0u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// Loads through addresses rebuilt from integers (readlane / shuffles) would be
-// compiled as flat accesses; these keep them in the global address space.
-typedef const v4u __attribute__((address_space(1))) g_v4u;
-typedef const int32_t __attribute__((address_space(1))) g_i32;
-template <bool NT>
-__device__ __forceinline__ v4u load_v4(uint64_t addr) {
-  if (NT) return __builtin_nontemporal_load(reinterpret_cast<g_v4u*>(addr));
-  return *reinterpret_cast<g_v4u*>(addr);
-}
-__device__ __forceinline__ int32_t load_i32(uint64_t addr) { return *reinterpret_cast<g_i32*>(addr); }
-
-// Inclusive prefix sum over the 64 lanes with DPP lane moves: shifts by
-// 1, 2, 4, 8 inside each row of 16 lanes, then row_bcast:15 adds the total of
-// rows 0 / 2 to rows 1 / 3 and row_bcast:31 adds the total of rows 0-1 to
-// rows 2-3.  Lanes without a source read 0.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15 into rows 1, 3
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31 into rows 2, 3
-  return v;
-}
-
-__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
-  const unsigned lo = (unsigned)__shfl((int)(unsigned)v, src, 64);
-  const unsigned hi = (unsigned)__shfl((int)(unsigned)(v >> 32), src, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int k) {
-  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)v, k);
-  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(v >> 32), k);
-  return ((uint64_t)hi << 32) | lo;
-}
 
 // ---------------------------------------------------------------------------
 // a1 + a3 (ranks): route filter, histogram and stable rank within a group.
@@ -677,502 +614,8 @@ __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
 }
 
 // ---------------------------------------------------------------------------
-// a7: grouped int8 expert FFN ([PTO] GMM1 / SwiGLU / GMM2 stages).
-//
-// Per local expert e, on its expert-major rows of expand_x:
-//   q1, s1 = per-row int8 quantisation of x (amax / 127, round half even)
-//   h      = (q1 . W1[e]^T) * s1[row] * w1s[e][n]          (int32 MFMA accumulate)
-//   g      = silu(h[:, j]) * h[:, j + N/2],  j < N/2        (fused in GMM1's epilogue)
-//   q2, s2 = per-row int8 quantisation of g (quantised while GMM2 loads its tiles)
-//   y      = bf16((q2 . W2[e]^T) * s2[row] * w2s[e][h])
-// The GEMMs use v_mfma_i32_32x32x32_i8 on 256-token x 256-weight-row tiles
-// (GMM1: 128 gate + 128 up weight rows per tile so gate and up land in the
-// same lanes), eight wavefronts (two per SIMD) each holding a 128 x 64 int32
-// accumulator block in AGPRs, k staged through a double-buffered LDS ring 128
-// bytes deep; the output tile leaves through LDS as whole rows.
-// ---------------------------------------------------------------------------
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-
-constexpr int kFfnBM = 256;        // token rows per tile
-constexpr int kFfnBW = 256;        // weight rows per tile (GMM1: 128 gate + 128 up)
-constexpr int kFfnBK = 128;        // k bytes per LDS stage
-constexpr int kFfnThreads = 512;   // 8 wavefronts: 2 along tokens x 4 along weight rows
-constexpr int kFfnStage = (kFfnBM + kFfnBW) * kFfnBK;   // bytes of one LDS stage
-constexpr int kFfnOutAlign = 128;  // GMM output widths (N/2 and H) must be multiples of this
-
-// Tile plan shared by both GEMMs.  Each local expert's rows (contiguous,
-// expert-major, clipped at A) split into m-tiles of kFfnBM rows.  The table
-// lists every full m-tile first (expert order), then each expert's partial
-// last m-tile by row count, largest first: the persistent GEMMs walk tiles
-// in table order, so the workgroups that run one tile more than the others
-// end on the cheapest tiles.  tiles[0].x = number of m-tiles; tiles[1 + m] =
-// {expert, first row, expert's end row, 0}.  One workgroup of 1024 threads;
-// L <= 2048 (two experts per thread).
-constexpr int kPlanThreads = 1024;
-
-// Exclusive prefix over the 2048 values held two per thread (elements 2t and
-// 2t + 1); returns the prefix of element 2t and the grand total.
-__device__ int64_t plan_scan_pair(int64_t a, int64_t b, int64_t* wsum, int64_t& total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t own = a + b;
-  int64_t s = own;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int64_t n = __shfl_up(s, o, 64);
-    if (lane >= o) s += n;
-  }
-  if (lane == 63) wsum[wave] = s;
-  __syncthreads();
-  if (tid == 0) {
-    int64_t run = 0;
-    for (int w = 0; w < kPlanThreads / 64; ++w) {
-      const int64_t x = wsum[w];
-      wsum[w] = run;
-      run += x;
-    }
-    wsum[kPlanThreads / 64] = run;
-  }
-  __syncthreads();
-  const int64_t excl = wsum[wave] + s - own;
-  total = wsum[kPlanThreads / 64];
-  __syncthreads();   // wsum is reused by the next scan
-  return excl;
-}
-
-__global__ __launch_bounds__(kPlanThreads) void k_ffn_plan(const int64_t* __restrict__ expert_nums, int L, int64_t A,
-                                                           int4* __restrict__ tiles) {
-  __shared__ int rem_s[2 * kPlanThreads];
-  __shared__ int64_t wsum[kPlanThreads / 64 + 1];
-  const int tid = threadIdx.x;
-  const int e0 = 2 * tid, e1 = 2 * tid + 1;
-  const int64_t c0 = e0 < L ? expert_nums[e0] : 0, c1 = e1 < L ? expert_nums[e1] : 0;
-  int64_t total;
-  const int64_t x0 = plan_scan_pair(c0, c1, wsum, total);   // first row of e0 (unclipped)
-  const int64_t x1 = x0 + c0;
-  const int lo0 = (int)min(x0, A), hi0 = (int)min(x0 + c0, A);
-  const int lo1 = (int)min(x1, A), hi1 = (int)min(x1 + c1, A);
-  const int f0 = (hi0 - lo0) / kFfnBM, f1 = (hi1 - lo1) / kFfnBM;   // full m-tiles
-  const int r0 = (hi0 - lo0) % kFfnBM, r1 = (hi1 - lo1) % kFfnBM;   // rows of the partial m-tile
-  rem_s[e0] = r0;
-  rem_s[e1] = r1;
-  int64_t nfull;
-  const int fp0 = (int)plan_scan_pair(f0, f1, wsum, nfull);          // table slot of e0's first full tile
-  int64_t npart;
-  (void)plan_scan_pair(r0 > 0, r1 > 0, wsum, npart);                // also orders rem_s writes before reads
-  for (int f = 0; f < f0; ++f) tiles[1 + fp0 + f] = int4{e0, lo0 + f * kFfnBM, hi0, 0};
-  for (int f = 0; f < f1; ++f) tiles[1 + fp0 + f0 + f] = int4{e1, lo1 + f * kFfnBM, hi1, 0};
-  // partial tiles: rank by rows, descending, ties by expert
-  for (int h = 0; h < 2; ++h) {
-    const int e = h ? e1 : e0, r = h ? r1 : r0;
-    if (e >= L || r == 0) continue;
-    int rank = 0;
-    for (int o = 0; o < L; ++o) {
-      const int ro = rem_s[o];
-      rank += (ro > r) || (ro == r && o < e);
-    }
-    const int lo = h ? lo1 : lo0, f = h ? f1 : f0, hi = h ? hi1 : hi0;
-    tiles[1 + (int)nfull + rank] = int4{e, lo + f * kFfnBM, hi, 0};
-  }
-  if (tid == 0) tiles[0] = int4{(int)(nfull + npart), 0, 0, 0};
-}
-
-__device__ __forceinline__ float ffn_silu(float a) { return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
-
-// Two fp32 -> two bf16 (round to nearest even, one v_cvt_pk_bf16_f32), lo in
-// the low half.
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t ffn_pack_bf16(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
-}
-
-// Per-row int8 quantisation of bf16 rows of `width` elements, decided in fp32
-// exactly as: amax = max|v|, inv = 127 / amax, q = clamp(rint(v * inv), -127,
-// 127), scale = amax / 127 (a zero row gives q = 0, scale = 0).  One
-// wavefront per row, rows [0, min(sum(expert_nums), A)) visited grid-stride;
-// rows of up to 64 * kQuantVec vectors stay in registers between the passes.
-constexpr int kQuantVec = 16;
-__global__ __launch_bounds__(256) void k_ffn_quant_rows(
-    const v4u* __restrict__ x, int8_t* __restrict__ q, float* __restrict__ scale,
-    const int64_t* __restrict__ expert_nums, int L, int64_t A, int nvec) {
-  const int lane = threadIdx.x & 63;
-  const int64_t nw = (int64_t)gridDim.x * 4;
-  int64_t total = 0;
-  for (int i = 0; i < L; ++i) total += expert_nums[i];
-  const int64_t rows = total < A ? total : A;
-  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += nw) {
-    const v4u* xr = x + row * nvec;
-    uint64_t* qr = reinterpret_cast<uint64_t*>(q + row * (int64_t)nvec * 8);
-    v4u cache[kQuantVec];
-    float amax = 0.f;
-    if (nvec <= 64 * kQuantVec) {
-#pragma unroll
-      for (int u = 0; u < kQuantVec; ++u) {
-        const int i = lane + 64 * u;
-        cache[u] = i < nvec ? xr[i] : v4u{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int u = 0; u < kQuantVec; ++u)
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(cache[u][w])), fabsf(bf16_hi(cache[u][w]))));
-    } else {
-      for (int i = lane; i < nvec; i += 64) {
-        const v4u v = xr[i];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[w])), fabsf(bf16_hi(v[w]))));
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-    const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-    auto quant8 = [&](const v4u& v) {
-      uint64_t packed = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float a = fminf(fmaxf(rintf(bf16_lo(v[w]) * inv), -127.f), 127.f);
-        const float b = fminf(fmaxf(rintf(bf16_hi(v[w]) * inv), -127.f), 127.f);
-        packed |= (uint64_t)(uint8_t)(int8_t)(int)a << (16 * w);
-        packed |= (uint64_t)(uint8_t)(int8_t)(int)b << (16 * w + 8);
-      }
-      return packed;
-    };
-    if (nvec <= 64 * kQuantVec) {
-#pragma unroll
-      for (int u = 0; u < kQuantVec; ++u) {
-        const int i = lane + 64 * u;
-        if (i < nvec) qr[i] = quant8(cache[u]);
-      }
-    } else {
-      for (int i = lane; i < nvec; i += 64) qr[i] = quant8(xr[i]);
-    }
-    if (lane == 0) scale[row] = amax / 127.0f;
-  }
-}
-
-// The k loop of one tile (see k_ffn_gemm).  Stage ks + 1 travels global ->
-// registers during stage ks - 1 and registers -> LDS during stage ks, into the
-// buffer nobody reads in stage ks; one barrier ends each stage.  Fragments of
-// k substep q + 1 are read while the MFMAs of substep q run, and the last
-// substep's MFMAs run after the stage barrier, beside the next stage's first
-// fragment reads.  Scheduling groups (sched_group_barrier masks: 0x8 MFMA,
-// 0x100 LDS read, 0x200 LDS write, 0x20 global read) interleave the memory
-// instructions with the MFMAs.
-struct FfnStaging {
-  __amdgpu_buffer_rsrc_t ra, rw;   // token rows, weight rows (range-checked)
-  unsigned va, vw;                 // lane offsets of this thread's i = 0 rows
-  unsigned whi;                    // extra weight offset of rows i >= 2 (GMM1: gate -> up)
-  int K;
-  int lds_off;                     // this thread's LDS byte offset for i = 0
-};
-
-// NB = number of the wavefront's 32-row token blocks that hold valid rows:
-// blocks past them stay zero, and their fragment reads and MFMAs are not
-// issued (an expert's short last m-tile is cheap).  NB = 0 still stages and
-// joins the barriers.
-template <bool GLU, int NB>
-__device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const FfnStaging& st, int wt, int wn,
-                                          const int (&fr)[4]) {
-  constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;
-  constexpr int NR = NB > 0 ? NB + 2 : 0;   // fragment reads per k substep
-  constexpr int NM = 2 * NB;                // MFMAs per k substep
-  // LDS row of weight block j (32 rows) within the stage's weight tile
-  auto wrow = [&](int j) {
-    if (GLU) return j == 0 ? wn * 32 : NCOLS + wn * 32;
-    return wn * 64 + 32 * j;
-  };
-  v4i sa[4], sw[4];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sa[i] = __builtin_amdgcn_raw_buffer_load_b128(st.ra, st.va + (unsigned)(64 * i * st.K), (unsigned)k0, 0);
-      sw[i] = __builtin_amdgcn_raw_buffer_load_b128(st.rw, st.vw + (unsigned)(64 * i * st.K) + (i >= 2 ? st.whi : 0u),
-                                                    (unsigned)k0, 0);
-    }
-  };
-  auto lwrite = [&](uint8_t* buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<v4i*>(buf + st.lds_off + 64 * i * kFfnBK) = sa[i];
-      *reinterpret_cast<v4i*>(buf + kFfnBM * kFfnBK + st.lds_off + 64 * i * kFfnBK) = sw[i];
-    }
-  };
-  auto frags = [&](const uint8_t* sb, int q, v4i (&tf)[4], v4i (&wf)[2]) {
-    if (NB == 0) return;
-#pragma unroll
-    for (int i = 0; i < NB; ++i) tf[i] = *reinterpret_cast<const v4i*>(sb + (wt * 128 + 32 * i) * kFfnBK + fr[q]);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      wf[j] = *reinterpret_cast<const v4i*>(sb + kFfnBM * kFfnBK + wrow(j) * kFfnBK + fr[q]);
-  };
-  auto mfmas = [&](const v4i (&tf)[4], const v4i (&wf)[2]) {
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j], tf[i], acc[j][i], 0, 0, 0);
-  };
-  auto interleave_reads = [&]() {
-#pragma unroll
-    for (int n = 0; n < NR; ++n) {
-      if (n < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto interleave_staging = [&]() {
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      if (n < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (n < 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      if (n < 8) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      if (n < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  const int nk = st.K / kFfnBK;
-  v4i tf[4], wf[2], tg[4], wg[2];
-  gload(0);
-  lwrite(lds);
-  __syncthreads();
-  gload(min(1, nk - 1) * kFfnBK);
-  frags(lds, 0, tf, wf);
-  for (int ks = 0; ks < nk; ++ks) {
-    uint8_t* cur = lds + (ks & 1) * kFfnStage;
-    uint8_t* nxt = lds + ((ks + 1) & 1) * kFfnStage;
-    frags(cur, 1, tg, wg);
-    mfmas(tf, wf);
-    interleave_reads();
-    // stage ks + 1: registers -> LDS, then stage ks + 2: global -> registers
-    // (the last iterations repeat the last stage; nobody reads it)
-    lwrite(nxt);
-    gload(min(ks + 2, nk - 1) * kFfnBK);
-    frags(cur, 2, tf, wf);
-    mfmas(tg, wg);
-    interleave_staging();
-    frags(cur, 3, tg, wg);
-    mfmas(tf, wf);
-    interleave_reads();
-    __syncthreads();
-    frags(nxt, 0, tf, wf);
-    mfmas(tg, wg);
-    interleave_reads();
-  }
-}
-
-// Persistent grouped GEMM, C = A . W[e]^T with A int8 [rows][K] (token rows
-// of expert e) and W int8 [L][Nw][K].  GLU = true (GMM1): each tile pairs 128
-// gate rows of W (columns n) with the 128 up rows (columns N/2 + n); the
-// epilogue dequantises both, applies silu(gate) * up and writes bf16 g.
-// GLU = false (GMM2): the epilogue dequantises and writes bf16 y.  Dequant:
-// acc * row_scale[row] * w_scale[e][col].
-//
-// MFMA v_mfma_i32_32x32x32_i8: lane l supplies row l % 32 and k bytes
-// 16 (l / 32) .. +16 of each 32 x 32 operand block and receives
-// C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32], r < 16.  The weight block is the
-// first operand and the token block the second, so each lane holds runs of 4
-// consecutive output columns of one token.  (This MFMA also updates its
-// accumulator in place, which the 16 x 16 shapes do not get from the
-// compiler: they copy accumulators every step.)
-//
-// Wavefront wv = 4 wt + wn holds tokens 128 wt .. +128 of the tile and weight
-// rows 32 wn .. +32 (GMM1: those gate rows and the matching up rows) or
-// 64 wn .. +64 (GMM2).  Two wavefronts per SIMD (one per token half) keep the
-// MFMAs busy while the other one waits on LDS.
-//
-// LDS: two stages, each [256 token rows][128 B] + [256 weight rows][128 B].
-// The 16-byte chunk c of row r sits at chunk c ^ ((r / 2) & 7) of that row,
-// so any 16 consecutive rows read at one chunk cover all 16 bank groups.
-// Out-of-range rows (past the expert's rows or past Nw) read as zero through
-// the buffer descriptors' range checks and are never stored.
-//
-// Epilogue, per token half: the wavefronts of that half write their bf16
-// outputs into LDS rows (row pitch padded by 8 bytes so 32 rows written at
-// one column fall in distinct banks), then all wavefronts store whole rows
-// with 16-byte stores.
-//
-// Tiles: T = (m-tiles of the plan) x (output columns / tile columns).
-// The launch holds one workgroup per CU; workgroup b walks tiles
-// i*G + (b % 8)*(G/8) + b / 8.  Hardware places workgroup b on XCD b % 8, so
-// each XCD walks a contiguous run of tiles; tiles are ordered in groups of 4
-// m-tiles x 8 n-tiles (m fastest), so the tiles an XCD runs together share A
-// and W tiles in its L2.
-template <bool GLU>
-__global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(
-    const int8_t* __restrict__ a_src, const float* __restrict__ row_scale,
-    const int8_t* __restrict__ w, const float* __restrict__ w_scale, uint16_t* __restrict__ out,
-    const int4* __restrict__ tiles, int K, int Nw, int Nout) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFfnStage];
-  __shared__ float sc_row[kFfnBM];   // row scales of the tile's token rows
-  __shared__ float sc_col[kFfnBW];   // weight-row scales (GMM1: 128 gate, then 128 up)
-  constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;   // output columns per tile
-  constexpr int OU = NCOLS / 8;                      // 16-byte output units per tile row
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  // wavefront-uniform values are read into scalar registers (readfirstlane)
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // SIMD s runs wavefronts s and s + 4: one of each token half
-  const int wt = wv >> 2;   // token half of the tile
-  const int wn = wv & 3;    // weight-row quarter of the tile
-  const int G = gridDim.x;
-  const int nn = (Nout + NCOLS - 1) / NCOLS;
-  constexpr int GM = 4, GN = 8;
-  const int MT = tiles[0].x;
-  const int64_t T = (int64_t)MT * nn;
-  const int b = blockIdx.x;
-  const int lin = (b % 8) * (G / 8) + b / 8;   // XCD-contiguous walk (G is a multiple of 8)
-
-  // staging: thread t moves chunk t & 7 of rows 64 i + t / 8 (i < 4) of both
-  // tiles; in LDS that chunk sits at slot (t & 7) ^ ((row / 2) & 7), and
-  // (row / 2) & 7 = (t / 16) & 7 for every i
-  const int st_row = tid >> 3;
-  const int st_chunk = tid & 7;
-  const int st_lds = st_row * kFfnBK + ((st_chunk ^ ((tid >> 4) & 7)) << 4);
-  // fragment reads: lane l reads row l & 31, chunk 2 s + l / 32 (k substep s)
-  int fr[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) fr[q] = (lane & 31) * kFfnBK + (((2 * q + (lane >> 5)) ^ ((lane >> 1) & 7)) << 4);
-
-  for (int64_t t = lin; t < T; t += G) {
-    // tile t -> (m-tile, n-tile): groups of GM m-tiles x GN n-tiles, m fastest
-    const int64_t band = (int64_t)GM * nn;
-    const int64_t mg = t / band;
-    const int64_t r = t - mg * band;
-    const int m_in_group = (int)min((int64_t)GM, (int64_t)MT - mg * GM);
-    const int64_t per_ng = (int64_t)m_in_group * GN;
-    const int64_t ng = r / per_ng;
-    const int64_t r2 = r - ng * per_ng;
-    const int n_in_group = (int)min((int64_t)GN, (int64_t)nn - ng * GN);
-    const int mt = (int)(mg * GM + r2 % m_in_group);
-    const int nt = (int)(ng * GN + (r2 / m_in_group) % n_in_group);
-    __syncthreads();   // the previous tile's epilogue is done with LDS
-    const int4 ti = tiles[1 + mt];
-    const int e = __builtin_amdgcn_readfirstlane(ti.x);
-    const int row0 = __builtin_amdgcn_readfirstlane(ti.y);
-    const int row_end = __builtin_amdgcn_readfirstlane(ti.z);
-    const int n0 = nt * NCOLS;
-
-    // buffer descriptors: token rows [row0, min(row_end, row0 + 256)) and
-    // weight rows [n0, Nw) of expert e (GMM1 up rows at Nw/2 + n0 + ...)
-    const int rows_here = min(row_end - row0, kFfnBM);
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t*>(a_src + (int64_t)row0 * K), (short)0, rows_here * K, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t*>(w + ((int64_t)e * Nw + n0) * K), (short)0, (Nw - n0) * K, 0x00020000);
-    // weight rows (relative to n0): i < 2 -> rows 64 i + t / 8 (GMM1: gate),
-    // i >= 2 -> GMM1: up rows Nw/2 + 64 (i - 2) + t / 8, GMM2: rows 64 i + t / 8
-    const unsigned whi = GLU ? (unsigned)((Nw / 2 - NCOLS) * K) : 0u;
-    const unsigned v0 = (unsigned)(st_row * K + st_chunk * 16);
-    const FfnStaging st{ra, rw, v0, v0, whi, K, st_lds};
-
-    // the epilogue's scales, read from LDS after the k loop's first barrier
-    if (tid < kFfnBM) {
-      sc_row[tid] = row_scale[min(row0 + tid, row_end - 1)];
-    } else {
-      const int c = tid - kFfnBM;
-      const int wr = GLU ? (c < NCOLS ? n0 + c : Nw / 2 + n0 + (c - NCOLS)) : min(n0 + c, Nw - 1);
-      sc_col[c] = w_scale[(int64_t)e * Nw + wr];
-    }
-
-    // acc[j][i]: weight block j (32 rows), token block i (32 rows)
-    v16i acc[2][4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[j][i] = v16i{};
-    // 32-row token blocks of this wavefront's half that hold valid rows
-    const int nblk = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows_here - wt * 128 + 31) / 32)));
-    switch (nblk) {
-      case 4: ffn_kloop<GLU, 4>(lds, acc, st, wt, wn, fr); break;
-      case 3: ffn_kloop<GLU, 3>(lds, acc, st, wt, wn, fr); break;
-      case 2: ffn_kloop<GLU, 2>(lds, acc, st, wt, wn, fr); break;
-      case 1: ffn_kloop<GLU, 1>(lds, acc, st, wt, wn, fr); break;
-      default: ffn_kloop<GLU, 0>(lds, acc, st, wt, wn, fr); break;
-    }
-
-    // Epilogue.  Lane l holds, for each (j, i) and run q < 4, token
-    // 32 i + (l & 31) of the wavefront's token half and weight rows
-    // 32 j + 8 q + 4 (l / 32) + 0..3 of its block j.  The bf16 tile goes to
-    // LDS as [256 rows][NCOLS] with 16-byte unit u of row r at unit
-    // u ^ (r % OU), then leaves as whole rows, 16 bytes per thread.
-    __syncthreads();   // every wavefront is done reading the k loop's stages
-    const int cq = 4 * (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int trow = wt * 128 + 32 * i + (lane & 31);
-      const float rs = sc_row[trow];
-      uint8_t* orow = lds + trow * (NCOLS * 2);
-      auto put = [&](int c, uint32_t lo, uint32_t hi) {   // c: tile column, multiple of 4
-        const int u = (c >> 3) ^ (trow % OU);
-        *reinterpret_cast<uint2*>(orow + u * 16 + (c & 4) * 2) = uint2{lo, hi};
-      };
-      if (GLU) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = wn * 32 + 8 * q + cq;
-          float v[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float hg = (float)acc[0][i][4 * q + jj] * rs * sc_col[c + jj];
-            const float hu = (float)acc[1][i][4 * q + jj] * rs * sc_col[NCOLS + c + jj];
-            v[jj] = ffn_silu(hg) * hu;
-          }
-          put(c, ffn_pack_bf16(v[0], v[1]), ffn_pack_bf16(v[2], v[3]));
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int c = wn * 64 + 32 * j + 8 * q + cq;
-            float v[4];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) v[jj] = (float)acc[j][i][4 * q + jj] * rs * sc_col[c + jj];
-            put(c, ffn_pack_bf16(v[0], v[1]), ffn_pack_bf16(v[2], v[3]));
-          }
-      }
-    }
-    __syncthreads();
-    {
-      const int u = tid % OU;
-      const int col = n0 + u * 8;
-#pragma unroll 4
-      for (int rr = tid / OU; rr < kFfnBM; rr += kFfnThreads / OU) {
-        const int row = row0 + rr;
-        if (row < row_end && col < Nout) {
-          const v4u v = *reinterpret_cast<const v4u*>(lds + rr * (NCOLS * 2) + ((u ^ (rr % OU)) * 16));
-          *reinterpret_cast<v4u*>(out + (int64_t)row * Nout + col) = v;
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
-inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-mdc_status check_shape(const mdc_shape* sh) {
-  if (sh == nullptr) return MDC_ERR_NULLPTR;
-  if (sh->world < 1 || sh->rank < 0 || sh->rank >= sh->world) return MDC_ERR_INVALID;
-  if (sh->bs < 0 || sh->hidden <= 0 || (sh->hidden % 8) != 0) return MDC_ERR_INVALID;
-  if (sh->topk < 1 || sh->topk > MDC_MAX_TOPK) return MDC_ERR_INVALID;
-  if (sh->num_experts <= 0 || (sh->num_experts % sh->world) != 0) return MDC_ERR_INVALID;
-  if (sh->num_experts / sh->world > MDC_MAX_LOCAL_EXPERTS) return MDC_ERR_INVALID;
-  if (sh->capacity < 0 || sh->capacity > INT32_MAX) return MDC_ERR_INVALID;
-  if ((int64_t)sh->world * sh->bs * sh->topk > INT32_MAX) return MDC_ERR_INVALID;
-  if (sh->world > 65535) return MDC_ERR_INVALID;
-  if (sh->mask_per_route != 0 && sh->mask_per_route != 1) return MDC_ERR_INVALID;
-  if (sh->zero_experts < 0 || sh->copy_experts < 0 || sh->reserved != 0) return MDC_ERR_INVALID;
-  if ((int64_t)sh->num_experts + sh->zero_experts + sh->copy_experts > INT32_MAX) return MDC_ERR_INVALID;
-  if (sh->topk > sh->num_experts + sh->zero_experts + sh->copy_experts) return MDC_ERR_INVALID;
-  return MDC_OK;
-}
-
 struct DispatchPlan {
   int W, d, BS, H, K, E, L, TPG, G, nvec, rank_threads, mask_per_route;
   int64_t A;
@@ -1203,8 +646,6 @@ DispatchPlan make_plan(const mdc_shape* sh) {
   if (p.bytes == 0) p.bytes = 256;
   return p;
 }
-
-mdc_status launched() { return hipGetLastError() == hipSuccess ? MDC_OK : MDC_ERR_HIP; }
 
 mdc_status layout_impl(const DispatchPlan& p, const int32_t* ids, const uint8_t* mask, char* ws, hipStream_t st) {
   int32_t* P = reinterpret_cast<int32_t*>(ws + p.off_p);
@@ -1270,74 +711,6 @@ mdc_status gather_q_impl(const DispatchPlan& p, const void* x, int8_t* expand_q,
   else if (vpl <= 12) MDC_LAUNCH_GQ(12);
   else MDC_LAUNCH_GQ(16);
 #undef MDC_LAUNCH_GQ
-  return launched();
-}
-
-struct FfnPlan {
-  int64_t A;
-  int H, N, L;
-  size_t off_q1, off_s1, off_g, off_q2, off_s2, off_tiles, bytes;
-};
-
-FfnPlan make_ffn_plan(const mdc_shape* sh, int inter_n) {
-  FfnPlan f;
-  f.A = sh->capacity;
-  f.H = sh->hidden;
-  f.N = inter_n;
-  f.L = sh->num_experts / sh->world;
-  f.off_q1 = 0;
-  f.off_s1 = round_up((size_t)f.A * f.H, 256);
-  f.off_g = f.off_s1 + round_up((size_t)f.A * 4, 256);
-  f.off_q2 = f.off_g + round_up((size_t)f.A * (f.N / 2) * 2, 256);
-  f.off_s2 = f.off_q2 + round_up((size_t)f.A * (f.N / 2), 256);
-  f.off_tiles = f.off_s2 + round_up((size_t)f.A * 4, 256);
-  // m-tile table: header + at most A / kFfnBM + L tiles
-  f.bytes = f.off_tiles + round_up((size_t)(2 + f.A / kFfnBM + f.L) * sizeof(int4), 256);
-  if (f.bytes == 0) f.bytes = 256;
-  return f;
-}
-
-mdc_status check_ffn(const mdc_shape* sh, int inter_n) {
-  const mdc_status st = check_shape(sh);
-  if (st != MDC_OK) return st;
-  if (inter_n <= 0 || (inter_n % (2 * kFfnOutAlign)) != 0) return MDC_ERR_INVALID;
-  if ((sh->hidden % kFfnOutAlign) != 0) return MDC_ERR_INVALID;
-  // one expert's weight matrix (N x H or H x N/2 bytes) is addressed with 32-bit offsets
-  if ((int64_t)inter_n * sh->hidden > INT32_MAX) return MDC_ERR_INVALID;
-  return MDC_OK;
-}
-
-mdc_status ffn_impl(const FfnPlan& f, const void* expand_x, const int8_t* expand_q, const float* dyn_scale,
-                    const int64_t* expert_token_nums, const int8_t* w1, const float* w1_scale, const int8_t* w2,
-                    const float* w2_scale, void* y, char* ws, hipStream_t s) {
-  int8_t* q1 = reinterpret_cast<int8_t*>(ws + f.off_q1);
-  float* s1 = reinterpret_cast<float*>(ws + f.off_s1);
-
-  uint16_t* g = reinterpret_cast<uint16_t*>(ws + f.off_g);
-  int8_t* q2 = reinterpret_cast<int8_t*>(ws + f.off_q2);
-  float* s2 = reinterpret_cast<float*>(ws + f.off_s2);
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const unsigned quant_wgs = (unsigned)(cus * 8);
-  // one workgroup per CU (128 KB of LDS each)
-  const unsigned g1 = (unsigned)(((cus + 7) / 8) * 8);
-  const unsigned g2 = g1;
-  (void)hipGetLastError();
-  if (expand_q == nullptr) {
-    hipLaunchKernelGGL(k_ffn_quant_rows, dim3(quant_wgs), dim3(256), 0, s, static_cast<const v4u*>(expand_x), q1,
-                       s1, expert_token_nums, f.L, f.A, f.H / 8);
-  } else {
-    q1 = const_cast<int8_t*>(expand_q);   // rows already quantised by mdc_dispatch_quant
-    s1 = const_cast<float*>(dyn_scale);
-  }
-  int4* tiles = reinterpret_cast<int4*>(ws + f.off_tiles);
-  hipLaunchKernelGGL(k_ffn_plan, dim3(1), dim3(kPlanThreads), 0, s, expert_token_nums, f.L, f.A, tiles);
-  hipLaunchKernelGGL(k_ffn_gemm<true>, dim3(g1), dim3(kFfnThreads), 0, s, q1, s1, w1, w1_scale, g, tiles, f.H, f.N,
-                     f.N / 2);
-  hipLaunchKernelGGL(k_ffn_quant_rows, dim3(quant_wgs), dim3(256), 0, s, reinterpret_cast<const v4u*>(g), q2, s2,
-                     expert_token_nums, f.L, f.A, f.N / 2 / 8);
-  hipLaunchKernelGGL(k_ffn_gemm<false>, dim3(g2), dim3(kFfnThreads), 0, s, q2, s2, w2, w2_scale,
-                     static_cast<uint16_t*>(y), tiles, f.N / 2, f.H, f.H);
   return launched();
 }
 
@@ -1525,47 +898,5 @@ mdc_status mdc_combine(const mdc_shape* shape, const void* const* expand_x, cons
   }
   return launched();
 }
-
-mdc_status mdc_ffn_workspace_size(const mdc_shape* shape, int32_t inter_n, size_t* bytes) {
-  if (bytes == nullptr) return MDC_ERR_NULLPTR;
-  const mdc_status st = check_ffn(shape, inter_n);
-  if (st != MDC_OK) return st;
-  *bytes = make_ffn_plan(shape, inter_n).bytes;
-  return MDC_OK;
-}
-
-mdc_status mdc_ffn(const mdc_shape* shape, int32_t inter_n, const void* expand_x, const int64_t* expert_token_nums,
-                   const int8_t* w1, const float* w1_scale, const int8_t* w2, const float* w2_scale, void* y,
-                   void* workspace, size_t workspace_bytes, void* stream) {
-  mdc_status st = check_ffn(shape, inter_n);
-  if (st != MDC_OK) return st;
-  const FfnPlan f = make_ffn_plan(shape, inter_n);
-  if (f.A == 0) return MDC_OK;
-  if (expand_x == nullptr || expert_token_nums == nullptr || w1 == nullptr || w1_scale == nullptr ||
-      w2 == nullptr || w2_scale == nullptr || y == nullptr || workspace == nullptr)
-    return MDC_ERR_NULLPTR;
-  if (!aligned16(expand_x) || !aligned16(w1) || !aligned16(w2) || !aligned16(y)) return MDC_ERR_INVALID;
-  if (workspace_bytes < f.bytes) return MDC_ERR_WORKSPACE;
-  return ffn_impl(f, expand_x, nullptr, nullptr, expert_token_nums, w1, w1_scale, w2, w2_scale, y,
-                  static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
-}
-
-mdc_status mdc_ffn_quant_input(const mdc_shape* shape, int32_t inter_n, const int8_t* expand_q,
-                               const float* dynamic_scales, const int64_t* expert_token_nums, const int8_t* w1,
-                               const float* w1_scale, const int8_t* w2, const float* w2_scale, void* y,
-                               void* workspace, size_t workspace_bytes, void* stream) {
-  mdc_status st = check_ffn(shape, inter_n);
-  if (st != MDC_OK) return st;
-  const FfnPlan f = make_ffn_plan(shape, inter_n);
-  if (f.A == 0) return MDC_OK;
-  if (expand_q == nullptr || dynamic_scales == nullptr || expert_token_nums == nullptr || w1 == nullptr ||
-      w1_scale == nullptr || w2 == nullptr || w2_scale == nullptr || y == nullptr || workspace == nullptr)
-    return MDC_ERR_NULLPTR;
-  if (!aligned16(expand_q) || !aligned16(w1) || !aligned16(w2) || !aligned16(y)) return MDC_ERR_INVALID;
-  if (workspace_bytes < f.bytes) return MDC_ERR_WORKSPACE;
-  return ffn_impl(f, nullptr, expand_q, dynamic_scales, expert_token_nums, w1, w1_scale, w2, w2_scale, y,
-                  static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
-}
-
 
 }  // extern "C"
