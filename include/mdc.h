@@ -280,15 +280,22 @@ mdc_status mdc_combine(const mdc_shape* shape,
  *   g      = silu(h[:, j]) * h[:, j + N/2], j < N/2, stored as bf16 (RNE)
  *   q2, s2 = per-row int8 quantisation of g, as for x
  *   y      = bf16_rne((q2 . w2[e]^T) * s2 * w2_scale[e][c]),  c < H
- * silu(a) = a / (1 + exp(-a)).  Which half goes through silu, the quantiser
- * and the intermediate precisions are this library's readings; the pages
- * name the stages and their order.
+ * silu(a) = a / (1 + exp(-a)), evaluated in fp32 with the hardware exp and
+ * reciprocal (about 1 ulp each); h and y are dequantised in fp32 and
+ * rounded to bf16 nearest-even by the hardware conversion.  Which half goes
+ * through silu, the quantiser and the intermediate precisions are this
+ * library's readings; the pages name the stages and their order.  The
+ * result is bitwise repeatable; against an exact (float64) evaluation of the
+ * same formula it differs by the bf16 roundings of g and y and by the int8
+ * quantisation of g that follows from them.
  *
  * Inputs (device): expand_x [A][H] bf16, expert_token_nums [L] int64 (from
  *   dispatch), w1 [L][N][H] int8, w1_scale [L][N] fp32, w2 [L][H][N/2] int8,
  *   w2_scale [L][H] fp32.   Output: y [A][H] bf16 (rows past the total are
- *   untouched).  inter_n = N must be a positive multiple of 256 and H a
- *   multiple of 128.
+ *   untouched).  inter_n = N must be a positive multiple of 256, H a
+ *   multiple of 128 and N * H < 2^31 (one expert's weight matrix is addressed
+ *   with 32-bit offsets).  The workspace holds q1, s1, g, q2, s2 and the
+ *   m-tile table of the grouped GEMMs.
  * ------------------------------------------------------------------------ */
 mdc_status mdc_ffn_workspace_size(const mdc_shape* shape, int32_t inter_n, size_t* bytes);
 
