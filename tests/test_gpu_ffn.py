@@ -67,6 +67,8 @@ def _run_ffn(w, inter, capacity=None, mask=None, rank=0):
     dict(world=2, bs=64, hidden=256, experts=4, topk=2, inter=512),
     dict(world=1, bs=300, hidden=384, experts=3, topk=2, inter=256),      # ragged tiles, 3 experts
     dict(world=4, bs=96, hidden=128, experts=16, topk=3, inter=768),
+    dict(world=1, bs=700, hidden=256, experts=37, topk=3, inter=512),     # 37 experts, one partial tile each
+    dict(world=1, bs=128, hidden=128, experts=2048, topk=16, inter=256),  # max L: 2048 experts of ~1 row
 ])
 def test_ffn_small(variant):
     inter = variant.pop("inter")

@@ -87,6 +87,7 @@ def test_skewed_full_size():
     dict(world=4, bs=64, hidden=64, experts=4, topk=1),              # K = 1, L = 1
     dict(world=5, bs=33, hidden=4104, experts=40, topk=8, shared=True),
     dict(world=8, bs=17, hidden=7168, experts=256, topk=9, shared=True),
+    dict(world=64, bs=6, hidden=136, experts=128, topk=4, shared=True),   # max combine world (W = 64)
 ])
 def test_ragged_shapes(variant):
     w = gen.workload("tiny", index=60 + len(str(variant)), **variant)
