@@ -254,6 +254,17 @@ def mdc_dispatch_quant(shape: Shape, x, expert_ids, x_active_mask, expand_q, dyn
     return st
 
 
+def mdc_dispatch_quant_gather(shape: Shape, x, expand_q, dynamic_scales, assist_info, ep_recv_counts,
+                              expert_token_nums, expanded_row_idx, workspace, stream=None, check: bool = True) -> int:
+    sh = shape.c()
+    st = _lib.mdc_dispatch_quant_gather(ctypes.byref(sh), _ptr(x), _ptr(expand_q), _ptr(dynamic_scales),
+                                        _ptr(assist_info), _ptr(ep_recv_counts), _ptr(expert_token_nums),
+                                        _ptr(expanded_row_idx), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    if check:
+        _check(st, "mdc_dispatch_quant_gather")
+    return st
+
+
 def prepare_dispatch_quant_gather(shape: Shape, x, expand_q, dynamic_scales, assist_info, ep_recv_counts,
                                   expert_token_nums, expanded_row_idx, workspace, stream=None) -> "Prepared":
     sh = shape.c()
@@ -306,6 +317,15 @@ class Prepared:
         st = self._fn(*self._args)
         if st != MDC_OK:
             raise MdcError(st, self._name)
+
+
+def prepare_dispatch(shape: Shape, x, expert_ids, x_active_mask, expand_x, assist_info, ep_recv_counts,
+                     expert_token_nums, expanded_row_idx, workspace, stream=None) -> Prepared:
+    sh = shape.c()
+    args = (ctypes.byref(sh), _ptr(x), _ptr(expert_ids), _ptr(x_active_mask), _ptr(expand_x), _ptr(assist_info),
+            _ptr(ep_recv_counts), _ptr(expert_token_nums), _ptr(expanded_row_idx), _ptr(workspace),
+            _nbytes(workspace), _stream(stream))
+    return Prepared(_lib.mdc_dispatch, args, "mdc_dispatch", (sh,))
 
 
 def prepare_dispatch_layout(shape: Shape, expert_ids, x_active_mask, workspace, stream=None) -> Prepared:

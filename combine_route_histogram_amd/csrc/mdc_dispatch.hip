@@ -444,6 +444,187 @@ __global__ __launch_bounds__(64) void k_dispatch_gather_q(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small batches: a1 - a5 in one launch.  When the whole route list is small
+// (decode-size batches), every workgroup loads it into LDS, recomputes the
+// per-(le, s) histogram and its scan, ranks its own token's routes (count of
+// earlier routes of the same source with the same expert, [TL] send loop),
+// places them and copies (QUANT: quantises) the token's row.  This replaces
+// the rank kernel and the gather kernel; the outputs are identical.  One
+// 256-thread workgroup per source token; workgroup 0 also writes
+// epRecvCounts and expertTokenNums.
+// ---------------------------------------------------------------------------
+constexpr int kSmallRoutes = 8192;                  // route keys held in LDS
+constexpr int kSmallCounters = 1024;                // L * W counters
+constexpr int64_t kSmallRereads = int64_t(1) << 20; // tokens x routes: ids every workgroup rereads
+constexpr int kSmallThreads = 256;
+constexpr int kSmallRowVec = 4;                     // row vectors per thread kept for the quantiser
+
+template <bool QUANT>
+__global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
+    const v4u* __restrict__ x, const int32_t* __restrict__ ids, const uint8_t* __restrict__ mask, int mask_per_route,
+    v4u* __restrict__ expand_x, int8_t* __restrict__ expand_q, float* __restrict__ dyn_scale,
+    int32_t* __restrict__ assist, int32_t* __restrict__ ep_recv, int64_t* __restrict__ expert_nums,
+    int32_t* __restrict__ row_idx, int W, int d, int BS, int K, int E, int L, int64_t A, int nvec) {
+  __shared__ int key_s[kSmallRoutes];
+  __shared__ int cnt_s[kSmallCounters];   // histogram, then its exclusive prefix
+  __shared__ int wsum[kSmallThreads / 64];
+  __shared__ int rank_s[MDC_MAX_TOPK];
+  __shared__ int row_s[MDC_MAX_TOPK];
+  __shared__ float amax_s[kSmallThreads / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int tok = blockIdx.x;   // s * BS + t
+  const int s = tok / BS, t = tok - s * BS;
+  const int n = W * BS * K;
+  const int nc = L * W;
+
+  // the token's row is loaded first: its latency overlaps the ranking below
+  const v4u* xr = x + (int64_t)tok * nvec;
+  v4u cache[kSmallRowVec];
+#pragma unroll
+  for (int u = 0; u < kSmallRowVec; ++u) {
+    const int i = tid + u * kSmallThreads;
+    cache[u] = i < nvec ? xr[i] : v4u{0u, 0u, 0u, 0u};
+  }
+
+  // keys: local expert of an active route sent to d, else -1
+  for (int f = tid; f < n; f += kSmallThreads) {
+    const int e = ids[f];
+    const bool active = mask == nullptr || mask[mask_per_route ? f : f / K] != 0;
+    const int q = e - d * L;
+    key_s[f] = (active && e >= 0 && e < E && q >= 0 && q < L) ? q : -1;
+  }
+  for (int i = tid; i < nc; i += kSmallThreads) cnt_s[i] = 0;
+  if (tid < MDC_MAX_TOPK) rank_s[tid] = 0;
+  __syncthreads();
+
+  // one pass over the keys: histogram cnt[le * W + s'], and the ranks of this
+  // token's routes (earlier routes of source s with the same key)
+  {
+    const int f_tok = tok * K, f_src = s * BS * K, routes_per_src = BS * K;
+    int kk[MDC_MAX_TOPK], c[MDC_MAX_TOPK];
+#pragma unroll
+    for (int k = 0; k < MDC_MAX_TOPK; ++k) {
+      kk[k] = k < K ? key_s[f_tok + k] : -1;
+      c[k] = 0;
+    }
+    for (int f = tid; f < n; f += kSmallThreads) {
+      const int key = key_s[f];
+      if (key < 0) continue;
+      atomicAdd(&cnt_s[key * W + f / routes_per_src], 1);
+      if (f >= f_src && f < f_tok + K) {
+#pragma unroll
+        for (int k = 0; k < MDC_MAX_TOPK; ++k) c[k] += (key == kk[k] && f < f_tok + k) ? 1 : 0;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < MDC_MAX_TOPK; ++k)
+      if (c[k] != 0) atomicAdd(&rank_s[k], c[k]);
+  }
+  __syncthreads();
+
+  // exclusive scan of the counters in (le-major, s-minor) order; thread j
+  // takes counters 4j .. 4j + 3
+  int v[4], sum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 4 * tid + j;
+    v[j] = i < nc ? cnt_s[i] : 0;
+    sum += v[j];
+  }
+  const int incl = wave_inclusive_scan(sum);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int run = incl - sum, total = 0;
+#pragma unroll
+  for (int w = 0; w < kSmallThreads / 64; ++w) {
+    run += w < wave ? wsum[w] : 0;
+    total += wsum[w];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 4 * tid + j;
+    if (i < nc) {
+      if (tok == 0) ep_recv[i] = run + v[j];   // inclusive ([TL] GetCumSum)
+      cnt_s[i] = run;
+    }
+    run += v[j];
+  }
+  __syncthreads();
+  if (tok == 0)
+    for (int le = tid; le < L; le += kSmallThreads)
+      expert_nums[le] = (int64_t)((le + 1 < L ? cnt_s[(le + 1) * W] : total) - cnt_s[le * W]);
+
+  // this token's rows, triplets and inverse-index entries
+  if (tid < K) {
+    const int f = tok * K + tid;
+    const int key = key_s[f];
+    int row = -1;
+    if (key >= 0) {
+      const int64_t r = (int64_t)cnt_s[key * W + s] + rank_s[tid];
+      row = r < A ? (int)r : -1;
+      row_idx[f] = row;
+      if (row >= 0) {
+        int32_t* a = assist + (int64_t)row * 3;
+        a[0] = s;
+        a[1] = t;
+        a[2] = tid;
+      }
+    }
+    row_s[tid] = row;
+  }
+  __syncthreads();
+  bool any = false;
+  for (int k = 0; k < K; ++k) any |= row_s[k] >= 0;
+  if (!any) return;
+
+  if (!QUANT) {
+    for (int k = 0; k < K; ++k) {
+      const int row = row_s[k];
+      if (row < 0) continue;
+      v4u* dst = expand_x + (int64_t)row * nvec;
+#pragma unroll
+      for (int u = 0; u < kSmallRowVec; ++u) {
+        const int i = tid + u * kSmallThreads;
+        if (i < nvec) dst[i] = cache[u];
+      }
+    }
+  } else {
+    // per-row int8 quantisation decided in fp32, as k_dispatch_gather_q
+    float amax = 0.f;
+#pragma unroll
+    for (int u = 0; u < kSmallRowVec; ++u)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(cache[u][w])), fabsf(bf16_hi(cache[u][w]))));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    if (lane == 0) amax_s[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(amax_s[0], amax_s[1]), fmaxf(amax_s[2], amax_s[3]));
+    const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+    const float scale = amax / 127.0f;
+    if (tid < K && row_s[tid] >= 0) dyn_scale[row_s[tid]] = scale;
+#pragma unroll
+    for (int u = 0; u < kSmallRowVec; ++u) {
+      const int i = tid + u * kSmallThreads;
+      if (i >= nvec) continue;
+      uint64_t packed = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float a = fminf(fmaxf(rintf(bf16_lo(cache[u][w]) * inv), -127.f), 127.f);
+        const float b = fminf(fmaxf(rintf(bf16_hi(cache[u][w]) * inv), -127.f), 127.f);
+        packed |= (uint64_t)(uint8_t)(int8_t)(int)a << (16 * w);
+        packed |= (uint64_t)(uint8_t)(int8_t)(int)b << (16 * w + 8);
+      }
+      for (int k = 0; k < K; ++k) {
+        const int row = row_s[k];
+        if (row >= 0) reinterpret_cast<uint64_t*>(expand_q + (int64_t)row * nvec * 8)[i] = packed;
+      }
+    }
+  }
+}
+
 // Empty batch: every count is zero.
 __global__ __launch_bounds__(64) void k_zero_counts(int32_t* __restrict__ ep_recv, int64_t* __restrict__ expert_nums,
                                                     int L, int W) {
@@ -714,6 +895,28 @@ mdc_status gather_q_impl(const DispatchPlan& p, const void* x, int8_t* expand_q,
   return launched();
 }
 
+// Decode-size batches: the one-shot entry points (mdc_dispatch,
+// mdc_dispatch_quant) run the whole dispatch as one launch of
+// k_dispatch_small instead of the rank and gather kernels.  The split-stage
+// entry points always take the two-kernel path (the gather stage does not
+// see the ids).
+bool small_path(const DispatchPlan& p) {
+  const int64_t routes = (int64_t)p.W * p.BS * p.K;
+  return routes > 0 && routes <= kSmallRoutes && (int64_t)p.L * p.W <= kSmallCounters &&
+         (int64_t)p.W * p.BS * routes <= kSmallRereads && p.nvec <= kSmallRowVec * kSmallThreads;
+}
+
+template <bool QUANT>
+mdc_status small_impl(const DispatchPlan& p, const void* x, const int32_t* ids, const uint8_t* mask, void* expand_x,
+                      int8_t* expand_q, float* dyn_scale, int32_t* assist, int32_t* ep_recv, int64_t* expert_nums,
+                      int32_t* row_idx, hipStream_t st) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_dispatch_small<QUANT>, dim3((unsigned)(p.W * p.BS)), dim3(kSmallThreads), 0, st,
+                     static_cast<const v4u*>(x), ids, mask, p.mask_per_route, static_cast<v4u*>(expand_x), expand_q,
+                     dyn_scale, assist, ep_recv, expert_nums, row_idx, p.W, p.d, p.BS, p.K, p.E, p.L, p.A, p.nvec);
+  return launched();
+}
+
 }  // namespace
 
 extern "C" {
@@ -779,6 +982,9 @@ mdc_status mdc_dispatch(const mdc_shape* shape, const void* x, const int32_t* ex
   if (workspace_bytes < p.bytes) return MDC_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (small_path(p))
+    return small_impl<false>(p, x, expert_ids, x_active_mask, expand_x, nullptr, nullptr, assist_info,
+                             ep_recv_counts, expert_token_nums, expanded_row_idx, s);
   st = layout_impl(p, expert_ids, x_active_mask, ws, s);
   if (st != MDC_OK) return st;
   return gather_impl(p, x, expand_x, assist_info, ep_recv_counts, expert_token_nums, expanded_row_idx, ws, s);
@@ -818,6 +1024,9 @@ mdc_status mdc_dispatch_quant(const mdc_shape* shape, const void* x, const int32
   if (workspace_bytes < p.bytes) return MDC_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (small_path(p))
+    return small_impl<true>(p, x, expert_ids, x_active_mask, nullptr, expand_q, dynamic_scales, assist_info,
+                            ep_recv_counts, expert_token_nums, expanded_row_idx, s);
   st = layout_impl(p, expert_ids, x_active_mask, ws, s);
   if (st != MDC_OK) return st;
   return gather_q_impl(p, x, expand_q, dynamic_scales, assist_info, ep_recv_counts, expert_token_nums,

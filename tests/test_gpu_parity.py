@@ -89,9 +89,12 @@ def test_skewed_full_size():
     dict(world=8, bs=17, hidden=7168, experts=256, topk=9, shared=True),
     dict(world=64, bs=6, hidden=136, experts=128, topk=4, shared=True),   # max combine world (W = 64)
 ])
-def test_ragged_shapes(variant):
+@pytest.mark.parametrize("split", [False, True], ids=["one_shot", "split_stages"])
+def test_ragged_shapes(variant, split):
+    # one-shot mdc_dispatch takes the one-launch path at these sizes where it
+    # applies; the split stages always take the rank + gather kernels
     w = gen.workload("tiny", index=60 + len(str(variant)), **variant)
-    _end_to_end(w, expert="pow2")
+    _end_to_end(w, expert="pow2", split=split)
 
 
 def test_capacity_overflow_drops_rows():

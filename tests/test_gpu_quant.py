@@ -27,7 +27,7 @@ def say(*a):
     sys.stdout.flush()
 
 
-def _quant_world(w, capacity=None):
+def _quant_world(w, capacity=None, split=False):
     cap = w.capacity if capacity is None else capacity
     wi = gen.world_inputs(w)
     shape = mdc.Shape(w.world, 0, w.bs, w.hidden, w.topk, w.experts, cap,
@@ -42,8 +42,13 @@ def _quant_world(w, capacity=None):
         o = mdc.alloc_dispatch_outputs(sh, G.DEV)
         o["expand_q"] = torch.empty((cap, w.hidden), dtype=torch.int8, device=G.DEV)
         o["scales"] = torch.empty((cap,), dtype=torch.float32, device=G.DEV)
-        mdc.mdc_dispatch_quant(sh, xd, idd, md, o["expand_q"], o["scales"], o["assist_info"], o["ep_recv_counts"],
-                               o["expert_token_nums"], row_idx, o["workspace"])
+        if split:
+            mdc.mdc_dispatch_layout(sh, idd, md, o["workspace"])
+            mdc.mdc_dispatch_quant_gather(sh, xd, o["expand_q"], o["scales"], o["assist_info"],
+                                          o["ep_recv_counts"], o["expert_token_nums"], row_idx, o["workspace"])
+        else:
+            mdc.mdc_dispatch_quant(sh, xd, idd, md, o["expand_q"], o["scales"], o["assist_info"],
+                                   o["ep_recv_counts"], o["expert_token_nums"], row_idx, o["workspace"])
         outs.append(o)
     torch.cuda.synchronize()
     return wi, shape, outs, row_idx
@@ -56,11 +61,12 @@ def _quant_world(w, capacity=None):
     dict(name="tiny", world=2, bs=40, hidden=8192, experts=4, topk=2, index=94),
     dict(name="share"),
 ])
-def test_dispatch_quant_matches_oracle(variant):
+@pytest.mark.parametrize("split", [False, True], ids=["one_shot", "split_stages"])
+def test_dispatch_quant_matches_oracle(variant, split):
     v = dict(variant)
     w = gen.workload(v.pop("name"), **v)
-    say(f"quant dispatch W={w.world} BS={w.bs} H={w.hidden} E={w.experts} K={w.topk}")
-    wi, shape, outs, row_idx = _quant_world(w)
+    say(f"quant dispatch W={w.world} BS={w.bs} H={w.hidden} E={w.experts} K={w.topk} split={split}")
+    wi, shape, outs, row_idx = _quant_world(w, split=split)
     ridx = row_idx.cpu().numpy()
     for d in range(w.world):
         ref, q, sc = O.dispatch_quant(wi.x, wi.ids, wi.mask, d, w.experts, w.capacity)
