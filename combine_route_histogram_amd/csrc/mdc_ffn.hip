@@ -4,6 +4,8 @@
 // Source: "PTO MegaMoE Dispatch + Combine Fusion Example", GMM1 / SwiGLU /
 // GMM2 stages and the per-token dynamic quantisation between them.
 
+#include <cstdlib>
+
 #include "mdc_common.h"
 
 namespace {
@@ -72,8 +74,12 @@ __device__ int64_t plan_scan_pair(int64_t a, int64_t b, int64_t* wsum, int64_t& 
   return excl;
 }
 
+// sync_words (optional, the fused kernel's): [0] queue head, [1] error,
+// done1 at [2, 2 + MT), ready at [2 + stride, 2 + stride + MT); amax_bits
+// for the rows in use.  All of them are zeroed here.
 __global__ __launch_bounds__(kPlanThreads) void k_ffn_plan(const int64_t* __restrict__ expert_nums, int L, int64_t A,
-                                                           int4* __restrict__ tiles) {
+                                                           int4* __restrict__ tiles, int* __restrict__ sync_words,
+                                                           int stride, uint32_t* __restrict__ amax_bits) {
   __shared__ int rem_s[2 * kPlanThreads];
   __shared__ int64_t wsum[kPlanThreads / 64 + 1];
   const int tid = threadIdx.x;
@@ -107,6 +113,16 @@ __global__ __launch_bounds__(kPlanThreads) void k_ffn_plan(const int64_t* __rest
     tiles[1 + (int)nfull + rank] = int4{e, lo + f * kFfnBM, hi, 0};
   }
   if (tid == 0) tiles[0] = int4{(int)(nfull + npart), 0, 0, 0};
+  if (sync_words != nullptr) {
+    const int MT = (int)(nfull + npart);
+    if (tid < 2) sync_words[tid] = 0;
+    for (int i = tid; i < MT; i += kPlanThreads) {
+      sync_words[2 + i] = 0;
+      sync_words[2 + stride + i] = 0;
+    }
+    const int64_t rows = min(total, A);
+    for (int64_t r = tid; r < rows; r += kPlanThreads) amax_bits[r] = 0u;
+  }
 }
 
 __device__ __forceinline__ float ffn_silu(float a) { return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
@@ -203,9 +219,12 @@ struct FfnStaging {
 // blocks past them stay zero, and their fragment reads and MFMAs are not
 // issued (an expert's short last m-tile is cheap).  NB = 0 still stages and
 // joins the barriers.
-template <bool GLU, int NB>
+template <bool GLU, int NB, bool COH>
 __device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const FfnStaging& st, int wt, int wn,
                                           const int (&fr)[4]) {
+  // COH: token rows are read with agent-coherent (sc1) loads: they were
+  // written in the same launch by another workgroup, possibly on another XCD
+  constexpr int kAux = COH ? 0x10 : 0;
   constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;
   constexpr int NR = NB > 0 ? NB + 2 : 0;   // fragment reads per k substep
   constexpr int NM = 2 * NB;                // MFMAs per k substep
@@ -218,7 +237,7 @@ __device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sa[i] = __builtin_amdgcn_raw_buffer_load_b128(st.ra, st.va + (unsigned)(64 * i * st.K), (unsigned)k0, 0);
+      sa[i] = __builtin_amdgcn_raw_buffer_load_b128(st.ra, st.va + (unsigned)(64 * i * st.K), (unsigned)k0, kAux);
       sw[i] = __builtin_amdgcn_raw_buffer_load_b128(st.rw, st.vw + (unsigned)(64 * i * st.K) + (i >= 2 ? st.whi : 0u),
                                                     (unsigned)k0, 0);
     }
@@ -331,14 +350,30 @@ __device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const
 // each XCD walks a contiguous run of tiles; tiles are ordered in groups of 4
 // m-tiles x 8 n-tiles (m fastest), so the tiles an XCD runs together share A
 // and W tiles in its L2.
-template <bool GLU>
-__global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(
-    const int8_t* __restrict__ a_src, const float* __restrict__ row_scale,
-    const int8_t* __restrict__ w, const float* __restrict__ w_scale, uint16_t* __restrict__ out,
-    const int4* __restrict__ tiles, int K, int Nw, int Nout) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFfnStage];
-  __shared__ float sc_row[kFfnBM];   // row scales of the tile's token rows
-  __shared__ float sc_col[kFfnBW];   // weight-row scales (GMM1: 128 gate, then 128 up)
+// Operands of one grouped GEMM.
+struct FfnGemm {
+  const int8_t* a_src;      // [rows][K] int8 token rows, expert-major
+  const float* row_scale;   // [rows]
+  const int8_t* w;          // [L][Nw][K] int8
+  const float* w_scale;     // [L][Nw]
+  uint16_t* out;            // [rows][Nout] bf16
+  int K, Nw, Nout;
+};
+
+// The kernel's LDS, shared by every tile it runs.
+struct FfnSmem {
+  uint8_t* lds;     // 2 * kFfnStage bytes: k stages, then the output tile
+  float* sc_row;    // [kFfnBM] row scales of the tile's token rows
+  float* sc_col;    // [kFfnBW] weight-row scales (GMM1: 128 gate, then 128 up)
+};
+
+// One output tile: token rows [row0, min(row_end, row0 + 256)) of expert e
+// (ti = {e, row0, row_end}) times n-tile nt.  GLU with amax_bits != NULL also
+// folds max |g| of every stored row into amax_bits[row] (fp32 bits; g >= 0
+// bit patterns order like the floats).
+template <bool GLU, bool COH = false>
+__device__ __forceinline__ void ffn_tile(const FfnGemm& g, int4 ti, int nt, const FfnSmem& sm,
+                                         uint32_t* __restrict__ amax_bits) {
   constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;   // output columns per tile
   constexpr int OU = NCOLS / 8;                      // 16-byte output units per tile row
   const int tid = threadIdx.x;
@@ -348,14 +383,6 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(
   // SIMD s runs wavefronts s and s + 4: one of each token half
   const int wt = wv >> 2;   // token half of the tile
   const int wn = wv & 3;    // weight-row quarter of the tile
-  const int G = gridDim.x;
-  const int nn = (Nout + NCOLS - 1) / NCOLS;
-  constexpr int GM = 4, GN = 8;
-  const int MT = tiles[0].x;
-  const int64_t T = (int64_t)MT * nn;
-  const int b = blockIdx.x;
-  const int lin = (b % 8) * (G / 8) + b / 8;   // XCD-contiguous walk (G is a multiple of 8)
-
   // staging: thread t moves chunk t & 7 of rows 64 i + t / 8 (i < 4) of both
   // tiles; in LDS that chunk sits at slot (t & 7) ^ ((row / 2) & 7), and
   // (row / 2) & 7 = (t / 16) & 7 for every i
@@ -367,117 +394,277 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(
 #pragma unroll
   for (int q = 0; q < 4; ++q) fr[q] = (lane & 31) * kFfnBK + (((2 * q + (lane >> 5)) ^ ((lane >> 1) & 7)) << 4);
 
-  for (int64_t t = lin; t < T; t += G) {
-    // tile t -> (m-tile, n-tile): groups of GM m-tiles x GN n-tiles, m fastest
-    const int64_t band = (int64_t)GM * nn;
-    const int64_t mg = t / band;
-    const int64_t r = t - mg * band;
-    const int m_in_group = (int)min((int64_t)GM, (int64_t)MT - mg * GM);
-    const int64_t per_ng = (int64_t)m_in_group * GN;
-    const int64_t ng = r / per_ng;
-    const int64_t r2 = r - ng * per_ng;
-    const int n_in_group = (int)min((int64_t)GN, (int64_t)nn - ng * GN);
-    const int mt = (int)(mg * GM + r2 % m_in_group);
-    const int nt = (int)(ng * GN + (r2 / m_in_group) % n_in_group);
-    __syncthreads();   // the previous tile's epilogue is done with LDS
-    const int4 ti = tiles[1 + mt];
-    const int e = __builtin_amdgcn_readfirstlane(ti.x);
-    const int row0 = __builtin_amdgcn_readfirstlane(ti.y);
-    const int row_end = __builtin_amdgcn_readfirstlane(ti.z);
-    const int n0 = nt * NCOLS;
+  const int K = g.K, Nw = g.Nw, Nout = g.Nout;
+  const int e = __builtin_amdgcn_readfirstlane(ti.x);
+  const int row0 = __builtin_amdgcn_readfirstlane(ti.y);
+  const int row_end = __builtin_amdgcn_readfirstlane(ti.z);
+  const int n0 = nt * NCOLS;
+  uint8_t* lds = sm.lds;
+  __syncthreads();   // the previous tile is done with LDS
 
-    // buffer descriptors: token rows [row0, min(row_end, row0 + 256)) and
-    // weight rows [n0, Nw) of expert e (GMM1 up rows at Nw/2 + n0 + ...)
-    const int rows_here = min(row_end - row0, kFfnBM);
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t*>(a_src + (int64_t)row0 * K), (short)0, rows_here * K, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t*>(w + ((int64_t)e * Nw + n0) * K), (short)0, (Nw - n0) * K, 0x00020000);
-    // weight rows (relative to n0): i < 2 -> rows 64 i + t / 8 (GMM1: gate),
-    // i >= 2 -> GMM1: up rows Nw/2 + 64 (i - 2) + t / 8, GMM2: rows 64 i + t / 8
-    const unsigned whi = GLU ? (unsigned)((Nw / 2 - NCOLS) * K) : 0u;
-    const unsigned v0 = (unsigned)(st_row * K + st_chunk * 16);
-    const FfnStaging st{ra, rw, v0, v0, whi, K, st_lds};
+  // buffer descriptors: token rows [row0, min(row_end, row0 + 256)) and
+  // weight rows [n0, Nw) of expert e (GMM1 up rows at Nw/2 + n0 + ...)
+  const int rows_here = min(row_end - row0, kFfnBM);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(g.a_src + (int64_t)row0 * K), (short)0, rows_here * K, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(g.w + ((int64_t)e * Nw + n0) * K), (short)0, (Nw - n0) * K, 0x00020000);
+  // weight rows (relative to n0): i < 2 -> rows 64 i + t / 8 (GMM1: gate),
+  // i >= 2 -> GMM1: up rows Nw/2 + 64 (i - 2) + t / 8, GMM2: rows 64 i + t / 8
+  const unsigned whi = GLU ? (unsigned)((Nw / 2 - NCOLS) * K) : 0u;
+  const unsigned v0 = (unsigned)(st_row * K + st_chunk * 16);
+  const FfnStaging st{ra, rw, v0, v0, whi, K, st_lds};
 
-    // the epilogue's scales, read from LDS after the k loop's first barrier
-    if (tid < kFfnBM) {
-      sc_row[tid] = row_scale[min(row0 + tid, row_end - 1)];
+  // the epilogue's scales, read from LDS after the k loop's first barrier
+  if (tid < kFfnBM) {
+    const float* rsp = g.row_scale + min(row0 + tid, row_end - 1);
+    sm.sc_row[tid] = COH ? __hip_atomic_load(rsp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *rsp;
+  } else {
+    const int c = tid - kFfnBM;
+    const int wr = GLU ? (c < NCOLS ? n0 + c : Nw / 2 + n0 + (c - NCOLS)) : min(n0 + c, Nw - 1);
+    sm.sc_col[c] = g.w_scale[(int64_t)e * Nw + wr];
+  }
+
+  // acc[j][i]: weight block j (32 rows), token block i (32 rows)
+  v16i acc[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[j][i] = v16i{};
+  // 32-row token blocks of this wavefront's half that hold valid rows
+  const int nblk = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows_here - wt * 128 + 31) / 32)));
+  switch (nblk) {
+    case 4: ffn_kloop<GLU, 4, COH>(lds, acc, st, wt, wn, fr); break;
+    case 3: ffn_kloop<GLU, 3, COH>(lds, acc, st, wt, wn, fr); break;
+    case 2: ffn_kloop<GLU, 2, COH>(lds, acc, st, wt, wn, fr); break;
+    case 1: ffn_kloop<GLU, 1, COH>(lds, acc, st, wt, wn, fr); break;
+    default: ffn_kloop<GLU, 0, COH>(lds, acc, st, wt, wn, fr); break;
+  }
+
+  // Epilogue.  Lane l holds, for each (j, i) and run q < 4, token
+  // 32 i + (l & 31) of the wavefront's token half and weight rows
+  // 32 j + 8 q + 4 (l / 32) + 0..3 of its block j.  The bf16 tile goes to
+  // LDS as [256 rows][NCOLS] with 16-byte unit u of row r at unit
+  // u ^ (r % OU), then leaves as whole rows, 16 bytes per thread.
+  __syncthreads();   // every wavefront is done reading the k loop's stages
+  const int cq = 4 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int trow = wt * 128 + 32 * i + (lane & 31);
+    const float rs = sm.sc_row[trow];
+    uint8_t* orow = lds + trow * (NCOLS * 2);
+    auto put = [&](int c, uint32_t lo, uint32_t hi) {   // c: tile column, multiple of 4
+      const int u = (c >> 3) ^ (trow % OU);
+      *reinterpret_cast<uint2*>(orow + u * 16 + (c & 4) * 2) = uint2{lo, hi};
+    };
+    if (GLU) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = wn * 32 + 8 * q + cq;
+        float v[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float hg = (float)acc[0][i][4 * q + jj] * rs * sm.sc_col[c + jj];
+          const float hu = (float)acc[1][i][4 * q + jj] * rs * sm.sc_col[NCOLS + c + jj];
+          v[jj] = ffn_silu(hg) * hu;
+        }
+        put(c, ffn_pack_bf16(v[0], v[1]), ffn_pack_bf16(v[2], v[3]));
+      }
     } else {
-      const int c = tid - kFfnBM;
-      const int wr = GLU ? (c < NCOLS ? n0 + c : Nw / 2 + n0 + (c - NCOLS)) : min(n0 + c, Nw - 1);
-      sc_col[c] = w_scale[(int64_t)e * Nw + wr];
-    }
-
-    // acc[j][i]: weight block j (32 rows), token block i (32 rows)
-    v16i acc[2][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[j][i] = v16i{};
-    // 32-row token blocks of this wavefront's half that hold valid rows
-    const int nblk = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows_here - wt * 128 + 31) / 32)));
-    switch (nblk) {
-      case 4: ffn_kloop<GLU, 4>(lds, acc, st, wt, wn, fr); break;
-      case 3: ffn_kloop<GLU, 3>(lds, acc, st, wt, wn, fr); break;
-      case 2: ffn_kloop<GLU, 2>(lds, acc, st, wt, wn, fr); break;
-      case 1: ffn_kloop<GLU, 1>(lds, acc, st, wt, wn, fr); break;
-      default: ffn_kloop<GLU, 0>(lds, acc, st, wt, wn, fr); break;
-    }
-
-    // Epilogue.  Lane l holds, for each (j, i) and run q < 4, token
-    // 32 i + (l & 31) of the wavefront's token half and weight rows
-    // 32 j + 8 q + 4 (l / 32) + 0..3 of its block j.  The bf16 tile goes to
-    // LDS as [256 rows][NCOLS] with 16-byte unit u of row r at unit
-    // u ^ (r % OU), then leaves as whole rows, 16 bytes per thread.
-    __syncthreads();   // every wavefront is done reading the k loop's stages
-    const int cq = 4 * (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int trow = wt * 128 + 32 * i + (lane & 31);
-      const float rs = sc_row[trow];
-      uint8_t* orow = lds + trow * (NCOLS * 2);
-      auto put = [&](int c, uint32_t lo, uint32_t hi) {   // c: tile column, multiple of 4
-        const int u = (c >> 3) ^ (trow % OU);
-        *reinterpret_cast<uint2*>(orow + u * 16 + (c & 4) * 2) = uint2{lo, hi};
-      };
-      if (GLU) {
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int c = wn * 32 + 8 * q + cq;
+          const int c = wn * 64 + 32 * j + 8 * q + cq;
           float v[4];
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float hg = (float)acc[0][i][4 * q + jj] * rs * sc_col[c + jj];
-            const float hu = (float)acc[1][i][4 * q + jj] * rs * sc_col[NCOLS + c + jj];
-            v[jj] = ffn_silu(hg) * hu;
-          }
+          for (int jj = 0; jj < 4; ++jj) v[jj] = (float)acc[j][i][4 * q + jj] * rs * sm.sc_col[c + jj];
           put(c, ffn_pack_bf16(v[0], v[1]), ffn_pack_bf16(v[2], v[3]));
         }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int c = wn * 64 + 32 * j + 8 * q + cq;
-            float v[4];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) v[jj] = (float)acc[j][i][4 * q + jj] * rs * sc_col[c + jj];
-            put(c, ffn_pack_bf16(v[0], v[1]), ffn_pack_bf16(v[2], v[3]));
-          }
-      }
     }
-    __syncthreads();
-    {
-      const int u = tid % OU;
-      const int col = n0 + u * 8;
+  }
+  __syncthreads();
+  const int u = tid % OU;
+  const int col = n0 + u * 8;
 #pragma unroll 4
-      for (int rr = tid / OU; rr < kFfnBM; rr += kFfnThreads / OU) {
-        const int row = row0 + rr;
-        if (row < row_end && col < Nout) {
-          const v4u v = *reinterpret_cast<const v4u*>(lds + rr * (NCOLS * 2) + ((u ^ (rr % OU)) * 16));
-          *reinterpret_cast<v4u*>(out + (int64_t)row * Nout + col) = v;
+  for (int rr = tid / OU; rr < kFfnBM; rr += kFfnThreads / OU) {
+    const int row = row0 + rr;
+    const v4u v = *reinterpret_cast<const v4u*>(lds + rr * (NCOLS * 2) + ((u ^ (rr % OU)) * 16));
+    if (row < row_end && col < Nout) *reinterpret_cast<v4u*>(g.out + (int64_t)row * Nout + col) = v;
+    if (GLU && amax_bits != nullptr) {
+      // max |g| over this row's NCOLS columns: the OU threads of a row are
+      // consecutive lanes of one wavefront
+      float m = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[w])), fabsf(bf16_hi(v[w]))));
+#pragma unroll
+      for (int o = OU / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      if (u == 0 && row < row_end) atomicMax(amax_bits + row, __float_as_uint(m));
+    }
+  }
+}
+
+// Tile t of a walk over T = MT x nn tiles -> (m-tile, n-tile): groups of GM
+// m-tiles x GN n-tiles, m fastest (the tiles run together share A and W
+// tiles in L2).
+__device__ __forceinline__ void ffn_decode_tile(int64_t t, int MT, int nn, int& mt, int& nt) {
+  constexpr int GM = 4, GN = 8;
+  const int64_t band = (int64_t)GM * nn;
+  const int64_t mg = t / band;
+  const int64_t r = t - mg * band;
+  const int m_in_group = (int)min((int64_t)GM, (int64_t)MT - mg * GM);
+  const int64_t per_ng = (int64_t)m_in_group * GN;
+  const int64_t ng = r / per_ng;
+  const int64_t r2 = r - ng * per_ng;
+  const int n_in_group = (int)min((int64_t)GN, (int64_t)nn - ng * GN);
+  mt = (int)(mg * GM + r2 % m_in_group);
+  nt = (int)(ng * GN + (r2 / m_in_group) % n_in_group);
+}
+
+// Persistent grouped GEMM over the plan's tiles (one workgroup per CU).
+template <bool GLU>
+__global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(FfnGemm g, const int4* __restrict__ tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFfnStage];
+  __shared__ float sc_row[kFfnBM];
+  __shared__ float sc_col[kFfnBW];
+  const FfnSmem sm{lds, sc_row, sc_col};
+  constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;
+  const int G = gridDim.x;
+  const int nn = (g.Nout + NCOLS - 1) / NCOLS;
+  const int MT = tiles[0].x;
+  const int64_t T = (int64_t)MT * nn;
+  const int b = blockIdx.x;
+  const int lin = (b % 8) * (G / 8) + b / 8;   // XCD-contiguous walk (G is a multiple of 8)
+  for (int64_t t = lin; t < T; t += G) {
+    int mt, nt;
+    ffn_decode_tile(t, MT, nn, mt, nt);
+    ffn_tile<GLU>(g, tiles[1 + mt], nt, sm, nullptr);
+  }
+}
+
+// Synchronisation words of the fused FFN kernel (workspace; the plan kernel
+// zeroes them before every call).
+struct FfnSync {
+  int* next;              // work-queue head
+  int* done1;             // [MT] GMM1 tiles finished per m-tile
+  int* ready;             // [MT] 1 once the m-tile's g rows are quantised
+  uint32_t* amax_bits;    // [rows] max |g| per row (fp32 bits)
+  int* error;             // set if a wait ran out of its bound (never expected)
+};
+
+// Quantises the g rows [r0, r1) of one m-tile (the last GMM1 tile of the
+// m-tile does it): codes clamp(rint(g * (127 / amax)), -127, 127) and scale
+// amax / 127, with amax the row's max |g| gathered by the GMM1 epilogues,
+// decided in fp32 as k_ffn_quant_rows decides them.
+__device__ void ffn_quant_mtile(const uint16_t* __restrict__ gsrc, int ncols, int8_t* __restrict__ q,
+                                float* __restrict__ scale, const uint32_t* __restrict__ amax_bits, int r0, int r1) {
+  const int tid = threadIdx.x;
+  const int nvec = ncols / 8;
+  const int total = (r1 - r0) * nvec;
+  constexpr int kBatch = 8;   // independent vectors in flight per thread
+  for (int base = 0; base < total; base += kFfnThreads * kBatch) {
+    v4u v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int idx = base + j * kFfnThreads + tid;
+      const int row = r0 + idx / nvec;
+      v[j] = idx < total ? *reinterpret_cast<const v4u*>(gsrc + (int64_t)row * ncols + (idx % nvec) * 8)
+                         : v4u{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int idx = base + j * kFfnThreads + tid;
+      if (idx >= total) continue;
+      const int row = r0 + idx / nvec;
+      const float amax = __uint_as_float(amax_bits[row]);
+      const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+      uint64_t packed = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float a = fminf(fmaxf(rintf(bf16_lo(v[j][w]) * inv), -127.f), 127.f);
+        const float b = fminf(fmaxf(rintf(bf16_hi(v[j][w]) * inv), -127.f), 127.f);
+        packed |= (uint64_t)(uint8_t)(int8_t)(int)a << (16 * w);
+        packed |= (uint64_t)(uint8_t)(int8_t)(int)b << (16 * w + 8);
+      }
+      *reinterpret_cast<uint64_t*>(q + (int64_t)row * ncols + (idx % nvec) * 8) = packed;
+    }
+  }
+  for (int row = r0 + tid; row < r1; row += kFfnThreads) scale[row] = __uint_as_float(amax_bits[row]) / 127.0f;
+}
+
+// NEXT-3 stage of the [PTO] fused pipeline: GMM1 + SwiGLU, the dynamic
+// quantisation of g and GMM2 in one persistent kernel.  Workgroups take
+// tiles from one queue: every GMM1 tile first (plan order), then every GMM2
+// tile (m-tiles in the same group order).  A GMM1 tile stores its g tile,
+// folds max |g| per row into amax_bits and counts itself in done1[m]; the
+// workgroup that finishes an m-tile's last GMM1 tile quantises the m-tile's
+// g rows and sets ready[m] ([PTO] ready flags between GMM1 and GMM2).  A
+// GMM2 tile waits for ready[m].  Every GMM1 tile leaves the queue before any
+// GMM2 tile, and GMM1 tiles wait on nothing, so every wait ends; each wait
+// is also bounded by spin_limit polls (error[0] is set if one ever runs
+// out).  The XCDs' L2s are not coherent with each other: writes are
+// published with agent-scope release fences (an L2 write-back, issued by
+// one thread per workgroup); the quantiser reads g after one acquire (an L2
+// invalidate) per m-tile, and GMM2 reads q2 and s2 with agent-coherent loads
+// instead of invalidating its XCD's L2 once per tile.
+__global__ __launch_bounds__(kFfnThreads) void k_ffn_fused(FfnGemm g1, FfnGemm g2, const int4* __restrict__ tiles,
+                                                            FfnSync sync, int spin_limit) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFfnStage];
+  __shared__ float sc_row[kFfnBM];
+  __shared__ float sc_col[kFfnBW];
+  __shared__ int bcast[2];
+  const FfnSmem sm{lds, sc_row, sc_col};
+  const int tid = threadIdx.x;
+  const int MT = tiles[0].x;
+  const int nn1 = (g1.Nout + kFfnBW / 2 - 1) / (kFfnBW / 2);
+  const int nn2 = (g2.Nout + kFfnBW - 1) / kFfnBW;
+  const int64_t T1 = (int64_t)MT * nn1, T2 = (int64_t)MT * nn2;
+  for (;;) {
+    __syncthreads();   // bcast is free
+    if (tid == 0) bcast[0] = atomicAdd(sync.next, 1);
+    __syncthreads();
+    const int64_t t = __builtin_amdgcn_readfirstlane(bcast[0]);
+    if (t >= T1 + T2) break;
+    if (t < T1) {
+      int mt, nt;
+      ffn_decode_tile(t, MT, nn1, mt, nt);
+      const int4 ti = tiles[1 + mt];
+      ffn_tile<true>(g1, ti, nt, sm, sync.amax_bits);
+      // Publish: the barrier orders every wavefront's g stores (workgroup
+      // scope) before thread 0's agent-scope release (one L2 write-back per
+      // tile), which precedes its count.
+      __syncthreads();
+      if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const bool last = atomicAdd(sync.done1 + mt, 1) == nn1 - 1;
+        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // see the other tiles' g and amax
+        bcast[1] = last;
+      }
+      __syncthreads();
+      if (bcast[1]) {
+        ffn_quant_mtile(g1.out, g1.Nout, const_cast<int8_t*>(g2.a_src), const_cast<float*>(g2.row_scale),
+                        sync.amax_bits, ti.y, min(ti.z, ti.y + kFfnBM));
+        __syncthreads();
+        // release q2 and s2 with the flag
+        if (tid == 0) __hip_atomic_store(sync.ready + mt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      int mt, nt;
+      ffn_decode_tile(t - T1, MT, nn2, mt, nt);
+      if (tid == 0) {
+        // poll with relaxed (agent-coherent) loads
+        int n = 0;
+        while (__hip_atomic_load(sync.ready + mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+          if (++n >= spin_limit) {
+            atomicExch(sync.error, 1);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
         }
       }
+      __syncthreads();
+      // q2 and s2 are read with agent-coherent loads (no L2 invalidate)
+      ffn_tile<false, true>(g2, tiles[1 + mt], nt, sm, nullptr);
     }
   }
 }
@@ -488,7 +675,7 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(
 struct FfnPlan {
   int64_t A;
   int H, N, L;
-  size_t off_q1, off_s1, off_g, off_q2, off_s2, off_tiles, bytes;
+  size_t off_q1, off_s1, off_g, off_q2, off_s2, off_tiles, off_amax, off_sync, bytes;
 };
 
 FfnPlan make_ffn_plan(const mdc_shape* sh, int inter_n) {
@@ -504,7 +691,10 @@ FfnPlan make_ffn_plan(const mdc_shape* sh, int inter_n) {
   f.off_s2 = f.off_q2 + round_up((size_t)f.A * (f.N / 2), 256);
   f.off_tiles = f.off_s2 + round_up((size_t)f.A * 4, 256);
   // m-tile table: header + at most A / kFfnBM + L tiles
-  f.bytes = f.off_tiles + round_up((size_t)(2 + f.A / kFfnBM + f.L) * sizeof(int4), 256);
+  const size_t max_mtiles = 2 + f.A / kFfnBM + f.L;
+  f.off_amax = f.off_tiles + round_up(max_mtiles * sizeof(int4), 256);
+  f.off_sync = f.off_amax + round_up((size_t)f.A * 4, 256);
+  f.bytes = f.off_sync + round_up((2 + 2 * max_mtiles) * sizeof(int), 256);
   if (f.bytes == 0) f.bytes = 256;
   return f;
 }
@@ -518,6 +708,16 @@ mdc_status check_ffn(const mdc_shape* sh, int inter_n) {
   if ((int64_t)inter_n * sh->hidden > INT32_MAX) return MDC_ERR_INVALID;
   return MDC_OK;
 }
+
+// GMM1 -> quantise g -> GMM2 runs as the one persistent k_ffn_fused launch
+// unless MDC_FFN_PIPELINE=0 is set in the environment (then as three
+// stream-ordered kernels; the results are identical).
+bool ffn_pipeline_enabled() {
+  const char* v = getenv("MDC_FFN_PIPELINE");   // read per call: cheap next to a GEMM launch
+  return v == nullptr || strcmp(v, "0") != 0;
+}
+// polls of a GMM2 tile's wait before it gives up and flags an error
+constexpr int kFfnSpinLimit = 1 << 24;
 
 mdc_status ffn_impl(const FfnPlan& f, const void* expand_x, const int8_t* expand_q, const float* dyn_scale,
                     const int64_t* expert_token_nums, const int8_t* w1, const float* w1_scale, const int8_t* w2,
@@ -543,13 +743,23 @@ mdc_status ffn_impl(const FfnPlan& f, const void* expand_x, const int8_t* expand
     s1 = const_cast<float*>(dyn_scale);
   }
   int4* tiles = reinterpret_cast<int4*>(ws + f.off_tiles);
-  hipLaunchKernelGGL(k_ffn_plan, dim3(1), dim3(kPlanThreads), 0, s, expert_token_nums, f.L, f.A, tiles);
-  hipLaunchKernelGGL(k_ffn_gemm<true>, dim3(g1), dim3(kFfnThreads), 0, s, q1, s1, w1, w1_scale, g, tiles, f.H, f.N,
-                     f.N / 2);
-  hipLaunchKernelGGL(k_ffn_quant_rows, dim3(quant_wgs), dim3(256), 0, s, reinterpret_cast<const v4u*>(g), q2, s2,
-                     expert_token_nums, f.L, f.A, f.N / 2 / 8);
-  hipLaunchKernelGGL(k_ffn_gemm<false>, dim3(g2), dim3(kFfnThreads), 0, s, q2, s2, w2, w2_scale,
-                     static_cast<uint16_t*>(y), tiles, f.N / 2, f.H, f.H);
+  uint32_t* amax = reinterpret_cast<uint32_t*>(ws + f.off_amax);
+  int* sync_words = reinterpret_cast<int*>(ws + f.off_sync);
+  const FfnGemm gemm1{q1, s1, w1, w1_scale, g, f.H, f.N, f.N / 2};
+  const FfnGemm gemm2{q2, s2, w2, w2_scale, static_cast<uint16_t*>(y), f.N / 2, f.H, f.H};
+  const bool fused = ffn_pipeline_enabled();
+  const int max_mtiles = (int)(2 + f.A / kFfnBM + f.L);
+  hipLaunchKernelGGL(k_ffn_plan, dim3(1), dim3(kPlanThreads), 0, s, expert_token_nums, f.L, f.A, tiles,
+                     fused ? sync_words : nullptr, max_mtiles, amax);
+  if (fused) {
+    const FfnSync sync{sync_words, sync_words + 2, sync_words + 2 + max_mtiles, amax, sync_words + 1};
+    hipLaunchKernelGGL(k_ffn_fused, dim3(g1), dim3(kFfnThreads), 0, s, gemm1, gemm2, tiles, sync, kFfnSpinLimit);
+  } else {
+    hipLaunchKernelGGL(k_ffn_gemm<true>, dim3(g1), dim3(kFfnThreads), 0, s, gemm1, tiles);
+    hipLaunchKernelGGL(k_ffn_quant_rows, dim3(quant_wgs), dim3(256), 0, s, reinterpret_cast<const v4u*>(g), q2, s2,
+                       expert_token_nums, f.L, f.A, f.N / 2 / 8);
+    hipLaunchKernelGGL(k_ffn_gemm<false>, dim3(g2), dim3(kFfnThreads), 0, s, gemm2, tiles);
+  }
   return launched();
 }
 

@@ -3,6 +3,7 @@
 The FFN is not bit-exact (fp32 epilogues on the GPU, float64 in the oracle;
 bf16 intermediate g): the bar is relative L2 error <= 2e-2 over all rows.
 """
+import os
 import sys
 
 import numpy as np
@@ -107,3 +108,46 @@ def test_ffn_full_size_then_combine():
     err2 = rel_l2(out, ref)
     say(f"  combine after FFN rel L2 {err2:.3e}")
     assert err2 <= REL_L2
+
+
+@pytest.mark.parametrize("variant", [
+    dict(world=4, bs=96, hidden=128, experts=16, topk=3, inter=768),
+    dict(world=1, bs=128, hidden=128, experts=2048, topk=16, inter=256),
+    dict(world=8, bs=2048, hidden=7168, experts=128, topk=8, inter=4096),
+])
+def test_ffn_pipeline_equals_stream_ordered_kernels(variant):
+    """The persistent GMM1 -> quantise -> GMM2 kernel (ready flags between the
+    GEMMs) gives y bit-identical to the three stream-ordered kernels."""
+    v = dict(variant)
+    inter = v.pop("inter")
+    name = "share" if v.get("bs") == 2048 else "tiny"
+    w = gen.workload(name, **({} if name == "share" else dict(index=80 + inter // 256, **v)))
+    say(f"ffn pipeline vs kernels W={w.world} BS={w.bs} H={w.hidden} E={w.experts} K={w.topk} N={inter}")
+    wi = gen.world_inputs(w)
+    fw = gen.ffn_weights(w, rank=0, inter=inter)
+    shape = mdc.Shape(w.world, 0, w.bs, w.hidden, w.topk, w.experts, w.capacity)
+    gw = G.dispatch_world(shape, wi.x, wi.ids, wi.mask)
+    o = gw.outs[0]
+    w1, s1, w2, s2 = _weights_dev(fw)
+    ws = torch.empty(mdc.mdc_ffn_workspace_size(shape, inter), dtype=torch.uint8, device=G.DEV)
+    ys = []
+    old = os.environ.get("MDC_FFN_PIPELINE")
+    try:
+        for flag in ("1", "0", "1"):
+            os.environ["MDC_FFN_PIPELINE"] = flag
+            y = torch.zeros_like(o["expand_x"])
+            mdc.mdc_ffn(shape, inter, o["expand_x"], o["expert_token_nums"], w1, s1, w2, s2, y, ws)
+            torch.cuda.synchronize()
+            ys.append(y)
+    finally:
+        if old is None:
+            os.environ.pop("MDC_FFN_PIPELINE", None)
+        else:
+            os.environ["MDC_FFN_PIPELINE"] = old
+    n = int(o["ep_recv_counts"][-1].item())
+    n = min(n, w.capacity)
+    assert n > 0
+    a, b, c = (t[:n].view(torch.int16) for t in ys)
+    assert torch.equal(a, b), f"pipeline vs kernels: {(a != b).sum().item()} values differ"
+    assert torch.equal(a, c), "pipeline not repeatable"
+    say(f"  y bit-identical over {n} rows")
