@@ -10,6 +10,13 @@
 //                     its rows on this rank, with the (src, token, k) triplets,
 //                     the route -> row inverse index, epRecvCounts and
 //                     expertTokenNums.  (mdc_dispatch_gather)
+//   k_dispatch_gather_q  as k_dispatch_gather with one wavefront per whole
+//                     row, writing each row as int8 codes plus a per-row
+//                     fp32 scale.  (mdc_dispatch_quant_gather)
+//   k_dispatch_small  decode-size batches: all of the above in one launch,
+//                     every workgroup re-deriving the histogram and its scan
+//                     from the route list in LDS.  (mdc_dispatch and
+//                     mdc_dispatch_quant when the route list is small)
 //   k_combine         one wavefront per (token, column tile) of the combining
 //                     rank: reads the token's present expert rows (and the
 //                     shared-expert row), accumulates in fp32 in ascending k,
@@ -17,8 +24,10 @@
 //
 // Sources: "dispatch_combine_shmem.py" (TileLang-Ascend example),
 // moe_dispatch_kernel / moe_combine_kernel; "aclnnMoeDistributeCombineV4",
-// Function formula and Function Prototype; "PTO MegaMoE Dispatch + Combine
-// Fusion Example", FrontReorder / Dispatch / Combine / Unpermute stages.
+// Function formula, Function Prototype and parameter notes (2D mask,
+// zero/copy experts, quantised communication); "PTO MegaMoE Dispatch +
+// Combine Fusion Example", FrontReorder / Dispatch / Combine / Unpermute
+// stages.
 //
 // Built with -ffp-contract=off: the combine's products and sums are rounded
 // to fp32 one by one, in the order the combine formula lists them.

@@ -17,13 +17,15 @@ namespace {
 //   q1, s1 = per-row int8 quantisation of x (amax / 127, round half even)
 //   h      = (q1 . W1[e]^T) * s1[row] * w1s[e][n]          (int32 MFMA accumulate)
 //   g      = silu(h[:, j]) * h[:, j + N/2],  j < N/2        (fused in GMM1's epilogue)
-//   q2, s2 = per-row int8 quantisation of g (quantised while GMM2 loads its tiles)
+//   q2, s2 = per-row int8 quantisation of g (per m-tile, once its GMM1 tiles are done)
 //   y      = bf16((q2 . W2[e]^T) * s2[row] * w2s[e][h])
 // The GEMMs use v_mfma_i32_32x32x32_i8 on 256-token x 256-weight-row tiles
 // (GMM1: 128 gate + 128 up weight rows per tile so gate and up land in the
 // same lanes), eight wavefronts (two per SIMD) each holding a 128 x 64 int32
-// accumulator block in AGPRs, k staged through a double-buffered LDS ring 128
-// bytes deep; the output tile leaves through LDS as whole rows.
+// accumulator block in registers, k staged through a double-buffered LDS ring
+// 128 bytes deep; the output tile leaves through LDS as whole rows.  By
+// default GMM1, the quantisation of g and GMM2 run as one persistent kernel
+// with ready counters between them (k_ffn_fused).
 // ---------------------------------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(256) void k_ffn_quant_rows(
   }
 }
 
-// The k loop of one tile (see k_ffn_gemm).  Stage ks + 1 travels global ->
+// The k loop of one tile (see ffn_tile).  Stage ks + 1 travels global ->
 // registers during stage ks - 1 and registers -> LDS during stage ks, into the
 // buffer nobody reads in stage ks; one barrier ends each stage.  Fragments of
 // k substep q + 1 are read while the MFMAs of substep q run, and the last
@@ -313,8 +315,8 @@ __device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const
   }
 }
 
-// Persistent grouped GEMM, C = A . W[e]^T with A int8 [rows][K] (token rows
-// of expert e) and W int8 [L][Nw][K].  GLU = true (GMM1): each tile pairs 128
+// Grouped GEMM tiles, C = A . W[e]^T with A int8 [rows][K] (token rows of
+// expert e) and W int8 [L][Nw][K].  GLU = true (GMM1): each tile pairs 128
 // gate rows of W (columns n) with the 128 up rows (columns N/2 + n); the
 // epilogue dequantises both, applies silu(gate) * up and writes bf16 g.
 // GLU = false (GMM2): the epilogue dequantises and writes bf16 y.  Dequant:
@@ -339,17 +341,17 @@ __device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const
 // Out-of-range rows (past the expert's rows or past Nw) read as zero through
 // the buffer descriptors' range checks and are never stored.
 //
-// Epilogue, per token half: the wavefronts of that half write their bf16
-// outputs into LDS rows (row pitch padded by 8 bytes so 32 rows written at
-// one column fall in distinct banks), then all wavefronts store whole rows
-// with 16-byte stores.
+// Epilogue: scales come from LDS; the wavefronts write their bf16 outputs
+// into the (now free) LDS as [256 rows][tile columns], 16-byte units XOR-
+// swizzled by row, then every thread stores 16 bytes of a whole row.
 //
-// Tiles: T = (m-tiles of the plan) x (output columns / tile columns).
-// The launch holds one workgroup per CU; workgroup b walks tiles
-// i*G + (b % 8)*(G/8) + b / 8.  Hardware places workgroup b on XCD b % 8, so
-// each XCD walks a contiguous run of tiles; tiles are ordered in groups of 4
-// m-tiles x 8 n-tiles (m fastest), so the tiles an XCD runs together share A
-// and W tiles in its L2.
+// Tiles: T = (m-tiles of the plan) x (output columns / tile columns).  The
+// launches hold one workgroup per CU.  k_ffn_gemm: workgroup b walks tiles
+// i*G + (b % 8)*(G/8) + b / 8; hardware places workgroup b on XCD b % 8, so
+// each XCD walks a contiguous run of tiles, ordered in groups of 4 m-tiles x
+// 8 n-tiles (m fastest) so the tiles an XCD runs together share A and W
+// tiles in its L2.  k_ffn_fused takes the same order from an atomic queue.
+
 // Operands of one grouped GEMM.
 struct FfnGemm {
   const int8_t* a_src;      // [rows][K] int8 token rows, expert-major
