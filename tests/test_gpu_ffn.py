@@ -70,6 +70,7 @@ def _run_ffn(w, inter, capacity=None, mask=None, rank=0):
     dict(world=4, bs=96, hidden=128, experts=16, topk=3, inter=768),
     dict(world=1, bs=700, hidden=256, experts=37, topk=3, inter=512),     # 37 experts, one partial tile each
     dict(world=1, bs=128, hidden=128, experts=2048, topk=16, inter=256),  # max L: 2048 experts of ~1 row
+    dict(world=8, bs=256, hidden=256, experts=128, topk=8, inter=512, routing="zipf"),  # skewed expert loads
 ])
 def test_ffn_small(variant):
     inter = variant.pop("inter")

@@ -218,3 +218,33 @@ def test_special_experts_and_route_mask_full_size():
     """Share shapes with 8 zero and 8 copy experts and a 2D route mask."""
     w = gen.workload("share", zero_experts=8, copy_experts=8, route_mask_frac=0.05, index=92)
     _end_to_end(w, ranks=[0, 4])
+
+
+def _random_cases(n=24, seed=20261202):
+    """Seeded random small worlds: ragged W/BS/H/E/K, 1D or 2D masks, zero/copy
+    experts, shared expert on or off, full or overflowing capacity, both
+    dispatch paths and both test experts."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        W = int(rng.integers(1, 9))
+        L = int(rng.integers(1, 41))
+        Z = int(rng.choice([0, 0, 1, 3]))
+        C = int(rng.choice([0, 0, 2]))
+        E = W * L
+        K = int(rng.integers(1, min(16, E + Z + C) + 1))
+        c = dict(world=W, bs=int(rng.integers(1, 201)), hidden=int(rng.choice([8, 64, 136, 520, 1032, 2056])),
+                 experts=E, topk=K, zero_experts=Z, copy_experts=C, shared=bool(rng.integers(0, 2)),
+                 inactive_frac=float(rng.choice([0.0, 0.2])), route_mask_frac=float(rng.choice([0.0, 0.0, 0.3])))
+        cap_scale = float(rng.choice([1.0, 1.0, 0.3]))
+        split = bool(rng.integers(0, 2))
+        expert = str(rng.choice(["identity", "pow2"]))
+        cases.append(pytest.param(i, c, cap_scale, split, expert, id=f"case{i}"))
+    return cases
+
+
+@pytest.mark.parametrize("i,cfg,cap_scale,split,expert", _random_cases())
+def test_random_shapes(i, cfg, cap_scale, split, expert):
+    w = gen.workload("tiny", index=200 + i, **cfg)
+    cap = max(0, int(round(w.capacity * cap_scale)))
+    _end_to_end(w, expert=expert, capacity=cap, split=split)
