@@ -468,6 +468,7 @@ constexpr int kSmallCounters = 1024;                // L * W counters
 constexpr int64_t kSmallRereads = int64_t(1) << 20; // tokens x routes: ids every workgroup rereads
 constexpr int kSmallThreads = 256;
 constexpr int kSmallRowVec = 4;                     // row vectors per thread kept for the quantiser
+constexpr int kSmallKeyBatch = 8;                   // route ids per thread in flight at once
 
 template <bool QUANT>
 __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
@@ -488,21 +489,50 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
   const int n = W * BS * K;
   const int nc = L * W;
 
-  // the token's row is loaded first: its latency overlaps the ranking below
+  // keys: local expert of an active route sent to d, else -1.  The route
+  // ids are read kSmallKeyBatch per thread at a time, every load issued
+  // before the first is used; the first batch goes out before the token's
+  // row, whose loads then overlap the ranking below.
+  int ev[kSmallKeyBatch];
+  uint8_t mv[kSmallKeyBatch];
+  // (indices past the end are clamped, not skipped, so that the loads are
+  // unconditional and the waits before their uses count them exactly)
+  auto load_keys = [&](int f0) {
+#pragma unroll
+    for (int j = 0; j < kSmallKeyBatch; ++j) {
+      const int f = min(f0 + tid + j * kSmallThreads, n - 1);
+      ev[j] = ids[f];
+    }
+    if (mask != nullptr) {
+#pragma unroll
+      for (int j = 0; j < kSmallKeyBatch; ++j) {
+        const int f = min(f0 + tid + j * kSmallThreads, n - 1);
+        mv[j] = mask[mask_per_route ? f : f / K];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSmallKeyBatch; ++j) mv[j] = 1;
+    }
+  };
+  load_keys(0);
+
+  // (clamped as well: vectors past the row's end are never stored, and the
+  // quantiser skips them)
   const v4u* xr = x + (int64_t)tok * nvec;
   v4u cache[kSmallRowVec];
 #pragma unroll
-  for (int u = 0; u < kSmallRowVec; ++u) {
-    const int i = tid + u * kSmallThreads;
-    cache[u] = i < nvec ? xr[i] : v4u{0u, 0u, 0u, 0u};
-  }
+  for (int u = 0; u < kSmallRowVec; ++u) cache[u] = xr[min(tid + u * kSmallThreads, nvec - 1)];
 
-  // keys: local expert of an active route sent to d, else -1
-  for (int f = tid; f < n; f += kSmallThreads) {
-    const int e = ids[f];
-    const bool active = mask == nullptr || mask[mask_per_route ? f : f / K] != 0;
-    const int q = e - d * L;
-    key_s[f] = (active && e >= 0 && e < E && q >= 0 && q < L) ? q : -1;
+  for (int f0 = 0;;) {
+#pragma unroll
+    for (int j = 0; j < kSmallKeyBatch; ++j) {
+      const int f = f0 + tid + j * kSmallThreads;
+      const int q = ev[j] - d * L;
+      if (f < n) key_s[f] = (mv[j] != 0 && ev[j] >= 0 && ev[j] < E && q >= 0 && q < L) ? q : -1;
+    }
+    f0 += kSmallKeyBatch * kSmallThreads;
+    if (f0 >= n) break;
+    load_keys(f0);
   }
   for (int i = tid; i < nc; i += kSmallThreads) cnt_s[i] = 0;
   if (tid < MDC_MAX_TOPK) rank_s[tid] = 0;
@@ -518,13 +548,22 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
       kk[k] = k < K ? key_s[f_tok + k] : -1;
       c[k] = 0;
     }
-    for (int f = tid; f < n; f += kSmallThreads) {
-      const int key = key_s[f];
-      if (key < 0) continue;
-      atomicAdd(&cnt_s[key * W + f / routes_per_src], 1);
-      if (f >= f_src && f < f_tok + K) {
+    for (int f0 = 0; f0 < n; f0 += kSmallKeyBatch * kSmallThreads) {
+      int key[kSmallKeyBatch];
 #pragma unroll
-        for (int k = 0; k < MDC_MAX_TOPK; ++k) c[k] += (key == kk[k] && f < f_tok + k) ? 1 : 0;
+      for (int j = 0; j < kSmallKeyBatch; ++j) {
+        const int f = f0 + tid + j * kSmallThreads;
+        key[j] = f < n ? key_s[f] : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < kSmallKeyBatch; ++j) {
+        const int f = f0 + tid + j * kSmallThreads;
+        if (key[j] < 0) continue;
+        atomicAdd(&cnt_s[key[j] * W + f / routes_per_src], 1);
+        if (f >= f_src && f < f_tok + K) {
+#pragma unroll
+          for (int k = 0; k < MDC_MAX_TOPK; ++k) c[k] += (key[j] == kk[k] && f < f_tok + k) ? 1 : 0;
+        }
       }
     }
 #pragma unroll
@@ -604,8 +643,9 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
     float amax = 0.f;
 #pragma unroll
     for (int u = 0; u < kSmallRowVec; ++u)
+      if (tid + u * kSmallThreads < nvec)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(cache[u][w])), fabsf(bf16_hi(cache[u][w]))));
+        for (int w = 0; w < 4; ++w) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(cache[u][w])), fabsf(bf16_hi(cache[u][w]))));
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
     if (lane == 0) amax_s[wave] = amax;
