@@ -324,7 +324,7 @@ def main():
                 "traffic": measured_traffic(w.name, dom[0]),
                 "bytes_per_launch": dom[2], "avg_launch_us": round(dom[3], 3)}
     if ffn_info is not None:
-        roofline = {"bound": "mfma", "kernel": "mdc_ffn_quant_input (k_ffn_plan + k_ffn_fused: GMM1, g quantisation, GMM2)",
+        roofline = {"bound": "mfma", "kernel": "mdc_ffn_quant_input (k_ffn_plan, k_ffn_gemm GMM1 + SwiGLU, k_ffn_quant_rows, k_ffn_gemm GMM2)",
                     "achieved": ffn_info["tops"], "peak": INT8_PEAK_TOPS, "unit": "TOP/s (int8)",
                     "frac": ffn_info["mfma_frac"], "traffic": None, "ops_per_launch": ffn_info["int8_ops"],
                     "avg_launch_us": ffn_info["us"]}

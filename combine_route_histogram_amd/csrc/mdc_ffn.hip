@@ -24,8 +24,10 @@ namespace {
 // same lanes), eight wavefronts (two per SIMD) each holding a 128 x 64 int32
 // accumulator block in registers, k staged through a double-buffered LDS ring
 // 128 bytes deep; the output tile leaves through LDS as whole rows.  By
-// default GMM1, the quantisation of g and GMM2 run as one persistent kernel
-// with ready counters between them (k_ffn_fused).
+// default GMM1, the quantisation of g and GMM2 run as three stream-ordered
+// kernels, each GEMM persistent and loading its next tile's first k stage
+// before the current tile's output stores; MDC_FFN_PIPELINE=1 runs them as
+// one persistent kernel with ready counters between them (k_ffn_fused).
 // ---------------------------------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -217,16 +219,38 @@ struct FfnStaging {
   int lds_off;                     // this thread's LDS byte offset for i = 0
 };
 
+// Stage 0 of a tile (k bytes 0 .. kFfnBK of this thread's staging rows)
+// and the epilogue scale this thread loads, in registers.  A persistent
+// kernel that knows its next tile loads them before the current tile's
+// output stores: loads and stores retire in order, so a load issued after
+// the stores would first wait for them to drain.
+struct FfnStage0 {
+  v4i sa[4], sw[4];
+  float sc;
+};
+
+// Loads k bytes k0 .. k0 + kFfnBK of this thread's staging rows (4 token
+// rows and 4 weight rows, 16 bytes each) into registers.
+template <bool COH>
+__device__ __forceinline__ void ffn_stage_load(const FfnStaging& st, int k0, v4i (&sa)[4], v4i (&sw)[4]) {
+  // COH: token rows are read with agent-coherent (sc1) loads: they were
+  // written in the same launch by another workgroup, possibly on another XCD
+  constexpr int kAux = COH ? 0x10 : 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sa[i] = __builtin_amdgcn_raw_buffer_load_b128(st.ra, st.va + (unsigned)(64 * i * st.K), (unsigned)k0, kAux);
+    sw[i] = __builtin_amdgcn_raw_buffer_load_b128(st.rw, st.vw + (unsigned)(64 * i * st.K) + (i >= 2 ? st.whi : 0u),
+                                                  (unsigned)k0, 0);
+  }
+}
+
 // NB = number of the wavefront's 32-row token blocks that hold valid rows:
 // blocks past them stay zero, and their fragment reads and MFMAs are not
 // issued (an expert's short last m-tile is cheap).  NB = 0 still stages and
 // joins the barriers.
 template <bool GLU, int NB, bool COH>
 __device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const FfnStaging& st, int wt, int wn,
-                                          const int (&fr)[4]) {
-  // COH: token rows are read with agent-coherent (sc1) loads: they were
-  // written in the same launch by another workgroup, possibly on another XCD
-  constexpr int kAux = COH ? 0x10 : 0;
+                                          const int (&fr)[4], const FfnStage0& s0, bool pre) {
   constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;
   constexpr int NR = NB > 0 ? NB + 2 : 0;   // fragment reads per k substep
   constexpr int NM = 2 * NB;                // MFMAs per k substep
@@ -236,14 +260,7 @@ __device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const
     return wn * 64 + 32 * j;
   };
   v4i sa[4], sw[4];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sa[i] = __builtin_amdgcn_raw_buffer_load_b128(st.ra, st.va + (unsigned)(64 * i * st.K), (unsigned)k0, kAux);
-      sw[i] = __builtin_amdgcn_raw_buffer_load_b128(st.rw, st.vw + (unsigned)(64 * i * st.K) + (i >= 2 ? st.whi : 0u),
-                                                    (unsigned)k0, 0);
-    }
-  };
+  auto gload = [&](int k0) { ffn_stage_load<COH>(st, k0, sa, sw); };
   auto lwrite = [&](uint8_t* buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -287,7 +304,15 @@ __device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const
 
   const int nk = st.K / kFfnBK;
   v4i tf[4], wf[2], tg[4], wg[2];
-  gload(0);
+  if (pre) {   // stage 0 is already in s0
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sa[i] = s0.sa[i];
+      sw[i] = s0.sw[i];
+    }
+  } else {
+    gload(0);
+  }
   lwrite(lds);
   __syncthreads();
   gload(min(1, nk - 1) * kFfnBK);
@@ -369,13 +394,75 @@ struct FfnSmem {
   float* sc_col;    // [kFfnBW] weight-row scales (GMM1: 128 gate, then 128 up)
 };
 
+// Buffer descriptors and this thread's staging offsets for tile (ti, nt):
+// token rows [row0, min(row_end, row0 + 256)) and weight rows [n0, Nw) of
+// expert e (GMM1: up rows at Nw/2 + n0 + ...).  Thread t moves chunk t & 7
+// of rows 64 i + t / 8 (i < 4) of both tiles; in LDS that chunk sits at
+// slot (t & 7) ^ ((row / 2) & 7), and (row / 2) & 7 = (t / 16) & 7 for every
+// i.  Weight rows relative to n0: i < 2 -> rows 64 i + t / 8 (GMM1: gate),
+// i >= 2 -> GMM1: up rows Nw/2 + 64 (i - 2) + t / 8, GMM2: rows 64 i + t / 8.
+template <bool GLU>
+__device__ __forceinline__ FfnStaging ffn_staging(const FfnGemm& g, int4 ti, int nt) {
+  constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;
+  const int tid = threadIdx.x;
+  const int st_row = tid >> 3;
+  const int st_chunk = tid & 7;
+  const int st_lds = st_row * kFfnBK + ((st_chunk ^ ((tid >> 4) & 7)) << 4);
+  const int K = g.K, Nw = g.Nw;
+  const int e = __builtin_amdgcn_readfirstlane(ti.x);
+  const int row0 = __builtin_amdgcn_readfirstlane(ti.y);
+  const int row_end = __builtin_amdgcn_readfirstlane(ti.z);
+  const int n0 = nt * NCOLS;
+  const int rows_here = min(row_end - row0, kFfnBM);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(g.a_src + (int64_t)row0 * K), (short)0, rows_here * K, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(g.w + ((int64_t)e * Nw + n0) * K), (short)0, (Nw - n0) * K, 0x00020000);
+  const unsigned whi = GLU ? (unsigned)((Nw / 2 - NCOLS) * K) : 0u;
+  const unsigned v0 = (unsigned)(st_row * K + st_chunk * 16);
+  return FfnStaging{ra, rw, v0, v0, whi, K, st_lds};
+}
+
+// This thread's epilogue scale of tile (ti, nt): threads t < kFfnBM take
+// the row scale of token row t, the others weight-row scale t - kFfnBM
+// (GMM1: 128 gate rows, then the 128 matching up rows).
+template <bool GLU, bool COH>
+__device__ __forceinline__ float ffn_scale(const FfnGemm& g, int4 ti, int nt) {
+  constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;
+  const int tid = threadIdx.x;
+  const int e = __builtin_amdgcn_readfirstlane(ti.x);
+  const int row0 = __builtin_amdgcn_readfirstlane(ti.y);
+  const int row_end = __builtin_amdgcn_readfirstlane(ti.z);
+  const int Nw = g.Nw, n0 = nt * NCOLS;
+  if (tid < kFfnBM) {
+    const float* rsp = g.row_scale + min(row0 + tid, row_end - 1);
+    return COH ? __hip_atomic_load(rsp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *rsp;
+  }
+  const int c = tid - kFfnBM;
+  const int wr = GLU ? (c < NCOLS ? n0 + c : Nw / 2 + n0 + (c - NCOLS)) : min(n0 + c, Nw - 1);
+  return g.w_scale[(int64_t)e * Nw + wr];
+}
+
 // One output tile: token rows [row0, min(row_end, row0 + 256)) of expert e
 // (ti = {e, row0, row_end}) times n-tile nt.  GLU with amax_bits != NULL also
 // folds max |g| of every stored row into amax_bits[row] (fp32 bits; g >= 0
-// bit patterns order like the floats).
-template <bool GLU, bool COH = false>
-__device__ __forceinline__ void ffn_tile(const FfnGemm& g, int4 ti, int nt, const FfnSmem& sm,
-                                         uint32_t* __restrict__ amax_bits) {
+// bit patterns order like the floats).  With have, cur already holds the
+// tile's stage 0 and scale.  PF: once the accumulators are spent, next()
+// (run by every thread) names the tile to load ahead, and nxt receives its
+// stage 0 and scale when the returned pf is set (else this tile's own
+// again, so that nxt is written on every call); cur is read before the k
+// loop and nxt written after it, so nxt may be cur.  Returns what next()
+// returned (PF) or pf = false.
+struct FfnNext {
+  bool pf;    // nxt holds stage 0 and scale of tile (ti, nt)
+  int4 ti;
+  int nt;
+};
+
+template <bool GLU, bool COH, bool PF, class NextF>
+__device__ __forceinline__ FfnNext ffn_tile(const FfnGemm& g, int4 ti, int nt, const FfnSmem& sm,
+                                            uint32_t* __restrict__ amax_bits, FfnStage0& cur, bool have,
+                                            FfnStage0& nxt, NextF&& next) {
   constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;   // output columns per tile
   constexpr int OU = NCOLS / 8;                      // 16-byte output units per tile row
   const int tid = threadIdx.x;
@@ -385,47 +472,23 @@ __device__ __forceinline__ void ffn_tile(const FfnGemm& g, int4 ti, int nt, cons
   // SIMD s runs wavefronts s and s + 4: one of each token half
   const int wt = wv >> 2;   // token half of the tile
   const int wn = wv & 3;    // weight-row quarter of the tile
-  // staging: thread t moves chunk t & 7 of rows 64 i + t / 8 (i < 4) of both
-  // tiles; in LDS that chunk sits at slot (t & 7) ^ ((row / 2) & 7), and
-  // (row / 2) & 7 = (t / 16) & 7 for every i
-  const int st_row = tid >> 3;
-  const int st_chunk = tid & 7;
-  const int st_lds = st_row * kFfnBK + ((st_chunk ^ ((tid >> 4) & 7)) << 4);
   // fragment reads: lane l reads row l & 31, chunk 2 s + l / 32 (k substep s)
   int fr[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) fr[q] = (lane & 31) * kFfnBK + (((2 * q + (lane >> 5)) ^ ((lane >> 1) & 7)) << 4);
 
-  const int K = g.K, Nw = g.Nw, Nout = g.Nout;
-  const int e = __builtin_amdgcn_readfirstlane(ti.x);
+  const int Nout = g.Nout;
   const int row0 = __builtin_amdgcn_readfirstlane(ti.y);
   const int row_end = __builtin_amdgcn_readfirstlane(ti.z);
   const int n0 = nt * NCOLS;
-  uint8_t* lds = sm.lds;
-  __syncthreads();   // the previous tile is done with LDS
-
-  // buffer descriptors: token rows [row0, min(row_end, row0 + 256)) and
-  // weight rows [n0, Nw) of expert e (GMM1 up rows at Nw/2 + n0 + ...)
   const int rows_here = min(row_end - row0, kFfnBM);
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(g.a_src + (int64_t)row0 * K), (short)0, rows_here * K, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(g.w + ((int64_t)e * Nw + n0) * K), (short)0, (Nw - n0) * K, 0x00020000);
-  // weight rows (relative to n0): i < 2 -> rows 64 i + t / 8 (GMM1: gate),
-  // i >= 2 -> GMM1: up rows Nw/2 + 64 (i - 2) + t / 8, GMM2: rows 64 i + t / 8
-  const unsigned whi = GLU ? (unsigned)((Nw / 2 - NCOLS) * K) : 0u;
-  const unsigned v0 = (unsigned)(st_row * K + st_chunk * 16);
-  const FfnStaging st{ra, rw, v0, v0, whi, K, st_lds};
-
+  uint8_t* lds = sm.lds;
+  const FfnStaging st = ffn_staging<GLU>(g, ti, nt);
+  const float scv = have ? cur.sc : ffn_scale<GLU, COH>(g, ti, nt);
+  __syncthreads();   // the previous tile is done with LDS
   // the epilogue's scales, read from LDS after the k loop's first barrier
-  if (tid < kFfnBM) {
-    const float* rsp = g.row_scale + min(row0 + tid, row_end - 1);
-    sm.sc_row[tid] = COH ? __hip_atomic_load(rsp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *rsp;
-  } else {
-    const int c = tid - kFfnBM;
-    const int wr = GLU ? (c < NCOLS ? n0 + c : Nw / 2 + n0 + (c - NCOLS)) : min(n0 + c, Nw - 1);
-    sm.sc_col[c] = g.w_scale[(int64_t)e * Nw + wr];
-  }
+  if (tid < kFfnBM) sm.sc_row[tid] = scv;
+  else sm.sc_col[tid - kFfnBM] = scv;
 
   // acc[j][i]: weight block j (32 rows), token block i (32 rows)
   v16i acc[2][4];
@@ -436,11 +499,11 @@ __device__ __forceinline__ void ffn_tile(const FfnGemm& g, int4 ti, int nt, cons
   // 32-row token blocks of this wavefront's half that hold valid rows
   const int nblk = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows_here - wt * 128 + 31) / 32)));
   switch (nblk) {
-    case 4: ffn_kloop<GLU, 4, COH>(lds, acc, st, wt, wn, fr); break;
-    case 3: ffn_kloop<GLU, 3, COH>(lds, acc, st, wt, wn, fr); break;
-    case 2: ffn_kloop<GLU, 2, COH>(lds, acc, st, wt, wn, fr); break;
-    case 1: ffn_kloop<GLU, 1, COH>(lds, acc, st, wt, wn, fr); break;
-    default: ffn_kloop<GLU, 0, COH>(lds, acc, st, wt, wn, fr); break;
+    case 4: ffn_kloop<GLU, 4, COH>(lds, acc, st, wt, wn, fr, cur, have); break;
+    case 3: ffn_kloop<GLU, 3, COH>(lds, acc, st, wt, wn, fr, cur, have); break;
+    case 2: ffn_kloop<GLU, 2, COH>(lds, acc, st, wt, wn, fr, cur, have); break;
+    case 1: ffn_kloop<GLU, 1, COH>(lds, acc, st, wt, wn, fr, cur, have); break;
+    default: ffn_kloop<GLU, 0, COH>(lds, acc, st, wt, wn, fr, cur, have); break;
   }
 
   // Epilogue.  Lane l holds, for each (j, i) and run q < 4, token
@@ -485,6 +548,15 @@ __device__ __forceinline__ void ffn_tile(const FfnGemm& g, int4 ti, int nt, cons
         }
     }
   }
+  // the accumulators are spent: load the next tile's stage 0 and scale now,
+  // ahead of this tile's output stores
+  const FfnNext nx = PF ? next() : FfnNext{false, ti, nt};
+  if (PF) {
+    const int4 pti = nx.pf ? nx.ti : ti;
+    const int pnt = nx.pf ? nx.nt : nt;
+    ffn_stage_load<COH>(ffn_staging<GLU>(g, pti, pnt), 0, nxt.sa, nxt.sw);
+    nxt.sc = ffn_scale<GLU, COH>(g, pti, pnt);
+  }
   __syncthreads();
   const int u = tid % OU;
   const int col = n0 + u * 8;
@@ -504,43 +576,96 @@ __device__ __forceinline__ void ffn_tile(const FfnGemm& g, int4 ti, int nt, cons
       if (u == 0 && row < row_end) atomicMax(amax_bits + row, __float_as_uint(m));
     }
   }
+  return nx;
 }
 
 // Tile t of a walk over T = MT x nn tiles -> (m-tile, n-tile): groups of GM
 // m-tiles x GN n-tiles, m fastest (the tiles run together share A and W
 // tiles in L2).
-__device__ __forceinline__ void ffn_decode_tile(int64_t t, int MT, int nn, int& mt, int& nt) {
+// All values are wavefront-uniform and below 2^31 (the host checks the
+// tile count), so the divisions run in 32 bits on scalar registers.
+__device__ __forceinline__ void ffn_decode_tile(int t, int MT, int nn, int& mt, int& nt) {
   constexpr int GM = 4, GN = 8;
-  const int64_t band = (int64_t)GM * nn;
-  const int64_t mg = t / band;
-  const int64_t r = t - mg * band;
-  const int m_in_group = (int)min((int64_t)GM, (int64_t)MT - mg * GM);
-  const int64_t per_ng = (int64_t)m_in_group * GN;
-  const int64_t ng = r / per_ng;
-  const int64_t r2 = r - ng * per_ng;
-  const int n_in_group = (int)min((int64_t)GN, (int64_t)nn - ng * GN);
-  mt = (int)(mg * GM + r2 % m_in_group);
-  nt = (int)(ng * GN + (r2 / m_in_group) % n_in_group);
+  t = __builtin_amdgcn_readfirstlane(t);
+  MT = __builtin_amdgcn_readfirstlane(MT);
+  nn = __builtin_amdgcn_readfirstlane(nn);
+  const int band = GM * nn;
+  const int mg = t / band;
+  const int r = t - mg * band;
+  const int m_in_group = min(GM, MT - mg * GM);
+  const int per_ng = m_in_group * GN;
+  const int ng = r / per_ng;
+  const int r2 = r - ng * per_ng;
+  const int n_in_group = min(GN, nn - ng * GN);
+  const int q = r2 / m_in_group;
+  mt = mg * GM + (r2 - q * m_in_group);
+  nt = ng * GN + q % n_in_group;
+}
+
+// The m-tile table, read by the persistent kernels once per tile.  With
+// TAB the kernel copies it into LDS at its start: a global read of a tile's
+// entry would wait behind the previous tile's output stores (loads and
+// stores retire in order), an LDS read does not.  The host takes TAB when
+// the table fits (kFfnTabCache entries); otherwise entries are read from
+// global memory.
+constexpr int kFfnTabCache = 1536;
+
+template <bool TAB>
+struct FfnTab {
+  const int4* g;   // the plan's table (entry m at g[1 + m])
+  int4* s;         // LDS copy (TAB)
+  __device__ __forceinline__ int4 at(int m) const { return TAB ? s[m] : g[1 + m]; }
+};
+
+template <bool TAB>
+__device__ __forceinline__ void ffn_cache_tab(const int4* __restrict__ tiles, int4* tab_s, int MT) {
+  if (!TAB) return;
+  const int n = min(MT, kFfnTabCache);   // MT <= kFfnTabCache whenever the host picks TAB
+  for (int i = threadIdx.x; i < n; i += kFfnThreads) tab_s[i] = tiles[1 + i];
+  __syncthreads();
 }
 
 // Persistent grouped GEMM over the plan's tiles (one workgroup per CU).
-template <bool GLU>
+template <bool GLU, bool TAB>
 __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(FfnGemm g, const int4* __restrict__ tiles) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFfnStage];
   __shared__ float sc_row[kFfnBM];
   __shared__ float sc_col[kFfnBW];
+  __shared__ int4 tab_s[TAB ? kFfnTabCache : 1];
   const FfnSmem sm{lds, sc_row, sc_col};
   constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;
   const int G = gridDim.x;
   const int nn = (g.Nout + NCOLS - 1) / NCOLS;
-  const int MT = tiles[0].x;
-  const int64_t T = (int64_t)MT * nn;
+  const int MT = __builtin_amdgcn_readfirstlane(tiles[0].x);
+  const int T = MT * nn;
   const int b = blockIdx.x;
   const int lin = (b % 8) * (G / 8) + b / 8;   // XCD-contiguous walk (G is a multiple of 8)
-  for (int64_t t = lin; t < T; t += G) {
-    int mt, nt;
-    ffn_decode_tile(t, MT, nn, mt, nt);
-    ffn_tile<GLU>(g, tiles[1 + mt], nt, sm, nullptr);
+  ffn_cache_tab<TAB>(tiles, tab_s, MT);
+  const FfnTab<TAB> tab{tiles, tab_s};
+  int t = lin;
+  if (t >= T) return;
+  int mt, nt;
+  ffn_decode_tile(t, MT, nn, mt, nt);
+  int4 ti = tab.at(mt);
+  FfnStage0 s0;
+  ffn_stage_load<false>(ffn_staging<GLU>(g, ti, nt), 0, s0.sa, s0.sw);
+  s0.sc = ffn_scale<GLU, false>(g, ti, nt);
+  for (;;) {
+    // the next tile of this workgroup's walk; its stage 0 is loaded before
+    // this tile's output stores
+    const int tn = t + G;
+    const bool has_next = tn < T;
+    int mtn = mt, ntn = nt;
+    if (has_next) ffn_decode_tile(tn, MT, nn, mtn, ntn);
+    const int4 te = tab.at(mtn);
+    const int4 tin = int4{__builtin_amdgcn_readfirstlane(te.x), __builtin_amdgcn_readfirstlane(te.y),
+                          __builtin_amdgcn_readfirstlane(te.z), 0};
+    ffn_tile<GLU, false, true>(g, ti, nt, sm, nullptr, s0, true, s0, [&]() { return FfnNext{has_next, tin, ntn}; });
+    if (!has_next) break;
+    t = tn;
+    mt = mtn;
+    nt = ntn;
+    ti = tin;
   }
 }
 
@@ -609,29 +734,35 @@ __device__ void ffn_quant_mtile(const uint16_t* __restrict__ gsrc, int ncols, in
 // one thread per workgroup); the quantiser reads g after one acquire (an L2
 // invalidate) per m-tile, and GMM2 reads q2 and s2 with agent-coherent loads
 // instead of invalidating its XCD's L2 once per tile.
+template <bool TAB>
 __global__ __launch_bounds__(kFfnThreads) void k_ffn_fused(FfnGemm g1, FfnGemm g2, const int4* __restrict__ tiles,
                                                             FfnSync sync, int spin_limit) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFfnStage];
   __shared__ float sc_row[kFfnBM];
   __shared__ float sc_col[kFfnBW];
+  __shared__ int4 tab_s[TAB ? kFfnTabCache : 1];
   __shared__ int bcast[2];
   const FfnSmem sm{lds, sc_row, sc_col};
   const int tid = threadIdx.x;
-  const int MT = tiles[0].x;
+  const int MT = __builtin_amdgcn_readfirstlane(tiles[0].x);
+  ffn_cache_tab<TAB>(tiles, tab_s, MT);
+  const FfnTab<TAB> tab{tiles, tab_s};
   const int nn1 = (g1.Nout + kFfnBW / 2 - 1) / (kFfnBW / 2);
   const int nn2 = (g2.Nout + kFfnBW - 1) / kFfnBW;
-  const int64_t T1 = (int64_t)MT * nn1, T2 = (int64_t)MT * nn2;
+  const int T1 = MT * nn1, T2 = MT * nn2, TT = T1 + T2;
+  const auto no_next = []() { return FfnNext{false, int4{0, 0, 0, 0}, 0}; };
   for (;;) {
     __syncthreads();   // bcast is free
     if (tid == 0) bcast[0] = atomicAdd(sync.next, 1);
     __syncthreads();
-    const int64_t t = __builtin_amdgcn_readfirstlane(bcast[0]);
-    if (t >= T1 + T2) break;
+    const int t = __builtin_amdgcn_readfirstlane(bcast[0]);
+    if (t >= TT) break;
+    FfnStage0 s0;
     if (t < T1) {
       int mt, nt;
       ffn_decode_tile(t, MT, nn1, mt, nt);
-      const int4 ti = tiles[1 + mt];
-      ffn_tile<true>(g1, ti, nt, sm, sync.amax_bits);
+      const int4 ti = tab.at(mt);
+      ffn_tile<true, false, false>(g1, ti, nt, sm, sync.amax_bits, s0, false, s0, no_next);
       // Publish: the barrier orders every wavefront's g stores (workgroup
       // scope) before thread 0's agent-scope release (one L2 write-back per
       // tile), which precedes its count.
@@ -666,7 +797,7 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_fused(FfnGemm g1, FfnGemm g
       }
       __syncthreads();
       // q2 and s2 are read with agent-coherent loads (no L2 invalidate)
-      ffn_tile<false, true>(g2, tiles[1 + mt], nt, sm, nullptr);
+      ffn_tile<false, true, false>(g2, tab.at(mt), nt, sm, nullptr, s0, false, s0, no_next);
     }
   }
 }
@@ -708,15 +839,21 @@ mdc_status check_ffn(const mdc_shape* sh, int inter_n) {
   if ((sh->hidden % kFfnOutAlign) != 0) return MDC_ERR_INVALID;
   // one expert's weight matrix (N x H or H x N/2 bytes) is addressed with 32-bit offsets
   if ((int64_t)inter_n * sh->hidden > INT32_MAX) return MDC_ERR_INVALID;
+  // tiles of both GEMMs (and the work-queue tickets) are counted in 32 bits
+  const int64_t L = sh->num_experts / sh->world;
+  const int64_t max_mtiles = 2 + sh->capacity / kFfnBM + L;
+  const int64_t per_mtile = inter_n / kFfnBW + (sh->hidden + kFfnBW - 1) / kFfnBW;
+  if (max_mtiles * per_mtile + 65536 > INT32_MAX) return MDC_ERR_INVALID;
   return MDC_OK;
 }
 
-// GMM1 -> quantise g -> GMM2 runs as the one persistent k_ffn_fused launch
-// unless MDC_FFN_PIPELINE=0 is set in the environment (then as three
-// stream-ordered kernels; the results are identical).
+// GMM1 -> quantise g -> GMM2 runs as three stream-ordered kernels, or as
+// the one persistent k_ffn_fused launch when MDC_FFN_PIPELINE=1 is set in the
+// environment (the results are identical; the stream-ordered GEMMs load
+// each next tile ahead and measure faster).
 bool ffn_pipeline_enabled() {
   const char* v = getenv("MDC_FFN_PIPELINE");   // read per call: cheap next to a GEMM launch
-  return v == nullptr || strcmp(v, "0") != 0;
+  return v != nullptr && strcmp(v, "1") == 0;
 }
 // polls of a GMM2 tile's wait before it gives up and flags an error
 constexpr int kFfnSpinLimit = 1 << 24;
@@ -753,14 +890,26 @@ mdc_status ffn_impl(const FfnPlan& f, const void* expand_x, const int8_t* expand
   const int max_mtiles = (int)(2 + f.A / kFfnBM + f.L);
   hipLaunchKernelGGL(k_ffn_plan, dim3(1), dim3(kPlanThreads), 0, s, expert_token_nums, f.L, f.A, tiles,
                      fused ? sync_words : nullptr, max_mtiles, amax);
+  const bool tab = max_mtiles <= kFfnTabCache;   // the m-tile table fits in LDS
   if (fused) {
     const FfnSync sync{sync_words, sync_words + 2, sync_words + 2 + max_mtiles, amax, sync_words + 1};
-    hipLaunchKernelGGL(k_ffn_fused, dim3(g1), dim3(kFfnThreads), 0, s, gemm1, gemm2, tiles, sync, kFfnSpinLimit);
+    if (tab)
+      hipLaunchKernelGGL(k_ffn_fused<true>, dim3(g1), dim3(kFfnThreads), 0, s, gemm1, gemm2, tiles, sync,
+                         kFfnSpinLimit);
+    else
+      hipLaunchKernelGGL(k_ffn_fused<false>, dim3(g1), dim3(kFfnThreads), 0, s, gemm1, gemm2, tiles, sync,
+                         kFfnSpinLimit);
   } else {
-    hipLaunchKernelGGL(k_ffn_gemm<true>, dim3(g1), dim3(kFfnThreads), 0, s, gemm1, tiles);
+    if (tab)
+      hipLaunchKernelGGL((k_ffn_gemm<true, true>), dim3(g1), dim3(kFfnThreads), 0, s, gemm1, tiles);
+    else
+      hipLaunchKernelGGL((k_ffn_gemm<true, false>), dim3(g1), dim3(kFfnThreads), 0, s, gemm1, tiles);
     hipLaunchKernelGGL(k_ffn_quant_rows, dim3(quant_wgs), dim3(256), 0, s, reinterpret_cast<const v4u*>(g), q2, s2,
                        expert_token_nums, f.L, f.A, f.N / 2 / 8);
-    hipLaunchKernelGGL(k_ffn_gemm<false>, dim3(g2), dim3(kFfnThreads), 0, s, gemm2, tiles);
+    if (tab)
+      hipLaunchKernelGGL((k_ffn_gemm<false, true>), dim3(g2), dim3(kFfnThreads), 0, s, gemm2, tiles);
+    else
+      hipLaunchKernelGGL((k_ffn_gemm<false, false>), dim3(g2), dim3(kFfnThreads), 0, s, gemm2, tiles);
   }
   return launched();
 }

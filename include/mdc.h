@@ -297,11 +297,11 @@ mdc_status mdc_combine(const mdc_shape* shape,
  *   with 32-bit offsets).  The workspace holds q1, s1, g, q2, s2, the
  *   m-tile table of the grouped GEMMs and the pipeline's ready counters.
  *
- * GMM1, the quantisation of g and GMM2 run as one persistent kernel whose
- * GMM2 tiles start as soon as their rows of g are quantised ([PTO] fused
- * pipeline: ready flags between the stages); setting the environment
- * variable MDC_FFN_PIPELINE=0 runs them as three stream-ordered kernels
- * instead.  Both give bit-identical y.
+ * GMM1, the quantisation of g and GMM2 run as three stream-ordered
+ * kernels.  Setting the environment variable MDC_FFN_PIPELINE=1 runs them
+ * instead as one persistent kernel whose GMM2 tiles start as soon as their
+ * rows of g are quantised ([PTO] fused pipeline: ready flags between the
+ * stages).  Both give bit-identical y.
  * ------------------------------------------------------------------------ */
 mdc_status mdc_ffn_workspace_size(const mdc_shape* shape, int32_t inter_n, size_t* bytes);
 
