@@ -294,7 +294,8 @@ mdc_status mdc_combine(const mdc_shape* shape,
  *   w2_scale [L][H] fp32.   Output: y [A][H] bf16 (rows past the total are
  *   untouched).  inter_n = N must be a positive multiple of 256, H a
  *   multiple of 128 and N * H < 2^31 (one expert's weight matrix is addressed
- *   with 32-bit offsets).  The workspace holds q1, s1, g, q2, s2, the
+ *   with 32-bit offsets); the GEMM tiles, (A / 256 + L + 2) * (N / 256 +
+ *   ceil(H / 256)), are counted in 32 bits and must stay below 2^31.  The workspace holds q1, s1, g, q2, s2, the
  *   m-tile table of the grouped GEMMs and the pipeline's ready counters.
  *
  * GMM1, the quantisation of g and GMM2 run as three stream-ordered

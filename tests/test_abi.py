@@ -119,6 +119,13 @@ def test_ffn_shape_checks():
     with pytest.raises(mdc.MdcError) as ei:
         mdc.mdc_ffn(ok, 4096, fake, None, fake, fake, fake, fake, fake, fake)
     assert ei.value.status == mdc.MDC_ERR_NULLPTR
+    # the GEMM tile count (A / 256 + L + 2) * (N / 256 + ceil(H / 256)) must stay below 2^31:
+    # at the largest capacity, N = 2^23 with H = 128 passes the N * H bound but not this one
+    big_a = mdc.Shape(world=8, rank=0, bs=16, hidden=128, topk=8, num_experts=128, capacity=2**31 - 1)
+    assert mdc.mdc_ffn_workspace_size(big_a, 256) > 0
+    with pytest.raises(mdc.MdcError) as ei:
+        mdc.mdc_ffn_workspace_size(big_a, 2**23)
+    assert ei.value.status == mdc.MDC_ERR_INVALID
 
 
 def test_combine_world_limit_and_nulls():
