@@ -203,14 +203,7 @@ __global__ __launch_bounds__(256) void k_ffn_quant_rows(
   }
 }
 
-// The k loop of one tile (see ffn_tile).  Stage ks + 1 travels global ->
-// registers during stage ks - 1 and registers -> LDS during stage ks, into the
-// buffer nobody reads in stage ks; one barrier ends each stage.  Fragments of
-// k substep q + 1 are read while the MFMAs of substep q run, and the last
-// substep's MFMAs run after the stage barrier, beside the next stage's first
-// fragment reads.  Scheduling groups (sched_group_barrier masks: 0x8 MFMA,
-// 0x100 LDS read, 0x200 LDS write, 0x20 global read) interleave the memory
-// instructions with the MFMAs.
+// Buffer descriptors and offsets with which one thread stages one tile.
 struct FfnStaging {
   __amdgpu_buffer_rsrc_t ra, rw;   // token rows, weight rows (range-checked)
   unsigned va, vw;                 // lane offsets of this thread's i = 0 rows
@@ -244,6 +237,15 @@ __device__ __forceinline__ void ffn_stage_load(const FfnStaging& st, int k0, v4i
   }
 }
 
+// The k loop of one tile (see ffn_tile).  Stage ks + 1 travels global ->
+// registers during stage ks - 1 and registers -> LDS during stage ks, into the
+// buffer nobody reads in stage ks; one barrier ends each stage.  Fragments of
+// k substep q + 1 are read while the MFMAs of substep q run, and the last
+// substep's MFMAs run after the stage barrier, beside the next stage's first
+// fragment reads.  Scheduling groups (sched_group_barrier masks: 0x8 MFMA,
+// 0x100 LDS read, 0x200 LDS write, 0x20 global read) interleave the memory
+// instructions with the MFMAs.
+//
 // NB = number of the wavefront's 32-row token blocks that hold valid rows:
 // blocks past them stay zero, and their fragment reads and MFMAs are not
 // issued (an expert's short last m-tile is cheap).  NB = 0 still stages and
