@@ -684,13 +684,24 @@ struct FfnSync {
 // Quantises the g rows [r0, r1) of one m-tile (the last GMM1 tile of the
 // m-tile does it): codes clamp(rint(g * (127 / amax)), -127, 127) and scale
 // amax / 127, with amax the row's max |g| gathered by the GMM1 epilogues,
-// decided in fp32 as k_ffn_quant_rows decides them.
+// decided in fp32 as k_ffn_quant_rows decides them.  inv_s: kFfnBM floats of
+// LDS.  One workgroup moves the whole m-tile, so it keeps 16 vectors per
+// thread in flight.
 __device__ void ffn_quant_mtile(const uint16_t* __restrict__ gsrc, int ncols, int8_t* __restrict__ q,
-                                float* __restrict__ scale, const uint32_t* __restrict__ amax_bits, int r0, int r1) {
+                                float* __restrict__ scale, const uint32_t* __restrict__ amax_bits, int r0, int r1,
+                                float* inv_s) {
   const int tid = threadIdx.x;
+  const int rows = r1 - r0;   // at most kFfnBM
+  // the m-tile's row scales first, with 127 / amax kept in LDS (inv_s)
+  if (tid < rows) {
+    const float amax = __uint_as_float(amax_bits[r0 + tid]);
+    inv_s[tid] = amax > 0.f ? 127.0f / amax : 0.f;
+    scale[r0 + tid] = amax / 127.0f;
+  }
+  __syncthreads();
   const int nvec = ncols / 8;
-  const int total = (r1 - r0) * nvec;
-  constexpr int kBatch = 8;   // independent vectors in flight per thread
+  const int total = rows * nvec;
+  constexpr int kBatch = 16;   // independent vectors in flight per thread
   for (int base = 0; base < total; base += kFfnThreads * kBatch) {
     v4u v[kBatch];
 #pragma unroll
@@ -704,9 +715,8 @@ __device__ void ffn_quant_mtile(const uint16_t* __restrict__ gsrc, int ncols, in
     for (int j = 0; j < kBatch; ++j) {
       const int idx = base + j * kFfnThreads + tid;
       if (idx >= total) continue;
-      const int row = r0 + idx / nvec;
-      const float amax = __uint_as_float(amax_bits[row]);
-      const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+      const int rr = idx / nvec;
+      const float inv = inv_s[rr];
       uint64_t packed = 0;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -715,10 +725,9 @@ __device__ void ffn_quant_mtile(const uint16_t* __restrict__ gsrc, int ncols, in
         packed |= (uint64_t)(uint8_t)(int8_t)(int)a << (16 * w);
         packed |= (uint64_t)(uint8_t)(int8_t)(int)b << (16 * w + 8);
       }
-      *reinterpret_cast<uint64_t*>(q + (int64_t)row * ncols + (idx % nvec) * 8) = packed;
+      *reinterpret_cast<uint64_t*>(q + (int64_t)(r0 + rr) * ncols + (idx % nvec) * 8) = packed;
     }
   }
-  for (int row = r0 + tid; row < r1; row += kFfnThreads) scale[row] = __uint_as_float(amax_bits[row]) / 127.0f;
 }
 
 // NEXT-3 stage of the [PTO] fused pipeline: GMM1 + SwiGLU, the dynamic
@@ -778,7 +787,7 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_fused(FfnGemm g1, FfnGemm g
       __syncthreads();
       if (bcast[1]) {
         ffn_quant_mtile(g1.out, g1.Nout, const_cast<int8_t*>(g2.a_src), const_cast<float*>(g2.row_scale),
-                        sync.amax_bits, ti.y, min(ti.z, ti.y + kFfnBM));
+                        sync.amax_bits, ti.y, min(ti.z, ti.y + kFfnBM), sm.sc_row);
         __syncthreads();
         // release q2 and s2 with the flag
         if (tid == 0) __hip_atomic_store(sync.ready + mt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
