@@ -150,8 +150,17 @@ __global__ __launch_bounds__(256) void k_ffn_quant_rows(
     const int64_t* __restrict__ expert_nums, int L, int64_t A, int nvec) {
   const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * 4;
+  // rows in use: sum of the expert counts, one load per lane and a
+  // wavefront sum (a loop of dependent loads would open every wavefront
+  // with L memory round trips)
   int64_t total = 0;
-  for (int i = 0; i < L; ++i) total += expert_nums[i];
+  for (int i = lane; i < L; i += 64) total += expert_nums[i];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const unsigned lo = __shfl_xor((unsigned)(uint64_t)total, o, 64);
+    const unsigned hi = __shfl_xor((unsigned)((uint64_t)total >> 32), o, 64);
+    total += (int64_t)(((uint64_t)hi << 32) | lo);
+  }
   const int64_t rows = total < A ? total : A;
   for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += nw) {
     const v4u* xr = x + row * nvec;
