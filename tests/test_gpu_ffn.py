@@ -111,6 +111,25 @@ def test_ffn_full_size_then_combine():
     assert err2 <= REL_L2
 
 
+@pytest.mark.parametrize("pipeline", ["0", "1"])
+def test_ffn_tile_table_in_global_memory(pipeline):
+    """A capacity of 400000 rows bounds the m-tile table above the 1536 entries
+    the persistent GEMMs cache in LDS: they read it from global memory."""
+    w = gen.workload("tiny", world=2, bs=64, hidden=128, experts=4, topk=2, index=90)
+    old = os.environ.get("MDC_FFN_PIPELINE")
+    try:
+        os.environ["MDC_FFN_PIPELINE"] = pipeline
+        got, want, *_ = _run_ffn(w, 256, capacity=400_000)
+    finally:
+        if old is None:
+            os.environ.pop("MDC_FFN_PIPELINE", None)
+        else:
+            os.environ["MDC_FFN_PIPELINE"] = old
+    err = rel_l2(got, want)
+    say(f"  pipeline={pipeline} rel L2 {err:.3e} over {got.shape[0]} rows")
+    assert err <= REL_L2
+
+
 @pytest.mark.parametrize("variant", [
     dict(world=4, bs=96, hidden=128, experts=16, topk=3, inter=768),
     dict(world=1, bs=128, hidden=128, experts=2048, topk=16, inter=256),
