@@ -468,9 +468,10 @@ constexpr int kSmallCounters = 1024;                // L * W counters
 constexpr int64_t kSmallRereads = int64_t(1) << 20; // tokens x routes: ids every workgroup rereads
 constexpr int kSmallThreads = 256;
 constexpr int kSmallRowVec = 4;                     // row vectors per thread kept for the quantiser
-constexpr int kSmallKeyBatch = 8;                   // route ids per thread in flight at once
+constexpr int kSmallKeyBatch = 8;                   // route ids per thread per batch of kSmallThreads * 8
+static_assert(kSmallRoutes == 4 * kSmallKeyBatch * kSmallThreads, "the small path loads its ids in 1 or 4 batches");
 
-template <bool QUANT>
+template <bool QUANT, int NB>
 __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
     const v4u* __restrict__ x, const int32_t* __restrict__ ids, const uint8_t* __restrict__ mask, int mask_per_route,
     v4u* __restrict__ expand_x, int8_t* __restrict__ expand_q, float* __restrict__ dyn_scale,
@@ -493,46 +494,40 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
   // ids are read kSmallKeyBatch per thread at a time, every load issued
   // before the first is used; the first batch goes out before the token's
   // row, whose loads then overlap the ranking below.
-  int ev[kSmallKeyBatch];
-  uint8_t mv[kSmallKeyBatch];
-  // (indices past the end are clamped, not skipped, so that the loads are
-  // unconditional and the waits before their uses count them exactly)
-  auto load_keys = [&](int f0) {
+  // Route ids and mask flags of all NB batches are loaded first, then the
+  // token's row, then the keys are stored: straight-line code, so the waits
+  // for the ids leave the row loads in flight.  Indices past the end are
+  // clamped, not skipped, and without a mask the mask loads read the first
+  // route id's bytes and are ignored, so that the loads are unconditional.
+  constexpr int kB = kSmallKeyBatch * NB;
+  int ev[kB];
+  uint8_t mv[kB];
+  const uint8_t* mptr = mask != nullptr ? mask : reinterpret_cast<const uint8_t*>(ids);
+  const int mmul = mask == nullptr ? 0 : 1;
+  const int mdiv = mask_per_route ? 1 : K;
 #pragma unroll
-    for (int j = 0; j < kSmallKeyBatch; ++j) {
-      const int f = min(f0 + tid + j * kSmallThreads, n - 1);
-      ev[j] = ids[f];
-    }
-    if (mask != nullptr) {
+  for (int j = 0; j < kB; ++j) ev[j] = ids[min(tid + j * kSmallThreads, n - 1)];
 #pragma unroll
-      for (int j = 0; j < kSmallKeyBatch; ++j) {
-        const int f = min(f0 + tid + j * kSmallThreads, n - 1);
-        mv[j] = mask[mask_per_route ? f : f / K];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kSmallKeyBatch; ++j) mv[j] = 1;
-    }
-  };
-  load_keys(0);
+  for (int j = 0; j < kB; ++j) mv[j] = mptr[(min(tid + j * kSmallThreads, n - 1) / mdiv) * mmul];
 
   // (clamped as well: vectors past the row's end are never stored, and the
-  // quantiser skips them)
+  // quantiser skips them).  The scheduling barriers keep every id and mask
+  // load ahead of the row loads.
   const v4u* xr = x + (int64_t)tok * nvec;
   v4u cache[kSmallRowVec];
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int u = 0; u < kSmallRowVec; ++u) cache[u] = xr[min(tid + u * kSmallThreads, nvec - 1)];
+  __builtin_amdgcn_sched_barrier(0);
 
-  for (int f0 = 0;;) {
+  // (stored for every f < kB * kSmallThreads <= kSmallRoutes, -1 past n: no
+  // branch for the compiler to sink the loads into)
 #pragma unroll
-    for (int j = 0; j < kSmallKeyBatch; ++j) {
-      const int f = f0 + tid + j * kSmallThreads;
-      const int q = ev[j] - d * L;
-      if (f < n) key_s[f] = (mv[j] != 0 && ev[j] >= 0 && ev[j] < E && q >= 0 && q < L) ? q : -1;
-    }
-    f0 += kSmallKeyBatch * kSmallThreads;
-    if (f0 >= n) break;
-    load_keys(f0);
+  for (int j = 0; j < kB; ++j) {
+    const int f = tid + j * kSmallThreads;
+    const int q = ev[j] - d * L;
+    const bool active = mask == nullptr || mv[j] != 0;
+    key_s[f] = (f < n && active && ev[j] >= 0 && ev[j] < E && q >= 0 && q < L) ? q : -1;
   }
   for (int i = tid; i < nc; i += kSmallThreads) cnt_s[i] = 0;
   if (tid < MDC_MAX_TOPK) rank_s[tid] = 0;
@@ -711,14 +706,20 @@ __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
   const int kk = lane < K ? lane : 0;
   const int64_t rt = (int64_t)t * K + kk;
 
-  const int e = ids[rt];
-  const int row = row_idx[rt];
-  const float sc = scales[rt];
-  const bool act = (mask == nullptr) || (mask[mask_per_route ? rt : (int64_t)t] != 0);
+  // First load level, all in flight together: the per-lane pointer tables
+  // (from the kernel arguments), then the route's id, row index, scale and
+  // mask flag.  Without a mask the flag load reads the id's first byte and
+  // is ignored, so that the load carries no branch.
   const int tl = lane < W ? lane : 0;
   const uint64_t yb = (uint64_t)tabs.y[tl];
   const uint64_t ab = (uint64_t)tabs.assist[tl];
   const uint64_t cb = (uint64_t)tabs.counts[tl];
+  const int e = ids[rt];
+  const int row = row_idx[rt];
+  const float sc = scales[rt];
+  const uint8_t mflag = mask != nullptr ? mask[mask_per_route ? rt : (int64_t)t]
+                                        : *reinterpret_cast<const uint8_t*>(ids + rt);
+  const bool act = (mask == nullptr) || (mflag != 0);
 
   const bool valid = (lane < K) && act && e >= 0 && e < E && A > 0;
   const int j = valid ? e / L : 0;
@@ -960,7 +961,9 @@ mdc_status small_impl(const DispatchPlan& p, const void* x, const int32_t* ids, 
                       int8_t* expand_q, float* dyn_scale, int32_t* assist, int32_t* ep_recv, int64_t* expert_nums,
                       int32_t* row_idx, hipStream_t st) {
   (void)hipGetLastError();
-  hipLaunchKernelGGL(k_dispatch_small<QUANT>, dim3((unsigned)(p.W * p.BS)), dim3(kSmallThreads), 0, st,
+  const bool one_batch = (int64_t)p.W * p.BS * p.K <= kSmallKeyBatch * kSmallThreads;
+  auto kern = one_batch ? k_dispatch_small<QUANT, 1> : k_dispatch_small<QUANT, 4>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(p.W * p.BS)), dim3(kSmallThreads), 0, st,
                      static_cast<const v4u*>(x), ids, mask, p.mask_per_route, static_cast<v4u*>(expand_x), expand_q,
                      dyn_scale, assist, ep_recv, expert_nums, row_idx, p.W, p.d, p.BS, p.K, p.E, p.L, p.A, p.nvec);
   return launched();
