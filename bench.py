@@ -308,8 +308,14 @@ def main():
     gb_gather = by["gather"] / (mean(t_gather) * 1e-6) / 1e9
     gb_comb = by["combine"] / (mean(t_comb) * 1e-6) / 1e9
     gb_step = step_bytes / (ms_per_step * 1e-3) / 1e9
+    if one_shot:
+        # one launch (k_dispatch_small) does the layout and the gather
+        d_kernel, d_bytes = "k_dispatch_small", by["layout"] + by["gather"]
+        gb_gather = d_bytes / (mean(t_gather) * 1e-6) / 1e9
+    else:
+        d_kernel, d_bytes = ("k_dispatch_gather_q" if w.inter else "k_dispatch_gather"), by["gather"]
     if mean(t_gather) >= mean(t_comb):
-        dom = ("k_dispatch_gather", gb_gather, by["gather"], mean(t_gather))
+        dom = (d_kernel, gb_gather, d_bytes, mean(t_gather))
     else:
         dom = ("k_combine", gb_comb, by["combine"], mean(t_comb))
     ffn_info = None
@@ -349,7 +355,9 @@ def main():
         "hbm_frac_of_peak": round(gb_step / HBM_PEAK_GBPS, 4),
         "step_bytes": step_bytes,
         "roofline": roofline,
-        "kernels_us": {"dispatch_layout": round(mean(t_layout), 3), "dispatch_gather": round(mean(t_gather), 3),
+        # (with the one-shot dispatch no kernel runs between the first two events)
+        "kernels_us": {"dispatch_layout": None if one_shot else round(mean(t_layout), 3),
+                       "dispatch_gather": round(mean(t_gather), 3),
                        "combine": round(mean(t_comb), 3), "step_events": round(mean(t_step_ev), 3),
                        "gather_gbps": round(gb_gather, 1), "combine_gbps": round(gb_comb, 1),
                        "gather_median": round(statistics.median(t_gather), 3),
