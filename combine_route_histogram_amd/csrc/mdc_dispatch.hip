@@ -460,15 +460,15 @@ __global__ __launch_bounds__(64) void k_dispatch_gather_q(
 // earlier routes of the same source with the same expert, [TL] send loop),
 // places them and copies (QUANT: quantises) the token's row.  This replaces
 // the rank kernel and the gather kernel; the outputs are identical.  One
-// 256-thread workgroup per source token; workgroup 0 also writes
+// 1024-thread workgroup per source token; workgroup 0 also writes
 // epRecvCounts and expertTokenNums.
 // ---------------------------------------------------------------------------
 constexpr int kSmallRoutes = 8192;                  // route keys held in LDS
 constexpr int kSmallCounters = 1024;                // L * W counters
 constexpr int64_t kSmallRereads = int64_t(1) << 20; // tokens x routes: ids every workgroup rereads
-constexpr int kSmallThreads = 256;
-constexpr int kSmallRowVec = 4;                     // row vectors per thread kept for the quantiser
-constexpr int kSmallKeyBatch = 8;                   // route ids per thread per batch of kSmallThreads * 8
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallRowVec = 1;                     // row vectors per thread kept for the quantiser
+constexpr int kSmallKeyBatch = 2;                   // route ids per thread per batch of kSmallThreads * 2
 static_assert(kSmallRoutes == 4 * kSmallKeyBatch * kSmallThreads, "the small path loads its ids in 1 or 4 batches");
 
 template <bool QUANT, int NB>
@@ -645,7 +645,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
     for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
     if (lane == 0) amax_s[wave] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(amax_s[0], amax_s[1]), fmaxf(amax_s[2], amax_s[3]));
+#pragma unroll
+    for (int w = 0; w < kSmallThreads / 64; ++w) amax = fmaxf(amax, amax_s[w]);
     const float inv = amax > 0.f ? 127.0f / amax : 0.f;
     const float scale = amax / 127.0f;
     if (tid < K && row_s[tid] >= 0) dyn_scale[row_s[tid]] = scale;
