@@ -142,12 +142,17 @@ __device__ __forceinline__ uint32_t ffn_pack_bf16(float lo, float hi) {
 // Per-row int8 quantisation of bf16 rows of `width` elements, decided in fp32
 // exactly as: amax = max|v|, inv = 127 / amax, q = clamp(rint(v * inv), -127,
 // 127), scale = amax / 127 (a zero row gives q = 0, scale = 0).  One
-// wavefront per row, rows [0, min(sum(expert_nums), A)) visited grid-stride;
-// rows of up to 64 * kQuantVec vectors stay in registers between the passes.
-constexpr int kQuantVec = 16;
+// wavefront per row, rows [0, min(sum(expert_nums), A)) visited grid-stride.
+// Rows of up to 64 * QV vectors stay in registers between the passes; with
+// QV <= 8 each wavefront loads its next row before it quantises the current
+// one (unconditional loads: vectors past the row's end reload its last
+// vector and are neither counted nor stored).  Longer rows are streamed
+// twice.
+template <int QV>
 __global__ __launch_bounds__(256) void k_ffn_quant_rows(
     const v4u* __restrict__ x, int8_t* __restrict__ q, float* __restrict__ scale,
     const int64_t* __restrict__ expert_nums, int L, int64_t A, int nvec) {
+  constexpr bool kPrefetch = QV <= 8;
   const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * 4;
   // rows in use: sum of the expert counts, one load per lane and a
@@ -162,22 +167,50 @@ __global__ __launch_bounds__(256) void k_ffn_quant_rows(
     total += (int64_t)(((uint64_t)hi << 32) | lo);
   }
   const int64_t rows = total < A ? total : A;
-  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += nw) {
+  const bool cached = nvec <= 64 * QV;
+  auto load_row = [&](int64_t row, auto& c) {   // c holds at least QV vectors
+    const v4u* xr = x + row * nvec;
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int u = 0; u < QV; ++u) c[u] = xr[min(lane + 64 * u, nvec - 1)];
+    } else {
+      // (guarded loads keep one base address with immediate offsets)
+#pragma unroll
+      for (int u = 0; u < QV; ++u) {
+        const int i = lane + 64 * u;
+        c[u] = i < nvec ? xr[i] : v4u{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto quant8 = [](const v4u& v, float inv) {
+    uint64_t packed = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = fminf(fmaxf(rintf(bf16_lo(v[w]) * inv), -127.f), 127.f);
+      const float b = fminf(fmaxf(rintf(bf16_hi(v[w]) * inv), -127.f), 127.f);
+      packed |= (uint64_t)(uint8_t)(int8_t)(int)a << (16 * w);
+      packed |= (uint64_t)(uint8_t)(int8_t)(int)b << (16 * w + 8);
+    }
+    return packed;
+  };
+  int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  v4u cache[QV], next[kPrefetch ? QV : 1];
+  if (cached) load_row(row, cache);
+  for (; row < rows; row += nw) {
     const v4u* xr = x + row * nvec;
     uint64_t* qr = reinterpret_cast<uint64_t*>(q + row * (int64_t)nvec * 8);
-    v4u cache[kQuantVec];
+    if constexpr (kPrefetch) {
+      if (cached) load_row(min(row + nw, rows - 1), next);
+    }
     float amax = 0.f;
-    if (nvec <= 64 * kQuantVec) {
+    if (cached) {
 #pragma unroll
-      for (int u = 0; u < kQuantVec; ++u) {
-        const int i = lane + 64 * u;
-        cache[u] = i < nvec ? xr[i] : v4u{0u, 0u, 0u, 0u};
-      }
+      for (int u = 0; u < QV; ++u)
+        if (lane + 64 * u < nvec)
 #pragma unroll
-      for (int u = 0; u < kQuantVec; ++u)
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(cache[u][w])), fabsf(bf16_hi(cache[u][w]))));
+          for (int w = 0; w < 4; ++w)
+            amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(cache[u][w])), fabsf(bf16_hi(cache[u][w]))));
     } else {
       for (int i = lane; i < nvec; i += 64) {
         const v4u v = xr[i];
@@ -188,28 +221,34 @@ __global__ __launch_bounds__(256) void k_ffn_quant_rows(
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
     const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-    auto quant8 = [&](const v4u& v) {
-      uint64_t packed = 0;
+    if (cached) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float a = fminf(fmaxf(rintf(bf16_lo(v[w]) * inv), -127.f), 127.f);
-        const float b = fminf(fmaxf(rintf(bf16_hi(v[w]) * inv), -127.f), 127.f);
-        packed |= (uint64_t)(uint8_t)(int8_t)(int)a << (16 * w);
-        packed |= (uint64_t)(uint8_t)(int8_t)(int)b << (16 * w + 8);
-      }
-      return packed;
-    };
-    if (nvec <= 64 * kQuantVec) {
-#pragma unroll
-      for (int u = 0; u < kQuantVec; ++u) {
+      for (int u = 0; u < QV; ++u) {
         const int i = lane + 64 * u;
-        if (i < nvec) qr[i] = quant8(cache[u]);
+        if (i < nvec) qr[i] = quant8(cache[u], inv);
       }
     } else {
-      for (int i = lane; i < nvec; i += 64) qr[i] = quant8(xr[i]);
+      for (int i = lane; i < nvec; i += 64) qr[i] = quant8(xr[i], inv);
     }
     if (lane == 0) scale[row] = amax / 127.0f;
+    if (cached) {
+      if constexpr (kPrefetch) {
+#pragma unroll
+        for (int u = 0; u < QV; ++u) cache[u] = next[u];
+      } else if (row + nw < rows) {
+        load_row(row + nw, cache);
+      }
+    }
   }
+}
+
+// Launches the quantiser instance for rows of nvec vectors.
+void launch_quant_rows(const v4u* x, int8_t* q, float* scale, const int64_t* expert_nums, int L, int64_t A, int nvec,
+                       unsigned wgs, hipStream_t s) {
+  if (nvec <= 64 * 4)
+    hipLaunchKernelGGL(k_ffn_quant_rows<4>, dim3(wgs), dim3(256), 0, s, x, q, scale, expert_nums, L, A, nvec);
+  else
+    hipLaunchKernelGGL(k_ffn_quant_rows<16>, dim3(wgs), dim3(256), 0, s, x, q, scale, expert_nums, L, A, nvec);
 }
 
 // Buffer descriptors and offsets with which one thread stages one tile.
@@ -895,8 +934,7 @@ mdc_status ffn_impl(const FfnPlan& f, const void* expand_x, const int8_t* expand
   const unsigned g2 = g1;
   (void)hipGetLastError();
   if (expand_q == nullptr) {
-    hipLaunchKernelGGL(k_ffn_quant_rows, dim3(quant_wgs), dim3(256), 0, s, static_cast<const v4u*>(expand_x), q1,
-                       s1, expert_token_nums, f.L, f.A, f.H / 8);
+    launch_quant_rows(static_cast<const v4u*>(expand_x), q1, s1, expert_token_nums, f.L, f.A, f.H / 8, quant_wgs, s);
   } else {
     q1 = const_cast<int8_t*>(expand_q);   // rows already quantised by mdc_dispatch_quant
     s1 = const_cast<float*>(dyn_scale);
@@ -924,8 +962,7 @@ mdc_status ffn_impl(const FfnPlan& f, const void* expand_x, const int8_t* expand
       hipLaunchKernelGGL((k_ffn_gemm<true, true>), dim3(g1), dim3(kFfnThreads), 0, s, gemm1, tiles);
     else
       hipLaunchKernelGGL((k_ffn_gemm<true, false>), dim3(g1), dim3(kFfnThreads), 0, s, gemm1, tiles);
-    hipLaunchKernelGGL(k_ffn_quant_rows, dim3(quant_wgs), dim3(256), 0, s, reinterpret_cast<const v4u*>(g), q2, s2,
-                       expert_token_nums, f.L, f.A, f.N / 2 / 8);
+    launch_quant_rows(reinterpret_cast<const v4u*>(g), q2, s2, expert_token_nums, f.L, f.A, f.N / 2 / 8, quant_wgs, s);
     if (tab)
       hipLaunchKernelGGL((k_ffn_gemm<false, true>), dim3(g2), dim3(kFfnThreads), 0, s, gemm2, tiles);
     else
