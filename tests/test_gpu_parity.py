@@ -220,10 +220,11 @@ def test_special_experts_and_route_mask_full_size():
     _end_to_end(w, ranks=[0, 4])
 
 
-def _random_cases(n=24, seed=20261202):
-    """Seeded random small worlds: ragged W/BS/H/E/K, 1D or 2D masks, zero/copy
-    experts, shared expert on or off, full or overflowing capacity, both
-    dispatch paths and both test experts."""
+def _random_cases(n=40, seed=20261202):
+    """Seeded random small worlds: ragged W/BS/H/E/K (BS up to 700, H up to
+    7168), uniform, Zipf, first-K or round-robin routing, 1D or 2D masks,
+    zero/copy experts, shared expert on or off, full or overflowing capacity,
+    both dispatch paths and both test experts."""
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -233,8 +234,12 @@ def _random_cases(n=24, seed=20261202):
         C = int(rng.choice([0, 0, 2]))
         E = W * L
         K = int(rng.integers(1, min(16, E + Z + C) + 1))
-        c = dict(world=W, bs=int(rng.integers(1, 201)), hidden=int(rng.choice([8, 64, 136, 520, 1032, 2056])),
-                 experts=E, topk=K, zero_experts=Z, copy_experts=C, shared=bool(rng.integers(0, 2)),
+        routing = str(rng.choice(["uniform", "uniform", "zipf", "first_k", "round_robin"]))
+        if Z or C or (routing == "zipf" and K > E):
+            routing = "uniform"   # the other generators draw routed experts only
+        c = dict(world=W, bs=int(rng.integers(1, 701)),
+                 hidden=int(rng.choice([8, 64, 136, 520, 1032, 2056, 2056, 7168])),
+                 experts=E, topk=K, zero_experts=Z, copy_experts=C, shared=bool(rng.integers(0, 2)), routing=routing,
                  inactive_frac=float(rng.choice([0.0, 0.2])), route_mask_frac=float(rng.choice([0.0, 0.0, 0.3])))
         cap_scale = float(rng.choice([1.0, 1.0, 0.3]))
         split = bool(rng.integers(0, 2))
