@@ -42,6 +42,8 @@ DESCR = {
     "tiny": "1 virtual rank, 8 experts, 16 tokens, H=128, top-2",
     "ffn": "share routing, then per local expert int8 GMM1 7168->4096, SwiGLU + dynamic int8 quant, "
            "int8 GMM2 2048->7168 (mdc_ffn) on destination 0's rows, then combine",
+    "special": "share shapes with 8 zero and 8 copy experts among the 144 ids drawn, a per-route [BS][K] "
+               "mask with 5% of routes off, shared expert, identity expert",
 }
 INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA
 
@@ -66,23 +68,35 @@ def algorithmic_bytes(w, ids, mask, d=0, r=0):
     """What the method must move for one step (dispatch share d, combine share r).
 
     With the FFN workload the dispatch writes int8 rows plus a 4-byte scale.
+    Zero-expert routes read nothing; copy-expert routes read the token's
+    original row once per token.
     """
     import numpy as np
     W, BS, K = ids.shape
     L = w.experts // W
     H2 = 2 * w.hidden
-    act = np.ones((W, BS), bool) if mask is None else mask.astype(bool)
-    valid = (ids >= 0) & (ids < w.experts) & act[:, :, None]
+    n_ids = w.experts + w.zero_experts + w.copy_experts
+    if mask is None:
+        act = np.ones((W, BS, K), bool)
+    elif mask.ndim == 2:
+        act = np.broadcast_to(mask.astype(bool)[:, :, None], (W, BS, K))
+    else:
+        act = mask.astype(bool)
+    valid = (ids >= 0) & (ids < w.experts) & act
     local = valid & ((ids // L) == d)
     R = int(local.sum())                      # routed rows written on rank d
     U = int(local.any(axis=2).sum())          # distinct source tokens read
-    present = int(valid[r].sum())             # routes of rank r combined
-    tok_any = int(valid[r].any(axis=1).sum())
-    layout = ids.size * 4 + (0 if mask is None else mask.size) + L * W * 4 + L * 8
+    present_r = (ids[r] >= 0) & (ids[r] < n_ids) & act[r]
+    routed_r = int(valid[r].sum())            # routes of rank r that read an expert row
+    copy_tok = int((present_r & (ids[r] >= w.experts + w.zero_experts)).any(axis=1).sum())
+    tok_any = int(present_r.any(axis=1).sum())
+    mask_bytes = 0 if mask is None else mask.size
+    layout = ids.size * 4 + mask_bytes + L * W * 4 + L * 8
     gather = U * H2 + R * ((w.hidden + 4 if w.inter else H2) + 12 + 4) + ids.size * 4
-    combine = (present * H2 + BS * K * 12 + (0 if mask is None else BS)
+    combine = (routed_r * H2 + BS * K * 12 + mask_bytes // W + copy_tok * H2
                + (tok_any * H2 if w.shared else 0) + BS * H2)
-    return {"R": R, "U": U, "present": present, "layout": layout, "gather": gather, "combine": combine}
+    return {"R": R, "U": U, "present": int(present_r.sum()), "layout": layout, "gather": gather,
+            "combine": combine}
 
 
 # sources of the dispatch/combine kernels (the ones the HBM-traffic summary measures)
@@ -139,7 +153,9 @@ def cpu_baseline(wi, w, budget_s, fw=None):
         ys = [y0] + [s.expand_x for s in segs[1:]]
         out = O.combine(ys, [s0.assist_info] + [s.assist_info for s in segs[1:]], 0, wi.ids[0],
                         None if wi.mask is None else wi.mask[0], wi.scales[0],
-                        None if wi.shared is None else wi.shared[0], w.hidden)
+                        None if wi.shared is None else wi.shared[0], w.hidden, experts=w.experts,
+                        zero_experts=w.zero_experts, copy_experts=w.copy_experts,
+                        ori_r=wi.x[0] if w.copy_experts else None)
         rates.append(w.bs / (time.perf_counter() - t0))
         reps += 1
     what = "dispatch share 0 + FFN + combine share 0" if fw is not None else "dispatch share 0 + combine share 0"
@@ -204,7 +220,8 @@ def main():
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     wi = gen.world_inputs(w)
     W, BS, K, H = w.world, w.bs, w.topk, w.hidden
-    shape = mdc.Shape(W, 0, BS, H, K, w.experts, w.capacity)
+    shape = mdc.Shape(W, 0, BS, H, K, w.experts, w.capacity, mask_per_route=1 if w.route_mask_frac > 0 else 0,
+                      zero_experts=w.zero_experts, copy_experts=w.copy_experts)
     stream = torch.cuda.current_stream()
 
     def bf16(a):
@@ -275,7 +292,7 @@ def main():
                                             [o["assist_info"] for o in bt["outs"]],
                                             [o["ep_recv_counts"] for o in bt["outs"]], bt["row0"], bt["ids0"],
                                             bt["scales0"], bt["mask0"], bt["shared0"], bt["x_out"],
-                                            stream=stream)
+                                            stream=stream, ori_x=bt["x"][0] if w.copy_experts else None)
 
     def step(bt, ev=None):
         if ev is None:
@@ -389,6 +406,8 @@ def main():
         "config": {"workload": f"{w.name}: {DESCR[w.name]}", "world": W, "bs": BS, "hidden": H,
                    "experts": w.experts, "topk": K, "capacity": w.capacity, "batches": args.batches,
                    "rows_received": by["R"], "source_rows_read": by["U"],
+                   "zero_experts": w.zero_experts, "copy_experts": w.copy_experts,
+                   "mask": None if wi.mask is None else ("per route" if wi.mask.ndim == 3 else "per token"),
                    "dispatch_call": "mdc_dispatch (one launch)" if one_shot else "mdc_dispatch_layout + gather"},
         "hbm_gbps": round(gb_step, 1),
         "hbm_frac_of_peak": round(gb_step / HBM_PEAK_GBPS, 4),

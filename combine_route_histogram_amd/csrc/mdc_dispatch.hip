@@ -742,16 +742,22 @@ __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
   }
   v4u* orow = out + (int64_t)t * nvec;
   // Zero experts [E, E+Z) and copy experts [E+Z, E+Z+C) are present without a
-  // dispatched row: output 0 (read from a valid row, then replaced by zero) or
-  // the token's own row ori[t].
+  // dispatched row: output 0 or the token's own row ori[t].
   const bool special = (lane < K) && act && e >= E && e - E < Z + C;
   const bool is_zero = special && e - E < Z;
   uint64_t yrow = yj + (uint64_t)rowc * (uint64_t)nvec * sizeof(v4u);
-  if (special) yrow = is_zero ? (uint64_t)orow : (uint64_t)(ori + (int64_t)t * nvec);
+  if (special && !is_zero) yrow = (uint64_t)(ori + (int64_t)t * nvec);
   ok = ok || special;
   const uint64_t has = __ballot(ok);
   const uint64_t zero_lanes = __ballot(is_zero);
   const int np = __popcll(has);
+  // A zero expert's slot is loaded and then replaced by zero: it reads a row
+  // this wavefront loads anyway (the first present non-zero route's, else the
+  // shared row), so the discarded load is served from cache, not HBM.
+  const uint64_t srow = (uint64_t)(shared + (int64_t)t * nvec);
+  const uint64_t nz = has & ~zero_lanes;
+  const uint64_t alias = nz ? readlane64(yrow, __ffsll((unsigned long long)nz) - 1) : (SHARED ? srow : (uint64_t)orow);
+  if (is_zero) yrow = alias;
   const int base = tile * 64 * V + lane;
 
   if (np == 0) {
@@ -781,7 +787,6 @@ __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
 
   v4u yv[KMAX][V];
   v4u shv[V];
-  const uint64_t srow = (uint64_t)(shared + (int64_t)t * nvec);
   const bool full = (tile + 1) * 64 * V <= nvec;
   if (full) {
 #pragma unroll

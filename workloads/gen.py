@@ -71,6 +71,10 @@ WORKLOADS = {
                        inactive_frac=0.1, shared=True),
     "decode": Workload("decode", 3, 8, 32, 7168, 256, 8, shared=True),
     "ffn": Workload("ffn", 4, 8, 2048, 7168, 128, 8, shared=True, inter=4096),
+    # share shapes with 8 zero and 8 copy experts drawn beside the 128 routed
+    # ones and a per-route [BS][K] mask with 5% of the routes off
+    "special": Workload("special", 5, 8, 2048, 7168, 128, 8, shared=True, zero_experts=8, copy_experts=8,
+                        route_mask_frac=0.05),
 }
 
 
