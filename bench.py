@@ -99,38 +99,43 @@ def algorithmic_bytes(w, ids, mask, d=0, r=0):
             "combine": combine}
 
 
-# sources of the dispatch/combine kernels (the ones the HBM-traffic summary measures)
+# sources of the dispatch/combine kernels (the ones the HBM-traffic summaries measure)
 TRAFFIC_SOURCES = ("mdc_common.h", "mdc_dispatch.hip")
 
 
-def dispatch_source_sha() -> str:
-    """sha256 over the dispatch/combine kernel sources, in TRAFFIC_SOURCES order."""
+def dispatch_source_sha(sources=TRAFFIC_SOURCES) -> str:
+    """sha256 over the named kernel sources, in the given order."""
     import hashlib
     h = hashlib.sha256()
-    for name in TRAFFIC_SOURCES:
+    for name in sources:
         h.update(open(os.path.join(ROOT, "combine_route_histogram_amd", "csrc", name), "rb").read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or None.
+def measured_traffic(workload: str, kernels):
+    """HBM bytes per launch from the committed counter summary, or None.
 
+    `kernels` is a kernel-name prefix, or a tuple of prefixes whose per-launch
+    bytes are summed (one launch of each, as one library call makes them).
     The summary records the sha256 of the kernel sources it was measured on
-    (dispatch_source_sha); once they differ the figure no longer describes
-    these kernels.
+    (its `sources`, by default TRAFFIC_SOURCES); once they differ the figure
+    no longer describes these kernels.
     """
     path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.json")
     try:
         prof = json.load(open(path))
-        sha = dispatch_source_sha()
+        sha = dispatch_source_sha(tuple(prof.get("sources", TRAFFIC_SOURCES)))
     except (OSError, ValueError):
         return None
     if prof.get("source_sha256") != sha:
         return None
-    for name, rec in prof.get("kernels", {}).items():
-        if name.startswith(kernel):
-            return int(round(rec["traffic_bytes"]))
-    return None
+    total = 0.0
+    for prefix in ((kernels,) if isinstance(kernels, str) else kernels):
+        recs = [rec for name, rec in prof.get("kernels", {}).items() if name.startswith(prefix)]
+        if len(recs) != 1:
+            return None
+        total += recs[0]["traffic_bytes"]
+    return int(round(total))
 
 
 def cpu_baseline(wi, w, budget_s, fw=None):
@@ -388,7 +393,10 @@ def main():
     if ffn_info is not None:
         roofline = {"bound": "mfma", "kernel": "mdc_ffn_quant_input (k_ffn_plan, k_ffn_gemm GMM1 + SwiGLU, k_ffn_quant_rows, k_ffn_gemm GMM2)",
                     "achieved": ffn_info["tops"], "peak": INT8_PEAK_TOPS, "unit": "TOP/s (int8)",
-                    "frac": ffn_info["mfma_frac"], "traffic": None, "ops_per_launch": ffn_info["int8_ops"],
+                    "frac": ffn_info["mfma_frac"],
+                    "traffic": measured_traffic(w.name, ("k_ffn_plan", "k_ffn_gemm<true", "k_ffn_quant_rows",
+                                                         "k_ffn_gemm<false")),
+                    "ops_per_launch": ffn_info["int8_ops"],
                     "avg_launch_us": ffn_info["us"]}
     result = {
         "metric": METRIC,

@@ -40,13 +40,16 @@ constexpr int kFfnStage = (kFfnBM + kFfnBW) * kFfnBK;   // bytes of one LDS stag
 constexpr int kFfnOutAlign = 128;  // GMM output widths (N/2 and H) must be multiples of this
 
 // Tile plan shared by both GEMMs.  Each local expert's rows (contiguous,
-// expert-major, clipped at A) split into m-tiles of kFfnBM rows.  The table
-// lists every full m-tile first (expert order), then each expert's partial
-// last m-tile by row count, largest first: the persistent GEMMs walk tiles
-// in table order, so the workgroups that run one tile more than the others
-// end on the cheapest tiles.  tiles[0].x = number of m-tiles; tiles[1 + m] =
-// {expert, first row, expert's end row, 0}.  One workgroup of 1024 threads;
-// L <= 2048 (two experts per thread).
+// expert-major, clipped at A) split into m-tiles of kFfnBM rows, the last
+// one partial.  The table lists them in expert order and cuts each expert's
+// run into chunks of at most kFfnChunkM consecutive m-tiles (sizes as equal
+// as possible); the GEMM walks a chunk's tiles together (ffn_decode_tile),
+// so an expert's partial m-tile runs beside its full ones and reads the
+// weight tiles they bring into L2.  tiles[0].x = number of m-tiles;
+// tiles[1 + m] = {expert, first row, expert's end row, (position in its
+// chunk << 8) | chunk size}.  One workgroup of 1024 threads; L <= 2048 (two
+// experts per thread).
+constexpr int kFfnChunkM = 8;
 constexpr int kPlanThreads = 1024;
 
 // Exclusive prefix over the 2048 values held two per thread (elements 2t and
@@ -84,7 +87,6 @@ __device__ int64_t plan_scan_pair(int64_t a, int64_t b, int64_t* wsum, int64_t& 
 __global__ __launch_bounds__(kPlanThreads) void k_ffn_plan(const int64_t* __restrict__ expert_nums, int L, int64_t A,
                                                            int4* __restrict__ tiles, int* __restrict__ sync_words,
                                                            int stride, uint32_t* __restrict__ amax_bits) {
-  __shared__ int rem_s[2 * kPlanThreads];
   __shared__ int64_t wsum[kPlanThreads / 64 + 1];
   const int tid = threadIdx.x;
   const int e0 = 2 * tid, e1 = 2 * tid + 1;
@@ -94,31 +96,30 @@ __global__ __launch_bounds__(kPlanThreads) void k_ffn_plan(const int64_t* __rest
   const int64_t x1 = x0 + c0;
   const int lo0 = (int)min(x0, A), hi0 = (int)min(x0 + c0, A);
   const int lo1 = (int)min(x1, A), hi1 = (int)min(x1 + c1, A);
-  const int f0 = (hi0 - lo0) / kFfnBM, f1 = (hi1 - lo1) / kFfnBM;   // full m-tiles
-  const int r0 = (hi0 - lo0) % kFfnBM, r1 = (hi1 - lo1) % kFfnBM;   // rows of the partial m-tile
-  rem_s[e0] = r0;
-  rem_s[e1] = r1;
-  int64_t nfull;
-  const int fp0 = (int)plan_scan_pair(f0, f1, wsum, nfull);          // table slot of e0's first full tile
-  int64_t npart;
-  (void)plan_scan_pair(r0 > 0, r1 > 0, wsum, npart);                // also orders rem_s writes before reads
-  for (int f = 0; f < f0; ++f) tiles[1 + fp0 + f] = int4{e0, lo0 + f * kFfnBM, hi0, 0};
-  for (int f = 0; f < f1; ++f) tiles[1 + fp0 + f0 + f] = int4{e1, lo1 + f * kFfnBM, hi1, 0};
-  // partial tiles: rank by rows, descending, ties by expert
+  const int n0 = (hi0 - lo0 + kFfnBM - 1) / kFfnBM, n1 = (hi1 - lo1 + kFfnBM - 1) / kFfnBM;   // m-tiles
+  int64_t nm;
+  const int p0 = (int)plan_scan_pair(n0, n1, wsum, nm);   // table slot of e0's first m-tile
   for (int h = 0; h < 2; ++h) {
-    const int e = h ? e1 : e0, r = h ? r1 : r0;
-    if (e >= L || r == 0) continue;
-    int rank = 0;
-    for (int o = 0; o < L; ++o) {
-      const int ro = rem_s[o];
-      rank += (ro > r) || (ro == r && o < e);
+    const int e = h ? e1 : e0, n = h ? n1 : n0, lo = h ? lo1 : lo0, hi = h ? hi1 : hi0;
+    const int slot = h ? p0 + n0 : p0;
+    // chunks: nch of them, the first `big` with base + 1 m-tiles, the rest with base
+    const int nch = (n + kFfnChunkM - 1) / kFfnChunkM;
+    const int base = nch ? n / nch : 0, big = nch ? n % nch : 0;
+    for (int j = 0; j < n; ++j) {
+      int pos, size;
+      if (j < big * (base + 1)) {
+        pos = j % (base + 1);
+        size = base + 1;
+      } else {
+        pos = (j - big * (base + 1)) % base;
+        size = base;
+      }
+      tiles[1 + slot + j] = int4{e, lo + j * kFfnBM, hi, (pos << 8) | size};
     }
-    const int lo = h ? lo1 : lo0, f = h ? f1 : f0, hi = h ? hi1 : hi0;
-    tiles[1 + (int)nfull + rank] = int4{e, lo + f * kFfnBM, hi, 0};
   }
-  if (tid == 0) tiles[0] = int4{(int)(nfull + npart), 0, 0, 0};
+  if (tid == 0) tiles[0] = int4{(int)nm, 0, 0, 0};
   if (sync_words != nullptr) {
-    const int MT = (int)(nfull + npart);
+    const int MT = (int)nm;
     if (tid < 2) sync_words[tid] = 0;
     for (int i = tid; i < MT; i += kPlanThreads) {
       sync_words[2 + i] = 0;
@@ -423,9 +424,10 @@ __device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const
 // Tiles: T = (m-tiles of the plan) x (output columns / tile columns).  The
 // launches hold one workgroup per CU.  k_ffn_gemm: workgroup b walks tiles
 // i*G + (b % 8)*(G/8) + b / 8; hardware places workgroup b on XCD b % 8, so
-// each XCD walks a contiguous run of tiles, ordered in groups of 4 m-tiles x
-// 8 n-tiles (m fastest) so the tiles an XCD runs together share A and W
-// tiles in its L2.  k_ffn_fused takes the same order from an atomic queue.
+// each XCD walks a contiguous run of tiles, ordered by ffn_decode_tile in
+// groups of up to 8 m-tiles of one expert x about 32 / (their number)
+// n-tiles (m fastest) so the tiles an XCD runs together share A and W tiles
+// in its L2.  k_ffn_fused takes the same order from an atomic queue.
 
 // Operands of one grouped GEMM.
 struct FfnGemm {
@@ -629,27 +631,28 @@ __device__ __forceinline__ FfnNext ffn_tile(const FfnGemm& g, int4 ti, int nt, c
   return nx;
 }
 
-// Tile t of a walk over T = MT x nn tiles -> (m-tile, n-tile): groups of GM
-// m-tiles x GN n-tiles, m fastest (the tiles run together share A and W
-// tiles in L2).
+// Tile t of a walk over T = MT x nn tiles -> (m-tile, n-tile).  The tiles
+// of a chunk of h m-tiles (see the plan) are t in [m0 nn, (m0 + h) nn); they
+// run in groups of h m-tiles x GN = 32 / h n-tiles, m fastest, so the about
+// 32 tiles an XCD runs together share A and W tiles in its L2.
 // All values are wavefront-uniform and below 2^31 (the host checks the
 // tile count), so the divisions run in 32 bits on scalar registers.
-__device__ __forceinline__ void ffn_decode_tile(int t, int MT, int nn, int& mt, int& nt) {
-  constexpr int GM = 4, GN = 8;
+template <typename Tab>
+__device__ __forceinline__ void ffn_decode_tile(int t, int nn, const Tab& tab, int& mt, int& nt) {
   t = __builtin_amdgcn_readfirstlane(t);
-  MT = __builtin_amdgcn_readfirstlane(MT);
   nn = __builtin_amdgcn_readfirstlane(nn);
-  const int band = GM * nn;
-  const int mg = t / band;
-  const int r = t - mg * band;
-  const int m_in_group = min(GM, MT - mg * GM);
-  const int per_ng = m_in_group * GN;
-  const int ng = r / per_ng;
-  const int r2 = r - ng * per_ng;
-  const int n_in_group = min(GN, nn - ng * GN);
-  const int q = r2 / m_in_group;
-  mt = mg * GM + (r2 - q * m_in_group);
-  nt = ng * GN + q % n_in_group;
+  const int mrow = t / nn;
+  const int w = __builtin_amdgcn_readfirstlane(tab.at(mrow).w);
+  const int h = w & 255;
+  const int m0 = mrow - (w >> 8);
+  const int r = t - m0 * nn;
+  const int gn = 32 / h;
+  const int band = h * gn;
+  const int ng = r / band;
+  const int r2 = r - ng * band;
+  const int q = r2 / h;
+  mt = m0 + (r2 - q * h);
+  nt = ng * gn + q;
 }
 
 // The m-tile table, read by the persistent kernels once per tile.  With
@@ -695,7 +698,7 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(FfnGemm g, const int4*
   int t = lin;
   if (t >= T) return;
   int mt, nt;
-  ffn_decode_tile(t, MT, nn, mt, nt);
+  ffn_decode_tile(t, nn, tab, mt, nt);
   int4 ti = tab.at(mt);
   FfnStage0 s0;
   ffn_stage_load<false>(ffn_staging<GLU>(g, ti, nt), 0, s0.sa, s0.sw);
@@ -706,7 +709,7 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(FfnGemm g, const int4*
     const int tn = t + G;
     const bool has_next = tn < T;
     int mtn = mt, ntn = nt;
-    if (has_next) ffn_decode_tile(tn, MT, nn, mtn, ntn);
+    if (has_next) ffn_decode_tile(tn, nn, tab, mtn, ntn);
     const int4 te = tab.at(mtn);
     const int4 tin = int4{__builtin_amdgcn_readfirstlane(te.x), __builtin_amdgcn_readfirstlane(te.y),
                           __builtin_amdgcn_readfirstlane(te.z), 0};
@@ -819,7 +822,7 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_fused(FfnGemm g1, FfnGemm g
     FfnStage0 s0;
     if (t < T1) {
       int mt, nt;
-      ffn_decode_tile(t, MT, nn1, mt, nt);
+      ffn_decode_tile(t, nn1, tab, mt, nt);
       const int4 ti = tab.at(mt);
       ffn_tile<true, false, false>(g1, ti, nt, sm, sync.amax_bits, s0, false, s0, no_next);
       // Publish: the barrier orders every wavefront's g stores (workgroup
@@ -842,7 +845,7 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_fused(FfnGemm g1, FfnGemm g
       }
     } else {
       int mt, nt;
-      ffn_decode_tile(t - T1, MT, nn2, mt, nt);
+      ffn_decode_tile(t - T1, nn2, tab, mt, nt);
       if (tid == 0) {
         // poll with relaxed (agent-coherent) loads
         int n = 0;
