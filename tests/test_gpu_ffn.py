@@ -82,6 +82,26 @@ def test_ffn_small(variant):
     assert err <= REL_L2
 
 
+@pytest.mark.parametrize("bs", [2500, 4700])
+def test_ffn_experts_with_several_tile_chunks(bs):
+    """Both experts receive every token: bs rows each, 10 or 19 m-tiles, cut
+    into chunks of 5 + 5 or 7 + 6 + 6 m-tiles.  H = N = 2048 give both GEMMs
+    8 n-tiles, more than one n-group of a chunk holds (6, 4 or 5), so the walk
+    crosses chunk and n-group boundaries.  Every row is checked on its own:
+    a tile the walk skipped or sent to the wrong rows shows there."""
+    w = gen.workload("tiny", world=1, bs=bs, hidden=2048, experts=2, topk=2, index=95)
+    say(f"ffn case W={w.world} BS={w.bs} H={w.hidden} E={w.experts} K={w.topk} N=2048")
+    got, want, *_ = _run_ffn(w, 2048)
+    assert got.shape[0] == 2 * bs
+    err = rel_l2(got, want)
+    a = O.bf16_to_f32(got).astype(np.float64)
+    b = O.bf16_to_f32(want).astype(np.float64)
+    row_err = np.linalg.norm(a - b, axis=1) / np.maximum(np.linalg.norm(b, axis=1), 1e-30)
+    say(f"  rel L2 {err:.3e}, worst row {row_err.max():.3e}")
+    assert err <= REL_L2
+    assert row_err.max() <= 3 * REL_L2
+
+
 def test_ffn_empty_expert_and_overflow():
     """Every route goes to experts 0..K-1 (A2 sample routing): other experts are empty; capacity cuts the tail."""
     w = gen.workload("tiny", world=2, bs=200, hidden=256, experts=8, topk=2, routing="first_k", index=85)
