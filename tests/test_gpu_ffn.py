@@ -102,6 +102,17 @@ def test_ffn_experts_with_several_tile_chunks(bs):
     assert row_err.max() <= 3 * REL_L2
 
 
+def test_ffn_hidden_past_the_quantiser_row_cache():
+    """H = 8320: 1040 vectors per row, more than the x quantiser keeps in
+    registers (1024), so it streams each row twice; 65 k stages per GMM1 tile."""
+    w = gen.workload("tiny", world=1, bs=96, hidden=8320, experts=2, topk=2, index=97)
+    say(f"ffn case W={w.world} BS={w.bs} H={w.hidden} E={w.experts} K={w.topk} N=256")
+    got, want, *_ = _run_ffn(w, 256)
+    err = rel_l2(got, want)
+    say(f"  rel L2 {err:.3e}")
+    assert err <= REL_L2
+
+
 def test_ffn_empty_expert_and_overflow():
     """Every route goes to experts 0..K-1 (A2 sample routing): other experts are empty; capacity cuts the tail."""
     w = gen.workload("tiny", world=2, bs=200, hidden=256, experts=8, topk=2, routing="first_k", index=85)

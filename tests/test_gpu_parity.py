@@ -97,6 +97,15 @@ def test_ragged_shapes(variant, split):
     _end_to_end(w, expert="pow2", split=split)
 
 
+@pytest.mark.parametrize("hidden,split", [(8192, False), (8200, False), (12296, False), (12296, True)])
+def test_large_hidden(hidden, split):
+    """H = 8192 is the one-launch dispatch's longest row (1024 vectors, one
+    per thread); 8200 falls back to the rank and gather kernels; 12296 spreads
+    a row over three gather tiles and 13 combine tiles, the last ones ragged."""
+    w = gen.workload("tiny", world=2, bs=40, hidden=hidden, experts=8, topk=3, shared=True, index=96)
+    _end_to_end(w, expert="pow2", split=split)
+
+
 def test_capacity_overflow_drops_rows():
     w = gen.workload("tiny", world=2, bs=64, hidden=64, experts=4, topk=2, index=70)
     _end_to_end(w, capacity=37)
