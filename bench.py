@@ -208,7 +208,7 @@ def graph_replay_us(mdc, torch, shape, batches, replays):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the expert-parallel "
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); the expert-parallel "
               "ranks are virtual buffers on that GPU. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

@@ -288,7 +288,8 @@ def quant_rows(v: np.ndarray):
     amax = max |v| over the row; q = clip(rint(v * (127 / amax)), -127, 127)
     with round-half-even; the dequant scale is amax / 127.  A zero row gives
     q = 0 and scale 0.  ([PTO] SwiGLU: dynamic quantisation to int8 plus a
-    per-token scale; the formula is this build's reading.)
+    per-token scale; the pages name the step but not its formula, so this is
+    the plain symmetric reading.)
     """
     v = np.asarray(v, dtype=np.float32)
     amax = np.max(np.abs(v), axis=1).astype(np.float32)
