@@ -40,6 +40,12 @@ namespace {
 #ifndef MDC_GATHER_VEC
 #define MDC_GATHER_VEC 8
 #endif
+#ifndef MDC_GATHER_SMALL_VEC
+#define MDC_GATHER_SMALL_VEC 2
+#endif
+#ifndef MDC_GATHER_FANOUT_SPLIT
+#define MDC_GATHER_FANOUT_SPLIT 2
+#endif
 #ifndef MDC_COMBINE_VEC
 #define MDC_COMBINE_VEC 1
 #endif
@@ -89,6 +95,9 @@ __host__ __device__ __forceinline__ int counter_slot(int i) {
   return c0 + (r % kScanIPL) * 64 + r / kScanIPL;
 }
 constexpr int kGatherVec = MDC_GATHER_VEC;
+constexpr int kGatherSmallVec = MDC_GATHER_SMALL_VEC;      // tile of the tokens with many rows here
+static_assert(kGatherSmallVec >= 1 && kGatherSmallVec < 5, "small tiles must be smaller than the tiles they replace");
+constexpr int kGatherFanoutSplit = MDC_GATHER_FANOUT_SPLIT;  // more rows than this: small tiles
 static_assert(kGatherVec >= 1 && kGatherVec <= 8, "gather tiles hold 1..8 vectors per lane");
 constexpr int kCombineVec = MDC_COMBINE_VEC;
 
@@ -259,42 +268,32 @@ __device__ int scan_lookup(const int32_t* __restrict__ cnt, int n, const int (&f
 // 0, tile 0 also writes epRecvCounts and expertTokenNums
 // ([TL] UpdateTokenNumsOut: per-local-expert counts).
 // ---------------------------------------------------------------------------
-template <int VPL>
-__global__ __launch_bounds__(64 * MDC_GATHER_WAVES) void k_dispatch_gather(
-    const v4u* __restrict__ x, const int32_t* __restrict__ P, const int32_t* __restrict__ cnt,
-    v4u* __restrict__ expand_x, int32_t* __restrict__ assist, int32_t* __restrict__ ep_recv,
-    int64_t* __restrict__ expert_nums, int32_t* __restrict__ row_idx,
-    int BS, int K, int L, int W, int TPG, int G, int64_t A, int nvec, int ntiles, unsigned n_items) {
-  const unsigned item = blockIdx.x * MDC_GATHER_WAVES + (threadIdx.x >> 6);
-  if (item >= n_items) return;
-  const unsigned gu = item / (unsigned)ntiles;
-  const int tile = (int)(item - gu * (unsigned)ntiles);
-  const int s = (int)(gu / (unsigned)BS);
-  const int t = (int)(gu - (unsigned)s * (unsigned)BS);
-  const int64_t g = gu;
-  const int lane = threadIdx.x & 63;
-
-  const bool writer = (g == 0) && (tile == 0);
+// One column tile (64 * V vectors from `tile * 64 * V`) of token g's row:
+// loads it, finds the token's rows (in-wavefront scan of the group
+// counters) and writes the tile to each of them; tile 0 also writes the
+// triplets and inverse-index entries, and the writer wavefront the counts.
+template <int V>
+__device__ __forceinline__ void gather_tile(
+    const v4u* __restrict__ x, const int32_t* __restrict__ cnt, v4u* __restrict__ expand_x,
+    int32_t* __restrict__ assist, int32_t* __restrict__ ep_recv, int64_t* __restrict__ expert_nums,
+    int32_t* __restrict__ row_idx, int64_t g, int s, int t, int tile, int lane, int p, bool mine, uint64_t has,
+    bool writer, int K, int L, int W, int TPG, int G, int64_t A, int nvec, int32_t* pref) {
   const int n_cnt = L * W * G;
   int cnt0[kScanIPL];
   load_counters(cnt, n_cnt, 0, lane, cnt0);
-  const int p = (lane < K) ? P[g * K + lane] : -1;
-  const bool mine = (p >= 0) && ((p & 0xFFFF) < L);
-  const uint64_t has = __ballot(mine);
-  if (has == 0 && !writer) return;
 
   // Column tile of the source row: issued before the scan so the loads overlap it.
-  const int base = tile * 64 * VPL + lane;
-  const bool full = (tile + 1) * 64 * VPL <= nvec;
+  const int base = tile * 64 * V + lane;
+  const bool full = (tile + 1) * 64 * V <= nvec;
   const uint64_t src = (uint64_t)(x + g * nvec);
-  v4u v[VPL];
+  v4u v[V];
   if (has != 0) {
     if (full) {
 #pragma unroll
-      for (int u = 0; u < VPL; ++u) v[u] = load_v4<MDC_GATHER_NT_LOADS != 0>(src + (uint64_t)(base + u * 64) * 16);
+      for (int u = 0; u < V; ++u) v[u] = load_v4<MDC_GATHER_NT_LOADS != 0>(src + (uint64_t)(base + u * 64) * 16);
     } else {
 #pragma unroll
-      for (int u = 0; u < VPL; ++u) {
+      for (int u = 0; u < V; ++u) {
         const int idx = base + u * 64;
         v[u] = idx < nvec ? load_v4<MDC_GATHER_NT_LOADS != 0>(src + (uint64_t)idx * 16) : v4u{0u, 0u, 0u, 0u};
       }
@@ -303,8 +302,7 @@ __global__ __launch_bounds__(64 * MDC_GATHER_WAVES) void k_dispatch_gather(
 
   const int le = p & 0xFFFF;
   const int q = mine ? ((le * W + s) * G + t / TPG) : -1;
-  __shared__ int32_t pref_all[MDC_GATHER_WAVES][kScanChunk];
-  const int first = scan_lookup(cnt, n_cnt, cnt0, q, G, writer, ep_recv, lane, pref_all[threadIdx.x >> 6]);
+  const int first = scan_lookup(cnt, n_cnt, cnt0, q, G, writer, ep_recv, lane, pref);
   if (writer) {
     for (int e = lane; e < L; e += 64) {
       int64_t sum = 0;
@@ -336,15 +334,54 @@ __global__ __launch_bounds__(64 * MDC_GATHER_WAVES) void k_dispatch_gather(
     v4u* dst = expand_x + (int64_t)rk * nvec;
     if (full) {
 #pragma unroll
-      for (int u = 0; u < VPL; ++u) store_v4<MDC_GATHER_NT_STORES != 0>(dst + base + u * 64, v[u]);
+      for (int u = 0; u < V; ++u) store_v4<MDC_GATHER_NT_STORES != 0>(dst + base + u * 64, v[u]);
     } else {
 #pragma unroll
-      for (int u = 0; u < VPL; ++u) {
+      for (int u = 0; u < V; ++u) {
         const int idx = base + u * 64;
         if (idx < nvec) store_v4<MDC_GATHER_NT_STORES != 0>(dst + idx, v[u]);
       }
     }
   }
+}
+
+// The launch has ntiles items per token: tiles of 64 * VS vectors.  A token
+// with more than kGatherFanoutSplit rows on this rank uses them all; one with
+// fewer uses the first ceil(nvec / (64 * VPL)) items for tiles of 64 * VPL
+// vectors and the others return.  (With VS == VPL every token uses tiles of
+// 64 * VPL vectors.)  Measured at the share shapes: with 5 rows per source
+// token (Zipf routes) 2-vector tiles are 13% faster than 7-vector ones, with
+// 1.5 rows per token 11% slower.
+template <int VPL, int VS>
+__global__ __launch_bounds__(64 * MDC_GATHER_WAVES) void k_dispatch_gather(
+    const v4u* __restrict__ x, const int32_t* __restrict__ P, const int32_t* __restrict__ cnt,
+    v4u* __restrict__ expand_x, int32_t* __restrict__ assist, int32_t* __restrict__ ep_recv,
+    int64_t* __restrict__ expert_nums, int32_t* __restrict__ row_idx,
+    int BS, int K, int L, int W, int TPG, int G, int64_t A, int nvec, int ntiles, unsigned n_items) {
+  const unsigned item = blockIdx.x * MDC_GATHER_WAVES + (threadIdx.x >> 6);
+  if (item >= n_items) return;
+  const unsigned gu = item / (unsigned)ntiles;
+  const int tile = (int)(item - gu * (unsigned)ntiles);
+  const int s = (int)(gu / (unsigned)BS);
+  const int t = (int)(gu - (unsigned)s * (unsigned)BS);
+  const int64_t g = gu;
+  const int lane = threadIdx.x & 63;
+
+  const bool writer = (g == 0) && (tile == 0);
+  const int p = (lane < K) ? P[g * K + lane] : -1;
+  const bool mine = (p >= 0) && ((p & 0xFFFF) < L);
+  const uint64_t has = __ballot(mine);
+  if (has == 0 && !writer) return;
+  __shared__ int32_t pref_all[MDC_GATHER_WAVES][kScanChunk];
+  int32_t* pref = pref_all[threadIdx.x >> 6];
+  if (VS < VPL && __popcll(has) > kGatherFanoutSplit) {
+    gather_tile<VS>(x, cnt, expand_x, assist, ep_recv, expert_nums, row_idx, g, s, t, tile, lane, p, mine, has,
+                    writer, K, L, W, TPG, G, A, nvec, pref);
+    return;
+  }
+  if (VS < VPL && tile * 64 * VPL >= nvec) return;   // (tile 0, the writer's, always has vectors)
+  gather_tile<VPL>(x, cnt, expand_x, assist, ep_recv, expert_nums, row_idx, g, s, t, tile, lane, p, mine, has,
+                   writer, K, L, W, TPG, G, A, nvec, pref);
 }
 
 // ---------------------------------------------------------------------------
@@ -909,23 +946,27 @@ mdc_status gather_impl(const DispatchPlan& p, const void* x, void* expand_x, int
     hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(64), 0, st, ep_recv, expert_nums, p.L, p.W);
     return launched();
   }
-  const int ntiles = (p.nvec + 64 * kGatherVec - 1) / (64 * kGatherVec);
-  const int vpl = (p.nvec + 64 * ntiles - 1) / (64 * ntiles);
+  // tiles of vpl vectors per lane (at most kGatherVec), and for vpl >= 5
+  // also small tiles of kGatherSmallVec vectors per lane
+  const int ntiles_big = (p.nvec + 64 * kGatherVec - 1) / (64 * kGatherVec);
+  const int vpl = (p.nvec + 64 * ntiles_big - 1) / (64 * ntiles_big);
+  const bool adaptive = vpl >= 5;   // the cases below that launch with VS = kGatherSmallVec < V
+  const int ntiles = adaptive ? (p.nvec + 64 * kGatherSmallVec - 1) / (64 * kGatherSmallVec) : ntiles_big;
   const unsigned n_items = (unsigned)(tokens * ntiles);
   const dim3 grid((n_items + MDC_GATHER_WAVES - 1) / MDC_GATHER_WAVES), block(64 * MDC_GATHER_WAVES);
-#define MDC_LAUNCH_GATHER(V)                                                                                  \
-  hipLaunchKernelGGL(k_dispatch_gather<V>, grid, block, 0, st, static_cast<const v4u*>(x), P, cnt,            \
+#define MDC_LAUNCH_GATHER(V, VS)                                                                              \
+  hipLaunchKernelGGL((k_dispatch_gather<V, VS>), grid, block, 0, st, static_cast<const v4u*>(x), P, cnt,      \
                      static_cast<v4u*>(expand_x), assist, ep_recv, expert_nums, row_idx, p.BS, p.K, p.L,        \
                      p.W, p.TPG, p.G, p.A, p.nvec, ntiles, n_items)
   switch (vpl) {
-    case 1: MDC_LAUNCH_GATHER(1); break;
-    case 2: MDC_LAUNCH_GATHER(2); break;
-    case 3: MDC_LAUNCH_GATHER(3); break;
-    case 4: MDC_LAUNCH_GATHER(4); break;
-    case 5: MDC_LAUNCH_GATHER(5); break;
-    case 6: MDC_LAUNCH_GATHER(6); break;
-    case 7: MDC_LAUNCH_GATHER(7); break;
-    default: MDC_LAUNCH_GATHER(8); break;
+    case 1: MDC_LAUNCH_GATHER(1, 1); break;
+    case 2: MDC_LAUNCH_GATHER(2, 2); break;
+    case 3: MDC_LAUNCH_GATHER(3, 3); break;
+    case 4: MDC_LAUNCH_GATHER(4, 4); break;
+    case 5: MDC_LAUNCH_GATHER(5, kGatherSmallVec); break;
+    case 6: MDC_LAUNCH_GATHER(6, kGatherSmallVec); break;
+    case 7: MDC_LAUNCH_GATHER(7, kGatherSmallVec); break;
+    default: MDC_LAUNCH_GATHER(8, kGatherSmallVec); break;
   }
 #undef MDC_LAUNCH_GATHER
   return launched();
