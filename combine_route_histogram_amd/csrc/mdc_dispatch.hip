@@ -9,7 +9,9 @@
 //                     routes, reads its row tile once and writes it to each of
 //                     its rows on this rank, with the (src, token, k) triplets,
 //                     the route -> row inverse index, epRecvCounts and
-//                     expertTokenNums.  (mdc_dispatch_gather)
+//                     expertTokenNums.  The tile size follows the token's
+//                     number of rows here (half rows for 1-2, 2 KB for more).
+//                     (mdc_dispatch_gather)
 //   k_dispatch_gather_q  as k_dispatch_gather with one wavefront per whole
 //                     row, writing each row as int8 codes plus a per-row
 //                     fp32 scale.  (mdc_dispatch_quant_gather)
