@@ -55,8 +55,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="share", choices=sorted(DESCR))
     ap.add_argument("--batches", type=int, default=2, help="rotated copies of every input buffer")
-    ap.add_argument("--event-every", type=int, default=10,
-                    help="record the per-kernel HIP events on every n-th timed step")
+    ap.add_argument("--event-samples", type=int, default=10,
+                    help="timed steps that carry per-kernel HIP events (spread evenly, the first timed step "
+                         "excluded)")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the memory-ceiling leg")
+    ap.add_argument("--ceiling-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -136,6 +139,119 @@ def measured_traffic(workload: str, kernels):
             return None
         total += recs[0]["traffic_bytes"]
     return int(round(total))
+
+
+def pct(v, q):
+    """q-th percentile (linear interpolation) of a list."""
+    v = sorted(v)
+    if not v:
+        return None
+    x = (len(v) - 1) * q / 100.0
+    lo = int(x)
+    hi = min(lo + 1, len(v) - 1)
+    return v[lo] + (v[hi] - v[lo]) * (x - lo)
+
+
+def spread(samples_us):
+    return {"median": round(statistics.median(samples_us), 3), "p10": round(pct(samples_us, 10), 3),
+            "p90": round(pct(samples_us, 90), 3), "n": len(samples_us)}
+
+
+def ceiling_leg(torch, mdc, w, wi, batches, stream, reps):
+    """Memory ceilings measured with the committed probe kernels (libmdc_probe), timed like the bench's kernels.
+
+    Each probe launch is bracketed by HIP events on the launch stream, after an
+    untimed 512 MiB write that flushes the 256 MB Infinity Cache.  Streaming
+    ceilings: 1 GiB read-only, 1 GiB write-only, 1 GiB copy (2 GiB moved).
+    Pattern probes (dispatch/combine workloads): the gather's read half (the U
+    distinct source rows), its write half (the R rows in the gather's
+    token-major fan-out order) and the combine's pattern (each token's present
+    rows plus one more row read, one row written) at the workload's own sizes.
+    """
+    import numpy as np
+    from combine_route_histogram_amd import probe
+    dev = "cuda:0"
+    st = stream.cuda_stream
+    GiB = 1 << 30
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+
+    def timed(fn):
+        out = []
+        for i in range(reps + 2):
+            probe.write(flush, flush.numel(), i, st)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                out.append(a.elapsed_time(b) * 1e3)
+        return out
+
+    res = {}
+    src = torch.empty(GiB, dtype=torch.uint8, device=dev)
+    dst = torch.empty(GiB, dtype=torch.uint8, device=dev)
+    probe.write(src, GiB, 1, st)
+    for name, nbytes, fn in (("read_1GiB", GiB, lambda: probe.read(src, GiB, sink, st)),
+                             ("write_1GiB", GiB, lambda: probe.write(dst, GiB, 3, st)),
+                             ("copy_1GiB", 2 * GiB, lambda: probe.copy(src, dst, GiB, st))):
+        t = timed(fn)
+        rate = [nbytes / (x * 1e-6) / 1e9 for x in t]
+        res[name] = {"bytes": nbytes, "us": spread(t), "gbps": round(statistics.median(rate), 1),
+                     "gbps_p10": round(pct(rate, 10), 1), "gbps_p90": round(pct(rate, 90), 1)}
+    del src, dst
+
+    pats = None
+    if not w.inter and w.name not in ("tiny",):
+        H2 = 2 * w.hidden
+        bt = batches[0]
+        o0 = bt["outs"][0]
+        # destination 0's dispatch of batch 0, so that its rows and triplets describe the step's pattern
+        if bt["layout"] is not None:
+            bt["layout"]()
+        bt["gather"]()
+        torch.cuda.synchronize()
+        R = int(o0["ep_recv_counts"][-1].item())
+        R = min(R, w.capacity)
+        tri = o0["assist_info"][:R].cpu().numpy().astype(np.int64)
+        tok = tri[:, 0] * w.bs + tri[:, 1]
+        order = np.lexsort((tri[:, 2], tok))          # token-major, k ascending: the gather's write order
+        tok_s, rows_s = tok[order], np.arange(R)[order]
+        uniq, start = np.unique(tok_s, return_index=True)
+        off = torch.from_numpy(np.concatenate([start, [R]]).astype(np.int32)).to(dev)
+        src_rows = torch.from_numpy(uniq.astype(np.int32)).to(dev)
+        dst_rows = torch.from_numpy(rows_s.astype(np.int32)).to(dev)
+        xflat = bt["x"]
+        spare = batches[1 % len(batches)]["outs"][0]["expand_x"]
+        t_r = timed(lambda: probe.rows_read(xflat, src_rows, H2, sink, st))
+        t_w = timed(lambda: probe.rows_write(spare, off, dst_rows, H2, st))
+        # combine pattern: rank 0's routes read the rows they read in the step (row numbers within the
+        # destination's buffer), here all from one buffer of the same size
+        row0 = bt["row0"].cpu().numpy()
+        ids0 = bt["ids0"].cpu().numpy()
+        L = w.experts // w.world
+        rr = np.where((ids0 >= 0) & (ids0 < w.experts) & (row0 >= 0), row0, -1).astype(np.int32)
+        if bt["mask0"] is not None:
+            m0 = bt["mask0"].cpu().numpy().astype(bool)
+            rr = np.where(m0 if m0.ndim == 2 else m0[:, None], rr, -1).astype(np.int32)
+        rows_k = torch.from_numpy(np.ascontiguousarray(rr)).to(dev)
+        own = bt["shared0"] if bt["shared0"] is not None else bt["x"][0]
+        out = torch.empty_like(bt["x_out"])
+        t_c = timed(lambda: probe.rows_reduce(bt["outs"][1]["expand_x"], rows_k, w.topk, own, out, H2, st))
+        n_read = int((rr >= 0).sum())
+        pats = {
+            "gather_read_us": spread(t_r), "gather_read_bytes": len(uniq) * H2,
+            "gather_write_us": spread(t_w), "gather_write_bytes": R * H2,
+            "gather_read_plus_write_us": round(statistics.median(t_r) + statistics.median(t_w), 3),
+            "combine_pattern_us": spread(t_c), "combine_pattern_bytes": (n_read + 2 * w.bs) * H2,
+            "what": "plain probe kernels (libmdc_probe) of each kernel's access pattern at this workload's sizes, "
+                    "no metadata work; median of HIP-event durations with the Infinity Cache flushed",
+        }
+    del flush
+    torch.cuda.synchronize()
+    return res, pats
 
 
 def cpu_baseline(wi, w, budget_s, fw=None):
@@ -320,6 +436,12 @@ def main():
         bt["combine"]()
         ev[3].record(stream)
 
+    ceil, pats = (None, None)
+    if not args.no_ceilings:
+        # also brings the GPU to its working clocks before the warmup
+        print("[bench] memory-ceiling leg", file=sys.stderr, flush=True)
+        ceil, pats = ceiling_leg(torch, mdc, w, wi, batches, stream, args.ceiling_reps)
+
     if args.calibrate_copy:
         # plain copy kernel of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -334,11 +456,12 @@ def main():
         step(batches[i % args.batches])
     torch.cuda.synchronize()
 
-    # Per-kernel HIP events are recorded on the launch stream on every n-th
-    # timed step (event packets add small gaps of their own, so they are not
-    # put on every step); the wall-clock total covers all steps.
-    every = max(1, args.event_every)
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(5)] for i in range(0, args.steps, every)}
+    # Per-kernel HIP events are recorded on the launch stream on about
+    # --event-samples timed steps, spread evenly over the run and never on the
+    # first timed step (it starts from an idle queue, right after a
+    # synchronisation); the wall-clock total covers all steps.
+    every = max(1, (args.steps - 1 + args.event_samples - 1) // max(1, args.event_samples))
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(5)] for i in range(1, args.steps, every)}
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     gc.collect()
     gc.disable()
@@ -349,6 +472,7 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gc.enable()
+    evs_idx = list(evs.keys())
     evs = list(evs.values())
 
     t_layout = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]     # us
@@ -360,19 +484,19 @@ def main():
     by = algorithmic_bytes(w, wi.ids, wi.mask)
     step_bytes = by["layout"] + by["gather"] + by["combine"]
     mean = statistics.fmean
-    gb_gather = by["gather"] / (mean(t_gather) * 1e-6) / 1e9
-    gb_comb = by["combine"] / (mean(t_comb) * 1e-6) / 1e9
+    med = statistics.median
     gb_step = step_bytes / (ms_per_step * 1e-3) / 1e9
     if one_shot:
         # one launch (k_dispatch_small) does the layout and the gather
         d_kernel, d_bytes = "k_dispatch_small", by["layout"] + by["gather"]
-        gb_gather = d_bytes / (mean(t_gather) * 1e-6) / 1e9
     else:
         d_kernel, d_bytes = ("k_dispatch_gather_q" if w.inter else "k_dispatch_gather"), by["gather"]
-    if mean(t_gather) >= mean(t_comb):
-        dom = (d_kernel, gb_gather, d_bytes, mean(t_gather))
+    gb_gather = d_bytes / (med(t_gather) * 1e-6) / 1e9
+    gb_comb = by["combine"] / (med(t_comb) * 1e-6) / 1e9
+    if med(t_gather) >= med(t_comb):
+        dom = (d_kernel, gb_gather, d_bytes, med(t_gather), t_gather)
     else:
-        dom = ("k_combine", gb_comb, by["combine"], mean(t_comb))
+        dom = ("k_combine", gb_comb, by["combine"], med(t_comb), t_comb)
     graph_info = None
     if one_shot:
         # launch-bound workloads: the same step replayed from a HIP graph
@@ -382,14 +506,20 @@ def main():
     ffn_info = None
     if w.inter:
         ops = 2.0 * by["R"] * (w.inter * H + H * (w.inter // 2))
-        tops = ops / (mean(t_ffn) * 1e-6) / 1e12
-        ffn_info = {"us": round(mean(t_ffn), 2), "median_us": round(statistics.median(t_ffn), 2),
-                    "int8_ops": ops, "tops": round(tops, 1), "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)}
+        tops = ops / (statistics.median(t_ffn) * 1e-6) / 1e12
+        ffn_info = {"us": round(statistics.median(t_ffn), 2), "mean_us": round(mean(t_ffn), 2),
+                    "spread_us": spread(t_ffn), "int8_ops": ops, "tops": round(tops, 1),
+                    "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)}
 
     roofline = {"bound": "hbm", "kernel": dom[0], "achieved": round(dom[1], 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(dom[1] / HBM_PEAK_GBPS, 4),
                 "traffic": measured_traffic(w.name, dom[0]),
-                "bytes_per_launch": dom[2], "avg_launch_us": round(dom[3], 3)}
+                "bytes_per_launch": dom[2], "avg_launch_us": round(dom[3], 3),
+                "launch_us": spread(dom[4]),
+                "launch_time_from": "median of HIP events on the launch stream around the kernel, on the timed "
+                                    "steps that carry events"}
+    if ceil is not None:
+        roofline["frac_of_copy_ceiling"] = round(dom[1] / ceil["copy_1GiB"]["gbps"], 4)
     if ffn_info is not None:
         roofline = {"bound": "mfma", "kernel": "mdc_ffn_quant_input (k_ffn_plan, k_ffn_gemm GMM1 + SwiGLU, k_ffn_quant_rows, k_ffn_gemm GMM2)",
                     "achieved": ffn_info["tops"], "peak": INT8_PEAK_TOPS, "unit": "TOP/s (int8)",
@@ -419,15 +549,18 @@ def main():
                    "dispatch_call": "mdc_dispatch (one launch)" if one_shot else "mdc_dispatch_layout + gather"},
         "hbm_gbps": round(gb_step, 1),
         "hbm_frac_of_peak": round(gb_step / HBM_PEAK_GBPS, 4),
+        "hbm_frac_of_copy_ceiling": None if ceil is None else round(gb_step / ceil["copy_1GiB"]["gbps"], 4),
         "step_bytes": step_bytes,
         "roofline": roofline,
+        "ceilings": ceil,
+        "pattern_probes": pats,
         # (with the one-shot dispatch no kernel runs between the first two events)
-        "kernels_us": {"dispatch_layout": None if one_shot else round(mean(t_layout), 3),
-                       "dispatch_gather": round(mean(t_gather), 3),
-                       "combine": round(mean(t_comb), 3), "step_events": round(mean(t_step_ev), 3),
+        "kernels_us": {"dispatch_layout": None if one_shot else spread(t_layout),
+                       "dispatch_gather": spread(t_gather),
+                       "combine": spread(t_comb), "step_events": spread(t_step_ev),
                        "gather_gbps": round(gb_gather, 1), "combine_gbps": round(gb_comb, 1),
-                       "gather_median": round(statistics.median(t_gather), 3),
-                       "combine_median": round(statistics.median(t_comb), 3)},
+                       "event_steps": sorted(evs_idx), "what": "median, p10, p90 over the timed steps that carry "
+                                                               "HIP events (the first timed step never does)"},
     }
     if ffn_info is not None:
         result["ffn"] = ffn_info

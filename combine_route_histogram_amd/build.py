@@ -14,6 +14,9 @@ ROOT = os.path.dirname(PKG)
 SRCS = [os.path.join(PKG, "csrc", "mdc_dispatch.hip"), os.path.join(PKG, "csrc", "mdc_ffn.hip")]
 INC = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libmdc.so")
+# the memory-ceiling probes the benchmark times beside the library (a library of their own)
+PROBE_SRCS = [os.path.join(PKG, "csrc", "mdc_probe.hip")]
+PROBE_OUT = os.path.join(PKG, "libmdc_probe.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -36,17 +39,23 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    tmp = OUT + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INC, *SRCS, "-o", tmp]
+def _build_one(srcs, out, verbose):
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libmdc.so")
-    os.replace(tmp, OUT)
-    return OUT
+        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libmdc.so and libmdc_probe.so (always, also where they exist)."""
+    _build_one(PROBE_SRCS, PROBE_OUT, verbose)
+    return _build_one(SRCS, OUT, verbose)
 
 
 if __name__ == "__main__":

@@ -76,20 +76,29 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int k) {
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Argument checks shared by every entry point.  MDC_ERR_INVALID: the fields do
+// not describe a well-formed problem; MDC_ERR_UNSUPPORTED: a well-formed
+// problem outside what this library handles ([CV4] Return Value: 161002 vs
+// 561002).
+constexpr uint32_t kKnownFlags = MDC_FLAG_FFN_PIPELINE | MDC_FLAG_SPIN_MASK;
+
 mdc_status check_shape(const mdc_shape* sh) {
   if (sh == nullptr) return MDC_ERR_NULLPTR;
   if (sh->world < 1 || sh->rank < 0 || sh->rank >= sh->world) return MDC_ERR_INVALID;
   if (sh->bs < 0 || sh->hidden <= 0 || (sh->hidden % 8) != 0) return MDC_ERR_INVALID;
-  if (sh->topk < 1 || sh->topk > MDC_MAX_TOPK) return MDC_ERR_INVALID;
+  if (sh->topk < 1) return MDC_ERR_INVALID;
   if (sh->num_experts <= 0 || (sh->num_experts % sh->world) != 0) return MDC_ERR_INVALID;
-  if (sh->num_experts / sh->world > MDC_MAX_LOCAL_EXPERTS) return MDC_ERR_INVALID;
-  if (sh->capacity < 0 || sh->capacity > INT32_MAX) return MDC_ERR_INVALID;
-  if ((int64_t)sh->world * sh->bs * sh->topk > INT32_MAX) return MDC_ERR_INVALID;
-  if (sh->world > 65535) return MDC_ERR_INVALID;
+  if (sh->capacity < 0) return MDC_ERR_INVALID;
   if (sh->mask_per_route != 0 && sh->mask_per_route != 1) return MDC_ERR_INVALID;
-  if (sh->zero_experts < 0 || sh->copy_experts < 0 || sh->reserved != 0) return MDC_ERR_INVALID;
-  if ((int64_t)sh->num_experts + sh->zero_experts + sh->copy_experts > INT32_MAX) return MDC_ERR_INVALID;
-  if (sh->topk > sh->num_experts + sh->zero_experts + sh->copy_experts) return MDC_ERR_INVALID;
+  if (sh->zero_experts < 0 || sh->copy_experts < 0) return MDC_ERR_INVALID;
+  if (((uint32_t)sh->flags & ~kKnownFlags) != 0) return MDC_ERR_INVALID;
+  if ((int64_t)sh->topk > (int64_t)sh->num_experts + sh->zero_experts + sh->copy_experts) return MDC_ERR_INVALID;
+  if (sh->topk > MDC_MAX_TOPK) return MDC_ERR_UNSUPPORTED;
+  if (sh->num_experts / sh->world > MDC_MAX_LOCAL_EXPERTS) return MDC_ERR_UNSUPPORTED;
+  if (sh->capacity > INT32_MAX) return MDC_ERR_UNSUPPORTED;
+  if ((int64_t)sh->world * sh->bs * sh->topk > INT32_MAX) return MDC_ERR_UNSUPPORTED;
+  if (sh->world > 65535) return MDC_ERR_UNSUPPORTED;
+  if ((int64_t)sh->num_experts + sh->zero_experts + sh->copy_experts > INT32_MAX) return MDC_ERR_UNSUPPORTED;
   return MDC_OK;
 }
 

@@ -119,12 +119,15 @@ constexpr int kCombineVec = MDC_COMBINE_VEC;
 //
 // P[f] = le | (rank << 16) for a route sent to d, else -1.
 // cnt[(le*W + s)*G + g] = routes of group g of source s sent to local expert le.
+// drop[s*G + g] = active routes of the group whose id lies outside [0, n_ids),
+// n_ids = E + Z + C (sent nowhere; reported in the status block).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void k_route_rank(
     const int32_t* __restrict__ ids, const uint8_t* __restrict__ mask,
-    int32_t* __restrict__ P, int32_t* __restrict__ cnt,
-    int BS, int K, int E, int L, int d, int W, int TPG, int G, int mask_per_route) {
+    int32_t* __restrict__ P, int32_t* __restrict__ cnt, int32_t* __restrict__ drop,
+    int BS, int K, int E, int L, int d, int W, int TPG, int G, int mask_per_route, int n_ids) {
   extern __shared__ int32_t sm[];  // carry[L], wave_cnt[nw][L]
+  __shared__ int32_t drop_s;
   const int nw = blockDim.x >> 6;
   int32_t* carry = sm;
   int32_t* wave_cnt = sm + L;
@@ -143,6 +146,7 @@ __global__ __launch_bounds__(1024) void k_route_rank(
   // steps are in flight together (a group holds at most kGroupRoutes routes).
   constexpr int kMaxSteps = kGroupRoutes / 256;
   int keys[kMaxSteps];
+  int dropped = 0;
 #pragma unroll
   for (int i = 0; i < kMaxSteps; ++i) {
     const int f = i * (int)blockDim.x + tid;
@@ -154,10 +158,12 @@ __global__ __launch_bounds__(1024) void k_route_rank(
                           (mask[mask_per_route ? f_base + f : (int64_t)s * BS + t] != 0);
       const int q = e - d * L;
       if (active && e >= 0 && e < E && q >= 0 && q < L) key = q;
+      dropped += (active && (e < 0 || e >= n_ids)) ? 1 : 0;
     }
     keys[i] = key;
   }
   for (int i = tid; i < L; i += blockDim.x) carry[i] = 0;
+  if (tid == 0) drop_s = 0;
 #pragma unroll
   for (int step = 0; step < kMaxSteps; ++step) {
     const int f0 = step * (int)blockDim.x;
@@ -191,6 +197,11 @@ __global__ __launch_bounds__(1024) void k_route_rank(
     __syncthreads();
   }
   for (int le = tid; le < L; le += blockDim.x) cnt[counter_slot((le * W + s) * G + g)] = carry[le];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) dropped += __shfl_xor(dropped, o, 64);
+  if (lane == 0 && dropped != 0) atomicAdd(&drop_s, dropped);
+  __syncthreads();
+  if (tid == 0) drop[s * G + g] = drop_s;
 }
 
 // ---------------------------------------------------------------------------
@@ -219,7 +230,8 @@ __device__ __forceinline__ void lds_wave_sync() {
 }
 
 __device__ int scan_lookup(const int32_t* __restrict__ cnt, int n, const int (&first)[kScanIPL], int q, int G,
-                           bool writer, int32_t* __restrict__ ep_recv, int lane, int32_t* __restrict__ pref) {
+                           bool writer, int32_t* __restrict__ ep_recv, int lane, int32_t* __restrict__ pref,
+                           int& total) {
   int carry = 0;
   int found = 0;
   for (int c0 = 0; c0 < n; c0 += kScanChunk) {
@@ -255,7 +267,32 @@ __device__ int scan_lookup(const int32_t* __restrict__ cnt, int n, const int (&f
     carry += __builtin_amdgcn_readlane(incl, 63);
     lds_wave_sync();
   }
+  total = carry;
   return found;
+}
+
+// The writer wavefront's part of the counts: expertTokenNums[le] = sum of the
+// group counters of le ([TL] UpdateTokenNumsOut), and the status block:
+// dropped ids summed over the rank groups, rows past the capacity.
+__device__ void write_totals(const int32_t* __restrict__ cnt, const int32_t* __restrict__ drop,
+                             int64_t* __restrict__ expert_nums, mdc_device_status* __restrict__ status, int L,
+                             int W, int G, int total, int64_t A, int lane) {
+  for (int e = lane; e < L; e += 64) {
+    int64_t sum = 0;
+    for (int i = 0; i < W * G; ++i) sum += cnt[counter_slot(e * W * G + i)];
+    expert_nums[e] = sum;
+  }
+  int dropped = 0;
+  for (int i = lane; i < W * G; i += 64) dropped += drop[i];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) dropped += __shfl_xor(dropped, o, 64);
+  if (lane == 0) {
+    const int64_t over = (int64_t)total - A;
+    status->dropped_ids = dropped;
+    status->overflow_rows = over > 0 ? (int32_t)over : 0;
+    status->wait_timeouts = 0;
+    status->reserved = 0;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -274,12 +311,39 @@ __device__ int scan_lookup(const int32_t* __restrict__ cnt, int n, const int (&f
 // loads it, finds the token's rows (in-wavefront scan of the group
 // counters) and writes the tile to each of them; tile 0 also writes the
 // triplets and inverse-index entries, and the writer wavefront the counts.
+// Pointers the gather kernels share beyond the rows themselves.
+struct GatherMeta {
+  const int32_t* P;           // packed (local expert, rank) per route
+  const int32_t* cnt;         // group counters (transposed chunks)
+  const int32_t* drop;        // dropped ids per rank group
+  mdc_device_status* status;  // the workspace's status block
+  const float* scales_in;     // [W][BS][K] route weights, or NULL
+  float* scales_out;          // [A] expand_scales, or NULL
+  int32_t* assist;
+  int32_t* ep_recv;
+  int64_t* expert_nums;
+  int32_t* row_idx;
+};
+
+// Tile-0 work of a route placed at `row`: inverse-index entry, triplet and
+// the weight that travels with the row.
+__device__ __forceinline__ void place_route(const GatherMeta& m, int64_t g, int K, int s, int t, int lane, int row) {
+  m.row_idx[g * K + lane] = row;
+  if (row >= 0) {
+    int32_t* a = m.assist + (int64_t)row * 3;
+    a[0] = s;
+    a[1] = t;
+    a[2] = lane;
+    if (m.scales_out != nullptr) m.scales_out[row] = m.scales_in[g * K + lane];
+  }
+}
+
 template <int V>
 __device__ __forceinline__ void gather_tile(
-    const v4u* __restrict__ x, const int32_t* __restrict__ cnt, v4u* __restrict__ expand_x,
-    int32_t* __restrict__ assist, int32_t* __restrict__ ep_recv, int64_t* __restrict__ expert_nums,
-    int32_t* __restrict__ row_idx, int64_t g, int s, int t, int tile, int lane, int p, bool mine, uint64_t has,
+    const v4u* __restrict__ x, const GatherMeta& m, v4u* __restrict__ expand_x,
+    int64_t g, int s, int t, int tile, int lane, int p, bool mine, uint64_t has,
     bool writer, int K, int L, int W, int TPG, int G, int64_t A, int nvec, int32_t* pref) {
+  const int32_t* __restrict__ cnt = m.cnt;
   const int n_cnt = L * W * G;
   int cnt0[kScanIPL];
   load_counters(cnt, n_cnt, 0, lane, cnt0);
@@ -304,14 +368,9 @@ __device__ __forceinline__ void gather_tile(
 
   const int le = p & 0xFFFF;
   const int q = mine ? ((le * W + s) * G + t / TPG) : -1;
-  const int first = scan_lookup(cnt, n_cnt, cnt0, q, G, writer, ep_recv, lane, pref);
-  if (writer) {
-    for (int e = lane; e < L; e += 64) {
-      int64_t sum = 0;
-      for (int i = 0; i < W * G; ++i) sum += cnt[counter_slot(e * W * G + i)];
-      expert_nums[e] = sum;
-    }
-  }
+  int total;
+  const int first = scan_lookup(cnt, n_cnt, cnt0, q, G, writer, m.ep_recv, lane, pref, total);
+  if (writer) write_totals(cnt, m.drop, m.expert_nums, m.status, L, W, G, total, A, lane);
   if (has == 0) return;
 
   int row = -1;
@@ -319,15 +378,7 @@ __device__ __forceinline__ void gather_tile(
     const int64_t r = (int64_t)first + (p >> 16);
     row = (r >= 0 && r < A) ? (int)r : -1;
   }
-  if (tile == 0 && mine) {
-    row_idx[g * K + lane] = row;
-    if (row >= 0) {
-      int32_t* a = assist + (int64_t)row * 3;
-      a[0] = s;
-      a[1] = t;
-      a[2] = lane;
-    }
-  }
+  if (tile == 0 && mine) place_route(m, g, K, s, t, lane, row);
   uint64_t rem = __ballot(row >= 0);
   while (rem) {
     const int k = __ffsll((unsigned long long)rem) - 1;
@@ -356,9 +407,7 @@ __device__ __forceinline__ void gather_tile(
 // 1.5 rows per token 11% slower.
 template <int VPL, int VS>
 __global__ __launch_bounds__(64 * MDC_GATHER_WAVES) void k_dispatch_gather(
-    const v4u* __restrict__ x, const int32_t* __restrict__ P, const int32_t* __restrict__ cnt,
-    v4u* __restrict__ expand_x, int32_t* __restrict__ assist, int32_t* __restrict__ ep_recv,
-    int64_t* __restrict__ expert_nums, int32_t* __restrict__ row_idx,
+    const v4u* __restrict__ x, GatherMeta m, v4u* __restrict__ expand_x,
     int BS, int K, int L, int W, int TPG, int G, int64_t A, int nvec, int ntiles, unsigned n_items) {
   const unsigned item = blockIdx.x * MDC_GATHER_WAVES + (threadIdx.x >> 6);
   if (item >= n_items) return;
@@ -370,20 +419,18 @@ __global__ __launch_bounds__(64 * MDC_GATHER_WAVES) void k_dispatch_gather(
   const int lane = threadIdx.x & 63;
 
   const bool writer = (g == 0) && (tile == 0);
-  const int p = (lane < K) ? P[g * K + lane] : -1;
+  const int p = (lane < K) ? m.P[g * K + lane] : -1;
   const bool mine = (p >= 0) && ((p & 0xFFFF) < L);
   const uint64_t has = __ballot(mine);
   if (has == 0 && !writer) return;
   __shared__ int32_t pref_all[MDC_GATHER_WAVES][kScanChunk];
   int32_t* pref = pref_all[threadIdx.x >> 6];
   if (VS < VPL && __popcll(has) > kGatherFanoutSplit) {
-    gather_tile<VS>(x, cnt, expand_x, assist, ep_recv, expert_nums, row_idx, g, s, t, tile, lane, p, mine, has,
-                    writer, K, L, W, TPG, G, A, nvec, pref);
+    gather_tile<VS>(x, m, expand_x, g, s, t, tile, lane, p, mine, has, writer, K, L, W, TPG, G, A, nvec, pref);
     return;
   }
   if (VS < VPL && tile * 64 * VPL >= nvec) return;   // (tile 0, the writer's, always has vectors)
-  gather_tile<VPL>(x, cnt, expand_x, assist, ep_recv, expert_nums, row_idx, g, s, t, tile, lane, p, mine, has,
-                   writer, K, L, W, TPG, G, A, nvec, pref);
+  gather_tile<VPL>(x, m, expand_x, g, s, t, tile, lane, p, mine, has, writer, K, L, W, TPG, G, A, nvec, pref);
 }
 
 // ---------------------------------------------------------------------------
@@ -399,10 +446,9 @@ constexpr int kQuantRowVec = 16;
 
 template <int VPL>
 __global__ __launch_bounds__(64) void k_dispatch_gather_q(
-    const v4u* __restrict__ x, const int32_t* __restrict__ P, const int32_t* __restrict__ cnt,
-    int8_t* __restrict__ expand_q, float* __restrict__ dyn_scale, int32_t* __restrict__ assist,
-    int32_t* __restrict__ ep_recv, int64_t* __restrict__ expert_nums, int32_t* __restrict__ row_idx,
+    const v4u* __restrict__ x, GatherMeta m, int8_t* __restrict__ expand_q, float* __restrict__ dyn_scale,
     int BS, int K, int L, int W, int TPG, int G, int64_t A, int nvec) {
+  const int32_t* __restrict__ cnt = m.cnt;
   const unsigned gu = blockIdx.x;
   const int s = (int)(gu / (unsigned)BS);
   const int t = (int)(gu - (unsigned)s * (unsigned)BS);
@@ -412,7 +458,7 @@ __global__ __launch_bounds__(64) void k_dispatch_gather_q(
   const int n_cnt = L * W * G;
   int cnt0[kScanIPL];
   load_counters(cnt, n_cnt, 0, lane, cnt0);
-  const int p = (lane < K) ? P[g * K + lane] : -1;
+  const int p = (lane < K) ? m.P[g * K + lane] : -1;
   const bool mine = (p >= 0) && ((p & 0xFFFF) < L);
   const uint64_t has = __ballot(mine);
   if (has == 0 && !writer) return;
@@ -429,14 +475,9 @@ __global__ __launch_bounds__(64) void k_dispatch_gather_q(
   const int le = p & 0xFFFF;
   const int q = mine ? ((le * W + s) * G + t / TPG) : -1;
   __shared__ int32_t pref_all[kScanChunk];
-  const int first = scan_lookup(cnt, n_cnt, cnt0, q, G, writer, ep_recv, lane, pref_all);
-  if (writer) {
-    for (int e = lane; e < L; e += 64) {
-      int64_t sum = 0;
-      for (int i = 0; i < W * G; ++i) sum += cnt[counter_slot(e * W * G + i)];
-      expert_nums[e] = sum;
-    }
-  }
+  int total;
+  const int first = scan_lookup(cnt, n_cnt, cnt0, q, G, writer, m.ep_recv, lane, pref_all, total);
+  if (writer) write_totals(cnt, m.drop, m.expert_nums, m.status, L, W, G, total, A, lane);
   if (has == 0) return;
 
   // per-row quantisation, decided in fp32
@@ -469,14 +510,8 @@ __global__ __launch_bounds__(64) void k_dispatch_gather_q(
     row = (r >= 0 && r < A) ? (int)r : -1;
   }
   if (mine) {
-    row_idx[g * K + lane] = row;
-    if (row >= 0) {
-      int32_t* a = assist + (int64_t)row * 3;
-      a[0] = s;
-      a[1] = t;
-      a[2] = lane;
-      dyn_scale[row] = scale;
-    }
+    place_route(m, g, K, s, t, lane, row);
+    if (row >= 0) dyn_scale[row] = scale;
   }
   uint64_t rem = __ballot(row >= 0);
   while (rem) {
@@ -518,10 +553,13 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
     const v4u* __restrict__ x, const int32_t* __restrict__ ids, const uint8_t* __restrict__ mask, int mask_per_route,
     v4u* __restrict__ expand_x, int8_t* __restrict__ expand_q, float* __restrict__ dyn_scale,
     int32_t* __restrict__ assist, int32_t* __restrict__ ep_recv, int64_t* __restrict__ expert_nums,
-    int32_t* __restrict__ row_idx, int W, int d, int BS, int K, int E, int L, int64_t A, int nvec) {
+    int32_t* __restrict__ row_idx, const float* __restrict__ scales_in, float* __restrict__ scales_out,
+    mdc_device_status* __restrict__ status, int W, int d, int BS, int K, int E, int L, int64_t A, int nvec,
+    int n_ids) {
   __shared__ int key_s[kSmallRoutes];
   __shared__ int cnt_s[kSmallCounters];   // histogram, then its exclusive prefix
   __shared__ int wsum[kSmallThreads / 64];
+  __shared__ int drop_s;
   __shared__ int rank_s[MDC_MAX_TOPK];
   __shared__ int row_s[MDC_MAX_TOPK];
   __shared__ float amax_s[kSmallThreads / 64];
@@ -564,16 +602,24 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
 
   // (stored for every f < kB * kSmallThreads <= kSmallRoutes, -1 past n: no
   // branch for the compiler to sink the loads into)
+  int dropped = 0;   // (workgroup 0 reports the active routes with ids outside [0, n_ids))
 #pragma unroll
   for (int j = 0; j < kB; ++j) {
     const int f = tid + j * kSmallThreads;
     const int q = ev[j] - d * L;
     const bool active = mask == nullptr || mv[j] != 0;
     key_s[f] = (f < n && active && ev[j] >= 0 && ev[j] < E && q >= 0 && q < L) ? q : -1;
+    dropped += (f < n && active && (ev[j] < 0 || ev[j] >= n_ids)) ? 1 : 0;
   }
   for (int i = tid; i < nc; i += kSmallThreads) cnt_s[i] = 0;
   if (tid < MDC_MAX_TOPK) rank_s[tid] = 0;
+  if (tid == 0) drop_s = 0;
   __syncthreads();
+  if (tok == 0) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) dropped += __shfl_xor(dropped, o, 64);
+    if (lane == 0 && dropped != 0) atomicAdd(&drop_s, dropped);
+  }
 
   // one pass over the keys: histogram cnt[le * W + s'], and the ranks of this
   // token's routes (earlier routes of source s with the same key)
@@ -637,9 +683,17 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
     run += v[j];
   }
   __syncthreads();
-  if (tok == 0)
+  if (tok == 0) {
     for (int le = tid; le < L; le += kSmallThreads)
       expert_nums[le] = (int64_t)((le + 1 < L ? cnt_s[(le + 1) * W] : total) - cnt_s[le * W]);
+    if (tid == 0) {
+      const int64_t over = (int64_t)total - A;
+      status->dropped_ids = drop_s;
+      status->overflow_rows = over > 0 ? (int32_t)over : 0;
+      status->wait_timeouts = 0;
+      status->reserved = 0;
+    }
+  }
 
   // this token's rows, triplets and inverse-index entries
   if (tid < K) {
@@ -655,6 +709,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
         a[0] = s;
         a[1] = t;
         a[2] = tid;
+        if (scales_out != nullptr) scales_out[row] = scales_in[f];
       }
     }
     row_s[tid] = row;
@@ -712,11 +767,12 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
   }
 }
 
-// Empty batch: every count is zero.
+// Empty batch: every count is zero, and so is the status block.
 __global__ __launch_bounds__(64) void k_zero_counts(int32_t* __restrict__ ep_recv, int64_t* __restrict__ expert_nums,
-                                                    int L, int W) {
+                                                    mdc_device_status* __restrict__ status, int L, int W) {
   for (int i = threadIdx.x; i < L * W; i += 64) ep_recv[i] = 0;
   for (int i = threadIdx.x; i < L; i += 64) expert_nums[i] = 0;
+  if (threadIdx.x == 0) *status = mdc_device_status{0, 0, 0, 0};
 }
 
 // ---------------------------------------------------------------------------
@@ -726,6 +782,14 @@ struct CombineTables {
   const v4u* y[MDC_MAX_COMBINE_WORLD];
   const int32_t* assist[MDC_MAX_COMBINE_WORLD];
   const int32_t* counts[MDC_MAX_COMBINE_WORLD];
+  const float* esc[MDC_MAX_COMBINE_WORLD];   // expand_scales per rank (all NULL without the table)
+};
+
+// With performance_info, every combine wavefront records (start, end, ranks
+// read) with the constant-rate real-time clock; k_combine_perf turns them
+// into per-rank waits.
+struct CombineRecord {
+  uint64_t t0, t1, ranks;
 };
 
 
@@ -734,15 +798,16 @@ struct CombineTables {
 // triplet (r, t, k).  The prologue is two load levels: (ids, row index,
 // scale, mask, pointer tables) then (count_j, triplet); every address is
 // kept inside its buffer so the loads can be issued without branches.
-template <int KMAX, int V, bool SHARED>
+template <int KMAX, int V, bool SHARED, bool TIMED>
 __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
     CombineTables tabs, const int32_t* __restrict__ row_idx, const int32_t* __restrict__ ids,
     const float* __restrict__ scales, const uint8_t* __restrict__ mask,
     const v4u* __restrict__ shared, const v4u* __restrict__ ori, v4u* __restrict__ out,
-    int r, int W, int K, int E, int L, int64_t A, int nvec, int ntiles, unsigned n_items,
-    int mask_per_route, int Z, int C) {
+    CombineRecord* __restrict__ rec, int r, int W, int K, int E, int L, int64_t A, int nvec, int ntiles,
+    unsigned n_items, int mask_per_route, int Z, int C, int has_esc) {
   const unsigned item = blockIdx.x * MDC_COMBINE_WAVES + (threadIdx.x >> 6);
   if (item >= n_items) return;
+  const uint64_t t_start = TIMED ? __builtin_amdgcn_s_memrealtime() : 0;
   const int t = (int)(item / (unsigned)ntiles);
   const int tile = (int)(item - (unsigned)t * (unsigned)ntiles);
   const int lane = threadIdx.x & 63;
@@ -759,7 +824,7 @@ __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
   const uint64_t cb = (uint64_t)tabs.counts[tl];
   const int e = ids[rt];
   const int row = row_idx[rt];
-  const float sc = scales[rt];
+  const float sc_route = scales[rt];
   const uint8_t mflag = mask != nullptr ? mask[mask_per_route ? rt : (int64_t)t]
                                         : *reinterpret_cast<const uint8_t*>(ids + rt);
   const bool act = (mask == nullptr) || (mflag != 0);
@@ -773,10 +838,16 @@ __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
   const uint64_t cj = shfl64(cb, j);
 
   bool ok = false;
+  float sc = sc_route;
   if (A > 0) {
     const int32_t total = load_i32(cj + ((uint64_t)L * W - 1) * 4);
     const uint64_t a = aj + (uint64_t)rowc * 12;
     const int a0 = load_i32(a), a1 = load_i32(a + 4), a2 = load_i32(a + 8);
+    if (has_esc) {   // the weight that travelled with the row (expand_scales of rank j)
+      const uint64_t ej = shfl64((uint64_t)tabs.esc[tl], j);
+      const float w = __builtin_bit_cast(float, load_i32(ej + (uint64_t)rowc * 4));
+      if (valid) sc = w;
+    }
     ok = valid && inrange && row < total && a0 == r && a1 == t && a2 == lane;
   }
   v4u* orow = out + (int64_t)t * nvec;
@@ -806,6 +877,7 @@ __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
       const int idx = base + u * 64;
       if (idx < nvec) store_v4<MDC_COMBINE_NT_STORES != 0>(orow + idx, z);
     }
+    if (TIMED && lane == 0) rec[item] = CombineRecord{t_start, t_start, 0};
     return;
   }
 
@@ -888,7 +960,61 @@ __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
     v4u o;
 #pragma unroll
     for (int w = 0; w < 4; ++w) o[w] = bf16_rne(acc[2 * w]) | (bf16_rne(acc[2 * w + 1]) << 16);
+    if (TIMED && u == V - 1) {
+      // every row load has returned (its values are in acc): this wavefront's
+      // arrival time for the ranks it read
+      uint64_t ranks = (ok && !special) ? (1ull << j) : 0ull;
+#pragma unroll
+      for (int o2 = 32; o2 >= 1; o2 >>= 1) {
+        const unsigned lo = __shfl_xor((unsigned)ranks, o2, 64), hi = __shfl_xor((unsigned)(ranks >> 32), o2, 64);
+        ranks |= ((uint64_t)hi << 32) | lo;
+      }
+      const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
+      if (lane == 0) rec[item] = CombineRecord{t_start, t_end, ranks};
+    }
     if (idx < nvec) store_v4<MDC_COMBINE_NT_STORES != 0>(orow + idx, o);
+  }
+}
+
+// performance_info[j] += the wait for rank j's data: from the earliest
+// wavefront start to the latest arrival of a row read from rank j, in whole
+// microseconds rounded up (at least 1 for a rank that sent rows); ranks no
+// row was read from are left unchanged.  One workgroup.
+__global__ __launch_bounds__(1024) void k_combine_perf(const CombineRecord* __restrict__ rec, unsigned n_items,
+                                                       int W, int64_t* __restrict__ perf, int64_t ticks_per_us) {
+  __shared__ unsigned long long end_s[MDC_MAX_COMBINE_WORLD];
+  __shared__ unsigned long long start_s[1024 / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < MDC_MAX_COMBINE_WORLD) end_s[tid] = 0ull;
+  __syncthreads();
+  unsigned long long t0 = ~0ull;
+  for (unsigned i = tid; i < n_items; i += 1024) {
+    const CombineRecord c = rec[i];
+    t0 = c.t0 < t0 ? c.t0 : t0;
+    uint64_t m = c.ranks;
+    while (m) {
+      const int jj = __ffsll((unsigned long long)m) - 1;
+      m &= m - 1;
+      atomicMax(&end_s[jj], (unsigned long long)c.t1);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const unsigned long long v = ((unsigned long long)(unsigned)__shfl_xor((unsigned)(t0 >> 32), o, 64) << 32) |
+                                 (unsigned)__shfl_xor((unsigned)t0, o, 64);
+    t0 = v < t0 ? v : t0;
+  }
+  if (lane == 0) start_s[wave] = t0;
+  __syncthreads();
+  if (tid < W) {
+    unsigned long long start = ~0ull;
+    for (int w = 0; w < 1024 / 64; ++w) start = start_s[w] < start ? start_s[w] : start;
+    const unsigned long long e = end_s[tid];
+    if (e != 0ull) {
+      const int64_t ticks = e > start ? (int64_t)(e - start) : 0;
+      const int64_t us = (ticks + ticks_per_us - 1) / ticks_per_us;
+      perf[tid] += us > 0 ? us : 1;
+    }
   }
 }
 
@@ -896,11 +1022,12 @@ __global__ __launch_bounds__(64 * MDC_COMBINE_WAVES) void k_combine(
 // Host side
 // ---------------------------------------------------------------------------
 struct DispatchPlan {
-  int W, d, BS, H, K, E, L, TPG, G, nvec, rank_threads, mask_per_route;
+  int W, d, BS, H, K, E, L, TPG, G, nvec, rank_threads, mask_per_route, n_ids;
   int64_t A;
-  size_t off_p, off_cnt, bytes;
+  size_t off_drop, off_p, off_cnt, bytes;
 };
 
+// Workspace: [status block][drop: W*G int32][P: W*BS*K int32][group counters].
 DispatchPlan make_plan(const mdc_shape* sh) {
   DispatchPlan p;
   p.W = sh->world;
@@ -912,6 +1039,7 @@ DispatchPlan make_plan(const mdc_shape* sh) {
   p.L = p.E / p.W;
   p.A = sh->capacity;
   p.mask_per_route = sh->mask_per_route;
+  p.n_ids = sh->num_experts + sh->zero_experts + sh->copy_experts;
   p.TPG = kGroupRoutes / p.K;
   p.G = (p.BS + p.TPG - 1) / p.TPG;
   p.nvec = p.H / 8;
@@ -919,33 +1047,38 @@ DispatchPlan make_plan(const mdc_shape* sh) {
   p.rank_threads = p.L <= 512 ? 1024 : 256;
   const size_t routes = (size_t)p.W * p.BS * p.K;
   const size_t counters = round_up((size_t)p.L * p.W * p.G, kScanChunk);
-  p.off_p = 0;
-  p.off_cnt = round_up(routes * 4, 256);
+  p.off_drop = MDC_STATUS_BYTES;
+  p.off_p = p.off_drop + round_up((size_t)p.W * p.G * 4, 256);
+  p.off_cnt = p.off_p + round_up(routes * 4, 256);
   p.bytes = p.off_cnt + round_up(counters * 4, 256);
-  if (p.bytes == 0) p.bytes = 256;
   return p;
+}
+
+GatherMeta make_meta(const DispatchPlan& p, char* ws, const float* scales_in, float* scales_out, int32_t* assist,
+                     int32_t* ep_recv, int64_t* expert_nums, int32_t* row_idx) {
+  return GatherMeta{reinterpret_cast<const int32_t*>(ws + p.off_p), reinterpret_cast<const int32_t*>(ws + p.off_cnt),
+                    reinterpret_cast<const int32_t*>(ws + p.off_drop), reinterpret_cast<mdc_device_status*>(ws),
+                    scales_in, scales_out, assist, ep_recv, expert_nums, row_idx};
 }
 
 mdc_status layout_impl(const DispatchPlan& p, const int32_t* ids, const uint8_t* mask, char* ws, hipStream_t st) {
   int32_t* P = reinterpret_cast<int32_t*>(ws + p.off_p);
   int32_t* cnt = reinterpret_cast<int32_t*>(ws + p.off_cnt);
+  int32_t* drop = reinterpret_cast<int32_t*>(ws + p.off_drop);
   if (p.G == 0) return MDC_OK;
   (void)hipGetLastError();
   const size_t lds = (size_t)(p.rank_threads / 64 + 1) * p.L * sizeof(int32_t);
   hipLaunchKernelGGL(k_route_rank, dim3(p.G, p.W), dim3(p.rank_threads), lds, st,
-                     ids, mask, P, cnt, p.BS, p.K, p.E, p.L, p.d, p.W, p.TPG, p.G, p.mask_per_route);
+                     ids, mask, P, cnt, drop, p.BS, p.K, p.E, p.L, p.d, p.W, p.TPG, p.G, p.mask_per_route, p.n_ids);
   return launched();
 }
 
-mdc_status gather_impl(const DispatchPlan& p, const void* x, void* expand_x, int32_t* assist, int32_t* ep_recv,
-                       int64_t* expert_nums, int32_t* row_idx, char* ws, hipStream_t st) {
-  const int32_t* P = reinterpret_cast<const int32_t*>(ws + p.off_p);
-  const int32_t* cnt = reinterpret_cast<const int32_t*>(ws + p.off_cnt);
+mdc_status gather_impl(const DispatchPlan& p, const void* x, const GatherMeta& m, void* expand_x, hipStream_t st) {
   (void)hipGetLastError();
   const int64_t tokens = (int64_t)p.W * p.BS;
   if (tokens == 0) {
-    // nothing routed: zero the counts with one wavefront of the gather kernel's writer path
-    hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(64), 0, st, ep_recv, expert_nums, p.L, p.W);
+    // nothing routed: zero the counts and the status block
+    hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(64), 0, st, m.ep_recv, m.expert_nums, m.status, p.L, p.W);
     return launched();
   }
   // tiles of vpl vectors per lane (at most kGatherVec), and for vpl >= 5
@@ -957,9 +1090,8 @@ mdc_status gather_impl(const DispatchPlan& p, const void* x, void* expand_x, int
   const unsigned n_items = (unsigned)(tokens * ntiles);
   const dim3 grid((n_items + MDC_GATHER_WAVES - 1) / MDC_GATHER_WAVES), block(64 * MDC_GATHER_WAVES);
 #define MDC_LAUNCH_GATHER(V, VS)                                                                              \
-  hipLaunchKernelGGL((k_dispatch_gather<V, VS>), grid, block, 0, st, static_cast<const v4u*>(x), P, cnt,      \
-                     static_cast<v4u*>(expand_x), assist, ep_recv, expert_nums, row_idx, p.BS, p.K, p.L,        \
-                     p.W, p.TPG, p.G, p.A, p.nvec, ntiles, n_items)
+  hipLaunchKernelGGL((k_dispatch_gather<V, VS>), grid, block, 0, st, static_cast<const v4u*>(x), m,            \
+                     static_cast<v4u*>(expand_x), p.BS, p.K, p.L, p.W, p.TPG, p.G, p.A, p.nvec, ntiles, n_items)
   switch (vpl) {
     case 1: MDC_LAUNCH_GATHER(1, 1); break;
     case 2: MDC_LAUNCH_GATHER(2, 2); break;
@@ -974,21 +1106,18 @@ mdc_status gather_impl(const DispatchPlan& p, const void* x, void* expand_x, int
   return launched();
 }
 
-mdc_status gather_q_impl(const DispatchPlan& p, const void* x, int8_t* expand_q, float* dyn_scale, int32_t* assist,
-                         int32_t* ep_recv, int64_t* expert_nums, int32_t* row_idx, char* ws, hipStream_t st) {
-  const int32_t* P = reinterpret_cast<const int32_t*>(ws + p.off_p);
-  const int32_t* cnt = reinterpret_cast<const int32_t*>(ws + p.off_cnt);
+mdc_status gather_q_impl(const DispatchPlan& p, const void* x, const GatherMeta& m, int8_t* expand_q, float* dyn_scale,
+                         hipStream_t st) {
   (void)hipGetLastError();
   const int64_t tokens = (int64_t)p.W * p.BS;
   if (tokens == 0) {
-    hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(64), 0, st, ep_recv, expert_nums, p.L, p.W);
+    hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(64), 0, st, m.ep_recv, m.expert_nums, m.status, p.L, p.W);
     return launched();
   }
   const int vpl = (p.nvec + 63) / 64;
 #define MDC_LAUNCH_GQ(V)                                                                                          \
   hipLaunchKernelGGL(k_dispatch_gather_q<V>, dim3((unsigned)tokens), dim3(64), 0, st, static_cast<const v4u*>(x), \
-                     P, cnt, expand_q, dyn_scale, assist, ep_recv, expert_nums, row_idx, p.BS, p.K, p.L, p.W,   \
-                     p.TPG, p.G, p.A, p.nvec)
+                     m, expand_q, dyn_scale, p.BS, p.K, p.L, p.W, p.TPG, p.G, p.A, p.nvec)
   if (vpl <= 4) MDC_LAUNCH_GQ(4);
   else if (vpl <= 8) MDC_LAUNCH_GQ(8);
   else if (vpl <= 12) MDC_LAUNCH_GQ(12);
@@ -1010,14 +1139,142 @@ bool small_path(const DispatchPlan& p) {
 
 template <bool QUANT>
 mdc_status small_impl(const DispatchPlan& p, const void* x, const int32_t* ids, const uint8_t* mask, void* expand_x,
-                      int8_t* expand_q, float* dyn_scale, int32_t* assist, int32_t* ep_recv, int64_t* expert_nums,
-                      int32_t* row_idx, hipStream_t st) {
+                      int8_t* expand_q, float* dyn_scale, const GatherMeta& m, hipStream_t st) {
   (void)hipGetLastError();
   const bool one_batch = (int64_t)p.W * p.BS * p.K <= kSmallKeyBatch * kSmallThreads;
   auto kern = one_batch ? k_dispatch_small<QUANT, 1> : k_dispatch_small<QUANT, 4>;
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.W * p.BS)), dim3(kSmallThreads), 0, st,
                      static_cast<const v4u*>(x), ids, mask, p.mask_per_route, static_cast<v4u*>(expand_x), expand_q,
-                     dyn_scale, assist, ep_recv, expert_nums, row_idx, p.W, p.d, p.BS, p.K, p.E, p.L, p.A, p.nvec);
+                     dyn_scale, m.assist, m.ep_recv, m.expert_nums, m.row_idx, m.scales_in, m.scales_out, m.status,
+                     p.W, p.d, p.BS, p.K, p.E, p.L, p.A, p.nvec, p.n_ids);
+  return launched();
+}
+
+// Pointer checks of the gather stage (shared by the four dispatch entry points
+// that place rows).  `rows` is expand_x or expand_q.
+mdc_status check_gather_args(const DispatchPlan& p, const void* x, const void* rows, const float* dyn_scale,
+                             bool quant, int32_t* assist, int32_t* ep_recv, int64_t* expert_nums, int32_t* row_idx,
+                             const float* scales_in, float* scales_out, const void* ws, size_t ws_bytes) {
+  if (quant && p.nvec > 64 * kQuantRowVec) return MDC_ERR_UNSUPPORTED;
+  if (ws == nullptr || ep_recv == nullptr || expert_nums == nullptr) return MDC_ERR_NULLPTR;
+  if (p.BS > 0 && (x == nullptr || row_idx == nullptr)) return MDC_ERR_NULLPTR;
+  if (p.BS > 0 && p.A > 0 && (rows == nullptr || assist == nullptr || (quant && dyn_scale == nullptr)))
+    return MDC_ERR_NULLPTR;
+  if (scales_out != nullptr && scales_in == nullptr) return MDC_ERR_NULLPTR;
+  if (!aligned16(x) || !aligned16(rows)) return MDC_ERR_INVALID;
+  if (ws_bytes < p.bytes) return MDC_ERR_WORKSPACE;
+  return MDC_OK;
+}
+
+// Combine tiles: 64 * kCombineVec vectors per lane for K <= 8, one vector
+// per lane otherwise.
+int combine_tiles(int nvec, int K) {
+  const int v = K <= 8 ? kCombineVec : 1;
+  return (nvec + 64 * v - 1) / (64 * v);
+}
+
+// Workspace of mdc_combine: one CombineRecord per wavefront, used only with
+// performance_info.
+size_t combine_workspace_bytes(const mdc_shape* sh) {
+  const size_t items = (size_t)sh->bs * combine_tiles(sh->hidden / 8, sh->topk);
+  return round_up(items * sizeof(CombineRecord), 256);
+}
+
+template <int KMAX, int V, bool SHARED, bool TIMED>
+void launch_combine(const CombineTables& tabs, const int32_t* row_idx, const int32_t* ids, const float* scales,
+                    const uint8_t* mask, const v4u* sh, const v4u* ori, v4u* out, CombineRecord* rec,
+                    const mdc_shape* shape, int ntiles, unsigned n_items, int has_esc, hipStream_t s) {
+  const int W = shape->world;
+  const dim3 grid((n_items + MDC_COMBINE_WAVES - 1) / MDC_COMBINE_WAVES), block(64 * MDC_COMBINE_WAVES);
+  hipLaunchKernelGGL((k_combine<KMAX, V, SHARED, TIMED>), grid, block, 0, s, tabs, row_idx, ids, scales, mask, sh,
+                     ori, out, rec, shape->rank, W, shape->topk, shape->num_experts, shape->num_experts / W,
+                     (int64_t)shape->capacity, shape->hidden / 8, ntiles, n_items, shape->mask_per_route,
+                     shape->zero_experts, shape->copy_experts, has_esc);
+}
+
+template <int KMAX, int V, bool TIMED>
+void launch_combine_s(bool shared, const CombineTables& tabs, const int32_t* row_idx, const int32_t* ids,
+                      const float* scales, const uint8_t* mask, const v4u* sh, const v4u* ori, v4u* out,
+                      CombineRecord* rec, const mdc_shape* shape, int ntiles, unsigned n_items, int has_esc,
+                      hipStream_t s) {
+  if (shared)
+    launch_combine<KMAX, V, true, TIMED>(tabs, row_idx, ids, scales, mask, sh, ori, out, rec, shape, ntiles, n_items,
+                                         has_esc, s);
+  else
+    launch_combine<KMAX, V, false, TIMED>(tabs, row_idx, ids, scales, mask, sh, ori, out, rec, shape, ntiles, n_items,
+                                          has_esc, s);
+}
+
+mdc_status combine_impl(const mdc_shape* shape, const void* const* expand_x, const int32_t* const* assist_info,
+                        const int32_t* const* ep_recv_counts, const int32_t* expanded_row_idx,
+                        const int32_t* expert_ids, const float* expert_scales, const uint8_t* x_active_mask,
+                        const float* const* expand_scales, const void* shared_expert_x, const void* ori_x,
+                        int64_t* perf, void* x_out, void* workspace, size_t workspace_bytes, hipStream_t s) {
+  mdc_status st = check_shape(shape);
+  if (st != MDC_OK) return st;
+  const int W = shape->world;
+  if (W > MDC_MAX_COMBINE_WORLD) return MDC_ERR_UNSUPPORTED;
+  const int BS = shape->bs;
+  if (BS == 0) return MDC_OK;
+  if (expand_x == nullptr || assist_info == nullptr || ep_recv_counts == nullptr) return MDC_ERR_NULLPTR;
+  if (expanded_row_idx == nullptr || expert_ids == nullptr || expert_scales == nullptr || x_out == nullptr)
+    return MDC_ERR_NULLPTR;
+  CombineTables tabs;
+  std::memset(&tabs, 0, sizeof(tabs));
+  for (int j = 0; j < W; ++j) {
+    if (ep_recv_counts[j] == nullptr) return MDC_ERR_NULLPTR;
+    if (shape->capacity > 0 && (expand_x[j] == nullptr || assist_info[j] == nullptr)) return MDC_ERR_NULLPTR;
+    if (shape->capacity > 0 && expand_scales != nullptr && expand_scales[j] == nullptr) return MDC_ERR_NULLPTR;
+    if (!aligned16(expand_x[j])) return MDC_ERR_INVALID;
+    tabs.y[j] = static_cast<const v4u*>(expand_x[j]);
+    tabs.assist[j] = assist_info[j];
+    tabs.counts[j] = ep_recv_counts[j];
+    tabs.esc[j] = expand_scales != nullptr ? expand_scales[j] : nullptr;
+  }
+  if (shape->copy_experts > 0 && ori_x == nullptr) return MDC_ERR_NULLPTR;
+  if (!aligned16(shared_expert_x) || !aligned16(x_out) || !aligned16(ori_x)) return MDC_ERR_INVALID;
+  CombineRecord* rec = nullptr;
+  int64_t ticks_per_us = 100;
+  if (perf != nullptr) {
+    if (workspace == nullptr) return MDC_ERR_NULLPTR;
+    if (workspace_bytes < combine_workspace_bytes(shape)) return MDC_ERR_WORKSPACE;
+    rec = static_cast<CombineRecord*>(workspace);
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) !=
+                                                hipSuccess || khz < 1000)
+      return MDC_ERR_HIP;
+    ticks_per_us = khz / 1000;
+  }
+  const int K = shape->topk;
+  const int nvec = shape->hidden / 8;
+  const v4u* sh = static_cast<const v4u*>(shared_expert_x);
+  v4u* out = static_cast<v4u*>(x_out);
+  const v4u* ori = static_cast<const v4u*>(ori_x);
+  const int has_esc = expand_scales != nullptr && shape->capacity > 0 ? 1 : 0;
+  const int ntiles = combine_tiles(nvec, K);
+  const unsigned n_items = (unsigned)((int64_t)BS * ntiles);
+  const bool shared = sh != nullptr;
+  (void)hipGetLastError();
+  if (K <= 8) {
+    if (perf)
+      launch_combine_s<8, kCombineVec, true>(shared, tabs, expanded_row_idx, expert_ids, expert_scales, x_active_mask,
+                                             sh, ori, out, rec, shape, ntiles, n_items, has_esc, s);
+    else
+      launch_combine_s<8, kCombineVec, false>(shared, tabs, expanded_row_idx, expert_ids, expert_scales,
+                                              x_active_mask, sh, ori, out, rec, shape, ntiles, n_items, has_esc, s);
+  } else {
+    if (perf)
+      launch_combine_s<16, 1, true>(shared, tabs, expanded_row_idx, expert_ids, expert_scales, x_active_mask, sh, ori,
+                                    out, rec, shape, ntiles, n_items, has_esc, s);
+    else
+      launch_combine_s<16, 1, false>(shared, tabs, expanded_row_idx, expert_ids, expert_scales, x_active_mask, sh,
+                                     ori, out, rec, shape, ntiles, n_items, has_esc, s);
+  }
+  if (perf != nullptr) {
+    st = launched();
+    if (st != MDC_OK) return st;
+    hipLaunchKernelGGL(k_combine_perf, dim3(1), dim3(1024), 0, s, rec, n_items, W, perf, ticks_per_us);
+  }
   return launched();
 }
 
@@ -1029,7 +1286,8 @@ const char* mdc_status_string(mdc_status status) {
   switch (status) {
     case MDC_OK: return "MDC_OK";
     case MDC_ERR_NULLPTR: return "MDC_ERR_NULLPTR: a required pointer is NULL";
-    case MDC_ERR_INVALID: return "MDC_ERR_INVALID: shape, alignment or value outside the supported range";
+    case MDC_ERR_INVALID: return "MDC_ERR_INVALID: misaligned tensor or shape fields that do not describe a problem";
+    case MDC_ERR_UNSUPPORTED: return "MDC_ERR_UNSUPPORTED: a value outside the range this library supports";
     case MDC_ERR_WORKSPACE: return "MDC_ERR_WORKSPACE: workspace smaller than the size query returned";
     case MDC_ERR_HIP: return "MDC_ERR_HIP: a HIP kernel launch failed";
   }
@@ -1038,12 +1296,16 @@ const char* mdc_status_string(mdc_status status) {
 
 int32_t mdc_abi_version(void) { return MDC_ABI_VERSION; }
 
-mdc_status mdc_dispatch_workspace_size(const mdc_shape* shape, size_t* bytes) {
+mdc_status mdc_dispatch_workspace(const mdc_shape* shape, size_t* bytes) {
   if (bytes == nullptr) return MDC_ERR_NULLPTR;
   const mdc_status st = check_shape(shape);
   if (st != MDC_OK) return st;
   *bytes = make_plan(shape).bytes;
   return MDC_OK;
+}
+
+mdc_status mdc_dispatch_workspace_size(const mdc_shape* shape, size_t* bytes) {
+  return mdc_dispatch_workspace(shape, bytes);
 }
 
 mdc_status mdc_dispatch_layout(const mdc_shape* shape, const int32_t* expert_ids, const uint8_t* x_active_mask,
@@ -1057,159 +1319,103 @@ mdc_status mdc_dispatch_layout(const mdc_shape* shape, const int32_t* expert_ids
   return layout_impl(p, expert_ids, x_active_mask, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
-mdc_status mdc_dispatch_gather(const mdc_shape* shape, const void* x, void* expand_x, int32_t* assist_info,
-                               int32_t* ep_recv_counts, int64_t* expert_token_nums, int32_t* expanded_row_idx,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+mdc_status mdc_dispatch_gather(const mdc_shape* shape, const void* x, const float* expert_scales, void* expand_x,
+                               int32_t* assist_info, int32_t* ep_recv_counts, int64_t* expert_token_nums,
+                               int32_t* expanded_row_idx, float* expand_scales, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   mdc_status st = check_shape(shape);
   if (st != MDC_OK) return st;
   const DispatchPlan p = make_plan(shape);
-  if (workspace == nullptr || ep_recv_counts == nullptr || expert_token_nums == nullptr) return MDC_ERR_NULLPTR;
-  if (p.BS > 0 && (x == nullptr || expanded_row_idx == nullptr)) return MDC_ERR_NULLPTR;
-  if (p.BS > 0 && p.A > 0 && (expand_x == nullptr || assist_info == nullptr)) return MDC_ERR_NULLPTR;
-  if (!aligned16(x) || !aligned16(expand_x)) return MDC_ERR_INVALID;
-  if (workspace_bytes < p.bytes) return MDC_ERR_WORKSPACE;
-  return gather_impl(p, x, expand_x, assist_info, ep_recv_counts, expert_token_nums, expanded_row_idx,
-                     static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  st = check_gather_args(p, x, expand_x, nullptr, false, assist_info, ep_recv_counts, expert_token_nums,
+                         expanded_row_idx, expert_scales, expand_scales, workspace, workspace_bytes);
+  if (st != MDC_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  const GatherMeta m = make_meta(p, ws, expert_scales, expand_scales, assist_info, ep_recv_counts,
+                                 expert_token_nums, expanded_row_idx);
+  return gather_impl(p, x, m, expand_x, static_cast<hipStream_t>(stream));
 }
 
 mdc_status mdc_dispatch(const mdc_shape* shape, const void* x, const int32_t* expert_ids,
-                        const uint8_t* x_active_mask, void* expand_x, int32_t* assist_info,
-                        int32_t* ep_recv_counts, int64_t* expert_token_nums, int32_t* expanded_row_idx,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        const uint8_t* x_active_mask, const float* expert_scales, void* expand_x,
+                        int32_t* assist_info, int32_t* ep_recv_counts, int64_t* expert_token_nums,
+                        int32_t* expanded_row_idx, float* expand_scales, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   mdc_status st = check_shape(shape);
   if (st != MDC_OK) return st;
   const DispatchPlan p = make_plan(shape);
-  if (ep_recv_counts == nullptr || expert_token_nums == nullptr || workspace == nullptr) return MDC_ERR_NULLPTR;
-  if (p.BS > 0 && (x == nullptr || expert_ids == nullptr || expanded_row_idx == nullptr)) return MDC_ERR_NULLPTR;
-  if (p.BS > 0 && p.A > 0 && (expand_x == nullptr || assist_info == nullptr)) return MDC_ERR_NULLPTR;
-  if (!aligned16(x) || !aligned16(expand_x)) return MDC_ERR_INVALID;
-  if (workspace_bytes < p.bytes) return MDC_ERR_WORKSPACE;
+  if (p.BS > 0 && expert_ids == nullptr) return MDC_ERR_NULLPTR;
+  st = check_gather_args(p, x, expand_x, nullptr, false, assist_info, ep_recv_counts, expert_token_nums,
+                         expanded_row_idx, expert_scales, expand_scales, workspace, workspace_bytes);
+  if (st != MDC_OK) return st;
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (small_path(p))
-    return small_impl<false>(p, x, expert_ids, x_active_mask, expand_x, nullptr, nullptr, assist_info,
-                             ep_recv_counts, expert_token_nums, expanded_row_idx, s);
+  const GatherMeta m = make_meta(p, ws, expert_scales, expand_scales, assist_info, ep_recv_counts,
+                                 expert_token_nums, expanded_row_idx);
+  if (small_path(p)) return small_impl<false>(p, x, expert_ids, x_active_mask, expand_x, nullptr, nullptr, m, s);
   st = layout_impl(p, expert_ids, x_active_mask, ws, s);
   if (st != MDC_OK) return st;
-  return gather_impl(p, x, expand_x, assist_info, ep_recv_counts, expert_token_nums, expanded_row_idx, ws, s);
+  return gather_impl(p, x, m, expand_x, s);
 }
 
-mdc_status mdc_dispatch_quant_gather(const mdc_shape* shape, const void* x, int8_t* expand_q, float* dynamic_scales,
-                                     int32_t* assist_info, int32_t* ep_recv_counts, int64_t* expert_token_nums,
-                                     int32_t* expanded_row_idx, void* workspace, size_t workspace_bytes,
-                                     void* stream) {
+mdc_status mdc_dispatch_quant_gather(const mdc_shape* shape, const void* x, const float* expert_scales,
+                                     int8_t* expand_q, float* dynamic_scales, int32_t* assist_info,
+                                     int32_t* ep_recv_counts, int64_t* expert_token_nums, int32_t* expanded_row_idx,
+                                     float* expand_scales, void* workspace, size_t workspace_bytes, void* stream) {
   mdc_status st = check_shape(shape);
   if (st != MDC_OK) return st;
   const DispatchPlan p = make_plan(shape);
-  if (p.nvec > 64 * kQuantRowVec) return MDC_ERR_INVALID;
-  if (workspace == nullptr || ep_recv_counts == nullptr || expert_token_nums == nullptr) return MDC_ERR_NULLPTR;
-  if (p.BS > 0 && (x == nullptr || expanded_row_idx == nullptr)) return MDC_ERR_NULLPTR;
-  if (p.BS > 0 && p.A > 0 && (expand_q == nullptr || dynamic_scales == nullptr || assist_info == nullptr))
-    return MDC_ERR_NULLPTR;
-  if (!aligned16(x) || !aligned16(expand_q)) return MDC_ERR_INVALID;
-  if (workspace_bytes < p.bytes) return MDC_ERR_WORKSPACE;
-  return gather_q_impl(p, x, expand_q, dynamic_scales, assist_info, ep_recv_counts, expert_token_nums,
-                       expanded_row_idx, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  st = check_gather_args(p, x, expand_q, dynamic_scales, true, assist_info, ep_recv_counts, expert_token_nums,
+                         expanded_row_idx, expert_scales, expand_scales, workspace, workspace_bytes);
+  if (st != MDC_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  const GatherMeta m = make_meta(p, ws, expert_scales, expand_scales, assist_info, ep_recv_counts,
+                                 expert_token_nums, expanded_row_idx);
+  return gather_q_impl(p, x, m, expand_q, dynamic_scales, static_cast<hipStream_t>(stream));
 }
 
 mdc_status mdc_dispatch_quant(const mdc_shape* shape, const void* x, const int32_t* expert_ids,
-                              const uint8_t* x_active_mask, int8_t* expand_q, float* dynamic_scales,
-                              int32_t* assist_info, int32_t* ep_recv_counts, int64_t* expert_token_nums,
-                              int32_t* expanded_row_idx, void* workspace, size_t workspace_bytes, void* stream) {
+                              const uint8_t* x_active_mask, const float* expert_scales, int8_t* expand_q,
+                              float* dynamic_scales, int32_t* assist_info, int32_t* ep_recv_counts,
+                              int64_t* expert_token_nums, int32_t* expanded_row_idx, float* expand_scales,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   mdc_status st = check_shape(shape);
   if (st != MDC_OK) return st;
   const DispatchPlan p = make_plan(shape);
-  if (p.nvec > 64 * kQuantRowVec) return MDC_ERR_INVALID;
-  if (ep_recv_counts == nullptr || expert_token_nums == nullptr || workspace == nullptr) return MDC_ERR_NULLPTR;
-  if (p.BS > 0 && (x == nullptr || expert_ids == nullptr || expanded_row_idx == nullptr)) return MDC_ERR_NULLPTR;
-  if (p.BS > 0 && p.A > 0 && (expand_q == nullptr || dynamic_scales == nullptr || assist_info == nullptr))
-    return MDC_ERR_NULLPTR;
-  if (!aligned16(x) || !aligned16(expand_q)) return MDC_ERR_INVALID;
-  if (workspace_bytes < p.bytes) return MDC_ERR_WORKSPACE;
+  if (p.BS > 0 && expert_ids == nullptr) return MDC_ERR_NULLPTR;
+  st = check_gather_args(p, x, expand_q, dynamic_scales, true, assist_info, ep_recv_counts, expert_token_nums,
+                         expanded_row_idx, expert_scales, expand_scales, workspace, workspace_bytes);
+  if (st != MDC_OK) return st;
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (small_path(p))
-    return small_impl<true>(p, x, expert_ids, x_active_mask, nullptr, expand_q, dynamic_scales, assist_info,
-                            ep_recv_counts, expert_token_nums, expanded_row_idx, s);
+  const GatherMeta m = make_meta(p, ws, expert_scales, expand_scales, assist_info, ep_recv_counts,
+                                 expert_token_nums, expanded_row_idx);
+  if (small_path(p)) return small_impl<true>(p, x, expert_ids, x_active_mask, nullptr, expand_q, dynamic_scales, m, s);
   st = layout_impl(p, expert_ids, x_active_mask, ws, s);
   if (st != MDC_OK) return st;
-  return gather_q_impl(p, x, expand_q, dynamic_scales, assist_info, ep_recv_counts, expert_token_nums,
-                       expanded_row_idx, ws, s);
+  return gather_q_impl(p, x, m, expand_q, dynamic_scales, s);
 }
 
-mdc_status mdc_combine_workspace_size(const mdc_shape* shape, size_t* bytes) {
+mdc_status mdc_combine_workspace(const mdc_shape* shape, size_t* bytes) {
   if (bytes == nullptr) return MDC_ERR_NULLPTR;
   const mdc_status st = check_shape(shape);
   if (st != MDC_OK) return st;
-  *bytes = 0;
+  *bytes = combine_workspace_bytes(shape);
   return MDC_OK;
+}
+
+mdc_status mdc_combine_workspace_size(const mdc_shape* shape, size_t* bytes) {
+  return mdc_combine_workspace(shape, bytes);
 }
 
 mdc_status mdc_combine(const mdc_shape* shape, const void* const* expand_x, const int32_t* const* assist_info,
                        const int32_t* const* ep_recv_counts, const int32_t* expanded_row_idx,
                        const int32_t* expert_ids, const float* expert_scales, const uint8_t* x_active_mask,
-                       const void* shared_expert_x, const void* ori_x, void* x_out, void* workspace,
-                       size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  mdc_status st = check_shape(shape);
-  if (st != MDC_OK) return st;
-  const int W = shape->world;
-  if (W > MDC_MAX_COMBINE_WORLD) return MDC_ERR_INVALID;
-  const int BS = shape->bs;
-  if (BS == 0) return MDC_OK;
-  if (expand_x == nullptr || assist_info == nullptr || ep_recv_counts == nullptr) return MDC_ERR_NULLPTR;
-  if (expanded_row_idx == nullptr || expert_ids == nullptr || expert_scales == nullptr || x_out == nullptr)
-    return MDC_ERR_NULLPTR;
-  CombineTables tabs;
-  std::memset(&tabs, 0, sizeof(tabs));
-  for (int j = 0; j < W; ++j) {
-    if (ep_recv_counts[j] == nullptr) return MDC_ERR_NULLPTR;
-    if (shape->capacity > 0 && (expand_x[j] == nullptr || assist_info[j] == nullptr)) return MDC_ERR_NULLPTR;
-    if (!aligned16(expand_x[j])) return MDC_ERR_INVALID;
-    tabs.y[j] = static_cast<const v4u*>(expand_x[j]);
-    tabs.assist[j] = assist_info[j];
-    tabs.counts[j] = ep_recv_counts[j];
-  }
-  if (shape->copy_experts > 0 && ori_x == nullptr) return MDC_ERR_NULLPTR;
-  if (!aligned16(shared_expert_x) || !aligned16(x_out) || !aligned16(ori_x)) return MDC_ERR_INVALID;
-  const int K = shape->topk;
-  const int E = shape->num_experts;
-  const int L = E / W;
-  const int nvec = shape->hidden / 8;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const v4u* sh = static_cast<const v4u*>(shared_expert_x);
-  v4u* out = static_cast<v4u*>(x_out);
-  const v4u* ori = static_cast<const v4u*>(ori_x);
-  const int r = shape->rank;
-  const int64_t A = shape->capacity;
-  (void)hipGetLastError();
-  if (K <= 8) {
-    const int ntiles = (nvec + 64 * kCombineVec - 1) / (64 * kCombineVec);
-    const unsigned n_items = (unsigned)((int64_t)BS * ntiles);
-    const dim3 grid((n_items + MDC_COMBINE_WAVES - 1) / MDC_COMBINE_WAVES), block(64 * MDC_COMBINE_WAVES);
-    if (sh)
-      hipLaunchKernelGGL((k_combine<8, kCombineVec, true>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
-                         expert_scales, x_active_mask, sh, ori, out, r, W, K, E, L, A, nvec, ntiles, n_items,
-                         shape->mask_per_route, shape->zero_experts, shape->copy_experts);
-    else
-      hipLaunchKernelGGL((k_combine<8, kCombineVec, false>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
-                         expert_scales, x_active_mask, sh, ori, out, r, W, K, E, L, A, nvec, ntiles, n_items,
-                         shape->mask_per_route, shape->zero_experts, shape->copy_experts);
-  } else {
-    const int ntiles = (nvec + 63) / 64;
-    const unsigned n_items = (unsigned)((int64_t)BS * ntiles);
-    const dim3 grid((n_items + MDC_COMBINE_WAVES - 1) / MDC_COMBINE_WAVES), block(64 * MDC_COMBINE_WAVES);
-    if (sh)
-      hipLaunchKernelGGL((k_combine<16, 1, true>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
-                         expert_scales, x_active_mask, sh, ori, out, r, W, K, E, L, A, nvec, ntiles, n_items,
-                         shape->mask_per_route, shape->zero_experts, shape->copy_experts);
-    else
-      hipLaunchKernelGGL((k_combine<16, 1, false>), grid, block, 0, s, tabs, expanded_row_idx, expert_ids,
-                         expert_scales, x_active_mask, sh, ori, out, r, W, K, E, L, A, nvec, ntiles, n_items,
-                         shape->mask_per_route, shape->zero_experts, shape->copy_experts);
-  }
-  return launched();
+                       const float* const* expand_scales, const void* shared_expert_x, const void* ori_x,
+                       int64_t* performance_info, void* x_out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return combine_impl(shape, expand_x, assist_info, ep_recv_counts, expanded_row_idx, expert_ids, expert_scales,
+                      x_active_mask, expand_scales, shared_expert_x, ori_x, performance_info, x_out, workspace,
+                      workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

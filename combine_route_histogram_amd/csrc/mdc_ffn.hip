@@ -4,8 +4,6 @@
 // Source: "PTO MegaMoE Dispatch + Combine Fusion Example", GMM1 / SwiGLU /
 // GMM2 stages and the per-token dynamic quantisation between them.
 
-#include <cstdlib>
-
 #include "mdc_common.h"
 
 namespace {
@@ -26,8 +24,8 @@ namespace {
 // 128 bytes deep; the output tile leaves through LDS as whole rows.  By
 // default GMM1, the quantisation of g and GMM2 run as three stream-ordered
 // kernels, each GEMM persistent and loading its next tile's first k stage
-// before the current tile's output stores; MDC_FFN_PIPELINE=1 runs them as
-// one persistent kernel with ready counters between them (k_ffn_fused).
+// before the current tile's output stores; with MDC_FLAG_FFN_PIPELINE they run
+// as one persistent kernel with ready counters between them (k_ffn_fused).
 // ---------------------------------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -81,12 +79,14 @@ __device__ int64_t plan_scan_pair(int64_t a, int64_t b, int64_t* wsum, int64_t& 
   return excl;
 }
 
-// sync_words (optional, the fused kernel's): [0] queue head, [1] error,
+// sync_words (optional, the fused kernel's): [0] queue head, [1] unused,
 // done1 at [2, 2 + MT), ready at [2 + stride, 2 + stride + MT); amax_bits
-// for the rows in use.  All of them are zeroed here.
+// for the rows in use.  All of them are zeroed here, and so is the
+// workspace's status block.
 __global__ __launch_bounds__(kPlanThreads) void k_ffn_plan(const int64_t* __restrict__ expert_nums, int L, int64_t A,
                                                            int4* __restrict__ tiles, int* __restrict__ sync_words,
-                                                           int stride, uint32_t* __restrict__ amax_bits) {
+                                                           int stride, uint32_t* __restrict__ amax_bits,
+                                                           mdc_device_status* __restrict__ status) {
   __shared__ int64_t wsum[kPlanThreads / 64 + 1];
   const int tid = threadIdx.x;
   const int e0 = 2 * tid, e1 = 2 * tid + 1;
@@ -117,7 +117,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_ffn_plan(const int64_t* __rest
       tiles[1 + slot + j] = int4{e, lo + j * kFfnBM, hi, (pos << 8) | size};
     }
   }
-  if (tid == 0) tiles[0] = int4{(int)nm, 0, 0, 0};
+  if (tid == 0) {
+    tiles[0] = int4{(int)nm, 0, 0, 0};
+    *status = mdc_device_status{0, 0, 0, 0};
+  }
   if (sync_words != nullptr) {
     const int MT = (int)nm;
     if (tid < 2) sync_words[tid] = 0;
@@ -729,8 +732,22 @@ struct FfnSync {
   int* done1;             // [MT] GMM1 tiles finished per m-tile
   int* ready;             // [MT] 1 once the m-tile's g rows are quantised
   uint32_t* amax_bits;    // [rows] max |g| per row (fp32 bits)
-  int* error;             // set if a wait ran out of its bound (never expected)
+  mdc_device_status* status;   // wait_timeouts counts the waits that ran out of their bound
 };
+
+// A GMM2 tile whose wait ran out does not read its rows of q2: its output
+// tile is written as quiet NaN, so that a silently wrong y cannot result.
+__device__ void ffn_poison_tile(const FfnGemm& g, int4 ti, int nt) {
+  const int row0 = ti.y, row_end = min(ti.z, ti.y + kFfnBM);
+  const int n0 = nt * kFfnBW, n1 = min(g.Nout, n0 + kFfnBW);
+  const int cols = n1 - n0;   // a multiple of 8 (Nout is a multiple of 128)
+  const int units = cols / 8;
+  const v4u nan = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+  for (int i = threadIdx.x; i < (row_end - row0) * units; i += kFfnThreads) {
+    const int r = row0 + i / units, c = n0 + (i % units) * 8;
+    *reinterpret_cast<v4u*>(g.out + (int64_t)r * g.Nout + c) = nan;
+  }
+}
 
 // Quantises the g rows [r0, r1) of one m-tile (the last GMM1 tile of the
 // m-tile does it): codes clamp(rint(g * (127 / amax)), -127, 127) and scale
@@ -781,7 +798,7 @@ __device__ void ffn_quant_mtile(const uint16_t* __restrict__ gsrc, int ncols, in
   }
 }
 
-// NEXT-3 stage of the [PTO] fused pipeline: GMM1 + SwiGLU, the dynamic
+// A stage of the [PTO] fused pipeline: GMM1 + SwiGLU, the dynamic
 // quantisation of g and GMM2 in one persistent kernel.  Workgroups take
 // tiles from one queue: every GMM1 tile first (plan order), then every GMM2
 // tile (m-tiles in the same group order).  A GMM1 tile stores its g tile,
@@ -790,8 +807,8 @@ __device__ void ffn_quant_mtile(const uint16_t* __restrict__ gsrc, int ncols, in
 // g rows and sets ready[m] ([PTO] ready flags between GMM1 and GMM2).  A
 // GMM2 tile waits for ready[m].  Every GMM1 tile leaves the queue before any
 // GMM2 tile, and GMM1 tiles wait on nothing, so every wait ends; each wait
-// is also bounded by spin_limit polls (error[0] is set if one ever runs
-// out).  The XCDs' L2s are not coherent with each other: writes are
+// is also bounded by spin_limit polls (one that runs out is counted in the
+// status block's wait_timeouts and its tile written as NaN).  The XCDs' L2s are not coherent with each other: writes are
 // published with agent-scope release fences (an L2 write-back, issued by
 // one thread per workgroup); the quantiser reads g after one acquire (an L2
 // invalidate) per m-tile, and GMM2 reads q2 and s2 with agent-coherent loads
@@ -849,15 +866,22 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_fused(FfnGemm g1, FfnGemm g
       if (tid == 0) {
         // poll with relaxed (agent-coherent) loads
         int n = 0;
+        bool late = false;
         while (__hip_atomic_load(sync.ready + mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
           if (++n >= spin_limit) {
-            atomicExch(sync.error, 1);
+            late = true;
+            atomicAdd(&sync.status->wait_timeouts, 1);
             break;
           }
           __builtin_amdgcn_s_sleep(2);
         }
+        bcast[1] = late;
       }
       __syncthreads();
+      if (bcast[1]) {
+        ffn_poison_tile(g2, tab.at(mt), nt);
+        continue;
+      }
       // q2 and s2 are read with agent-coherent loads (no L2 invalidate)
       ffn_tile<false, true, false>(g2, tab.at(mt), nt, sm, nullptr, s0, false, s0, no_next);
     }
@@ -873,14 +897,15 @@ struct FfnPlan {
   size_t off_q1, off_s1, off_g, off_q2, off_s2, off_tiles, off_amax, off_sync, bytes;
 };
 
+// Workspace: [status block][q1][s1][g][q2][s2][m-tile table][amax][sync words].
 FfnPlan make_ffn_plan(const mdc_shape* sh, int inter_n) {
   FfnPlan f;
   f.A = sh->capacity;
   f.H = sh->hidden;
   f.N = inter_n;
   f.L = sh->num_experts / sh->world;
-  f.off_q1 = 0;
-  f.off_s1 = round_up((size_t)f.A * f.H, 256);
+  f.off_q1 = MDC_STATUS_BYTES;
+  f.off_s1 = f.off_q1 + round_up((size_t)f.A * f.H, 256);
   f.off_g = f.off_s1 + round_up((size_t)f.A * 4, 256);
   f.off_q2 = f.off_g + round_up((size_t)f.A * (f.N / 2) * 2, 256);
   f.off_s2 = f.off_q2 + round_up((size_t)f.A * (f.N / 2), 256);
@@ -890,39 +915,39 @@ FfnPlan make_ffn_plan(const mdc_shape* sh, int inter_n) {
   f.off_amax = f.off_tiles + round_up(max_mtiles * sizeof(int4), 256);
   f.off_sync = f.off_amax + round_up((size_t)f.A * 4, 256);
   f.bytes = f.off_sync + round_up((2 + 2 * max_mtiles) * sizeof(int), 256);
-  if (f.bytes == 0) f.bytes = 256;
   return f;
 }
 
 mdc_status check_ffn(const mdc_shape* sh, int inter_n) {
   const mdc_status st = check_shape(sh);
   if (st != MDC_OK) return st;
-  if (inter_n <= 0 || (inter_n % (2 * kFfnOutAlign)) != 0) return MDC_ERR_INVALID;
-  if ((sh->hidden % kFfnOutAlign) != 0) return MDC_ERR_INVALID;
+  if (inter_n <= 0) return MDC_ERR_INVALID;
+  if ((inter_n % (2 * kFfnOutAlign)) != 0) return MDC_ERR_UNSUPPORTED;
+  if ((sh->hidden % kFfnOutAlign) != 0) return MDC_ERR_UNSUPPORTED;
   // one expert's weight matrix (N x H or H x N/2 bytes) is addressed with 32-bit offsets
-  if ((int64_t)inter_n * sh->hidden > INT32_MAX) return MDC_ERR_INVALID;
+  if ((int64_t)inter_n * sh->hidden > INT32_MAX) return MDC_ERR_UNSUPPORTED;
   // tiles of both GEMMs (and the work-queue tickets) are counted in 32 bits
   const int64_t L = sh->num_experts / sh->world;
   const int64_t max_mtiles = 2 + sh->capacity / kFfnBM + L;
   const int64_t per_mtile = inter_n / kFfnBW + (sh->hidden + kFfnBW - 1) / kFfnBW;
-  if (max_mtiles * per_mtile + 65536 > INT32_MAX) return MDC_ERR_INVALID;
+  if (max_mtiles * per_mtile + 65536 > INT32_MAX) return MDC_ERR_UNSUPPORTED;
   return MDC_OK;
 }
 
 // GMM1 -> quantise g -> GMM2 runs as three stream-ordered kernels, or as
-// the one persistent k_ffn_fused launch when MDC_FFN_PIPELINE=1 is set in the
-// environment (the results are identical; the stream-ordered GEMMs load
-// each next tile ahead and measure faster).
-bool ffn_pipeline_enabled() {
-  const char* v = getenv("MDC_FFN_PIPELINE");   // read per call: cheap next to a GEMM launch
-  return v != nullptr && strcmp(v, "1") == 0;
+// the one persistent k_ffn_fused launch with MDC_FLAG_FFN_PIPELINE (the
+// results are identical; the stream-ordered GEMMs load each next tile ahead
+// and measure faster).  Polls of a GMM2 tile's wait before it gives up:
+// 2^24, or 2^s with s from the flags' spin field.
+int ffn_spin_limit(uint32_t flags) {
+  const uint32_t sft = (flags & MDC_FLAG_SPIN_MASK) >> MDC_FLAG_SPIN_SHIFT;
+  return sft != 0 ? (1 << (sft > 30 ? 30 : sft)) : (1 << 24);
 }
-// polls of a GMM2 tile's wait before it gives up and flags an error
-constexpr int kFfnSpinLimit = 1 << 24;
 
-mdc_status ffn_impl(const FfnPlan& f, const void* expand_x, const int8_t* expand_q, const float* dyn_scale,
-                    const int64_t* expert_token_nums, const int8_t* w1, const float* w1_scale, const int8_t* w2,
-                    const float* w2_scale, void* y, char* ws, hipStream_t s) {
+mdc_status ffn_impl(const FfnPlan& f, uint32_t flags, const void* expand_x, const int8_t* expand_q,
+                    const float* dyn_scale, const int64_t* expert_token_nums, const int8_t* w1, const float* w1_scale,
+                    const int8_t* w2, const float* w2_scale, void* y, char* ws, hipStream_t s) {
+  mdc_device_status* status = reinterpret_cast<mdc_device_status*>(ws);
   int8_t* q1 = reinterpret_cast<int8_t*>(ws + f.off_q1);
   float* s1 = reinterpret_cast<float*>(ws + f.off_s1);
 
@@ -947,19 +972,18 @@ mdc_status ffn_impl(const FfnPlan& f, const void* expand_x, const int8_t* expand
   int* sync_words = reinterpret_cast<int*>(ws + f.off_sync);
   const FfnGemm gemm1{q1, s1, w1, w1_scale, g, f.H, f.N, f.N / 2};
   const FfnGemm gemm2{q2, s2, w2, w2_scale, static_cast<uint16_t*>(y), f.N / 2, f.H, f.H};
-  const bool fused = ffn_pipeline_enabled();
+  const bool fused = (flags & MDC_FLAG_FFN_PIPELINE) != 0;
   const int max_mtiles = (int)(2 + f.A / kFfnBM + f.L);
   hipLaunchKernelGGL(k_ffn_plan, dim3(1), dim3(kPlanThreads), 0, s, expert_token_nums, f.L, f.A, tiles,
-                     fused ? sync_words : nullptr, max_mtiles, amax);
+                     fused ? sync_words : nullptr, max_mtiles, amax, status);
   const bool tab = max_mtiles <= kFfnTabCache;   // the m-tile table fits in LDS
   if (fused) {
-    const FfnSync sync{sync_words, sync_words + 2, sync_words + 2 + max_mtiles, amax, sync_words + 1};
+    const FfnSync sync{sync_words, sync_words + 2, sync_words + 2 + max_mtiles, amax, status};
+    const int spin = ffn_spin_limit(flags);
     if (tab)
-      hipLaunchKernelGGL(k_ffn_fused<true>, dim3(g1), dim3(kFfnThreads), 0, s, gemm1, gemm2, tiles, sync,
-                         kFfnSpinLimit);
+      hipLaunchKernelGGL(k_ffn_fused<true>, dim3(g1), dim3(kFfnThreads), 0, s, gemm1, gemm2, tiles, sync, spin);
     else
-      hipLaunchKernelGGL(k_ffn_fused<false>, dim3(g1), dim3(kFfnThreads), 0, s, gemm1, gemm2, tiles, sync,
-                         kFfnSpinLimit);
+      hipLaunchKernelGGL(k_ffn_fused<false>, dim3(g1), dim3(kFfnThreads), 0, s, gemm1, gemm2, tiles, sync, spin);
   } else {
     if (tab)
       hipLaunchKernelGGL((k_ffn_gemm<true, true>), dim3(g1), dim3(kFfnThreads), 0, s, gemm1, tiles);
@@ -978,12 +1002,16 @@ mdc_status ffn_impl(const FfnPlan& f, const void* expand_x, const int8_t* expand
 
 extern "C" {
 
-mdc_status mdc_ffn_workspace_size(const mdc_shape* shape, int32_t inter_n, size_t* bytes) {
+mdc_status mdc_ffn_workspace(const mdc_shape* shape, int32_t inter_n, size_t* bytes) {
   if (bytes == nullptr) return MDC_ERR_NULLPTR;
   const mdc_status st = check_ffn(shape, inter_n);
   if (st != MDC_OK) return st;
   *bytes = make_ffn_plan(shape, inter_n).bytes;
   return MDC_OK;
+}
+
+mdc_status mdc_ffn_workspace_size(const mdc_shape* shape, int32_t inter_n, size_t* bytes) {
+  return mdc_ffn_workspace(shape, inter_n, bytes);
 }
 
 mdc_status mdc_ffn(const mdc_shape* shape, int32_t inter_n, const void* expand_x, const int64_t* expert_token_nums,
@@ -998,8 +1026,8 @@ mdc_status mdc_ffn(const mdc_shape* shape, int32_t inter_n, const void* expand_x
     return MDC_ERR_NULLPTR;
   if (!aligned16(expand_x) || !aligned16(w1) || !aligned16(w2) || !aligned16(y)) return MDC_ERR_INVALID;
   if (workspace_bytes < f.bytes) return MDC_ERR_WORKSPACE;
-  return ffn_impl(f, expand_x, nullptr, nullptr, expert_token_nums, w1, w1_scale, w2, w2_scale, y,
-                  static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  return ffn_impl(f, (uint32_t)shape->flags, expand_x, nullptr, nullptr, expert_token_nums, w1, w1_scale, w2,
+                  w2_scale, y, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 mdc_status mdc_ffn_quant_input(const mdc_shape* shape, int32_t inter_n, const int8_t* expand_q,
@@ -1015,8 +1043,8 @@ mdc_status mdc_ffn_quant_input(const mdc_shape* shape, int32_t inter_n, const in
     return MDC_ERR_NULLPTR;
   if (!aligned16(expand_q) || !aligned16(w1) || !aligned16(w2) || !aligned16(y)) return MDC_ERR_INVALID;
   if (workspace_bytes < f.bytes) return MDC_ERR_WORKSPACE;
-  return ffn_impl(f, nullptr, expand_q, dynamic_scales, expert_token_nums, w1, w1_scale, w2, w2_scale, y,
-                  static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  return ffn_impl(f, (uint32_t)shape->flags, nullptr, expand_q, dynamic_scales, expert_token_nums, w1, w1_scale,
+                  w2, w2_scale, y, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 

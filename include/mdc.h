@@ -31,9 +31,10 @@
  *   - A route is (s, t, k): source rank s, token t, top-k slot k.
  *   - Argument errors are reported synchronously by the return value, before
  *     anything is enqueued (codes mirror [CV4] Return Value: null tensor,
- *     unsupported type/shape, value out of range).  Conditions found in the
- *     data (ids outside [0, E), too many rows for the capacity) are not
- *     errors: see each call.
+ *     malformed arguments, values outside the supported range).  Conditions
+ *     found in the data (ids outside [0, E+Z+C), too many rows for the
+ *     capacity, a pipeline wait that ran out) are not errors: the device
+ *     reports them in the workspace's status block (mdc_device_status).
  *   - Results are bitwise deterministic: no floating-point atomics, fixed
  *     summation order ([CV4] Constraints, deterministic computation).
  *   - Calls that share a workspace must not overlap (use one stream or order
@@ -49,19 +50,51 @@
 extern "C" {
 #endif
 
-#define MDC_ABI_VERSION 2
+#define MDC_ABI_VERSION 3
 #define MDC_MAX_TOPK 16        /* 0 < K <= 16 ([CV4] shape-variable table) */
 #define MDC_MAX_LOCAL_EXPERTS 2048
 #define MDC_MAX_COMBINE_WORLD 64 /* W limit of mdc_combine (pointer tables travel by value) */
 
 typedef enum {
     MDC_OK = 0,
-    MDC_ERR_NULLPTR = 1,    /* a required pointer is NULL (cf. ACLNN_ERR_PARAM_NULLPTR) */
-    MDC_ERR_INVALID = 2,    /* shape, alignment or value outside the supported range
-                               (cf. ACLNN_ERR_PARAM_INVALID / ACLNN_ERR_INNER_TILING_ERROR) */
-    MDC_ERR_WORKSPACE = 3,  /* workspace smaller than the size query returned */
-    MDC_ERR_HIP = 4         /* a HIP kernel launch failed */
+    MDC_ERR_NULLPTR = 1,     /* a required pointer is NULL (cf. ACLNN_ERR_PARAM_NULLPTR, 161001) */
+    MDC_ERR_INVALID = 2,     /* the arguments do not describe a well-formed problem: a misaligned
+                                tensor, shape fields inconsistent with each other (E % W != 0,
+                                H % 8 != 0, rank outside [0, W), a negative size), unknown flag
+                                bits, a nonzero reserved field (cf. ACLNN_ERR_PARAM_INVALID, 161002) */
+    MDC_ERR_UNSUPPORTED = 3, /* a well-formed problem outside the range this library supports:
+                                K > 16, L > 2048, W > 64 for combine, H > 8192 for the quantised
+                                dispatch, FFN widths that are not multiples of its tiles, sizes
+                                past the 32-bit index limits (cf. ACLNN_ERR_INNER_TILING_ERROR,
+                                561002: shape or parameter value outside the supported range) */
+    MDC_ERR_WORKSPACE = 4,   /* workspace smaller than the size query returned */
+    MDC_ERR_HIP = 5          /* a HIP kernel launch failed */
 } mdc_status;
+
+/* Flags (mdc_shape.flags). */
+#define MDC_FLAG_FFN_PIPELINE 0x1u   /* mdc_ffn*: run GMM1, the quantisation of g and GMM2 as one
+                                        persistent kernel with ready flags between them */
+#define MDC_FLAG_SPIN_SHIFT 8        /* bits 8..12: if nonzero, s, the pipeline's bounded waits give
+                                        up after 2^s polls instead of 2^24 (a test of the time-out
+                                        path forces it with a small s) */
+#define MDC_FLAG_SPIN_MASK (0x1Fu << MDC_FLAG_SPIN_SHIFT)
+
+/* Device status block.  The first MDC_STATUS_BYTES bytes of the dispatch and FFN
+ * workspaces hold one mdc_device_status, which each call rewrites on its stream
+ * ([CV4] Return Value: argument errors are returned by the call; conditions
+ * found in the data are not errors, so the device reports them here instead).
+ * Read it (e.g. copy the 16 bytes to the host) after the call's work has
+ * completed; the next call on the same workspace overwrites it. */
+#define MDC_STATUS_BYTES 256
+typedef struct {
+    int32_t dropped_ids;    /* dispatch: active routes of all W sources whose expert id lies
+                               outside [0, E + Z + C) (never sent anywhere, no part in combine) */
+    int32_t overflow_rows;  /* dispatch: max(0, R - A): received rows not written for lack of
+                               capacity */
+    int32_t wait_timeouts;  /* FFN pipeline: GMM2 tiles whose bounded wait for their quantised
+                               rows ran out (their y rows are written as NaN) */
+    int32_t reserved;
+} mdc_device_status;
 
 /* Problem shape.  `rank` is the destination rank for dispatch and the source
  * rank whose tokens are combined for combine. */
@@ -83,7 +116,7 @@ typedef struct {
     int32_t copy_experts;   /* C >= 0: ids in [E+Z, E+Z+C) are copy experts ([CV4]
                                copyExpertNum): never dispatched; output ori_x[t] in
                                combine.  K <= E + Z + C. */
-    int32_t reserved;       /* must be 0 */
+    int32_t flags;          /* MDC_FLAG_* bits; the others must be 0 */
 } mdc_shape;
 
 const char* mdc_status_string(mdc_status status);
@@ -121,9 +154,17 @@ int32_t mdc_abi_version(void);
  *                     -1 if that row is >= A.  Entries of routes not sent to d
  *                     are left untouched, so the W dispatches of one step fill
  *                     disjoint parts of one shared table.
- *   Only rows [0, min(R, A)) of expand_x / assist_info are written; rows with
- *   index >= A are dropped while the counts still include them, so overflow
- *   shows as ep_recv_counts[L*W-1] > A.  Rows past the total are untouched.
+ *   expand_scales     [A] fp32 or NULL: row i = expert_scales[s][t][k] of the
+ *                     route at row i, the weight that travels with the row
+ *                     ([CV4] parameter table: expandScalesOptional, the
+ *                     dispatch's expandScales output, 1D of shape (A,) in the
+ *                     A2 notes).  Written iff expert_scales is given.
+ *   workspace status  the dispatch fills the workspace's mdc_device_status
+ *                     (dropped_ids, overflow_rows; wait_timeouts = 0).
+ *   Only rows [0, min(R, A)) of expand_x / assist_info / expand_scales are
+ *   written; rows with index >= A are dropped while the counts still include
+ *   them, so overflow shows as ep_recv_counts[L*W-1] > A (and in
+ *   overflow_rows).  Rows past the total are untouched.
  *
  * Inputs
  *   x                 [W][BS][H] bf16, the virtual source ranks' tokens.
@@ -131,15 +172,22 @@ int32_t mdc_abi_version(void);
  *   x_active_mask     [W][BS] uint8 (nonzero = active), or [W][BS][K] with
  *                     mask_per_route, or NULL (all active); any order of active
  *                     and inactive entries is accepted.
+ *   expert_scales     [W][BS][K] fp32, the routes' weights, or NULL (then
+ *                     expand_scales must be NULL too).
  *
  * The call is split in two stages that may be enqueued separately (same
  * stream, same workspace, in this order); mdc_dispatch enqueues both.
  *   mdc_dispatch_layout  route filter, histogram and stable ranks
  *                        ([PTO] FrontReorder Stage); writes only the workspace.
- *   mdc_dispatch_gather  scan, rows, triplets, inverse index, epRecvCounts and
- *                        expertTokenNums ([PTO] Dispatch Stage), from the
- *                        workspace the layout stage filled.
+ *   mdc_dispatch_gather  scan, rows, triplets, inverse index, epRecvCounts,
+ *                        expertTokenNums, expandScales and the status block
+ *                        ([PTO] Dispatch Stage), from the workspace the
+ *                        layout stage filled.
+ * The workspace size comes from mdc_dispatch_workspace ([CV4] Function
+ * Prototype: the first phase returns the workspace size);
+ * mdc_dispatch_workspace_size is the same query under its earlier name.
  * ------------------------------------------------------------------------ */
+mdc_status mdc_dispatch_workspace(const mdc_shape* shape, size_t* bytes);
 mdc_status mdc_dispatch_workspace_size(const mdc_shape* shape, size_t* bytes);
 
 mdc_status mdc_dispatch_layout(const mdc_shape* shape,
@@ -150,11 +198,13 @@ mdc_status mdc_dispatch_layout(const mdc_shape* shape,
 
 mdc_status mdc_dispatch_gather(const mdc_shape* shape,
                                const void* x,
+                               const float* expert_scales,
                                void* expand_x,
                                int32_t* assist_info,
                                int32_t* ep_recv_counts,
                                int64_t* expert_token_nums,
                                int32_t* expanded_row_idx,
+                               float* expand_scales,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
 
@@ -162,11 +212,13 @@ mdc_status mdc_dispatch(const mdc_shape* shape,
                         const void* x,
                         const int32_t* expert_ids,
                         const uint8_t* x_active_mask,
+                        const float* expert_scales,
                         void* expand_x,
                         int32_t* assist_info,
                         int32_t* ep_recv_counts,
                         int64_t* expert_token_nums,
                         int32_t* expanded_row_idx,
+                        float* expand_scales,
                         void* workspace, size_t workspace_bytes,
                         void* stream);
 
@@ -176,22 +228,26 @@ mdc_status mdc_dispatch(const mdc_shape* shape,
  * FrontReorder Stage: quantised token rows carrying their scale).
  *
  * As mdc_dispatch / mdc_dispatch_gather (same placement, triplets, inverse
- * index and counts, same workspace and layout stage), but each received row
- * is the int8 quantisation of its source token's row, decided in fp32:
- * amax = max|x|, codes clamp(rint(x * (127 / amax)), -127, 127), and
- * dynamic_scales[row] = amax / 127 (a zero row gives codes 0 and scale 0).
+ * index, counts, expand_scales and status, same workspace and layout stage),
+ * but each received row is the int8 quantisation of its source token's row,
+ * decided in fp32: amax = max|x|, codes clamp(rint(x * (127 / amax)), -127,
+ * 127), and dynamic_scales[row] = amax / 127 (a zero row gives codes 0 and
+ * scale 0).
  *   expand_q        [A][H] int8 (16-byte aligned)
  *   dynamic_scales  [A] fp32
- * H <= 8192 (a whole row is held in one wavefront's registers).
+ * H <= 8192 (a whole row is held in one wavefront's registers; larger H
+ * returns MDC_ERR_UNSUPPORTED).
  * ------------------------------------------------------------------------ */
 mdc_status mdc_dispatch_quant_gather(const mdc_shape* shape,
                                      const void* x,
+                                     const float* expert_scales,
                                      int8_t* expand_q,
                                      float* dynamic_scales,
                                      int32_t* assist_info,
                                      int32_t* ep_recv_counts,
                                      int64_t* expert_token_nums,
                                      int32_t* expanded_row_idx,
+                                     float* expand_scales,
                                      void* workspace, size_t workspace_bytes,
                                      void* stream);
 
@@ -199,12 +255,14 @@ mdc_status mdc_dispatch_quant(const mdc_shape* shape,
                               const void* x,
                               const int32_t* expert_ids,
                               const uint8_t* x_active_mask,
+                              const float* expert_scales,
                               int8_t* expand_q,
                               float* dynamic_scales,
                               int32_t* assist_info,
                               int32_t* ep_recv_counts,
                               int64_t* expert_token_nums,
                               int32_t* expanded_row_idx,
+                              float* expand_scales,
                               void* workspace, size_t workspace_bytes,
                               void* stream);
 
@@ -214,7 +272,7 @@ mdc_status mdc_dispatch_quant(const mdc_shape* shape,
  *
  * For source rank r = shape->rank and every token t:
  *     xOut[t] = bf16_rne( sum over k = 0..K-1 ascending, route present, of
- *                         ( s[t][k]*y[t][k] + s[t][k]*sharedX[t] ) )
+ *                         ( w[t][k]*y[t][k] + w[t][k]*sharedX[t] ) )
  * with an fp32 accumulator starting at +0.0 and every product and sum
  * rounded to fp32 separately (no fused multiply-add), then rounded to bf16
  * nearest-even ([TL] combine: fp32 accumulate, CAST_RINT).  The shared term
@@ -225,9 +283,14 @@ mdc_status mdc_dispatch_quant(const mdc_shape* shape,
  *     j = e / L, i.e. expand_x[j]: data returns along the dispatch path
  *     ([CV4] Function note and API matching constraints).  The route is
  *     present iff that row is < min(ep_recv_counts[j][L*W-1], A) and
- *     assist_info[j] at that row holds (r, t, k);
- *   - E <= e < E+Z (zero expert): present with y = 0;
- *   - E+Z <= e < E+Z+C (copy expert): present with y = ori_x[t];
+ *     assist_info[j] at that row holds (r, t, k).  Its weight w[t][k] is
+ *     expand_scales[j][row] when the expand_scales table is given (the
+ *     dispatch's expandScales, [CV4] expandScalesOptional), else
+ *     expert_scales[t][k]; the two are equal when the table comes from the
+ *     dispatch of these routes;
+ *   - E <= e < E+Z (zero expert): present with y = 0 and w = expert_scales[t][k];
+ *   - E+Z <= e < E+Z+C (copy expert): present with y = ori_x[t] and
+ *     w = expert_scales[t][k];
  *   - otherwise the route contributes nothing.
  * A token with no present route gives a +0.0 row.
  *
@@ -240,15 +303,31 @@ mdc_status mdc_dispatch_quant(const mdc_shape* shape,
  *                     dispatches filled.
  *   expert_ids        [BS][K] int32 of rank r.
  *   expert_scales     [BS][K] fp32 of rank r.
- *   x_active_mask     [BS] uint8 of rank r, or NULL (all active).
+ *   x_active_mask     [BS] uint8 of rank r ([BS][K] with mask_per_route), or
+ *                     NULL (all active).
+ *   expand_scales     host array of W device pointers to rank j's [A] fp32
+ *                     expand_scales, or NULL.
  *   shared_expert_x   [BS][H] bf16, or NULL.
  *   ori_x             [BS][H] bf16, rank r's unprocessed tokens ([CV4]
  *                     oriXOptional); required when copy_experts > 0, else
  *                     may be NULL.
+ *   performance_info  [W] int64 or NULL ([CV4] Function: communication
+ *                     latency collection; parameter table: performanceInfoOptional,
+ *                     per-rank wait for data in microseconds, accumulated by
+ *                     every call, cleared by the caller).  With virtual ranks
+ *                     the wait for rank j's data is the time from the start
+ *                     of the call to the arrival of the last row this call
+ *                     reads from rank j (the device's constant-rate real-time
+ *                     clock), rounded up to whole microseconds and added to
+ *                     performance_info[j]; ranks the call reads nothing from
+ *                     get 0.  It needs the workspace; without it the
+ *                     workspace may be NULL.
  * Output
  *   x_out             [BS][H] bf16.
- * W must be <= MDC_MAX_COMBINE_WORLD.
+ * W must be <= MDC_MAX_COMBINE_WORLD.  mdc_combine_workspace returns the
+ * workspace size (mdc_combine_workspace_size is its earlier name).
  * ------------------------------------------------------------------------ */
+mdc_status mdc_combine_workspace(const mdc_shape* shape, size_t* bytes);
 mdc_status mdc_combine_workspace_size(const mdc_shape* shape, size_t* bytes);
 
 mdc_status mdc_combine(const mdc_shape* shape,
@@ -259,8 +338,10 @@ mdc_status mdc_combine(const mdc_shape* shape,
                        const int32_t* expert_ids,
                        const float* expert_scales,
                        const uint8_t* x_active_mask,
+                       const float* const* expand_scales,
                        const void* shared_expert_x,
                        const void* ori_x,
+                       int64_t* performance_info,
                        void* x_out,
                        void* workspace, size_t workspace_bytes,
                        void* stream);
@@ -295,15 +376,21 @@ mdc_status mdc_combine(const mdc_shape* shape,
  *   untouched).  inter_n = N must be a positive multiple of 256, H a
  *   multiple of 128 and N * H < 2^31 (one expert's weight matrix is addressed
  *   with 32-bit offsets); the GEMM tiles, (A / 256 + L + 2) * (N / 256 +
- *   ceil(H / 256)), are counted in 32 bits and must stay below 2^31.  The workspace holds q1, s1, g, q2, s2, the
- *   m-tile table of the grouped GEMMs and the pipeline's ready counters.
+ *   ceil(H / 256)), are counted in 32 bits and must stay below 2^31 (else
+ *   MDC_ERR_UNSUPPORTED).  The workspace (size from mdc_ffn_workspace;
+ *   mdc_ffn_workspace_size is its earlier name) holds the status block, q1,
+ *   s1, g, q2, s2, the m-tile table of the grouped GEMMs and the pipeline's
+ *   ready counters.
  *
- * GMM1, the quantisation of g and GMM2 run as three stream-ordered
- * kernels.  Setting the environment variable MDC_FFN_PIPELINE=1 runs them
- * instead as one persistent kernel whose GMM2 tiles start as soon as their
- * rows of g are quantised ([PTO] fused pipeline: ready flags between the
- * stages).  Both give bit-identical y.
+ * GMM1, the quantisation of g and GMM2 run as three stream-ordered kernels.
+ * With MDC_FLAG_FFN_PIPELINE in shape->flags they run instead as one
+ * persistent kernel whose GMM2 tiles start as soon as their rows of g are
+ * quantised ([PTO] fused pipeline: ready flags between the stages).  Both
+ * give bit-identical y.  The pipeline's waits are bounded: a GMM2 tile whose
+ * wait runs out writes NaN rows and counts itself in the workspace status
+ * block's wait_timeouts (never expected; every kernel still exits).
  * ------------------------------------------------------------------------ */
+mdc_status mdc_ffn_workspace(const mdc_shape* shape, int32_t inter_n, size_t* bytes);
 mdc_status mdc_ffn_workspace_size(const mdc_shape* shape, int32_t inter_n, size_t* bytes);
 
 mdc_status mdc_ffn(const mdc_shape* shape,

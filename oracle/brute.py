@@ -60,6 +60,29 @@ def bf16_round(v: float) -> int:
     return sign | pick
 
 
+def dropped(ids, mask, n_ids):
+    """Active routes whose id is below 0 or at least n_ids, counted one by one over a flat list of routes."""
+    flat = []
+    for s, rank_ids in enumerate(ids):
+        for t, tok in enumerate(rank_ids):
+            for k, e in enumerate(tok):
+                flat.append((s, t, k, int(e)))
+    n = 0
+    for s, t, k, e in flat:
+        if mask is not None:
+            m = mask[s][t]
+            if not (m[k] if isinstance(m, (list, tuple)) else m):
+                continue
+        if not (0 <= e < n_ids):
+            n += 1
+    return n
+
+
+def expand_scales(rows, scales):
+    """Weight of each received row's route, looked up by its (s, t, k) triplet."""
+    return [f32(float(scales[s][t][k])) for (s, t, k) in rows]
+
+
 def dispatch(ids, mask, d, experts, capacity, x=None):
     """Brute-force dispatch: returns (rows list of (s,t,k), counts dict, epRecvCounts list, expertTokenNums list, expand rows)."""
     W = len(ids)

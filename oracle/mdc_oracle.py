@@ -36,7 +36,11 @@ notes):
     never dispatched; in combine such a route is present with output 0 (zero)
     or the token's own unprocessed row oriX[t] (copy) ([CV4] parameter notes on
     zeroExpertNum, copyExpertNum and oriXOptional);
-  * ids outside [0, E) are dropped;
+  * ids outside [0, E) are not dispatched; of them, those outside
+    [0, E+Z+C) (no routed, zero or copy expert) on active routes are counted
+    as dropped ids;
+  * expandScales, the dispatch output the combine may take back, holds each
+    received row's route weight;
   * rows whose index would reach the capacity A are not written; counts still
     include them, so overflow is visible from epRecvCounts;
   * the shared-expert term is weighted per k, literally as the [CV4] formula
@@ -97,6 +101,9 @@ class DispatchResult:
     counts: np.ndarray            # [L][W] int32 (per (le, src) histogram)
     total: int                    # number of routes received (may exceed capacity)
     expanded_row_idx: dict        # (src, token, k) -> row, for written rows
+    dropped_ids: int = 0          # active routes (all sources) whose id is outside [0, E+Z+C)
+    overflow_rows: int = 0        # max(0, total - capacity)
+    expand_scales: Optional[np.ndarray] = None   # [n_rows] fp32 route weights, when scales were given
 
 
 def route_active(mask: Optional[np.ndarray], t: int, k: int) -> bool:
@@ -130,8 +137,30 @@ def local_routes(ids: np.ndarray, mask: Optional[np.ndarray], d: int, experts: i
     return out
 
 
+def dropped_ids(ids: np.ndarray, mask: Optional[np.ndarray], n_ids: int) -> int:
+    """Active routes of every source rank whose expert id lies outside [0, n_ids), n_ids = E + Z + C.
+
+    Such an id names no routed, zero or copy expert ([CV4] parameter notes:
+    the valid id ranges of routed, zero and copy experts), so the route is
+    sent nowhere and takes no part in combine; the dispatch reports how many
+    there were.  Inactive routes are not counted (they are not sent anyway).
+    """
+    W, BS, K = ids.shape
+    n = 0
+    for s in range(W):
+        for t in range(BS):
+            for k in range(K):
+                if mask is not None and not route_active(mask[s], t, k):
+                    continue
+                e = int(ids[s][t][k])
+                if e < 0 or e >= n_ids:
+                    n += 1
+    return n
+
+
 def dispatch(x: Optional[np.ndarray], ids: np.ndarray, mask: Optional[np.ndarray],
-             d: int, experts: int, capacity: int) -> DispatchResult:
+             d: int, experts: int, capacity: int, zero_experts: int = 0, copy_experts: int = 0,
+             scales: Optional[np.ndarray] = None) -> DispatchResult:
     """Expert-major dispatch for destination rank d.
 
     Rows are laid out by local expert, then source rank, then (token, k):
@@ -139,7 +168,10 @@ def dispatch(x: Optional[np.ndarray], ids: np.ndarray, mask: Optional[np.ndarray
     ([TL] rank-within-expert = number of earlier routes with the same id,
     window slot per (src, expert), local copy in status-row order le*W + src;
     [PTO] Dispatch: a group's rows ordered by source rank).
-    x may be None to compute the layout only.
+    x may be None to compute the layout only.  With scales ([W][BS][K] fp32
+    route weights) the result also carries expand_scales: each row's route
+    weight, the weight that travels with the row ([CV4] expandScalesOptional,
+    the dispatch's expandScales of shape (A,)).
     """
     W, BS, K = ids.shape
     L = experts // W
@@ -169,11 +201,18 @@ def dispatch(x: Optional[np.ndarray], ids: np.ndarray, mask: Optional[np.ndarray
             ex[row] = x[s][t]          # bitwise row copy ([TL] send loop row put)
     else:
         ex = np.zeros((n_rows, 0), dtype=np.uint16)
-    return DispatchResult(ex, assist, ep_recv_counts, expert_token_nums, counts, total, rowmap)
+    esc = None
+    if scales is not None:
+        esc = np.zeros(n_rows, dtype=np.float32)
+        for row, (le, s, t, k) in enumerate(ordered[:n_rows]):
+            esc[row] = scales[s][t][k]
+    return DispatchResult(ex, assist, ep_recv_counts, expert_token_nums, counts, total, rowmap,
+                          dropped_ids(ids, mask, experts + zero_experts + copy_experts),
+                          max(0, total - capacity), esc)
 
 
 def dispatch_quant(x: np.ndarray, ids: np.ndarray, mask: Optional[np.ndarray], d: int, experts: int,
-                   capacity: int):
+                   capacity: int, zero_experts: int = 0, copy_experts: int = 0, scales: Optional[np.ndarray] = None):
     """Quantised dispatch: the rows of dispatch(), each the per-row int8 quantisation of its token.
 
     [CV4] parameter notes: commQuantMode 2 quantises communicated rows to int8
@@ -181,7 +220,7 @@ def dispatch_quant(x: np.ndarray, ids: np.ndarray, mask: Optional[np.ndarray], d
     token rows.  The quantiser is quant_rows (fp32 decisions).  Returns the
     DispatchResult and (codes [n][H] int8, scales [n] fp32).
     """
-    res = dispatch(x, ids, mask, d, experts, capacity)
+    res = dispatch(x, ids, mask, d, experts, capacity, zero_experts, copy_experts, scales)
     q, sc = quant_rows(bf16_to_f32(res.expand_x)) if res.expand_x.shape[0] else (
         np.zeros((0, x.shape[-1]), np.int8), np.zeros(0, np.float32))
     return res, q, sc

@@ -3,8 +3,8 @@
 The FFN is not bit-exact (fp32 epilogues on the GPU, float64 in the oracle;
 bf16 intermediate g): the bar is relative L2 error <= 2e-2 over all rows.
 """
-import os
 import sys
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -42,13 +42,13 @@ def _weights_dev(fw):
             torch.from_numpy(fw.w2).to(d), torch.from_numpy(fw.w2_scale).to(d))
 
 
-def _run_ffn(w, inter, capacity=None, mask=None, rank=0):
+def _run_ffn(w, inter, capacity=None, mask=None, rank=0, flags=0):
     cap = w.capacity if capacity is None else capacity
     wi = gen.world_inputs(w)
     if mask is not None:
         wi.mask = mask
     fw = gen.ffn_weights(w, rank=rank, inter=inter)
-    shape = mdc.Shape(w.world, 0, w.bs, w.hidden, w.topk, w.experts, cap)
+    shape = mdc.Shape(w.world, 0, w.bs, w.hidden, w.topk, w.experts, cap, flags=flags)
     gw = G.dispatch_world(shape, wi.x, wi.ids, wi.mask)
     o = gw.outs[rank]
     y = torch.empty_like(o["expand_x"])
@@ -142,20 +142,12 @@ def test_ffn_full_size_then_combine():
     assert err2 <= REL_L2
 
 
-@pytest.mark.parametrize("pipeline", ["0", "1"])
+@pytest.mark.parametrize("pipeline", [0, 1])
 def test_ffn_tile_table_in_global_memory(pipeline):
     """A capacity of 400000 rows bounds the m-tile table above the 1536 entries
     the persistent GEMMs cache in LDS: they read it from global memory."""
     w = gen.workload("tiny", world=2, bs=64, hidden=128, experts=4, topk=2, index=90)
-    old = os.environ.get("MDC_FFN_PIPELINE")
-    try:
-        os.environ["MDC_FFN_PIPELINE"] = pipeline
-        got, want, *_ = _run_ffn(w, 256, capacity=400_000)
-    finally:
-        if old is None:
-            os.environ.pop("MDC_FFN_PIPELINE", None)
-        else:
-            os.environ["MDC_FFN_PIPELINE"] = old
+    got, want, *_ = _run_ffn(w, 256, capacity=400_000, flags=mdc.MDC_FLAG_FFN_PIPELINE if pipeline else 0)
     err = rel_l2(got, want)
     say(f"  pipeline={pipeline} rel L2 {err:.3e} over {got.shape[0]} rows")
     assert err <= REL_L2
@@ -180,21 +172,17 @@ def test_ffn_pipeline_equals_stream_ordered_kernels(variant):
     gw = G.dispatch_world(shape, wi.x, wi.ids, wi.mask)
     o = gw.outs[0]
     w1, s1, w2, s2 = _weights_dev(fw)
-    ws = torch.empty(mdc.mdc_ffn_workspace_size(shape, inter), dtype=torch.uint8, device=G.DEV)
+    ws = torch.empty(mdc.mdc_ffn_workspace(shape, inter), dtype=torch.uint8, device=G.DEV)
     ys = []
-    old = os.environ.get("MDC_FFN_PIPELINE")
-    try:
-        for flag in ("1", "0", "1"):
-            os.environ["MDC_FFN_PIPELINE"] = flag
-            y = torch.zeros_like(o["expand_x"])
-            mdc.mdc_ffn(shape, inter, o["expand_x"], o["expert_token_nums"], w1, s1, w2, s2, y, ws)
-            torch.cuda.synchronize()
-            ys.append(y)
-    finally:
-        if old is None:
-            os.environ.pop("MDC_FFN_PIPELINE", None)
-        else:
-            os.environ["MDC_FFN_PIPELINE"] = old
+    for flag in (mdc.MDC_FLAG_FFN_PIPELINE, 0, mdc.MDC_FLAG_FFN_PIPELINE):
+        y = torch.zeros_like(o["expand_x"])
+        ws[:16].fill_(0x7F)   # the call must rewrite its status block
+        mdc.mdc_ffn(replace(shape, flags=flag), inter, o["expand_x"], o["expert_token_nums"], w1, s1, w2, s2, y, ws)
+        torch.cuda.synchronize()
+        st = mdc.read_status(ws)
+        assert st["wait_timeouts"] == 0, st      # no pipeline wait ran out of its bound
+        assert st["dropped_ids"] == 0 and st["overflow_rows"] == 0, st
+        ys.append(y)
     n = int(o["ep_recv_counts"][-1].item())
     n = min(n, w.capacity)
     assert n > 0
@@ -202,3 +190,94 @@ def test_ffn_pipeline_equals_stream_ordered_kernels(variant):
     assert torch.equal(a, b), f"pipeline vs kernels: {(a != b).sum().item()} values differ"
     assert torch.equal(a, c), "pipeline not repeatable"
     say(f"  y bit-identical over {n} rows")
+
+
+def test_ffn_pipeline_wait_timeout_is_reported():
+    """A bounded wait that runs out is reported, never silent.  The spin field
+    of the flags lets each GMM2 tile poll its ready flag at most twice
+    (2^1 polls): tiles whose rows of g are not quantised by then give up,
+    count themselves in the status block's wait_timeouts and write NaN rows.
+    Every kernel still exits; the tiles whose flag was set in time match the
+    stream-ordered result bit for bit."""
+    w = gen.workload("tiny", world=2, bs=512, hidden=1024, experts=4, topk=2, index=98)
+    inter = 2048
+    say(f"ffn pipeline forced time-out W={w.world} BS={w.bs} H={w.hidden} E={w.experts} K={w.topk} N={inter}")
+    wi = gen.world_inputs(w)
+    fw = gen.ffn_weights(w, rank=0, inter=inter)
+    shape = mdc.Shape(w.world, 0, w.bs, w.hidden, w.topk, w.experts, w.capacity)
+    gw = G.dispatch_world(shape, wi.x, wi.ids, wi.mask)
+    o = gw.outs[0]
+    w1, s1, w2, s2 = _weights_dev(fw)
+    ws = torch.empty(mdc.mdc_ffn_workspace(shape, inter), dtype=torch.uint8, device=G.DEV)
+    n = min(int(o["ep_recv_counts"][-1].item()), w.capacity)
+    y_ref = torch.zeros_like(o["expand_x"])
+    mdc.mdc_ffn(shape, inter, o["expand_x"], o["expert_token_nums"], w1, s1, w2, s2, y_ref, ws)
+    y = torch.zeros_like(o["expand_x"])
+    quick = mdc.MDC_FLAG_FFN_PIPELINE | (1 << mdc.MDC_FLAG_SPIN_SHIFT)
+    mdc.mdc_ffn(replace(shape, flags=quick), inter, o["expand_x"], o["expert_token_nums"], w1, s1, w2, s2, y, ws)
+    torch.cuda.synchronize()
+    st = mdc.read_status(ws)
+    a = y[:n].view(torch.int16)
+    nan_rows = torch.isnan(y[:n].float()).any(dim=1)
+    say(f"  wait_timeouts {st['wait_timeouts']}, rows with NaN {int(nan_rows.sum())} of {n}")
+    assert st["wait_timeouts"] > 0
+    assert int(nan_rows.sum()) > 0
+    # a poisoned tile is NaN in all its values; every other value equals the stream-ordered result
+    fine = ~torch.isnan(y[:n].float())
+    assert torch.equal(a[fine], y_ref[:n].view(torch.int16)[fine])
+    # the default wait bound: nothing runs out, and the status block is rewritten by the next call
+    mdc.mdc_ffn(replace(shape, flags=mdc.MDC_FLAG_FFN_PIPELINE), inter, o["expand_x"], o["expert_token_nums"],
+                w1, s1, w2, s2, y, ws)
+    torch.cuda.synchronize()
+    assert mdc.read_status(ws)["wait_timeouts"] == 0
+    assert torch.equal(y[:n].view(torch.int16), y_ref[:n].view(torch.int16))
+
+
+def test_ffn_bench_composition_full_size():
+    """The ffn step as timed: quantised dispatch (mdc_dispatch_layout +
+    mdc_dispatch_quant_gather) -> mdc_ffn_quant_input -> mdc_combine, at the
+    full ffn shape, against the oracle (dispatch -> ffn -> combine) on y and
+    on xOut."""
+    w = gen.workload("ffn")
+    say("ffn bench composition, full size: generating inputs and weights")
+    wi = gen.world_inputs(w)
+    fw = gen.ffn_weights(w, rank=0)
+    shape = mdc.Shape(w.world, 0, w.bs, w.hidden, w.topk, w.experts, w.capacity)
+    gw = G.dispatch_world(shape, wi.x, wi.ids, wi.mask)       # every destination's bf16 rows (identity elsewhere)
+    o = gw.outs[0]
+    q = torch.empty((w.capacity, w.hidden), dtype=torch.int8, device=G.DEV)
+    qs = torch.empty((w.capacity,), dtype=torch.float32, device=G.DEV)
+    ws = torch.empty(mdc.mdc_dispatch_workspace(shape), dtype=torch.uint8, device=G.DEV)
+    ai = torch.empty_like(o["assist_info"])
+    ep = torch.empty_like(o["ep_recv_counts"])
+    etn = torch.empty_like(o["expert_token_nums"])
+    row_idx = gw.row_idx.clone()
+    mdc.mdc_dispatch_layout(shape, gw.ids, gw.mask, ws)
+    mdc.mdc_dispatch_quant_gather(shape, gw.x, q, qs, ai, ep, etn, row_idx, ws)
+    w1, s1, w2, s2 = _weights_dev(fw)
+    fws = torch.empty(mdc.mdc_ffn_workspace(shape, w.inter), dtype=torch.uint8, device=G.DEV)
+    y = torch.empty((w.capacity, w.hidden), dtype=torch.bfloat16, device=G.DEV)
+    mdc.mdc_ffn_quant_input(shape, w.inter, q, qs, etn, w1, s1, w2, s2, y, fws)
+    torch.cuda.synchronize()
+    ref = O.dispatch(wi.x, wi.ids, wi.mask, 0, w.experts, w.capacity)
+    n = ref.assist_info.shape[0]
+    assert np.array_equal(ai[:n].cpu().numpy(), ref.assist_info)
+    assert np.array_equal(row_idx.cpu().numpy(), gw.row_idx.cpu().numpy())
+    row_expert = np.repeat(np.arange(w.local_experts), ref.expert_token_nums)[:n]
+    want = O.ffn(ref.expand_x, row_expert, fw.w1, fw.w1_scale, fw.w2, fw.w2_scale)
+    err = rel_l2(G.bits(y[:n]), want)
+    say(f"  y rel L2 {err:.3e} over {n} rows")
+    assert err <= REL_L2
+    ys = [y] + [oo["expand_x"] for oo in gw.outs[1:]]
+    aid = [ai] + [oo["assist_info"] for oo in gw.outs[1:]]
+    epd = [ep] + [oo["ep_recv_counts"] for oo in gw.outs[1:]]
+    out = torch.empty((w.bs, w.hidden), dtype=torch.bfloat16, device=G.DEV)
+    mdc.mdc_combine(shape, ys, aid, epd, row_idx[0].contiguous(), gw.ids[0].contiguous(),
+                    torch.from_numpy(wi.scales[0]).to(G.DEV), None, G.to_dev_bf16(wi.shared[0]), out)
+    torch.cuda.synchronize()
+    segs = [O.dispatch(wi.x, wi.ids, None, d, w.experts, w.capacity) for d in range(w.world)]
+    oys = [want] + [sg.expand_x for sg in segs[1:]]
+    xo = O.combine(oys, [sg.assist_info for sg in segs], 0, wi.ids[0], None, wi.scales[0], wi.shared[0], w.hidden)
+    err2 = rel_l2(G.bits(out), xo)
+    say(f"  xOut rel L2 {err2:.3e}")
+    assert err2 <= REL_L2

@@ -34,22 +34,31 @@ def _shape(w: gen.Workload, capacity=None):
                      copy_experts=w.copy_experts)
 
 
-def _end_to_end(w: gen.Workload, expert="identity", capacity=None, ranks=None, split=False):
+def _end_to_end(w: gen.Workload, expert="identity", capacity=None, ranks=None, split=False, expand_scales=None):
+    """Dispatch every rank, apply the test expert, combine the given ranks; compare all with the oracle.
+
+    The dispatches also carry the routes' weights to expand_scales (checked
+    bit-exactly).  The combine takes its weights from those expand_scales on
+    odd ranks (or on every rank with expand_scales=True, none with False) and
+    from expert_scales otherwise; the result must be the same.
+    """
     say(f"case {w.name} W={w.world} BS={w.bs} H={w.hidden} E={w.experts} K={w.topk} routing={w.routing} "
         f"inactive={w.inactive_frac} route_mask={w.route_mask_frac} Z={w.zero_experts} C={w.copy_experts} "
         f"shared={w.shared} expert={expert} cap={capacity}")
     wi = gen.world_inputs(w)
     cap = w.capacity if capacity is None else capacity
-    gw = G.dispatch_world(_shape(w, cap), wi.x, wi.ids, wi.mask, split=split)
-    segs, oys = G.oracle_segments(wi.x, wi.ids, wi.mask, w.experts, cap, expert)
+    gw = G.dispatch_world(_shape(w, cap), wi.x, wi.ids, wi.mask, split=split, scales=wi.scales)
+    segs, oys = G.oracle_segments(wi.x, wi.ids, wi.mask, w.experts, cap, expert, w.zero_experts, w.copy_experts,
+                                  wi.scales)
     G.check_dispatch(gw, wi.x, wi.ids, wi.mask, w.experts, cap, refs=segs)
-    say("  dispatch bit-exact on every rank")
+    say("  dispatch bit-exact on every rank (rows, triplets, counts, expand_scales, status)")
     ys = G.apply_expert(gw, expert, w.experts)
     for r in (range(w.world) if ranks is None else ranks):
         sh = None if wi.shared is None else wi.shared[r]
         m = None if wi.mask is None else wi.mask[r]
         ori = wi.x[r] if w.copy_experts else None
-        got = G.bits(G.run_combine(gw, ys, r, wi.scales[r], sh, ori))
+        use_esc = (r % 2 == 1) if expand_scales is None else expand_scales
+        got = G.bits(G.run_combine(gw, ys, r, wi.scales[r], sh, ori, use_expand_scales=use_esc))
         want = O.combine(oys, [s.assist_info for s in segs], r, wi.ids[r], m, wi.scales[r], sh, w.hidden,
                          experts=w.experts, zero_experts=w.zero_experts, copy_experts=w.copy_experts, ori_r=ori)
         assert G.ulp_diff(got, want) <= 1, f"combine r={r} beyond 1 ulp"
@@ -76,8 +85,8 @@ def test_share_full_size():
 
 
 def test_skewed_full_size():
-    """Zipf(1.2) routing with 10% inactive tokens at the full share shape, power-of-two expert."""
-    _end_to_end(gen.workload("skewed"), expert="pow2", ranks=[0, 3, 7])
+    """Zipf(1.2) routing with 10% inactive tokens at the full share shape, power-of-two expert, every rank."""
+    _end_to_end(gen.workload("skewed"), expert="pow2")
 
 
 @pytest.mark.parametrize("variant", [
@@ -148,14 +157,20 @@ def test_empty_batch():
         assert not o["ep_recv_counts"].any() and not o["expert_token_nums"].any()
 
 
-def test_invalid_and_duplicate_ids():
+@pytest.mark.parametrize("split", [False, True], ids=["one_shot", "split_stages"])
+def test_invalid_and_duplicate_ids(split):
+    """Out-of-range ids are dropped and counted in the status block, as many as the oracle counts."""
     g = np.random.default_rng(5)
     W, BS, K, E, H = 2, 50, 4, 8, 64
     ids = g.integers(-3, E + 3, size=(W, BS, K)).astype(np.int32)   # duplicates and out-of-range ids
     x = gen.bf16_from_f32(g.standard_normal((W, BS, H), dtype=np.float32))
     sh = mdc.Shape(W, 0, BS, H, K, E, W * BS * K)
-    gw = G.dispatch_world(sh, x, ids, None)
+    gw = G.dispatch_world(sh, x, ids, None, split=split)
     G.check_dispatch(gw, x, ids, None, E, W * BS * K)
+    want = O.dispatch(None, ids, None, 0, E, W * BS * K).dropped_ids
+    assert want == int(((ids < 0) | (ids >= E)).sum()) > 0
+    for o in gw.outs:
+        assert mdc.read_status(o["workspace"])["dropped_ids"] == want
     ys = G.apply_expert(gw, "identity", E)
     segs, oys = G.oracle_segments(x, ids, None, E, W * BS * K, "identity")
     sc = g.standard_normal((BS, K)).astype(np.float32)
@@ -262,3 +277,64 @@ def test_random_shapes(i, cfg, cap_scale, split, expert):
     w = gen.workload("tiny", index=200 + i, **cfg)
     cap = max(0, int(round(w.capacity * cap_scale)))
     _end_to_end(w, expert=expert, capacity=cap, split=split)
+
+
+@pytest.mark.parametrize("split", [False, True], ids=["one_shot", "split_stages"])
+def test_dropped_ids_beside_zero_and_copy_experts_and_masks(split):
+    """Ids in [E, E+Z+C) are zero/copy experts, not dropped; ids outside [0, E+Z+C) on active routes are
+    dropped; masked-off routes never count.  Share-size ranks so the split path uses several rank groups."""
+    g = np.random.default_rng(11)
+    W, BS, K, E, Z, C, H = 4, 700, 6, 32, 3, 2, 136
+    ids = g.integers(-4, E + Z + C + 4, size=(W, BS, K)).astype(np.int32)
+    mask = (g.random((W, BS, K)) >= 0.25).astype(np.uint8)
+    x = gen.bf16_from_f32(g.standard_normal((W, BS, H), dtype=np.float32))
+    sc = g.random((W, BS, K)).astype(np.float32)
+    sh = mdc.Shape(W, 0, BS, H, K, E, W * BS * K, mask_per_route=1, zero_experts=Z, copy_experts=C)
+    gw = G.dispatch_world(sh, x, ids, mask, split=split, scales=sc)
+    G.check_dispatch(gw, x, ids, mask, E, W * BS * K, scales=sc)
+    want = O.dispatch(None, ids, mask, 0, E, 1, Z, C).dropped_ids
+    assert want == int((((ids < 0) | (ids >= E + Z + C)) & (mask != 0)).sum()) > 0
+
+
+def test_overflow_rows_reported():
+    w = gen.workload("tiny", world=2, bs=64, hidden=64, experts=4, topk=2, index=70)
+    wi = gen.world_inputs(w)
+    gw = G.dispatch_world(_shape(w, 37), wi.x, wi.ids, None)
+    G.check_dispatch(gw, wi.x, wi.ids, None, w.experts, 37)
+    for d, o in enumerate(gw.outs):
+        total = int(o["ep_recv_counts"][-1].item())
+        assert mdc.read_status(o["workspace"])["overflow_rows"] == max(0, total - 37) > 0
+
+
+@pytest.mark.parametrize("name", ["share", "decode"])
+def test_performance_info_per_rank_waits(name):
+    """performance_info[j] accumulates the wait for rank j's rows: nonzero for every rank the combine reads
+    rows from, untouched for ranks it reads nothing from; a second call adds to it.  The output is the
+    same as without timing."""
+    w = gen.workload(name)
+    if name == "share":
+        # ranks 5..7 hold no expert any token of rank 0 routes to: draw ids from ranks 0..4 only
+        w = gen.workload(name, bs=512, index=120)
+    wi = gen.world_inputs(w)
+    L = w.experts // w.world
+    ids = wi.ids.copy()
+    if name == "share":
+        ids[0] = ids[0] % (5 * L)
+        g = np.random.default_rng(3)
+        for t in range(w.bs):   # keep each token's experts distinct
+            ids[0, t] = g.permutation(5 * L)[:w.topk]
+    gw = G.dispatch_world(_shape(w), wi.x, ids, wi.mask)
+    ys = G.apply_expert(gw, "identity", w.experts)
+    sh0 = None if wi.shared is None else wi.shared[0]
+    plain = G.run_combine(gw, ys, 0, wi.scales[0], sh0)
+    perf = torch.full((w.world,), 7, dtype=torch.int64, device=G.DEV)
+    timed = G.run_combine(gw, ys, 0, wi.scales[0], sh0, perf=perf)
+    assert torch.equal(plain.view(torch.int16), timed.view(torch.int16))
+    p1 = perf.cpu().numpy().copy()
+    read = np.zeros(w.world, bool)
+    read[np.unique(ids[0] // L)] = True
+    say(f"  waits (us, +7): {p1.tolist()}; ranks read {np.nonzero(read)[0].tolist()}")
+    assert np.all(p1[read] > 7) and np.all(p1[~read] == 7)
+    G.run_combine(gw, ys, 0, wi.scales[0], sh0, perf=perf)
+    p2 = perf.cpu().numpy()
+    assert np.all(p2[read] > p1[read]) and np.all(p2[~read] == 7)

@@ -73,6 +73,47 @@ def test_dispatch_matches_brute_force(case):
             assert o.expand_x.tolist() == (ex if ex else [])
 
 
+@pytest.mark.parametrize("case", _tiny_cases()[1::7])
+def test_dispatch_status_and_expand_scales_match_brute_force(case):
+    """Dropped-id count, overflow rows and the expandScales rows against the brute-force twin.
+
+    Some ids are made invalid (< 0 or >= E+Z+C) and some land on zero/copy
+    experts ([E, E+Z+C)), which are not dispatched and not dropped.
+    """
+    seed, W, BS, E, K, mk, dup, _ = case
+    ids, mask, x = _tiny_world(seed, W, BS, E, K, mk, dup and E >= K, True)
+    g = np.random.default_rng(seed + 5000)
+    Z, C = int(g.integers(0, 3)), int(g.integers(0, 3))
+    special = g.random(ids.shape) < 0.15
+    if Z + C:
+        ids[special] = E + g.integers(0, Z + C, size=int(special.sum()))
+    scales = g.standard_normal(ids.shape).astype(np.float32)
+    mask_l = None if mask is None else mask.tolist()
+    want_drop = B.dropped(ids.tolist(), mask_l, E + Z + C)
+    for cap in (10 ** 6, 3):
+        for d in range(W):
+            o = O.dispatch(x, ids, mask, d, E, cap, Z, C, scales)
+            rows, cnt, ep, etn, _ = B.dispatch(ids.tolist(), mask_l, d, E, cap)
+            assert o.dropped_ids == want_drop
+            assert o.overflow_rows == max(0, ep[-1] - cap)
+            assert o.expand_scales.dtype == np.float32
+            assert o.expand_scales.tolist() == B.expand_scales(rows, scales.tolist())
+
+
+def test_dropped_ids_closed_forms():
+    """All ids valid -> 0; every id invalid -> every active route; inactive routes never count."""
+    ids = np.tile(np.arange(4, dtype=np.int32), (2, 5, 1))          # W=2, BS=5, K=4, E=8
+    assert O.dispatch(None, ids, None, 0, 8, 100).dropped_ids == 0
+    bad = np.full((2, 5, 4), 9, np.int32)                           # 9 >= E+Z+C = 8+1
+    assert O.dispatch(None, bad, None, 0, 8, 100, zero_experts=1).dropped_ids == 40
+    assert O.dispatch(None, bad, None, 0, 8, 100, zero_experts=2).dropped_ids == 0   # 9 is a zero expert
+    mask = np.zeros((2, 5), np.uint8)
+    mask[1, 2] = 1
+    assert O.dispatch(None, bad, mask, 0, 8, 100).dropped_ids == 4   # one active token, K ids
+    neg = -np.ones((2, 5, 4), np.int32)
+    assert O.dispatch(None, neg, None, 1, 8, 100, zero_experts=3, copy_experts=3).dropped_ids == 40
+
+
 def test_single_rank_dispatch_is_stable_counting_sort():
     """W = 1, L = E: the expert-major layout is a stable sort of the flattened ids."""
     g = np.random.default_rng(7)
