@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--event-samples", type=int, default=10,
                     help="timed steps that carry per-kernel HIP events (spread evenly, the first timed step "
                          "excluded)")
+    ap.add_argument("--breakdown-steps", type=int, default=20,
+                    help="steps of the per-kernel breakdown pass after the timed region")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the memory-ceiling leg")
     ap.add_argument("--ceiling-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -155,6 +157,58 @@ def pct(v, q):
 def spread(samples_us):
     return {"median": round(statistics.median(samples_us), 3), "p10": round(pct(samples_us, 10), 3),
             "p90": round(pct(samples_us, 90), 3), "n": len(samples_us)}
+
+
+class HipEvents:
+    """Timing events created with hipEventDisableSystemFence through the HIP runtime torch loaded.
+
+    A default event (torch.cuda.Event) writes back and invalidates the caches
+    when it is recorded, which costs about 2.5 us of GPU time per event between
+    kernels; an event without the system-scope fence only takes a timestamp,
+    which is all a duration needs.
+    """
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")   # the runtime already loaded by torch (same SONAME)
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def make(self):
+        e = self.ct.c_void_p()
+        st = self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+        self.made.append(e)
+        return e
+
+    def pair(self):
+        return [self.make(), self.make()]
+
+    def five(self):
+        return [self.make() for _ in range(5)]
+
+    def record(self, e, stream):
+        if self.hip.hipEventRecord(e, stream.cuda_stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_us(self, a, b):
+        f = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(f), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value * 1e3
+
+    def __del__(self):
+        try:
+            for e in self.made:
+                self.hip.hipEventDestroy(e)
+        except Exception:   # interpreter shutdown: the runtime may already be gone
+            pass
 
 
 def ceiling_leg(torch, mdc, w, wi, batches, stream, reps):
@@ -415,26 +469,41 @@ def main():
                                             bt["scales0"], bt["mask0"], bt["shared0"], bt["x_out"],
                                             stream=stream, ori_x=bt["x"][0] if w.copy_experts else None)
 
-    def step(bt, ev=None):
-        if ev is None:
+    hip_ev = HipEvents()
+    dom_stage = "ffn" if w.inter else "gather"   # the kernel the roofline is quoted on
+
+    def step(bt, ev=None, bracket=None):
+        """One step; ev = events to record: around stage `bracket` only (2), or around every stage (5)."""
+        def rec(k):
+            if ev is not None and k < len(ev):
+                hip_ev.record(ev[k], stream)
+        if ev is None or bracket is not None:
             if bt["layout"] is not None:
                 bt["layout"]()
+            if bracket == "gather":
+                rec(0)
             bt["gather"]()
+            if bracket == "gather":
+                rec(1)
             if bt["ffn"] is not None:
+                if bracket == "ffn":
+                    rec(0)
                 bt["ffn"]()
+                if bracket == "ffn":
+                    rec(1)
             bt["combine"]()
             return
-        ev[0].record(stream)
+        rec(0)
         if bt["layout"] is not None:
             bt["layout"]()
-        ev[1].record(stream)
+        rec(1)
         bt["gather"]()
-        ev[2].record(stream)
+        rec(2)
         if bt["ffn"] is not None:
             bt["ffn"]()
-        ev[4].record(stream)
+        rec(4)
         bt["combine"]()
-        ev[3].record(stream)
+        rec(3)
 
     ceil, pats = (None, None)
     if not args.no_ceilings:
@@ -456,30 +525,43 @@ def main():
         step(batches[i % args.batches])
     torch.cuda.synchronize()
 
-    # Per-kernel HIP events are recorded on the launch stream on about
-    # --event-samples timed steps, spread evenly over the run and never on the
-    # first timed step (it starts from an idle queue, right after a
-    # synchronisation); the wall-clock total covers all steps.
+    # The dominant kernel is bracketed by two HIP events on the launch stream on
+    # about --event-samples timed steps, spread evenly and never on the first
+    # timed step (it starts from an idle queue, right after a synchronisation).
+    # The events skip the system-scope fence (no cache write-back at the
+    # event), so a bracketed step runs about as fast as the others; the
+    # wall-clock total covers all steps.
     every = max(1, (args.steps - 1 + args.event_samples - 1) // max(1, args.event_samples))
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(5)] for i in range(1, args.steps, every)}
+    evs = {i: hip_ev.pair() for i in range(1, args.steps, every)}
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     gc.collect()
     gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(batches[i % args.batches], evs.get(i))
+        step(batches[i % args.batches], evs.get(i), dom_stage)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gc.enable()
-    evs_idx = list(evs.keys())
-    evs = list(evs.values())
+    evs_idx = sorted(evs.keys())
+    t_dom = [hip_ev.elapsed_us(evs[i][0], evs[i][1]) for i in evs_idx]
 
-    t_layout = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]     # us
-    t_gather = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
-    t_ffn = [e[2].elapsed_time(e[4]) * 1e3 for e in evs]
-    t_comb = [e[4].elapsed_time(e[3]) * 1e3 for e in evs]
-    t_step_ev = [e[0].elapsed_time(e[3]) * 1e3 for e in evs]
+    # Per-kernel breakdown: a separate pass after the timed region, every step
+    # carrying events around each stage (these steps are not part of `value`).
+    br = [hip_ev.five() for _ in range(args.breakdown_steps)]
+    torch.cuda.synchronize()
+    for i, ev in enumerate(br):
+        step(batches[i % args.batches], ev)
+    torch.cuda.synchronize()
+    t_layout = [hip_ev.elapsed_us(e[0], e[1]) for e in br]     # us
+    t_gather = [hip_ev.elapsed_us(e[1], e[2]) for e in br]
+    t_ffn = [hip_ev.elapsed_us(e[2], e[4]) for e in br]
+    t_comb = [hip_ev.elapsed_us(e[4], e[3]) for e in br]
+    t_step_ev = [hip_ev.elapsed_us(e[0], e[3]) for e in br]
+    if dom_stage == "gather":
+        t_gather_timed, t_ffn_timed = t_dom, t_ffn
+    else:
+        t_gather_timed, t_ffn_timed = t_gather, t_dom
     ms_per_step = elapsed * 1e3 / args.steps
     by = algorithmic_bytes(w, wi.ids, wi.mask)
     step_bytes = by["layout"] + by["gather"] + by["combine"]
@@ -491,12 +573,9 @@ def main():
         d_kernel, d_bytes = "k_dispatch_small", by["layout"] + by["gather"]
     else:
         d_kernel, d_bytes = ("k_dispatch_gather_q" if w.inter else "k_dispatch_gather"), by["gather"]
-    gb_gather = d_bytes / (med(t_gather) * 1e-6) / 1e9
+    gb_gather = d_bytes / (med(t_gather_timed) * 1e-6) / 1e9
     gb_comb = by["combine"] / (med(t_comb) * 1e-6) / 1e9
-    if med(t_gather) >= med(t_comb):
-        dom = (d_kernel, gb_gather, d_bytes, med(t_gather), t_gather)
-    else:
-        dom = ("k_combine", gb_comb, by["combine"], med(t_comb), t_comb)
+    dom = (d_kernel, gb_gather, d_bytes, med(t_gather_timed), t_gather_timed)
     graph_info = None
     if one_shot:
         # launch-bound workloads: the same step replayed from a HIP graph
@@ -506,9 +585,9 @@ def main():
     ffn_info = None
     if w.inter:
         ops = 2.0 * by["R"] * (w.inter * H + H * (w.inter // 2))
-        tops = ops / (statistics.median(t_ffn) * 1e-6) / 1e12
-        ffn_info = {"us": round(statistics.median(t_ffn), 2), "mean_us": round(mean(t_ffn), 2),
-                    "spread_us": spread(t_ffn), "int8_ops": ops, "tops": round(tops, 1),
+        tops = ops / (statistics.median(t_ffn_timed) * 1e-6) / 1e12
+        ffn_info = {"us": round(statistics.median(t_ffn_timed), 2), "mean_us": round(mean(t_ffn_timed), 2),
+                    "spread_us": spread(t_ffn_timed), "int8_ops": ops, "tops": round(tops, 1),
                     "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)}
 
     roofline = {"bound": "hbm", "kernel": dom[0], "achieved": round(dom[1], 1), "peak": HBM_PEAK_GBPS,
@@ -516,8 +595,8 @@ def main():
                 "traffic": measured_traffic(w.name, dom[0]),
                 "bytes_per_launch": dom[2], "avg_launch_us": round(dom[3], 3),
                 "launch_us": spread(dom[4]),
-                "launch_time_from": "median of HIP events on the launch stream around the kernel, on the timed "
-                                    "steps that carry events"}
+                "launch_time_from": "median of two fence-free HIP events on the launch stream around the kernel, "
+                                    f"on timed steps {evs_idx[:3]}..{evs_idx[-1:]} (never the first)"}
     if ceil is not None:
         roofline["frac_of_copy_ceiling"] = round(dom[1] / ceil["copy_1GiB"]["gbps"], 4)
     if ffn_info is not None:
@@ -527,7 +606,9 @@ def main():
                     "traffic": measured_traffic(w.name, ("k_ffn_plan", "k_ffn_gemm<true", "k_ffn_quant_rows",
                                                          "k_ffn_gemm<false")),
                     "ops_per_launch": ffn_info["int8_ops"],
-                    "avg_launch_us": ffn_info["us"]}
+                    "avg_launch_us": ffn_info["us"], "launch_us": ffn_info["spread_us"],
+                    "launch_time_from": "median of two fence-free HIP events on the launch stream around the "
+                                        f"mdc_ffn_quant_input call, on timed steps {evs_idx[:3]}..{evs_idx[-1:]}"}
     result = {
         "metric": METRIC,
         "value": round(BS / (ms_per_step * 1e-3), 1),
@@ -559,8 +640,9 @@ def main():
                        "dispatch_gather": spread(t_gather),
                        "combine": spread(t_comb), "step_events": spread(t_step_ev),
                        "gather_gbps": round(gb_gather, 1), "combine_gbps": round(gb_comb, 1),
-                       "event_steps": sorted(evs_idx), "what": "median, p10, p90 over the timed steps that carry "
-                                                               "HIP events (the first timed step never does)"},
+                       "what": f"median, p10, p90 over a {args.breakdown_steps}-step pass after the timed region "
+                               "with fence-free HIP events around every stage (not part of value); the dominant "
+                               "kernel's in-region samples are under roofline.launch_us"},
     }
     if ffn_info is not None:
         result["ffn"] = ffn_info

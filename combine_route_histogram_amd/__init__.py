@@ -265,7 +265,8 @@ class Prepared:
     """A C entry point with its arguments marshalled once, for repeated launches.
 
     Calling it enqueues the same work again on the stream captured at
-    preparation; the referenced tensors must stay alive.
+    preparation.  It holds references to the tensors it was prepared with, so
+    their memory stays allocated while the object lives.
     """
     __slots__ = ("_fn", "_args", "_name", "_keep")
 
@@ -276,6 +277,17 @@ class Prepared:
         st = self._fn(*self._args)
         if st != MDC_OK:
             raise MdcError(st, self._name)
+
+
+def _tensors(names: dict) -> tuple:
+    """The tensor arguments among a prepare_* call's locals (and inside its pointer-table lists)."""
+    out = []
+    for v in names.values():
+        if isinstance(v, torch.Tensor):
+            out.append(v)
+        elif isinstance(v, (list, tuple)):
+            out.extend(t for t in v if isinstance(t, torch.Tensor))
+    return tuple(out)
 
 
 def _run(p: Prepared, check: bool) -> int:
@@ -291,7 +303,7 @@ def prepare_dispatch_layout(shape: Shape, expert_ids, x_active_mask, workspace, 
     sh = shape.c()
     args = (ctypes.byref(sh), _ptr(expert_ids), _ptr(x_active_mask), _ptr(workspace), _nbytes(workspace),
             _stream(stream))
-    return Prepared(_lib.mdc_dispatch_layout, args, "mdc_dispatch_layout", (sh,))
+    return Prepared(_lib.mdc_dispatch_layout, args, "mdc_dispatch_layout", (sh, _tensors(locals())))
 
 
 def prepare_dispatch_gather(shape: Shape, x, expand_x, assist_info, ep_recv_counts, expert_token_nums,
@@ -304,7 +316,7 @@ def prepare_dispatch_gather(shape: Shape, x, expand_x, assist_info, ep_recv_coun
     args = (ctypes.byref(sh), _ptr(x), _ptr(expert_scales), _ptr(expand_x), _ptr(assist_info), _ptr(ep_recv_counts),
             _ptr(expert_token_nums), _ptr(expanded_row_idx), _ptr(expand_scales), _ptr(workspace),
             _nbytes(workspace), _stream(stream))
-    return Prepared(_lib.mdc_dispatch_gather, args, "mdc_dispatch_gather", (sh,))
+    return Prepared(_lib.mdc_dispatch_gather, args, "mdc_dispatch_gather", (sh, _tensors(locals())))
 
 
 def prepare_dispatch(shape: Shape, x, expert_ids, x_active_mask, expand_x, assist_info, ep_recv_counts,
@@ -317,7 +329,7 @@ def prepare_dispatch(shape: Shape, x, expert_ids, x_active_mask, expand_x, assis
     args = (ctypes.byref(sh), _ptr(x), _ptr(expert_ids), _ptr(x_active_mask), _ptr(expert_scales), _ptr(expand_x),
             _ptr(assist_info), _ptr(ep_recv_counts), _ptr(expert_token_nums), _ptr(expanded_row_idx),
             _ptr(expand_scales), _ptr(workspace), _nbytes(workspace), _stream(stream))
-    return Prepared(_lib.mdc_dispatch, args, "mdc_dispatch", (sh,))
+    return Prepared(_lib.mdc_dispatch, args, "mdc_dispatch", (sh, _tensors(locals())))
 
 
 def prepare_dispatch_quant_gather(shape: Shape, x, expand_q, dynamic_scales, assist_info, ep_recv_counts,
@@ -330,7 +342,7 @@ def prepare_dispatch_quant_gather(shape: Shape, x, expand_q, dynamic_scales, ass
     args = (ctypes.byref(sh), _ptr(x), _ptr(expert_scales), _ptr(expand_q), _ptr(dynamic_scales), _ptr(assist_info),
             _ptr(ep_recv_counts), _ptr(expert_token_nums), _ptr(expanded_row_idx), _ptr(expand_scales),
             _ptr(workspace), _nbytes(workspace), _stream(stream))
-    return Prepared(_lib.mdc_dispatch_quant_gather, args, "mdc_dispatch_quant_gather", (sh,))
+    return Prepared(_lib.mdc_dispatch_quant_gather, args, "mdc_dispatch_quant_gather", (sh, _tensors(locals())))
 
 
 def prepare_dispatch_quant(shape: Shape, x, expert_ids, x_active_mask, expand_q, dynamic_scales, assist_info,
@@ -343,7 +355,7 @@ def prepare_dispatch_quant(shape: Shape, x, expert_ids, x_active_mask, expand_q,
     args = (ctypes.byref(sh), _ptr(x), _ptr(expert_ids), _ptr(x_active_mask), _ptr(expert_scales), _ptr(expand_q),
             _ptr(dynamic_scales), _ptr(assist_info), _ptr(ep_recv_counts), _ptr(expert_token_nums),
             _ptr(expanded_row_idx), _ptr(expand_scales), _ptr(workspace), _nbytes(workspace), _stream(stream))
-    return Prepared(_lib.mdc_dispatch_quant, args, "mdc_dispatch_quant", (sh,))
+    return Prepared(_lib.mdc_dispatch_quant, args, "mdc_dispatch_quant", (sh, _tensors(locals())))
 
 
 def _table(items: Optional[Sequence]):
@@ -386,7 +398,7 @@ def prepare_combine(shape: Shape, expand_x: Sequence, assist_info: Sequence, ep_
             _ptr(expanded_row_idx), _ptr(expert_ids), _ptr(expert_scales), _ptr(x_active_mask),
             None if te is None else ctypes.cast(te, _P), _ptr(shared_expert_x), _ptr(ori_x),
             _ptr(performance_info), _ptr(x_out), _ptr(workspace), _nbytes(workspace), _stream(stream))
-    return Prepared(_lib.mdc_combine, args, "mdc_combine", (sh, ty, ta, tc, te))
+    return Prepared(_lib.mdc_combine, args, "mdc_combine", (sh, ty, ta, tc, te, _tensors(locals())))
 
 
 def _check_ffn_weights(shape: Shape, inter_n: int, expert_token_nums, w1, w1_scale, w2, w2_scale, y) -> None:
@@ -406,7 +418,7 @@ def prepare_ffn(shape: Shape, inter_n: int, expand_x, expert_token_nums, w1, w1_
     sh = shape.c()
     args = (ctypes.byref(sh), int(inter_n), _ptr(expand_x), _ptr(expert_token_nums), _ptr(w1), _ptr(w1_scale),
             _ptr(w2), _ptr(w2_scale), _ptr(y), _ptr(workspace), _nbytes(workspace), _stream(stream))
-    return Prepared(_lib.mdc_ffn, args, "mdc_ffn", (sh,))
+    return Prepared(_lib.mdc_ffn, args, "mdc_ffn", (sh, _tensors(locals())))
 
 
 def prepare_ffn_quant_input(shape: Shape, inter_n: int, expand_q, dynamic_scales, expert_token_nums, w1, w1_scale,
@@ -418,7 +430,7 @@ def prepare_ffn_quant_input(shape: Shape, inter_n: int, expand_q, dynamic_scales
     args = (ctypes.byref(sh), int(inter_n), _ptr(expand_q), _ptr(dynamic_scales), _ptr(expert_token_nums), _ptr(w1),
             _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(y), _ptr(workspace), _nbytes(workspace),
             _stream(stream))
-    return Prepared(_lib.mdc_ffn_quant_input, args, "mdc_ffn_quant_input", (sh,))
+    return Prepared(_lib.mdc_ffn_quant_input, args, "mdc_ffn_quant_input", (sh, _tensors(locals())))
 
 
 # ----------------------------------------------------------------------------
