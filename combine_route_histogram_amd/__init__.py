@@ -50,7 +50,7 @@ EXPORTS = (
     "mdc_dispatch_workspace", "mdc_dispatch_workspace_size", "mdc_dispatch_layout", "mdc_dispatch_gather",
     "mdc_dispatch", "mdc_combine_workspace", "mdc_combine_workspace_size", "mdc_combine",
     "mdc_ffn_workspace", "mdc_ffn_workspace_size", "mdc_ffn", "mdc_dispatch_quant", "mdc_dispatch_quant_gather",
-    "mdc_ffn_quant_input",
+    "mdc_ffn_quant_input", "mdc_dispatch_noalloc",
 )
 
 
@@ -91,6 +91,8 @@ _sig("mdc_dispatch_quant", _SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
 _sig("mdc_combine", _SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P)
 _sig("mdc_ffn", _SHP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P)
 _sig("mdc_ffn_quant_input", _SHP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P)
+_sig("mdc_dispatch_noalloc", _SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P)
+MDC_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class MdcError(RuntimeError):
@@ -433,6 +435,19 @@ def prepare_ffn_quant_input(shape: Shape, inter_n: int, expand_q, dynamic_scales
     return Prepared(_lib.mdc_ffn_quant_input, args, "mdc_ffn_quant_input", (sh, _tensors(locals())))
 
 
+def prepare_dispatch_noalloc(shape: Shape, x, expert_ids, x_active_mask, expand_x, assist_info, ep_recv_counts,
+                             expert_token_nums, expanded_row_idx, stream=None, expert_scales=None,
+                             expand_scales=None) -> Prepared:
+    _check_dispatch_inputs(shape, x, expert_ids, x_active_mask, expert_scales)
+    _check_dispatch_outputs(shape, expand_x, _BF16, assist_info, ep_recv_counts, expert_token_nums,
+                            expanded_row_idx, expand_scales)
+    sh = shape.c()
+    args = (ctypes.byref(sh), _ptr(x), _ptr(expert_ids), _ptr(x_active_mask), _ptr(expert_scales), _ptr(expand_x),
+            _ptr(assist_info), _ptr(ep_recv_counts), _ptr(expert_token_nums), _ptr(expanded_row_idx),
+            _ptr(expand_scales), _stream(stream))
+    return Prepared(_lib.mdc_dispatch_noalloc, args, "mdc_dispatch_noalloc", (sh, _tensors(locals())))
+
+
 # ----------------------------------------------------------------------------
 # one-shot calls (marshal and launch)
 # ----------------------------------------------------------------------------
@@ -491,6 +506,14 @@ def mdc_ffn_quant_input(shape: Shape, inter_n: int, expand_q, dynamic_scales, ex
                         w2_scale, y, workspace, stream=None, check: bool = True) -> int:
     return _run(prepare_ffn_quant_input(shape, inter_n, expand_q, dynamic_scales, expert_token_nums, w1, w1_scale,
                                         w2, w2_scale, y, workspace, stream), check)
+
+
+def mdc_dispatch_noalloc(shape: Shape, x, expert_ids, x_active_mask, expand_x, assist_info, ep_recv_counts,
+                         expert_token_nums, expanded_row_idx, stream=None, check: bool = True, expert_scales=None,
+                         expand_scales=None) -> int:
+    return _run(prepare_dispatch_noalloc(shape, x, expert_ids, x_active_mask, expand_x, assist_info, ep_recv_counts,
+                                         expert_token_nums, expanded_row_idx, stream, expert_scales, expand_scales),
+                check)
 
 
 def alloc_dispatch_outputs(shape: Shape, device="cuda"):

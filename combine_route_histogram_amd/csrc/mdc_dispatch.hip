@@ -34,7 +34,15 @@
 // Built with -ffp-contract=off: the combine's products and sums are rounded
 // to fp32 one by one, in the order the combine formula lists them.
 
+#include <mutex>
+
 #include "mdc_common.h"
+
+// Workspace of mdc_dispatch_noalloc, for callers that cannot allocate: one
+// copy per device, zero at load, held until the process ends.  Host code
+// never passes this name to a kernel (on the host it is only a stand-in for
+// the symbol); it uses the device address from noalloc_scratch() instead.
+static __device__ __align__(256) unsigned char scratch[MDC_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -1278,6 +1286,25 @@ mdc_status combine_impl(const mdc_shape* shape, const void* const* expand_x, con
   return launched();
 }
 
+// Device address of this device's scratch array, looked up once per device
+// (hipGetSymbolAddress with that device current) and kept; NULL if the lookup
+// fails.
+constexpr int kNoAllocMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoAllocMaxDevices] = {};
+
+void* noalloc_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -1355,6 +1382,23 @@ mdc_status mdc_dispatch(const mdc_shape* shape, const void* x, const int32_t* ex
   st = layout_impl(p, expert_ids, x_active_mask, ws, s);
   if (st != MDC_OK) return st;
   return gather_impl(p, x, m, expand_x, s);
+}
+
+mdc_status mdc_dispatch_noalloc(const mdc_shape* shape, const void* x, const int32_t* expert_ids,
+                                const uint8_t* x_active_mask, const float* expert_scales, void* expand_x,
+                                int32_t* assist_info, int32_t* ep_recv_counts, int64_t* expert_token_nums,
+                                int32_t* expanded_row_idx, float* expand_scales, void* stream) {
+  mdc_status st = check_shape(shape);
+  if (st != MDC_OK) return st;
+  const DispatchPlan p = make_plan(shape);
+  if (p.bytes > (size_t)MDC_NOALLOC_SCRATCH_BYTES) return MDC_ERR_UNSUPPORTED;
+  void* ws = noalloc_scratch();
+  if (ws == nullptr) return MDC_ERR_HIP;
+  // every workspace region the dispatch reads is written earlier in the same
+  // call, so the scratch needs no clearing between calls
+  return mdc_dispatch(shape, x, expert_ids, x_active_mask, expert_scales, expand_x, assist_info, ep_recv_counts,
+                      expert_token_nums, expanded_row_idx, expand_scales, ws, (size_t)MDC_NOALLOC_SCRATCH_BYTES,
+                      stream);
 }
 
 mdc_status mdc_dispatch_quant_gather(const mdc_shape* shape, const void* x, const float* expert_scales,

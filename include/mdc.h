@@ -223,6 +223,35 @@ mdc_status mdc_dispatch(const mdc_shape* shape,
                         void* stream);
 
 /* ------------------------------------------------------------------------
+ * mdc_dispatch without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments and results as
+ * mdc_dispatch minus the workspace: the workspace is the library's own
+ * static device array of MDC_NOALLOC_SCRATCH_BYTES, one per device, held
+ * until the process ends.  Shapes whose mdc_dispatch_workspace exceeds that
+ * size return MDC_ERR_UNSUPPORTED (at the share shape the workspace is about
+ * 0.53 MB; 8 MiB covers about two million routes).  The call allocates
+ * nothing; its first call on a device looks up that device's array.  All
+ * calls on one device share its array: calls that overlap on one device
+ * (other streams, other threads) race and must be ordered by the caller.
+ * The status block lives in that array and is not exposed by this call.
+ * ------------------------------------------------------------------------ */
+#define MDC_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+mdc_status mdc_dispatch_noalloc(const mdc_shape* shape,
+                                const void* x,
+                                const int32_t* expert_ids,
+                                const uint8_t* x_active_mask,
+                                const float* expert_scales,
+                                void* expand_x,
+                                int32_t* assist_info,
+                                int32_t* ep_recv_counts,
+                                int64_t* expert_token_nums,
+                                int32_t* expanded_row_idx,
+                                float* expand_scales,
+                                void* stream);
+
+/* ------------------------------------------------------------------------
  * Quantised dispatch ([CV4] parameter notes: commQuantMode 2 = int8
  * quantisation during communication, with per-row dynamic scales; [PTO]
  * FrontReorder Stage: quantised token rows carrying their scale).
