@@ -214,8 +214,8 @@ class HipEvents:
 def ceiling_leg(torch, mdc, w, wi, batches, stream, reps):
     """Memory ceilings measured with the committed probe kernels (libmdc_probe), timed like the bench's kernels.
 
-    Each probe launch is bracketed by HIP events on the launch stream, after an
-    untimed 512 MiB write that flushes the 256 MB Infinity Cache.  Streaming
+    Each probe launch is bracketed by two fence-free HIP events on the launch
+    stream, after an untimed 512 MiB write that flushes the 256 MB Infinity Cache.  Streaming
     ceilings: 1 GiB read-only, 1 GiB write-only, 1 GiB copy (2 GiB moved).
     Pattern probes (dispatch/combine workloads): the gather's read half (the U
     distinct source rows), its write half (the R rows in the gather's
@@ -230,18 +230,19 @@ def ceiling_leg(torch, mdc, w, wi, batches, stream, reps):
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1024, dtype=torch.int32, device=dev)
 
+    hip_ev = HipEvents()
+
     def timed(fn):
         out = []
         for i in range(reps + 2):
             probe.write(flush, flush.numel(), i, st)
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
+            a, b = hip_ev.pair()
+            hip_ev.record(a, stream)
             fn()
-            b.record(stream)
+            hip_ev.record(b, stream)
             torch.cuda.synchronize()
             if i >= 2:
-                out.append(a.elapsed_time(b) * 1e3)
+                out.append(hip_ev.elapsed_us(a, b))
         return out
 
     res = {}
@@ -301,7 +302,7 @@ def ceiling_leg(torch, mdc, w, wi, batches, stream, reps):
             "gather_read_plus_write_us": round(statistics.median(t_r) + statistics.median(t_w), 3),
             "combine_pattern_us": spread(t_c), "combine_pattern_bytes": (n_read + 2 * w.bs) * H2,
             "what": "plain probe kernels (libmdc_probe) of each kernel's access pattern at this workload's sizes, "
-                    "no metadata work; median of HIP-event durations with the Infinity Cache flushed",
+                    "no metadata work; median of fence-free HIP-event durations with the Infinity Cache flushed",
         }
     del flush
     torch.cuda.synchronize()
