@@ -219,8 +219,10 @@ def ceiling_leg(torch, mdc, w, wi, batches, stream, reps):
     ceilings: 1 GiB read-only, 1 GiB write-only, 1 GiB copy (2 GiB moved).
     Pattern probes (dispatch/combine workloads): the gather's read half (the U
     distinct source rows), its write half (the R rows in the gather's
-    token-major fan-out order) and the combine's pattern (each token's present
-    rows plus one more row read, one row written) at the workload's own sizes.
+    token-major fan-out order), both in one kernel (each source row read once
+    and written to its rows), and the combine's pattern (each token's present
+    rows, each destination's in its own memory region, plus one more row read,
+    one row written) at the workload's own sizes.
     """
     import numpy as np
     from combine_route_histogram_amd import probe
@@ -282,12 +284,21 @@ def ceiling_leg(torch, mdc, w, wi, batches, stream, reps):
         spare = batches[1 % len(batches)]["outs"][0]["expand_x"]
         t_r = timed(lambda: probe.rows_read(xflat, src_rows, H2, sink, st))
         t_w = timed(lambda: probe.rows_write(spare, off, dst_rows, H2, st))
+        t_f = timed(lambda: probe.rows_fanout(xflat, src_rows, off, dst_rows, spare, H2, st))
         # combine pattern: rank 0's routes read the rows they read in the step (row numbers within the
         # destination's buffer), here all from one buffer of the same size
         row0 = bt["row0"].cpu().numpy()
         ids0 = bt["ids0"].cpu().numpy()
         L = w.experts // w.world
-        rr = np.where((ids0 >= 0) & (ids0 < w.experts) & (row0 >= 0), row0, -1).astype(np.int32)
+        # destination j's rows live in region j of one buffer (regions sized by each destination's
+        # received rows), so that, as in the step, rows of different destinations are different memory
+        recv = np.array([min(int(o["ep_recv_counts"][-1].item()), w.capacity) for o in bt["outs"]], np.int64)
+        start_j = np.concatenate([[0], np.cumsum(recv)[:-1]])
+        dest = np.where((ids0 >= 0) & (ids0 < w.experts), ids0 // L, 0)
+        ok = (ids0 >= 0) & (ids0 < w.experts) & (row0 >= 0) & (row0 < recv[dest])
+        flat = start_j[dest] + row0
+        ok &= flat < w.capacity
+        rr = np.where(ok, flat, -1).astype(np.int32)
         if bt["mask0"] is not None:
             m0 = bt["mask0"].cpu().numpy().astype(bool)
             rr = np.where(m0 if m0.ndim == 2 else m0[:, None], rr, -1).astype(np.int32)
@@ -300,6 +311,7 @@ def ceiling_leg(torch, mdc, w, wi, batches, stream, reps):
             "gather_read_us": spread(t_r), "gather_read_bytes": len(uniq) * H2,
             "gather_write_us": spread(t_w), "gather_write_bytes": R * H2,
             "gather_read_plus_write_us": round(statistics.median(t_r) + statistics.median(t_w), 3),
+            "gather_fanout_us": spread(t_f), "gather_fanout_bytes": (len(uniq) + R) * H2,
             "combine_pattern_us": spread(t_c), "combine_pattern_bytes": (n_read + 2 * w.bs) * H2,
             "what": "plain probe kernels (libmdc_probe) of each kernel's access pattern at this workload's sizes, "
                     "no metadata work; median of fence-free HIP-event durations with the Infinity Cache flushed",

@@ -15,6 +15,9 @@
 //   probe_rows_write  write a constant to whole rows, each source row's
 //                     destination rows listed contiguously (the gather's
 //                     token-major fan-out write half)
+//   probe_rows_fanout read each listed source row once and write it to its
+//                     listed destination rows (the gather's data movement
+//                     without its metadata work)
 //   probe_rows_reduce for each output row, read its listed rows and one more
 //                     row of its own and write the XOR of them (the combine's
 //                     access pattern without its metadata prologue)
@@ -112,6 +115,31 @@ __global__ __launch_bounds__(64) void k_rows_write(v4u* __restrict__ dst, const 
   }
 }
 
+// Read source row src_rows[item] once (tile of 64 * VT vectors) and write it
+// to destination rows dst_rows[off[item] .. off[item+1]).
+template <int VT>
+__global__ __launch_bounds__(64) void k_rows_fanout(const v4u* __restrict__ src, const int32_t* __restrict__ src_rows,
+                                                    const int32_t* __restrict__ off, const int32_t* __restrict__ dst_rows,
+                                                    v4u* __restrict__ dst, int n_src, int nvec, int ntiles) {
+  const int item = blockIdx.x / ntiles, tile = blockIdx.x - item * ntiles;
+  if (item >= n_src) return;
+  const v4u* r = src + (int64_t)src_rows[item] * nvec;
+  v4u v[VT];
+#pragma unroll
+  for (int u = 0; u < VT; ++u) {
+    const int i = tile * 64 * VT + u * 64 + threadIdx.x;
+    v[u] = i < nvec ? ld(r + i) : v4u{0u, 0u, 0u, 0u};
+  }
+  for (int j = off[item]; j < off[item + 1]; ++j) {
+    v4u* d = dst + (int64_t)dst_rows[j] * nvec;
+#pragma unroll
+    for (int u = 0; u < VT; ++u) {
+      const int i = tile * 64 * VT + u * 64 + threadIdx.x;
+      if (i < nvec) st(d + i, v[u]);
+    }
+  }
+}
+
 // For output row t: read rows[t*K .. t*K + K) (entries < 0 are absent) of src
 // and row t of own, write their XOR to row t of dst.  One vector per lane;
 // KM >= K row slots, all loads issued before the first is used.
@@ -194,6 +222,20 @@ int mdc_probe_rows_write(void* dst, const int32_t* offsets, const int32_t* rows,
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_rows_write<7>, dim3((unsigned)((int64_t)n_src * ntiles)), dim3(64), 0, (hipStream_t)stream,
                      (v4u*)dst, offsets, rows, n_src, nvec, ntiles);
+  return status_of(hipGetLastError());
+}
+
+int mdc_probe_rows_fanout(const void* src, const int32_t* src_rows, const int32_t* offsets, const int32_t* dst_rows,
+                          void* dst, int32_t n_src, int32_t row_bytes, void* stream) {
+  if (src == nullptr || src_rows == nullptr || offsets == nullptr || dst_rows == nullptr || dst == nullptr ||
+      n_src < 0 || row_bytes <= 0 || (row_bytes & 15))
+    return 2;
+  if (n_src == 0) return 0;
+  const int nvec = row_bytes / 16;
+  const int ntiles = (nvec + 64 * 7 - 1) / (64 * 7);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_rows_fanout<7>, dim3((unsigned)((int64_t)n_src * ntiles)), dim3(64), 0, (hipStream_t)stream,
+                     (const v4u*)src, src_rows, offsets, dst_rows, (v4u*)dst, n_src, nvec, ntiles);
   return status_of(hipGetLastError());
 }
 

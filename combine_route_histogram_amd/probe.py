@@ -20,7 +20,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 EXPORTS = ("mdc_probe_read", "mdc_probe_write", "mdc_probe_copy", "mdc_probe_rows_read", "mdc_probe_rows_write",
-           "mdc_probe_rows_reduce")
+           "mdc_probe_rows_fanout", "mdc_probe_rows_reduce")
 
 _P, _U64, _I32, _U32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_uint32
 _lib.mdc_probe_read.argtypes = [_P, _U64, _P, _P]
@@ -28,6 +28,7 @@ _lib.mdc_probe_write.argtypes = [_P, _U64, _U32, _P]
 _lib.mdc_probe_copy.argtypes = [_P, _P, _U64, _P]
 _lib.mdc_probe_rows_read.argtypes = [_P, _P, _I32, _I32, _P, _P]
 _lib.mdc_probe_rows_write.argtypes = [_P, _P, _P, _I32, _I32, _P]
+_lib.mdc_probe_rows_fanout.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _P]
 _lib.mdc_probe_rows_reduce.argtypes = [_P, _P, _I32, _P, _P, _I32, _I32, _P]
 for _n in EXPORTS:
     getattr(_lib, _n).restype = ctypes.c_int
@@ -69,6 +70,14 @@ def rows_write(dst, offsets, rows, row_bytes: int, stream) -> None:
     assert offsets.dtype == torch.int32 and rows.dtype == torch.int32
     _ok(_lib.mdc_probe_rows_write(dst.data_ptr(), offsets.data_ptr(), rows.data_ptr(), offsets.numel() - 1,
                                   row_bytes, stream), "mdc_probe_rows_write")
+
+
+def rows_fanout(src, src_rows, offsets, dst_rows, dst, row_bytes: int, stream) -> None:
+    """src_rows: int32 [n_src]; offsets: int32 [n_src + 1] into dst_rows (int32 row indices of dst)."""
+    assert src_rows.dtype == offsets.dtype == dst_rows.dtype == torch.int32
+    assert offsets.numel() == src_rows.numel() + 1
+    _ok(_lib.mdc_probe_rows_fanout(src.data_ptr(), src_rows.data_ptr(), offsets.data_ptr(), dst_rows.data_ptr(),
+                                   dst.data_ptr(), src_rows.numel(), row_bytes, stream), "mdc_probe_rows_fanout")
 
 
 def rows_reduce(src, rows, k: int, own, dst, row_bytes: int, stream) -> None:

@@ -47,6 +47,13 @@ int mdc_probe_rows_read(const void* src, const int32_t* rows, int32_t n_rows, in
 int mdc_probe_rows_write(void* dst, const int32_t* offsets, const int32_t* rows, int32_t n_src, int32_t row_bytes,
                          void* stream);
 
+/* For each source item i < n_src, read row src_rows[i] of src once and write it
+ * to rows dst_rows[offsets[i] .. offsets[i+1]) of dst: the dispatch gather's
+ * whole data movement (read once, token-major fan-out writes) without its
+ * placement work. */
+int mdc_probe_rows_fanout(const void* src, const int32_t* src_rows, const int32_t* offsets, const int32_t* dst_rows,
+                          void* dst, int32_t n_src, int32_t row_bytes, void* stream);
+
 /* For each output row t < n_out, read rows rows[t*k .. t*k + k) of src
  * (negative entries are absent) and row t of own, and write their XOR to row t
  * of dst: the combine's access pattern (k <= 16). */
