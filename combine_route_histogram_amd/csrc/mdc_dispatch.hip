@@ -630,15 +630,16 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
   }
 
   // one pass over the keys: histogram cnt[le * W + s'], and the ranks of this
-  // token's routes (earlier routes of source s with the same key)
+  // token's routes (earlier routes of source s with the same key).  A rank is
+  // counted per wavefront with one ballot per top-k slot, only in the
+  // wavefronts that hold routes of [f_src, f_tok + K), and added to rank_s by
+  // one lane: at most K LDS atomics per such wavefront instead of one per
+  // matching route.
   {
     const int f_tok = tok * K, f_src = s * BS * K, routes_per_src = BS * K;
-    int kk[MDC_MAX_TOPK], c[MDC_MAX_TOPK];
+    int kk[MDC_MAX_TOPK];
 #pragma unroll
-    for (int k = 0; k < MDC_MAX_TOPK; ++k) {
-      kk[k] = k < K ? key_s[f_tok + k] : -1;
-      c[k] = 0;
-    }
+    for (int k = 0; k < MDC_MAX_TOPK; ++k) kk[k] = k < K ? key_s[f_tok + k] : -1;
     for (int f0 = 0; f0 < n; f0 += kSmallKeyBatch * kSmallThreads) {
       int key[kSmallKeyBatch];
 #pragma unroll
@@ -649,17 +650,18 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
 #pragma unroll
       for (int j = 0; j < kSmallKeyBatch; ++j) {
         const int f = f0 + tid + j * kSmallThreads;
-        if (key[j] < 0) continue;
-        atomicAdd(&cnt_s[key[j] * W + f / routes_per_src], 1);
-        if (f >= f_src && f < f_tok + K) {
+        if (key[j] >= 0) atomicAdd(&cnt_s[key[j] * W + f / routes_per_src], 1);
+        const bool near = key[j] >= 0 && f >= f_src && f < f_tok + K;
+        if (__ballot(near) != 0) {
 #pragma unroll
-          for (int k = 0; k < MDC_MAX_TOPK; ++k) c[k] += (key[j] == kk[k] && f < f_tok + k) ? 1 : 0;
+          for (int k = 0; k < MDC_MAX_TOPK; ++k) {
+            if (k >= K) break;
+            const uint64_t m = __ballot(near && key[j] == kk[k] && f < f_tok + k);
+            if (lane == 0 && m != 0) atomicAdd(&rank_s[k], __popcll(m));
+          }
         }
       }
     }
-#pragma unroll
-    for (int k = 0; k < MDC_MAX_TOPK; ++k)
-      if (c[k] != 0) atomicAdd(&rank_s[k], c[k]);
   }
   __syncthreads();
 
