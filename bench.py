@@ -27,6 +27,7 @@ import os
 import statistics
 import sys
 import time
+from dataclasses import replace
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -64,6 +65,10 @@ def parse():
     ap.add_argument("--ceiling-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget")
+    ap.add_argument("--ffn-path", default="kernels", choices=("kernels", "fused", "pipeline"),
+                    help="ffn workload: quantised gather then the FFN's stream-ordered kernels (mdc_dispatch_quant_"
+                         "gather + mdc_ffn_quant_input); the same with the FFN as one persistent kernel "
+                         "(MDC_FLAG_FFN_PIPELINE); or the dispatch and FFN as one pipeline (mdc_dispatch_ffn)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run three 256 MiB device copies (counter calibration)")
     return ap.parse_args()
@@ -452,6 +457,7 @@ def main():
     # runs the whole dispatch as one kernel at these sizes; the others use the two
     # stages so the rank and gather kernels are timed apart.
     one_shot = w.name in ("decode", "tiny")
+    pipelined = bool(w.inter) and args.ffn_path == "pipeline"
     for bt in batches:
         o0 = bt["outs"][0]
         bt["layout"] = mdc.prepare_dispatch_layout(shape, bt["ids"], bt["mask"], o0["workspace"], stream)
@@ -460,6 +466,8 @@ def main():
             bt["gather"] = mdc.prepare_dispatch(shape, bt["x"], bt["ids"], bt["mask"], o0["expand_x"],
                                                 o0["assist_info"], o0["ep_recv_counts"], o0["expert_token_nums"],
                                                 bt["row_idx"], o0["workspace"], stream)
+        elif w.inter and pipelined:
+            bt["gather"] = None   # the dispatch runs inside the FFN pipeline
         elif w.inter:
             # the FFN workload dispatches int8 rows with per-row scales and feeds them to the FFN
             bt["gather"] = mdc.prepare_dispatch_quant_gather(shape, bt["x"], o0["expand_q"], o0["dyn_scales"],
@@ -472,8 +480,14 @@ def main():
                                                        bt["row_idx"], o0["workspace"], stream)
         seg0 = o0["expand_x"]
         bt["ffn"] = None
-        if ffn_w is not None:
-            bt["ffn"] = mdc.prepare_ffn_quant_input(shape, w.inter, o0["expand_q"], o0["dyn_scales"],
+        if ffn_w is not None and pipelined:
+            bt["ffn"] = mdc.prepare_dispatch_ffn(shape, w.inter, bt["x"], o0["expand_q"], o0["dyn_scales"],
+                                                 o0["assist_info"], o0["ep_recv_counts"], o0["expert_token_nums"],
+                                                 bt["row_idx"], *ffn_w, o0["y"], o0["workspace"], ffn_ws, stream)
+            seg0 = o0["y"]
+        elif ffn_w is not None:
+            fsh = replace(shape, flags=mdc.MDC_FLAG_FFN_PIPELINE) if args.ffn_path == "fused" else shape
+            bt["ffn"] = mdc.prepare_ffn_quant_input(fsh, w.inter, o0["expand_q"], o0["dyn_scales"],
                                                     o0["expert_token_nums"], *ffn_w, o0["y"], ffn_ws, stream)
             seg0 = o0["y"]
         bt["combine"] = mdc.prepare_combine(shape, [seg0] + [o["expand_x"] for o in bt["outs"][1:]],
@@ -495,7 +509,8 @@ def main():
                 bt["layout"]()
             if bracket == "gather":
                 rec(0)
-            bt["gather"]()
+            if bt["gather"] is not None:
+                bt["gather"]()
             if bracket == "gather":
                 rec(1)
             if bt["ffn"] is not None:
@@ -510,7 +525,8 @@ def main():
         if bt["layout"] is not None:
             bt["layout"]()
         rec(1)
-        bt["gather"]()
+        if bt["gather"] is not None:
+            bt["gather"]()
         rec(2)
         if bt["ffn"] is not None:
             bt["ffn"]()
@@ -612,11 +628,25 @@ def main():
                                     f"on timed steps {evs_idx[:3]}..{evs_idx[-1:]} (never the first)"}
     if ceil is not None:
         roofline["frac_of_copy_ceiling"] = round(dom[1] / ceil["copy_1GiB"]["gbps"], 4)
-    if ffn_info is not None:
-        roofline = {"bound": "mfma", "kernel": "mdc_ffn_quant_input (k_ffn_plan, k_ffn_gemm GMM1 + SwiGLU, k_ffn_quant_rows, k_ffn_gemm GMM2)",
+    if ffn_info is not None and pipelined:
+        roofline = {"bound": "mfma", "kernel": "mdc_dispatch_ffn (k_dfn_plan, k_dfn_route, k_ffn_fused: quantised "
+                                              "dispatch, GMM1 + SwiGLU, quantisation of g, GMM2)",
                     "achieved": ffn_info["tops"], "peak": INT8_PEAK_TOPS, "unit": "TOP/s (int8)",
                     "frac": ffn_info["mfma_frac"],
-                    "traffic": measured_traffic(w.name, ("k_ffn_plan", "k_ffn_gemm<true", "k_ffn_quant_rows",
+                    "traffic": measured_traffic(w.name + "_pipeline", ("k_dfn_plan", "k_dfn_route", "k_ffn_fused")),
+                    "ops_per_launch": ffn_info["int8_ops"],
+                    "avg_launch_us": ffn_info["us"], "launch_us": ffn_info["spread_us"],
+                    "launch_time_from": "median of two fence-free HIP events on the launch stream around the "
+                                        f"mdc_dispatch_ffn call (its dispatch included), on timed steps "
+                                        f"{evs_idx[:3]}..{evs_idx[-1:]}"}
+    elif ffn_info is not None:
+        roofline = {"bound": "mfma", "kernel": "mdc_ffn_quant_input (k_ffn_plan, k_ffn_fused: GMM1 + SwiGLU, quantisation "
+                                              "of g, GMM2)" if args.ffn_path == "fused" else
+                    "mdc_ffn_quant_input (k_ffn_plan, k_ffn_gemm GMM1 + SwiGLU, k_ffn_quant_rows, k_ffn_gemm GMM2)",
+                    "achieved": ffn_info["tops"], "peak": INT8_PEAK_TOPS, "unit": "TOP/s (int8)",
+                    "frac": ffn_info["mfma_frac"],
+                    "traffic": None if args.ffn_path == "fused" else
+                    measured_traffic(w.name, ("k_ffn_plan", "k_ffn_gemm<true", "k_ffn_quant_rows",
                                                          "k_ffn_gemm<false")),
                     "ops_per_launch": ffn_info["int8_ops"],
                     "avg_launch_us": ffn_info["us"], "launch_us": ffn_info["spread_us"],
@@ -640,7 +670,9 @@ def main():
                    "rows_received": by["R"], "source_rows_read": by["U"],
                    "zero_experts": w.zero_experts, "copy_experts": w.copy_experts,
                    "mask": None if wi.mask is None else ("per route" if wi.mask.ndim == 3 else "per token"),
-                   "dispatch_call": "mdc_dispatch (one launch)" if one_shot else "mdc_dispatch_layout + gather"},
+                   "dispatch_call": "mdc_dispatch (one launch)" if one_shot else
+                   ("mdc_dispatch_layout + mdc_dispatch_ffn (dispatch inside the FFN pipeline)" if pipelined
+                    else "mdc_dispatch_layout + gather")},
         "hbm_gbps": round(gb_step, 1),
         "hbm_frac_of_peak": round(gb_step / HBM_PEAK_GBPS, 4),
         "hbm_frac_of_copy_ceiling": None if ceil is None else round(gb_step / ceil["copy_1GiB"]["gbps"], 4),

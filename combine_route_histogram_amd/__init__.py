@@ -31,7 +31,7 @@ import torch  # noqa: E402
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-MDC_ABI_VERSION = 3
+MDC_ABI_VERSION = 4
 MDC_OK = 0
 MDC_ERR_NULLPTR = 1
 MDC_ERR_INVALID = 2
@@ -50,7 +50,7 @@ EXPORTS = (
     "mdc_dispatch_workspace", "mdc_dispatch_workspace_size", "mdc_dispatch_layout", "mdc_dispatch_gather",
     "mdc_dispatch", "mdc_combine_workspace", "mdc_combine_workspace_size", "mdc_combine",
     "mdc_ffn_workspace", "mdc_ffn_workspace_size", "mdc_ffn", "mdc_dispatch_quant", "mdc_dispatch_quant_gather",
-    "mdc_ffn_quant_input", "mdc_dispatch_noalloc",
+    "mdc_ffn_quant_input", "mdc_dispatch_noalloc", "mdc_dispatch_ffn",
 )
 
 
@@ -92,6 +92,8 @@ _sig("mdc_combine", _SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S
 _sig("mdc_ffn", _SHP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P)
 _sig("mdc_ffn_quant_input", _SHP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P)
 _sig("mdc_dispatch_noalloc", _SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P)
+_sig("mdc_dispatch_ffn", _SHP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P,
+     _SZ, _P)
 MDC_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
@@ -448,6 +450,23 @@ def prepare_dispatch_noalloc(shape: Shape, x, expert_ids, x_active_mask, expand_
     return Prepared(_lib.mdc_dispatch_noalloc, args, "mdc_dispatch_noalloc", (sh, _tensors(locals())))
 
 
+def prepare_dispatch_ffn(shape: Shape, inter_n: int, x, expand_q, dynamic_scales, assist_info, ep_recv_counts,
+                         expert_token_nums, expanded_row_idx, w1, w1_scale, w2, w2_scale, y, dispatch_workspace,
+                         ffn_workspace, stream=None, expert_scales=None, expand_scales=None) -> Prepared:
+    """Quantised dispatch + grouped FFN as one pipeline (after mdc_dispatch_layout on dispatch_workspace)."""
+    _check_dispatch_inputs(shape, x, None, None, expert_scales)
+    _check_dispatch_outputs(shape, expand_q, torch.int8, assist_info, ep_recv_counts, expert_token_nums,
+                            expanded_row_idx, expand_scales, dynamic_scales)
+    _check_ffn_weights(shape, inter_n, expert_token_nums, w1, w1_scale, w2, w2_scale, y)
+    sh = shape.c()
+    args = (ctypes.byref(sh), int(inter_n), _ptr(x), _ptr(expert_scales), _ptr(expand_q), _ptr(dynamic_scales),
+            _ptr(assist_info), _ptr(ep_recv_counts), _ptr(expert_token_nums), _ptr(expanded_row_idx),
+            _ptr(expand_scales), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(y),
+            _ptr(dispatch_workspace), _nbytes(dispatch_workspace), _ptr(ffn_workspace), _nbytes(ffn_workspace),
+            _stream(stream))
+    return Prepared(_lib.mdc_dispatch_ffn, args, "mdc_dispatch_ffn", (sh, _tensors(locals())))
+
+
 # ----------------------------------------------------------------------------
 # one-shot calls (marshal and launch)
 # ----------------------------------------------------------------------------
@@ -514,6 +533,14 @@ def mdc_dispatch_noalloc(shape: Shape, x, expert_ids, x_active_mask, expand_x, a
     return _run(prepare_dispatch_noalloc(shape, x, expert_ids, x_active_mask, expand_x, assist_info, ep_recv_counts,
                                          expert_token_nums, expanded_row_idx, stream, expert_scales, expand_scales),
                 check)
+
+
+def mdc_dispatch_ffn(shape: Shape, inter_n: int, x, expand_q, dynamic_scales, assist_info, ep_recv_counts,
+                     expert_token_nums, expanded_row_idx, w1, w1_scale, w2, w2_scale, y, dispatch_workspace,
+                     ffn_workspace, stream=None, check: bool = True, expert_scales=None, expand_scales=None) -> int:
+    return _run(prepare_dispatch_ffn(shape, inter_n, x, expand_q, dynamic_scales, assist_info, ep_recv_counts,
+                                     expert_token_nums, expanded_row_idx, w1, w1_scale, w2, w2_scale, y,
+                                     dispatch_workspace, ffn_workspace, stream, expert_scales, expand_scales), check)
 
 
 def alloc_dispatch_outputs(shape: Shape, device="cuda"):

@@ -36,7 +36,7 @@
 
 #include <mutex>
 
-#include "mdc_common.h"
+#include "mdc_route.h"
 
 // Workspace of mdc_dispatch_noalloc, for callers that cannot allocate: one
 // copy per device, zero at load, held until the process ends.  Host code
@@ -82,28 +82,6 @@ namespace {
 #ifndef MDC_COMBINE_NT_STORES
 #define MDC_COMBINE_NT_STORES 1
 #endif
-// Routes per rank group: 1024 (one step of a 1024-thread rank workgroup)
-// measured 0.9 us faster per share step than 2048; 512 makes every gather
-// wavefront scan 8 counter chunks, and 4096 halves the rank kernel's width.
-#ifndef MDC_GROUP_ROUTES
-#define MDC_GROUP_ROUTES 1024
-#endif
-#ifndef MDC_SCAN_IPL
-#define MDC_SCAN_IPL 16
-#endif
-constexpr int kGroupRoutes = MDC_GROUP_ROUTES;  // routes of one source ranked by one k_route_rank workgroup
-constexpr int kScanIPL = MDC_SCAN_IPL;           // group counters per lane per scan chunk
-constexpr int kScanChunk = 64 * kScanIPL;
-
-// Group counters are scanned in chunks of kScanChunk, lane l taking the
-// kScanIPL consecutive counters l*kScanIPL.. of a chunk.  They are stored
-// transposed inside each chunk (counter j of lane l at j*64 + l) so that the
-// j-th load of all 64 lanes reads 64 consecutive words.
-__host__ __device__ __forceinline__ int counter_slot(int i) {
-  const int c0 = i - i % kScanChunk;
-  const int r = i - c0;
-  return c0 + (r % kScanIPL) * 64 + r / kScanIPL;
-}
 constexpr int kGatherVec = MDC_GATHER_VEC;
 constexpr int kGatherSmallVec = MDC_GATHER_SMALL_VEC;      // tile of the tokens with many rows here
 static_assert(kGatherSmallVec >= 1 && kGatherSmallVec < 5, "small tiles must be smaller than the tiles they replace");
@@ -319,32 +297,6 @@ __device__ void write_totals(const int32_t* __restrict__ cnt, const int32_t* __r
 // loads it, finds the token's rows (in-wavefront scan of the group
 // counters) and writes the tile to each of them; tile 0 also writes the
 // triplets and inverse-index entries, and the writer wavefront the counts.
-// Pointers the gather kernels share beyond the rows themselves.
-struct GatherMeta {
-  const int32_t* P;           // packed (local expert, rank) per route
-  const int32_t* cnt;         // group counters (transposed chunks)
-  const int32_t* drop;        // dropped ids per rank group
-  mdc_device_status* status;  // the workspace's status block
-  const float* scales_in;     // [W][BS][K] route weights, or NULL
-  float* scales_out;          // [A] expand_scales, or NULL
-  int32_t* assist;
-  int32_t* ep_recv;
-  int64_t* expert_nums;
-  int32_t* row_idx;
-};
-
-// Tile-0 work of a route placed at `row`: inverse-index entry, triplet and
-// the weight that travels with the row.
-__device__ __forceinline__ void place_route(const GatherMeta& m, int64_t g, int K, int s, int t, int lane, int row) {
-  m.row_idx[g * K + lane] = row;
-  if (row >= 0) {
-    int32_t* a = m.assist + (int64_t)row * 3;
-    a[0] = s;
-    a[1] = t;
-    a[2] = lane;
-    if (m.scales_out != nullptr) m.scales_out[row] = m.scales_in[g * K + lane];
-  }
-}
 
 template <int V>
 __device__ __forceinline__ void gather_tile(
@@ -450,7 +402,6 @@ __global__ __launch_bounds__(64 * MDC_GATHER_WAVES) void k_dispatch_gather(
 // triplets, inverse index and counts are those of k_dispatch_gather.
 // Rows of up to 64 * 16 vectors (H <= 8192) are held in registers.
 // ---------------------------------------------------------------------------
-constexpr int kQuantRowVec = 16;
 
 template <int VPL>
 __global__ __launch_bounds__(64) void k_dispatch_gather_q(
@@ -488,29 +439,8 @@ __global__ __launch_bounds__(64) void k_dispatch_gather_q(
   if (writer) write_totals(cnt, m.drop, m.expert_nums, m.status, L, W, G, total, A, lane);
   if (has == 0) return;
 
-  // per-row quantisation, decided in fp32
-  float amax = 0.f;
-#pragma unroll
-  for (int u = 0; u < VPL; ++u)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[u][w])), fabsf(bf16_hi(v[u][w]))));
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-  const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-  const float scale = amax / 127.0f;
   uint64_t qv[VPL];
-#pragma unroll
-  for (int u = 0; u < VPL; ++u) {
-    uint64_t packed = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float a = fminf(fmaxf(rintf(bf16_lo(v[u][w]) * inv), -127.f), 127.f);
-      const float b = fminf(fmaxf(rintf(bf16_hi(v[u][w]) * inv), -127.f), 127.f);
-      packed |= (uint64_t)(uint8_t)(int8_t)(int)a << (16 * w);
-      packed |= (uint64_t)(uint8_t)(int8_t)(int)b << (16 * w + 8);
-    }
-    qv[u] = packed;
-  }
+  const float scale = quant_row<VPL>(v, qv);
 
   int row = -1;
   if (mine) {
@@ -1031,45 +961,7 @@ __global__ __launch_bounds__(1024) void k_combine_perf(const CombineRecord* __re
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-struct DispatchPlan {
-  int W, d, BS, H, K, E, L, TPG, G, nvec, rank_threads, mask_per_route, n_ids;
-  int64_t A;
-  size_t off_drop, off_p, off_cnt, bytes;
-};
 
-// Workspace: [status block][drop: W*G int32][P: W*BS*K int32][group counters].
-DispatchPlan make_plan(const mdc_shape* sh) {
-  DispatchPlan p;
-  p.W = sh->world;
-  p.d = sh->rank;
-  p.BS = sh->bs;
-  p.H = sh->hidden;
-  p.K = sh->topk;
-  p.E = sh->num_experts;
-  p.L = p.E / p.W;
-  p.A = sh->capacity;
-  p.mask_per_route = sh->mask_per_route;
-  p.n_ids = sh->num_experts + sh->zero_experts + sh->copy_experts;
-  p.TPG = kGroupRoutes / p.K;
-  p.G = (p.BS + p.TPG - 1) / p.TPG;
-  p.nvec = p.H / 8;
-  // wave_cnt[nw][L] + carry[L] must fit in LDS: 16 wavefronts up to L = 512, 4 beyond
-  p.rank_threads = p.L <= 512 ? 1024 : 256;
-  const size_t routes = (size_t)p.W * p.BS * p.K;
-  const size_t counters = round_up((size_t)p.L * p.W * p.G, kScanChunk);
-  p.off_drop = MDC_STATUS_BYTES;
-  p.off_p = p.off_drop + round_up((size_t)p.W * p.G * 4, 256);
-  p.off_cnt = p.off_p + round_up(routes * 4, 256);
-  p.bytes = p.off_cnt + round_up(counters * 4, 256);
-  return p;
-}
-
-GatherMeta make_meta(const DispatchPlan& p, char* ws, const float* scales_in, float* scales_out, int32_t* assist,
-                     int32_t* ep_recv, int64_t* expert_nums, int32_t* row_idx) {
-  return GatherMeta{reinterpret_cast<const int32_t*>(ws + p.off_p), reinterpret_cast<const int32_t*>(ws + p.off_cnt),
-                    reinterpret_cast<const int32_t*>(ws + p.off_drop), reinterpret_cast<mdc_device_status*>(ws),
-                    scales_in, scales_out, assist, ep_recv, expert_nums, row_idx};
-}
 
 mdc_status layout_impl(const DispatchPlan& p, const int32_t* ids, const uint8_t* mask, char* ws, hipStream_t st) {
   int32_t* P = reinterpret_cast<int32_t*>(ws + p.off_p);
@@ -1162,19 +1054,6 @@ mdc_status small_impl(const DispatchPlan& p, const void* x, const int32_t* ids, 
 
 // Pointer checks of the gather stage (shared by the four dispatch entry points
 // that place rows).  `rows` is expand_x or expand_q.
-mdc_status check_gather_args(const DispatchPlan& p, const void* x, const void* rows, const float* dyn_scale,
-                             bool quant, int32_t* assist, int32_t* ep_recv, int64_t* expert_nums, int32_t* row_idx,
-                             const float* scales_in, float* scales_out, const void* ws, size_t ws_bytes) {
-  if (quant && p.nvec > 64 * kQuantRowVec) return MDC_ERR_UNSUPPORTED;
-  if (ws == nullptr || ep_recv == nullptr || expert_nums == nullptr) return MDC_ERR_NULLPTR;
-  if (p.BS > 0 && (x == nullptr || row_idx == nullptr)) return MDC_ERR_NULLPTR;
-  if (p.BS > 0 && p.A > 0 && (rows == nullptr || assist == nullptr || (quant && dyn_scale == nullptr)))
-    return MDC_ERR_NULLPTR;
-  if (scales_out != nullptr && scales_in == nullptr) return MDC_ERR_NULLPTR;
-  if (!aligned16(x) || !aligned16(rows)) return MDC_ERR_INVALID;
-  if (ws_bytes < p.bytes) return MDC_ERR_WORKSPACE;
-  return MDC_OK;
-}
 
 // Combine tiles: 64 * kCombineVec vectors per lane for K <= 8, one vector
 // per lane otherwise.
@@ -1327,9 +1206,11 @@ int32_t mdc_abi_version(void) { return MDC_ABI_VERSION; }
 
 mdc_status mdc_dispatch_workspace(const mdc_shape* shape, size_t* bytes) {
   if (bytes == nullptr) return MDC_ERR_NULLPTR;
-  const mdc_status st = check_shape(shape);
+  mdc_status st = check_shape(shape);
   if (st != MDC_OK) return st;
-  *bytes = make_plan(shape).bytes;
+  const DispatchPlan p = make_plan(shape);
+  if ((st = check_plan(p)) != MDC_OK) return st;
+  *bytes = p.bytes;
   return MDC_OK;
 }
 
@@ -1342,6 +1223,7 @@ mdc_status mdc_dispatch_layout(const mdc_shape* shape, const int32_t* expert_ids
   mdc_status st = check_shape(shape);
   if (st != MDC_OK) return st;
   const DispatchPlan p = make_plan(shape);
+  if ((st = check_plan(p)) != MDC_OK) return st;
   if (workspace == nullptr) return MDC_ERR_NULLPTR;
   if (p.BS > 0 && expert_ids == nullptr) return MDC_ERR_NULLPTR;
   if (workspace_bytes < p.bytes) return MDC_ERR_WORKSPACE;
@@ -1355,6 +1237,7 @@ mdc_status mdc_dispatch_gather(const mdc_shape* shape, const void* x, const floa
   mdc_status st = check_shape(shape);
   if (st != MDC_OK) return st;
   const DispatchPlan p = make_plan(shape);
+  if ((st = check_plan(p)) != MDC_OK) return st;
   st = check_gather_args(p, x, expand_x, nullptr, false, assist_info, ep_recv_counts, expert_token_nums,
                          expanded_row_idx, expert_scales, expand_scales, workspace, workspace_bytes);
   if (st != MDC_OK) return st;
@@ -1372,6 +1255,7 @@ mdc_status mdc_dispatch(const mdc_shape* shape, const void* x, const int32_t* ex
   mdc_status st = check_shape(shape);
   if (st != MDC_OK) return st;
   const DispatchPlan p = make_plan(shape);
+  if ((st = check_plan(p)) != MDC_OK) return st;
   if (p.BS > 0 && expert_ids == nullptr) return MDC_ERR_NULLPTR;
   st = check_gather_args(p, x, expand_x, nullptr, false, assist_info, ep_recv_counts, expert_token_nums,
                          expanded_row_idx, expert_scales, expand_scales, workspace, workspace_bytes);
@@ -1393,6 +1277,7 @@ mdc_status mdc_dispatch_noalloc(const mdc_shape* shape, const void* x, const int
   mdc_status st = check_shape(shape);
   if (st != MDC_OK) return st;
   const DispatchPlan p = make_plan(shape);
+  if ((st = check_plan(p)) != MDC_OK) return st;
   if (p.bytes > (size_t)MDC_NOALLOC_SCRATCH_BYTES) return MDC_ERR_UNSUPPORTED;
   void* ws = noalloc_scratch();
   if (ws == nullptr) return MDC_ERR_HIP;
@@ -1410,6 +1295,7 @@ mdc_status mdc_dispatch_quant_gather(const mdc_shape* shape, const void* x, cons
   mdc_status st = check_shape(shape);
   if (st != MDC_OK) return st;
   const DispatchPlan p = make_plan(shape);
+  if ((st = check_plan(p)) != MDC_OK) return st;
   st = check_gather_args(p, x, expand_q, dynamic_scales, true, assist_info, ep_recv_counts, expert_token_nums,
                          expanded_row_idx, expert_scales, expand_scales, workspace, workspace_bytes);
   if (st != MDC_OK) return st;
@@ -1427,6 +1313,7 @@ mdc_status mdc_dispatch_quant(const mdc_shape* shape, const void* x, const int32
   mdc_status st = check_shape(shape);
   if (st != MDC_OK) return st;
   const DispatchPlan p = make_plan(shape);
+  if ((st = check_plan(p)) != MDC_OK) return st;
   if (p.BS > 0 && expert_ids == nullptr) return MDC_ERR_NULLPTR;
   st = check_gather_args(p, x, expand_q, dynamic_scales, true, assist_info, ep_recv_counts, expert_token_nums,
                          expanded_row_idx, expert_scales, expand_scales, workspace, workspace_bytes);

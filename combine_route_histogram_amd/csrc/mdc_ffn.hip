@@ -4,7 +4,7 @@
 // Source: "PTO MegaMoE Dispatch + Combine Fusion Example", GMM1 / SwiGLU /
 // GMM2 stages and the per-token dynamic quantisation between them.
 
-#include "mdc_common.h"
+#include "mdc_route.h"
 
 namespace {
 
@@ -28,6 +28,7 @@ namespace {
 // as one persistent kernel with ready counters between them (k_ffn_fused).
 // ---------------------------------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kFfnBM = 256;        // token rows per tile
@@ -79,18 +80,33 @@ __device__ int64_t plan_scan_pair(int64_t a, int64_t b, int64_t* wsum, int64_t& 
   return excl;
 }
 
-// sync_words (optional, the fused kernel's): [0] queue head, [1] unused,
-// done1 at [2, 2 + MT), ready at [2 + stride, 2 + stride + MT); amax_bits
-// for the rows in use.  All of them are zeroed here, and so is the
+// The fused kernel's synchronisation words (sync_words, stride = the
+// table's capacity in m-tiles): [0] queue head, [1] unused, then done1,
+// ready and rows_ready at [2 + i * stride, 2 + i * stride + MT) for
+// i = 0, 1, 2, then emt[L] (first m-tile of each expert) and elo[L] (its
+// first row).
+struct FfnSyncLayout {
+  int* w;
+  int stride, L;
+  __host__ __device__ int* next() const { return w; }
+  __host__ __device__ int* done1() const { return w + 2; }
+  __host__ __device__ int* ready() const { return w + 2 + stride; }
+  __host__ __device__ int* rows_ready() const { return w + 2 + 2 * stride; }
+  __host__ __device__ int* emt() const { return w + 2 + 3 * stride; }
+  __host__ __device__ int* elo() const { return w + 2 + 3 * stride + L; }
+  __host__ __device__ static size_t words(int stride, int L) { return 2 + 3 * (size_t)stride + 2 * (size_t)L; }
+};
+
+// Builds the tile plan from the expert counts c0, c1 of experts 2t and
+// 2t + 1 (thread t; zero past L); with sw.w != NULL it also zeroes the
+// fused kernel's synchronisation words and amax_bits for the rows in use
+// and records each expert's first m-tile and first row.  Zeroes the
 // workspace's status block.
-__global__ __launch_bounds__(kPlanThreads) void k_ffn_plan(const int64_t* __restrict__ expert_nums, int L, int64_t A,
-                                                           int4* __restrict__ tiles, int* __restrict__ sync_words,
-                                                           int stride, uint32_t* __restrict__ amax_bits,
-                                                           mdc_device_status* __restrict__ status) {
-  __shared__ int64_t wsum[kPlanThreads / 64 + 1];
+__device__ void ffn_plan_body(int64_t c0, int64_t c1, int L, int64_t A, int4* __restrict__ tiles, FfnSyncLayout sw,
+                              uint32_t* __restrict__ amax_bits, mdc_device_status* __restrict__ status,
+                              int64_t* wsum) {
   const int tid = threadIdx.x;
   const int e0 = 2 * tid, e1 = 2 * tid + 1;
-  const int64_t c0 = e0 < L ? expert_nums[e0] : 0, c1 = e1 < L ? expert_nums[e1] : 0;
   int64_t total;
   const int64_t x0 = plan_scan_pair(c0, c1, wsum, total);   // first row of e0 (unclipped)
   const int64_t x1 = x0 + c0;
@@ -116,21 +132,129 @@ __global__ __launch_bounds__(kPlanThreads) void k_ffn_plan(const int64_t* __rest
       }
       tiles[1 + slot + j] = int4{e, lo + j * kFfnBM, hi, (pos << 8) | size};
     }
+    if (sw.w != nullptr && e < L) {
+      sw.emt()[e] = slot;
+      sw.elo()[e] = lo;
+    }
   }
   if (tid == 0) {
     tiles[0] = int4{(int)nm, 0, 0, 0};
     *status = mdc_device_status{0, 0, 0, 0};
   }
-  if (sync_words != nullptr) {
+  if (sw.w != nullptr) {
     const int MT = (int)nm;
-    if (tid < 2) sync_words[tid] = 0;
+    if (tid < 2) sw.w[tid] = 0;
     for (int i = tid; i < MT; i += kPlanThreads) {
-      sync_words[2 + i] = 0;
-      sync_words[2 + stride + i] = 0;
+      sw.done1()[i] = 0;
+      sw.ready()[i] = 0;
+      sw.rows_ready()[i] = 0;
     }
     const int64_t rows = min(total, A);
     for (int64_t r = tid; r < rows; r += kPlanThreads) amax_bits[r] = 0u;
   }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void k_ffn_plan(const int64_t* __restrict__ expert_nums, int L, int64_t A,
+                                                           int4* __restrict__ tiles, FfnSyncLayout sw,
+                                                           uint32_t* __restrict__ amax_bits,
+                                                           mdc_device_status* __restrict__ status) {
+  __shared__ int64_t wsum[kPlanThreads / 64 + 1];
+  const int e0 = 2 * threadIdx.x, e1 = e0 + 1;
+  const int64_t c0 = e0 < L ? expert_nums[e0] : 0, c1 = e1 < L ? expert_nums[e1] : 0;
+  ffn_plan_body(c0, c1, L, A, tiles, sw, amax_bits, status, wsum);
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined dispatch + FFN (mdc_dispatch_ffn), launch 1 of 3.  One workgroup
+// scans the group counters left by mdc_dispatch_layout once, in (le, s, g)
+// order ([TL] GetCumSum; [PTO] FrontReorder publishes the prefix metadata
+// once for every later stage): the exclusive prefix at a group is the first
+// row of its routes (base), the inclusive prefix at (le, s, G - 1) is
+// epRecvCounts[le*W + s], the difference across le's groups is
+// expertTokenNums[le].  It fills the dispatch status block as the gather
+// kernels do, then builds the FFN tile plan from the counts.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kPlanThreads) void k_dfn_plan(
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ drop, int32_t* __restrict__ base, int L, int W,
+    int G, int64_t A, int32_t* __restrict__ ep_recv, int64_t* __restrict__ expert_nums,
+    mdc_device_status* __restrict__ dstatus, int4* __restrict__ tiles, FfnSyncLayout sw,
+    uint32_t* __restrict__ amax_bits, mdc_device_status* __restrict__ fstatus) {
+  __shared__ int64_t wsum[kPlanThreads / 64 + 1];
+  __shared__ int ecnt[2 * kPlanThreads];   // per-expert counts (L <= 2048)
+  __shared__ int drop_s;
+  const int tid = threadIdx.x;
+  const int n = L * W * G;   // below 2^31 (host check)
+  const int span = W * G;    // counters per expert
+  constexpr int kPer = 4;    // consecutive counters per thread per chunk
+  for (int e = tid; e < L; e += kPlanThreads) ecnt[e] = 0;
+  if (tid == 0) drop_s = 0;
+  int dropped = 0;
+  for (int i = tid; i < span; i += kPlanThreads) dropped += drop[i];
+  __syncthreads();
+  if (dropped != 0) atomicAdd(&drop_s, dropped);
+  int64_t carry = 0;
+  for (int c0 = 0; c0 < n; c0 += kPlanThreads * kPer) {
+    const int i0 = c0 + tid * kPer;
+    int v[kPer];
+    int64_t own = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      v[j] = i0 + j < n ? cnt[counter_slot(i0 + j)] : 0;
+      own += v[j];
+    }
+    int64_t tot;
+    int64_t run = carry + plan_scan_pair(own, 0, wsum, tot);
+    // bases, epRecvCounts (inclusive prefix at each (le, s)'s last group) and
+    // the per-expert sums, from the counters this thread holds
+    int e_cur = -1, e_sum = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = i0 + j;
+      if (i < n) {
+        base[i] = (int32_t)run;
+        if (i % G == G - 1) ep_recv[i / G] = (int32_t)(run + v[j]);
+        const int e = i / span;
+        if (e != e_cur) {
+          if (e_sum != 0) atomicAdd(&ecnt[e_cur], e_sum);
+          e_cur = e;
+          e_sum = 0;
+        }
+        e_sum += v[j];
+      }
+      run += v[j];
+    }
+    if (e_sum != 0) atomicAdd(&ecnt[e_cur], e_sum);
+    carry += tot;
+  }
+  if (tid == 0) base[n] = (int32_t)carry;
+  if (G == 0)   // no tokens: no groups, every count is zero
+    for (int i = tid; i < L * W; i += kPlanThreads) ep_recv[i] = 0;
+  __syncthreads();
+  const int e0 = 2 * tid, e1 = e0 + 1;
+  const int64_t c0 = e0 < L ? ecnt[e0] : 0, c1 = e1 < L ? ecnt[e1] : 0;
+  if (e0 < L) expert_nums[e0] = c0;
+  if (e1 < L) expert_nums[e1] = c1;
+  if (tid == 0) {
+    const int64_t over = carry - A;
+    *dstatus = mdc_device_status{drop_s, over > 0 ? (int32_t)over : 0, 0, 0};
+  }
+  ffn_plan_body(c0, c1, L, A, tiles, sw, amax_bits, fstatus, wsum);
+}
+
+// Launch 2 of 3: places every route sent here (one thread per route):
+// row = base of its group + its rank, dropped past the capacity; writes the
+// inverse index, the (source, token, k) triplet and the route's weight as
+// the gather kernels' tile-0 work does.
+__global__ __launch_bounds__(256) void k_dfn_route(GatherMeta m, const int32_t* __restrict__ base, int BS, int K,
+                                                   int L, int W, int TPG, int G, int64_t A, int n_routes) {
+  const int f = blockIdx.x * 256 + threadIdx.x;
+  if (f >= n_routes) return;
+  const int p = m.P[f];
+  if (p < 0 || (p & 0xFFFF) >= L) return;
+  const int g = f / K, k = f - g * K;
+  const int s = g / BS, t = g - s * BS;
+  const int64_t r = (int64_t)base[((p & 0xFFFF) * W + s) * G + t / TPG] + (p >> 16);
+  place_route(m, g, K, s, t, k, r < A ? (int)r : -1);
 }
 
 __device__ __forceinline__ float ffn_silu(float a) { return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
@@ -731,21 +855,104 @@ struct FfnSync {
   int* next;              // work-queue head
   int* done1;             // [MT] GMM1 tiles finished per m-tile
   int* ready;             // [MT] 1 once the m-tile's g rows are quantised
+  int* rows_ready;        // [MT] rows of the m-tile dispatched (pipelined dispatch only)
   uint32_t* amax_bits;    // [rows] max |g| per row (fp32 bits)
   mdc_device_status* status;   // wait_timeouts counts the waits that ran out of their bound
 };
 
-// A GMM2 tile whose wait ran out does not read its rows of q2: its output
-// tile is written as quiet NaN, so that a silently wrong y cannot result.
-__device__ void ffn_poison_tile(const FfnGemm& g, int4 ti, int nt) {
+// A tile whose wait ran out does not read its inputs: its output tile is
+// written as quiet NaN (GMM1: and its rows' max |g| as NaN, so that their
+// quantised g and y follow), so that a silently wrong y cannot result.
+// ncols: output columns per n-tile.
+__device__ void ffn_poison_tile(const FfnGemm& g, int4 ti, int nt, int ncols, uint32_t* amax_bits) {
   const int row0 = ti.y, row_end = min(ti.z, ti.y + kFfnBM);
-  const int n0 = nt * kFfnBW, n1 = min(g.Nout, n0 + kFfnBW);
-  const int cols = n1 - n0;   // a multiple of 8 (Nout is a multiple of 128)
-  const int units = cols / 8;
+  const int n0 = nt * ncols, n1 = min(g.Nout, n0 + ncols);
+  const int units = (n1 - n0) / 8;   // Nout is a multiple of 128
   const v4u nan = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
   for (int i = threadIdx.x; i < (row_end - row0) * units; i += kFfnThreads) {
     const int r = row0 + i / units, c = n0 + (i % units) * 8;
     *reinterpret_cast<v4u*>(g.out + (int64_t)r * g.Nout + c) = nan;
+  }
+  if (amax_bits != nullptr)
+    for (int r = row0 + (int)threadIdx.x; r < row_end; r += kFfnThreads) atomicMax(amax_bits + r, 0x7FC00000u);
+}
+
+// Waits (thread 0; the caller broadcasts the result) until *word >= need,
+// polling with agent-coherent relaxed loads, at most spin_limit times.
+// Returns true when the bound ran out, counted in the status block.
+__device__ bool ffn_wait_at_least(const int* word, int need, int spin_limit, mdc_device_status* status) {
+  int n = 0;
+  while (__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+    if (++n >= spin_limit) {
+      atomicAdd(&status->wait_timeouts, 1);
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return false;
+}
+
+// Makes every wavefront's global stores of the workgroup visible at agent
+// scope before thread 0's next atomic: each wavefront waits for its own
+// stores to complete (vmcnt 0), the barrier joins them, and thread 0 issues
+// one agent-scope release (an L2 write-back).  Ends with a barrier.
+__device__ __forceinline__ void ffn_publish_begin() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt untouched
+  __syncthreads();
+  if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+}
+
+// The pipelined dispatch's inputs to the fused kernel.
+struct FfnDispatchIn {
+  const v4u* x;            // [W][BS][H] bf16 source rows
+  const int32_t* assist;   // [A][3] (source, token, k) of each row, placed by k_dfn_route
+  int BS, nvec;
+};
+
+// Dispatch work of one queue item: rows [lo, hi) of one m-tile, each read
+// from its source row (assist triplet), quantised per row (quant_row, as the
+// quantised gather does) and written as int8 codes and a scale.  Wavefront w
+// handles rows lo + R w .. + R, then + 8 R (R = kDfnInflight rows in flight).
+// Rows move through buffer descriptors (one per row, lane offset 16 l,
+// vector u at u * 1 KB): the range check zero-fills the vectors past the row
+// and drops their stores.
+#ifndef MDC_DFN_INFLIGHT
+#define MDC_DFN_INFLIGHT 1
+#endif
+constexpr int kDfnInflight = MDC_DFN_INFLIGHT;
+__device__ void dfn_copy_rows(const FfnDispatchIn& din, int8_t* __restrict__ q, float* __restrict__ scale, int lo,
+                              int hi) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nvec = din.nvec;
+  for (int r = lo + kDfnInflight * wv; r < hi; r += kDfnInflight * (kFfnThreads / 64)) {
+    v4u v[kDfnInflight][kQuantRowVec];
+#pragma unroll
+    for (int h = 0; h < kDfnInflight; ++h) {
+      const int row = min(r + h, hi - 1);
+      const int s = __builtin_amdgcn_readfirstlane(din.assist[(int64_t)row * 3]);
+      const int t = __builtin_amdgcn_readfirstlane(din.assist[(int64_t)row * 3 + 1]);
+      const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<v4u*>(din.x + ((int64_t)s * din.BS + t) * nvec), (short)0, nvec * 16, 0x00020000);
+#pragma unroll
+      for (int u = 0; u < kQuantRowVec; ++u)
+        v[h][u] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(src, (unsigned)lane * 16u,
+                                                                                 (unsigned)u * 1024u, 0));
+    }
+#pragma unroll
+    for (int h = 0; h < kDfnInflight; ++h) {
+      const int row = r + h;
+      if (row >= hi) break;
+      uint64_t qv[kQuantRowVec];
+      const float sc = quant_row<kQuantRowVec>(v[h], qv);
+      const __amdgpu_buffer_rsrc_t dst =
+          __builtin_amdgcn_make_buffer_rsrc(q + (int64_t)row * nvec * 8, (short)0, nvec * 8, 0x00020000);
+#pragma unroll
+      for (int u = 0; u < kQuantRowVec; ++u)
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, qv[u]), dst, (unsigned)lane * 8u,
+                                              (unsigned)u * 512u, 0);
+      if (lane == 0) scale[row] = sc;
+    }
   }
 }
 
@@ -798,24 +1005,46 @@ __device__ void ffn_quant_mtile(const uint16_t* __restrict__ gsrc, int ncols, in
   }
 }
 
-// A stage of the [PTO] fused pipeline: GMM1 + SwiGLU, the dynamic
-// quantisation of g and GMM2 in one persistent kernel.  Workgroups take
-// tiles from one queue: every GMM1 tile first (plan order), then every GMM2
-// tile (m-tiles in the same group order).  A GMM1 tile stores its g tile,
-// folds max |g| per row into amax_bits and counts itself in done1[m]; the
-// workgroup that finishes an m-tile's last GMM1 tile quantises the m-tile's
-// g rows and sets ready[m] ([PTO] ready flags between GMM1 and GMM2).  A
-// GMM2 tile waits for ready[m].  Every GMM1 tile leaves the queue before any
-// GMM2 tile, and GMM1 tiles wait on nothing, so every wait ends; each wait
-// is also bounded by spin_limit polls (one that runs out is counted in the
-// status block's wait_timeouts and its tile written as NaN).  The XCDs' L2s are not coherent with each other: writes are
-// published with agent-scope release fences (an L2 write-back, issued by
-// one thread per workgroup); the quantiser reads g after one acquire (an L2
-// invalidate) per m-tile, and GMM2 reads q2 and s2 with agent-coherent loads
-// instead of invalidating its XCD's L2 once per tile.
-template <bool TAB>
+// The [PTO] fused pipeline as one persistent kernel: GMM1 + SwiGLU, the
+// dynamic quantisation of g and GMM2 ([PTO] Overall Architecture: stages
+// joined by ready flags), and with DISPATCH also the dispatch of the rows
+// (mdc_dispatch_ffn).  Workgroups take items from one queue.
+//
+// Without DISPATCH the queue holds every GMM1 tile (plan order), then every
+// GMM2 tile.  With DISPATCH it starts with the dispatch items of the first
+// kDfnLead m-tiles (kDfnParts items of kFfnBM / kDfnParts rows per m-tile),
+// then for j = 0 .. MT - 1 the dispatch items of m-tile j + kDfnLead
+// followed by GMM1 tiles j*nn1 .. (j + 1)*nn1 - 1, then the GMM2 tiles: an
+// m-tile's rows are dispatched while GMM1 runs on the m-tiles before it
+// ([PTO] Dispatch of group i + 1 beside GMM1 of group i, D2C flags).  GMM1
+// tile t belongs to a chunk of at most kFfnChunkM = kDfnLead m-tiles that
+// starts at or before m-tile t / nn1, so every m-tile it reads had all of
+// its dispatch items earlier in the queue.
+//
+// A dispatch item writes its rows' codes and scales and adds its row count
+// to rows_ready[m]; a GMM1 tile waits until rows_ready[m] covers its m-tile.
+// A GMM1 tile stores its g tile, folds max |g| per row into amax_bits and
+// counts itself in done1[m]; the workgroup that finishes an m-tile's last
+// GMM1 tile quantises the m-tile's g rows ([PTO] segmented SwiGLU: one
+// segment per m-tile) and sets ready[m] (C2V / V2C flags); a GMM2 tile waits
+// for ready[m].  Every wait is on an item that left the queue earlier, and
+// items that left the queue are run by workgroups that are running, so every
+// wait ends; each one is also bounded by spin_limit polls (one that runs out
+// is counted in the status block's wait_timeouts and its tile written as
+// NaN).  The XCDs' L2s are not coherent with each other: writes are
+// published with agent-scope release fences (ffn_publish_begin: one L2
+// write-back per item); the quantiser reads g after one acquire (an L2
+// invalidate) per m-tile, and tiles read rows written in the same launch
+// (dispatched q1 and s1, quantised q2 and s2) with agent-coherent loads
+// instead of invalidating their XCD's L2 once per tile.
+constexpr int kDfnParts = 8;               // dispatch items per m-tile
+constexpr int kDfnRows = kFfnBM / kDfnParts;
+constexpr int kDfnLead = kFfnChunkM;       // m-tiles dispatched ahead of GMM1
+static_assert(kDfnLead >= kFfnChunkM, "a chunk's m-tiles must be dispatched before its first GMM1 tile");
+
+template <bool TAB, bool DISPATCH>
 __global__ __launch_bounds__(kFfnThreads) void k_ffn_fused(FfnGemm g1, FfnGemm g2, const int4* __restrict__ tiles,
-                                                            FfnSync sync, int spin_limit) {
+                                                            FfnSync sync, int spin_limit, FfnDispatchIn din) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFfnStage];
   __shared__ float sc_row[kFfnBM];
   __shared__ float sc_col[kFfnBW];
@@ -828,7 +1057,9 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_fused(FfnGemm g1, FfnGemm g
   const FfnTab<TAB> tab{tiles, tab_s};
   const int nn1 = (g1.Nout + kFfnBW / 2 - 1) / (kFfnBW / 2);
   const int nn2 = (g2.Nout + kFfnBW - 1) / kFfnBW;
-  const int T1 = MT * nn1, T2 = MT * nn2, TT = T1 + T2;
+  const int PRO = DISPATCH ? kDfnParts * min(kDfnLead, MT) : 0;
+  const int T1 = DISPATCH ? PRO + MT * (kDfnParts + nn1) : MT * nn1;
+  const int TT = T1 + MT * nn2;
   const auto no_next = []() { return FfnNext{false, int4{0, 0, 0, 0}, 0}; };
   for (;;) {
     __syncthreads();   // bcast is free
@@ -838,16 +1069,47 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_fused(FfnGemm g1, FfnGemm g
     if (t >= TT) break;
     FfnStage0 s0;
     if (t < T1) {
+      int t1 = t;
+      if (DISPATCH) {
+        int item = t;   // dispatch item (m-tile * kDfnParts + part), or -1
+        if (t >= PRO) {
+          const int j = (t - PRO) / (kDfnParts + nn1), r = t - PRO - j * (kDfnParts + nn1);
+          item = r < kDfnParts ? (j + kDfnLead) * kDfnParts + r : -1;
+          t1 = j * nn1 + (r - kDfnParts);
+        }
+        if (item >= 0) {
+          const int m = item / kDfnParts;
+          if (m >= MT) continue;   // past the last m-tile: nothing to dispatch
+          const int4 ti = tab.at(m);
+          const int lo = ti.y + (item - m * kDfnParts) * kDfnRows;
+          const int hi = min(min(ti.z, ti.y + kFfnBM), lo + kDfnRows);
+          if (lo >= hi) continue;
+          dfn_copy_rows(din, const_cast<int8_t*>(g1.a_src), const_cast<float*>(g1.row_scale), lo, hi);
+          ffn_publish_begin();
+          if (tid == 0) atomicAdd(sync.rows_ready + m, hi - lo);
+          continue;
+        }
+      }
       int mt, nt;
-      ffn_decode_tile(t, nn1, tab, mt, nt);
+      ffn_decode_tile(t1, nn1, tab, mt, nt);
       const int4 ti = tab.at(mt);
-      ffn_tile<true, false, false>(g1, ti, nt, sm, sync.amax_bits, s0, false, s0, no_next);
-      // Publish: the barrier orders every wavefront's g stores (workgroup
-      // scope) before thread 0's agent-scope release (one L2 write-back per
-      // tile), which precedes its count.
-      __syncthreads();
+      bool late = false;
+      if (DISPATCH) {
+        if (tid == 0)
+          bcast[1] = ffn_wait_at_least(sync.rows_ready + mt, min(ti.z, ti.y + kFfnBM) - ti.y, spin_limit,
+                                       sync.status);
+        __syncthreads();
+        late = bcast[1] != 0;
+      }
+      if (late) {
+        ffn_poison_tile(g1, ti, nt, kFfnBW / 2, sync.amax_bits);
+      } else {
+        // dispatched rows are read with agent-coherent loads
+        ffn_tile<true, DISPATCH, false>(g1, ti, nt, sm, sync.amax_bits, s0, false, s0, no_next);
+      }
+      // Publish the g tile (and max |g|) before counting it.
+      ffn_publish_begin();
       if (tid == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const bool last = atomicAdd(sync.done1 + mt, 1) == nn1 - 1;
         if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // see the other tiles' g and amax
         bcast[1] = last;
@@ -863,23 +1125,10 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_fused(FfnGemm g1, FfnGemm g
     } else {
       int mt, nt;
       ffn_decode_tile(t - T1, nn2, tab, mt, nt);
-      if (tid == 0) {
-        // poll with relaxed (agent-coherent) loads
-        int n = 0;
-        bool late = false;
-        while (__hip_atomic_load(sync.ready + mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
-          if (++n >= spin_limit) {
-            late = true;
-            atomicAdd(&sync.status->wait_timeouts, 1);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-        }
-        bcast[1] = late;
-      }
+      if (tid == 0) bcast[1] = ffn_wait_at_least(sync.ready + mt, 1, spin_limit, sync.status);
       __syncthreads();
       if (bcast[1]) {
-        ffn_poison_tile(g2, tab.at(mt), nt);
+        ffn_poison_tile(g2, tab.at(mt), nt, kFfnBW, nullptr);
         continue;
       }
       // q2 and s2 are read with agent-coherent loads (no L2 invalidate)
@@ -914,7 +1163,7 @@ FfnPlan make_ffn_plan(const mdc_shape* sh, int inter_n) {
   const size_t max_mtiles = 2 + f.A / kFfnBM + f.L;
   f.off_amax = f.off_tiles + round_up(max_mtiles * sizeof(int4), 256);
   f.off_sync = f.off_amax + round_up((size_t)f.A * 4, 256);
-  f.bytes = f.off_sync + round_up((2 + 2 * max_mtiles) * sizeof(int), 256);
+  f.bytes = f.off_sync + round_up(FfnSyncLayout::words((int)max_mtiles, f.L) * sizeof(int), 256);
   return f;
 }
 
@@ -944,6 +1193,26 @@ int ffn_spin_limit(uint32_t flags) {
   return sft != 0 ? (1 << (sft > 30 ? 30 : sft)) : (1 << 24);
 }
 
+// Capacity of the m-tile table, and the fused kernel's synchronisation
+// words (w = NULL for the stream-ordered kernels, which use none).
+int ffn_max_mtiles(const FfnPlan& f) { return (int)(2 + f.A / kFfnBM + f.L); }
+
+FfnSyncLayout ffn_sync_layout(const FfnPlan& f, char* ws, bool fused) {
+  return FfnSyncLayout{fused ? reinterpret_cast<int*>(ws + f.off_sync) : nullptr, ffn_max_mtiles(f), f.L};
+}
+
+FfnSync ffn_sync(const FfnSyncLayout& sw, uint32_t* amax, mdc_device_status* status) {
+  return FfnSync{sw.next(), sw.done1(), sw.ready(), sw.rows_ready(), amax, status};
+}
+
+// Workgroups of the persistent GEMM launches: one per CU (128 KB of LDS
+// each), a multiple of 8 so that every XCD gets the same number.
+unsigned ffn_persistent_grid() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  return (unsigned)(((cus + 7) / 8) * 8);
+}
+
 mdc_status ffn_impl(const FfnPlan& f, uint32_t flags, const void* expand_x, const int8_t* expand_q,
                     const float* dyn_scale, const int64_t* expert_token_nums, const int8_t* w1, const float* w1_scale,
                     const int8_t* w2, const float* w2_scale, void* y, char* ws, hipStream_t s) {
@@ -954,12 +1223,8 @@ mdc_status ffn_impl(const FfnPlan& f, uint32_t flags, const void* expand_x, cons
   uint16_t* g = reinterpret_cast<uint16_t*>(ws + f.off_g);
   int8_t* q2 = reinterpret_cast<int8_t*>(ws + f.off_q2);
   float* s2 = reinterpret_cast<float*>(ws + f.off_s2);
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const unsigned quant_wgs = (unsigned)(cus * 8);
-  // one workgroup per CU (128 KB of LDS each)
-  const unsigned g1 = (unsigned)(((cus + 7) / 8) * 8);
-  const unsigned g2 = g1;
+  const unsigned g1 = ffn_persistent_grid(), g2 = g1;
+  const unsigned quant_wgs = g1 * 8;
   (void)hipGetLastError();
   if (expand_q == nullptr) {
     launch_quant_rows(static_cast<const v4u*>(expand_x), q1, s1, expert_token_nums, f.L, f.A, f.H / 8, quant_wgs, s);
@@ -969,21 +1234,23 @@ mdc_status ffn_impl(const FfnPlan& f, uint32_t flags, const void* expand_x, cons
   }
   int4* tiles = reinterpret_cast<int4*>(ws + f.off_tiles);
   uint32_t* amax = reinterpret_cast<uint32_t*>(ws + f.off_amax);
-  int* sync_words = reinterpret_cast<int*>(ws + f.off_sync);
   const FfnGemm gemm1{q1, s1, w1, w1_scale, g, f.H, f.N, f.N / 2};
   const FfnGemm gemm2{q2, s2, w2, w2_scale, static_cast<uint16_t*>(y), f.N / 2, f.H, f.H};
   const bool fused = (flags & MDC_FLAG_FFN_PIPELINE) != 0;
-  const int max_mtiles = (int)(2 + f.A / kFfnBM + f.L);
-  hipLaunchKernelGGL(k_ffn_plan, dim3(1), dim3(kPlanThreads), 0, s, expert_token_nums, f.L, f.A, tiles,
-                     fused ? sync_words : nullptr, max_mtiles, amax, status);
-  const bool tab = max_mtiles <= kFfnTabCache;   // the m-tile table fits in LDS
+  const FfnSyncLayout sw = ffn_sync_layout(f, ws, fused);
+  hipLaunchKernelGGL(k_ffn_plan, dim3(1), dim3(kPlanThreads), 0, s, expert_token_nums, f.L, f.A, tiles, sw, amax,
+                     status);
+  const bool tab = sw.stride <= kFfnTabCache;   // the m-tile table fits in LDS
   if (fused) {
-    const FfnSync sync{sync_words, sync_words + 2, sync_words + 2 + max_mtiles, amax, status};
+    const FfnSync sync = ffn_sync(sw, amax, status);
     const int spin = ffn_spin_limit(flags);
+    const FfnDispatchIn none{nullptr, nullptr, 0, 0};
     if (tab)
-      hipLaunchKernelGGL(k_ffn_fused<true>, dim3(g1), dim3(kFfnThreads), 0, s, gemm1, gemm2, tiles, sync, spin);
+      hipLaunchKernelGGL((k_ffn_fused<true, false>), dim3(g1), dim3(kFfnThreads), 0, s, gemm1, gemm2, tiles, sync,
+                         spin, none);
     else
-      hipLaunchKernelGGL(k_ffn_fused<false>, dim3(g1), dim3(kFfnThreads), 0, s, gemm1, gemm2, tiles, sync, spin);
+      hipLaunchKernelGGL((k_ffn_fused<false, false>), dim3(g1), dim3(kFfnThreads), 0, s, gemm1, gemm2, tiles, sync,
+                         spin, none);
   } else {
     if (tab)
       hipLaunchKernelGGL((k_ffn_gemm<true, true>), dim3(g1), dim3(kFfnThreads), 0, s, gemm1, tiles);
@@ -994,6 +1261,44 @@ mdc_status ffn_impl(const FfnPlan& f, uint32_t flags, const void* expand_x, cons
       hipLaunchKernelGGL((k_ffn_gemm<false, true>), dim3(g2), dim3(kFfnThreads), 0, s, gemm2, tiles);
     else
       hipLaunchKernelGGL((k_ffn_gemm<false, false>), dim3(g2), dim3(kFfnThreads), 0, s, gemm2, tiles);
+  }
+  return launched();
+}
+
+// mdc_dispatch_ffn: the plan (scan of the layout's group counters + FFN
+// tile plan), the route placement, then the persistent pipeline with the
+// dispatch items in its queue.
+mdc_status dispatch_ffn_impl(const DispatchPlan& p, const FfnPlan& f, uint32_t flags, const void* x,
+                             const GatherMeta& m, int8_t* expand_q, float* dyn_scale, const int8_t* w1,
+                             const float* w1_scale, const int8_t* w2, const float* w2_scale, void* y, char* dws,
+                             char* fws, hipStream_t s) {
+  int32_t* base = reinterpret_cast<int32_t*>(dws + p.off_base);
+  int4* tiles = reinterpret_cast<int4*>(fws + f.off_tiles);
+  uint32_t* amax = reinterpret_cast<uint32_t*>(fws + f.off_amax);
+  mdc_device_status* fstatus = reinterpret_cast<mdc_device_status*>(fws);
+  const FfnSyncLayout sw = ffn_sync_layout(f, fws, true);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_dfn_plan, dim3(1), dim3(kPlanThreads), 0, s, m.cnt, m.drop, base, p.L, p.W, p.G, p.A,
+                     m.ep_recv, m.expert_nums, m.status, tiles, sw, amax, fstatus);
+  const int n_routes = p.W * p.BS * p.K;
+  if (n_routes > 0)
+    hipLaunchKernelGGL(k_dfn_route, dim3((n_routes + 255) / 256), dim3(256), 0, s, m, base, p.BS, p.K, p.L, p.W,
+                       p.TPG, p.G, p.A, n_routes);
+  if (n_routes > 0 && f.A > 0) {
+    const FfnGemm gemm1{expand_q, dyn_scale, w1, w1_scale, reinterpret_cast<uint16_t*>(fws + f.off_g), f.H, f.N,
+                        f.N / 2};
+    const FfnGemm gemm2{reinterpret_cast<int8_t*>(fws + f.off_q2), reinterpret_cast<float*>(fws + f.off_s2), w2,
+                        w2_scale, static_cast<uint16_t*>(y), f.N / 2, f.H, f.H};
+    const FfnSync sync = ffn_sync(sw, amax, fstatus);
+    const FfnDispatchIn din{static_cast<const v4u*>(x), m.assist, p.BS, p.nvec};
+    const int spin = ffn_spin_limit(flags);
+    const unsigned grid = ffn_persistent_grid();
+    if (sw.stride <= kFfnTabCache)
+      hipLaunchKernelGGL((k_ffn_fused<true, true>), dim3(grid), dim3(kFfnThreads), 0, s, gemm1, gemm2, tiles, sync,
+                         spin, din);
+    else
+      hipLaunchKernelGGL((k_ffn_fused<false, true>), dim3(grid), dim3(kFfnThreads), 0, s, gemm1, gemm2, tiles, sync,
+                         spin, din);
   }
   return launched();
 }
@@ -1047,5 +1352,33 @@ mdc_status mdc_ffn_quant_input(const mdc_shape* shape, int32_t inter_n, const in
                   w2, w2_scale, y, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
+
+mdc_status mdc_dispatch_ffn(const mdc_shape* shape, int32_t inter_n, const void* x, const float* expert_scales,
+                            int8_t* expand_q, float* dynamic_scales, int32_t* assist_info, int32_t* ep_recv_counts,
+                            int64_t* expert_token_nums, int32_t* expanded_row_idx, float* expand_scales,
+                            const int8_t* w1, const float* w1_scale, const int8_t* w2, const float* w2_scale, void* y,
+                            void* dispatch_workspace, size_t dispatch_workspace_bytes, void* ffn_workspace,
+                            size_t ffn_workspace_bytes, void* stream) {
+  mdc_status st = check_ffn(shape, inter_n);
+  if (st != MDC_OK) return st;
+  const DispatchPlan p = make_plan(shape);
+  st = check_plan(p);
+  if (st != MDC_OK) return st;
+  st = check_gather_args(p, x, expand_q, dynamic_scales, true, assist_info, ep_recv_counts, expert_token_nums,
+                         expanded_row_idx, expert_scales, expand_scales, dispatch_workspace, dispatch_workspace_bytes);
+  if (st != MDC_OK) return st;
+  const FfnPlan f = make_ffn_plan(shape, inter_n);
+  if (ffn_workspace == nullptr) return MDC_ERR_NULLPTR;
+  if (p.BS > 0 && f.A > 0 &&
+      (w1 == nullptr || w1_scale == nullptr || w2 == nullptr || w2_scale == nullptr || y == nullptr))
+    return MDC_ERR_NULLPTR;
+  if (!aligned16(w1) || !aligned16(w2) || !aligned16(y)) return MDC_ERR_INVALID;
+  if (ffn_workspace_bytes < f.bytes) return MDC_ERR_WORKSPACE;
+  char* dws = static_cast<char*>(dispatch_workspace);
+  const GatherMeta m = make_meta(p, dws, expert_scales, expand_scales, assist_info, ep_recv_counts,
+                                 expert_token_nums, expanded_row_idx);
+  return dispatch_ffn_impl(p, f, (uint32_t)shape->flags, x, m, expand_q, dynamic_scales, w1, w1_scale, w2, w2_scale,
+                           y, dws, static_cast<char*>(ffn_workspace), static_cast<hipStream_t>(stream));
+}
 
 }  // extern "C"

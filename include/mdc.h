@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MDC_ABI_VERSION 3
+#define MDC_ABI_VERSION 4
 #define MDC_MAX_TOPK 16        /* 0 < K <= 16 ([CV4] shape-variable table) */
 #define MDC_MAX_LOCAL_EXPERTS 2048
 #define MDC_MAX_COMBINE_WORLD 64 /* W limit of mdc_combine (pointer tables travel by value) */
@@ -73,7 +73,8 @@ typedef enum {
 
 /* Flags (mdc_shape.flags). */
 #define MDC_FLAG_FFN_PIPELINE 0x1u   /* mdc_ffn*: run GMM1, the quantisation of g and GMM2 as one
-                                        persistent kernel with ready flags between them */
+                                        persistent kernel with ready flags between them
+                                        (mdc_dispatch_ffn always does) */
 #define MDC_FLAG_SPIN_SHIFT 8        /* bits 8..12: if nonzero, s, the pipeline's bounded waits give
                                         up after 2^s polls instead of 2^24 (a test of the time-out
                                         path forces it with a small s) */
@@ -91,8 +92,9 @@ typedef struct {
                                outside [0, E + Z + C) (never sent anywhere, no part in combine) */
     int32_t overflow_rows;  /* dispatch: max(0, R - A): received rows not written for lack of
                                capacity */
-    int32_t wait_timeouts;  /* FFN pipeline: GMM2 tiles whose bounded wait for their quantised
-                               rows ran out (their y rows are written as NaN) */
+    int32_t wait_timeouts;  /* FFN pipeline: tiles whose bounded wait for their input rows ran
+                               out (GMM1 tiles waiting for dispatched rows in mdc_dispatch_ffn,
+                               GMM2 tiles waiting for quantised g); their y rows are NaN */
     int32_t reserved;
 } mdc_device_status;
 
@@ -173,7 +175,7 @@ int32_t mdc_abi_version(void);
  *                     mask_per_route, or NULL (all active); any order of active
  *                     and inactive entries is accepted.
  *   expert_scales     [W][BS][K] fp32, the routes' weights, or NULL (then
- *                     expand_scales must be NULL too).
+ *                     expand_scales must be NULL too, unless BS == 0).
  *
  * The call is split in two stages that may be enqueued separately (same
  * stream, same workspace, in this order); mdc_dispatch enqueues both.
@@ -449,6 +451,60 @@ mdc_status mdc_ffn_quant_input(const mdc_shape* shape,
                                void* y,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/* ------------------------------------------------------------------------
+ * Quantised dispatch and grouped FFN as one pipeline ([PTO] Overall
+ * Architecture: Dispatch -> GMM1 -> SwiGLU -> GMM2 per local-expert group,
+ * joined by ready flags; Dispatch Stage: the destination pulls each expert
+ * group's rows and sets the group's GMM1-ready flag; Optimization Notes:
+ * expert-level overlap and segmented SwiGLU).
+ *
+ * Computes exactly what mdc_dispatch_quant_gather followed by
+ * mdc_ffn_quant_input computes, with the same arguments (shape->rank is the
+ * destination rank): every output of the quantised gather (expand_q,
+ * dynamic_scales, assist_info, ep_recv_counts, expert_token_nums, the
+ * inverse index, expand_scales, the dispatch status block) and y, bit for
+ * bit.  Precondition as for mdc_dispatch_quant_gather: mdc_dispatch_layout
+ * ran on dispatch_workspace earlier on the same stream.
+ *
+ * Three launches: one workgroup scans the layout's group counters once
+ * (counts, epRecvCounts, status, the FFN's m-tile plan); one thread per
+ * route places the routes sent here (inverse index, triplets, weights);
+ * then one persistent kernel whose queue interleaves the dispatch of each
+ * 256-row m-tile's rows (read from x through their triplets, quantised per
+ * row, written to expand_q) with GMM1 tiles of earlier m-tiles, followed by
+ * GMM2 tiles: GMM1 on an m-tile starts once its rows are written, GMM2 once
+ * its rows of g are quantised.  Its waits are bounded as for
+ * MDC_FLAG_FFN_PIPELINE (the spin field of shape->flags applies; a wait that
+ * runs out is counted in the FFN workspace's status block and leaves NaN in
+ * the tile's y rows).  The dispatch status block (dropped ids, overflow
+ * rows) is in dispatch_workspace as for the gather.
+ *
+ * Requirements: those of mdc_dispatch_quant_gather (H <= 8192) and of
+ * mdc_ffn (inter_n, H multiple of 128, tile counts); dispatch_workspace from
+ * mdc_dispatch_workspace, ffn_workspace from mdc_ffn_workspace (the FFN
+ * workspace is always required; the weights and y may be NULL only when
+ * nothing can be received: BS == 0 or A == 0).
+ * ------------------------------------------------------------------------ */
+mdc_status mdc_dispatch_ffn(const mdc_shape* shape,
+                            int32_t inter_n,
+                            const void* x,
+                            const float* expert_scales,
+                            int8_t* expand_q,
+                            float* dynamic_scales,
+                            int32_t* assist_info,
+                            int32_t* ep_recv_counts,
+                            int64_t* expert_token_nums,
+                            int32_t* expanded_row_idx,
+                            float* expand_scales,
+                            const int8_t* w1,
+                            const float* w1_scale,
+                            const int8_t* w2,
+                            const float* w2_scale,
+                            void* y,
+                            void* dispatch_workspace, size_t dispatch_workspace_bytes,
+                            void* ffn_workspace, size_t ffn_workspace_bytes,
+                            void* stream);
 
 #ifdef __cplusplus
 }

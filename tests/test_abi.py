@@ -79,7 +79,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert mdc.mdc_abi_version() == 3
+    assert mdc.mdc_abi_version() == 4
     for code in range(6):
         assert mdc.mdc_status_string(code).startswith("MDC_")
 
@@ -203,6 +203,39 @@ def test_ffn_shape_checks():
     with pytest.raises(mdc.MdcError) as ei:
         mdc.mdc_ffn_workspace(big_a, 2**23)
     assert ei.value.status == mdc.MDC_ERR_UNSUPPORTED
+
+
+def test_dispatch_ffn_argument_checks():
+    """mdc_dispatch_ffn checks the quantised gather's arguments, the FFN's, and both workspaces."""
+    sh_py = mdc.Shape(world=8, rank=0, bs=2048, hidden=7168, topk=8, num_experts=128, capacity=131072)
+    lib = ctypes.CDLL(mdc.LIB_PATH)
+    fake = 1 << 20
+    dws, fws = mdc.mdc_dispatch_workspace(sh_py), mdc.mdc_ffn_workspace(sh_py, 4096)
+    sh = sh_py.c()
+    P = ctypes.c_void_p
+
+    def call(shape=sh, inter=4096, x=fake, scales=None, q=fake, dyn=fake, assist=fake, recv=fake, etn=fake,
+             ridx=fake, esc=None, w1=fake, w1s=fake, w2=fake, w2s=fake, y=fake, dw=fake, dwb=dws, fw=fake, fwb=fws):
+        return lib.mdc_dispatch_ffn(ctypes.byref(shape), ctypes.c_int32(inter), P(x), P(scales), P(q), P(dyn),
+                                    P(assist), P(recv), P(etn), P(ridx), P(esc), P(w1), P(w1s), P(w2), P(w2s), P(y),
+                                    P(dw), ctypes.c_size_t(dwb), P(fw), ctypes.c_size_t(fwb), None)
+
+    for kw in (dict(x=None), dict(q=None), dict(dyn=None), dict(assist=None), dict(recv=None), dict(etn=None),
+               dict(ridx=None), dict(esc=fake), dict(w1=None), dict(w1s=None), dict(w2=None), dict(w2s=None),
+               dict(y=None), dict(dw=None), dict(fw=None)):
+        assert call(**kw) == mdc.MDC_ERR_NULLPTR, kw
+    assert call(dwb=dws - 1) == mdc.MDC_ERR_WORKSPACE
+    assert call(fwb=fws - 1) == mdc.MDC_ERR_WORKSPACE
+    assert call(x=fake + 2) == mdc.MDC_ERR_INVALID
+    assert call(y=fake + 2) == mdc.MDC_ERR_INVALID
+    assert call(inter=0) == mdc.MDC_ERR_INVALID
+    assert call(inter=4096 + 128) == mdc.MDC_ERR_UNSUPPORTED
+    wide = mdc.Shape(world=2, rank=0, bs=4, hidden=8320, topk=2, num_experts=4, capacity=16).c()
+    assert call(shape=wide, inter=256, dwb=1 << 30, fwb=1 << 30) == mdc.MDC_ERR_UNSUPPORTED
+    # nothing to receive (A = 0): the weights and y may be NULL; the FFN workspace may not
+    empty_py = mdc.Shape(world=8, rank=0, bs=2048, hidden=7168, topk=8, num_experts=128, capacity=0)
+    empty = empty_py.c()
+    assert call(shape=empty, fw=None, fwb=mdc.mdc_ffn_workspace(empty_py, 4096)) == mdc.MDC_ERR_NULLPTR
 
 
 def test_combine_world_limit_and_nulls():
