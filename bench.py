@@ -110,7 +110,7 @@ def algorithmic_bytes(w, ids, mask, d=0, r=0):
 
 
 # sources of the dispatch/combine kernels (the ones the HBM-traffic summaries measure)
-TRAFFIC_SOURCES = ("mdc_common.h", "mdc_dispatch.hip")
+TRAFFIC_SOURCES = ("mdc_common.h", "mdc_route.h", "mdc_dispatch.hip")
 
 
 def dispatch_source_sha(sources=TRAFFIC_SOURCES) -> str:

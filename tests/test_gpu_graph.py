@@ -1,8 +1,8 @@
 """HIP graph capture of the decode-size step (one-shot mdc_dispatch, then
-mdc_combine): the captured graph is replayed several times, with eager work
-between the replays, and every replay's outputs must equal the eager run's
-bit for bit (and the oracle's).  The kernels issue no memset, so the graph
-holds kernel nodes only.
+mdc_combine) and of the pipelined dispatch + FFN: each captured graph is
+replayed several times, with eager work between the replays, and every
+replay's outputs must equal the eager run's bit for bit (and the oracle's).
+The kernels issue no memset, so the graphs hold kernel nodes only.
 """
 import sys
 
@@ -99,4 +99,79 @@ def test_graph_replays_equal_eager(name):
         got = _outputs(o, out, row, n)
         for i, (a, b) in enumerate(zip(got, want)):
             assert torch.equal(a, b), f"replay {rep}: output {i} differs from the eager run"
+        say(f"  replay {rep}: bit-exact")
+
+
+def test_graph_replays_of_the_dispatch_ffn_pipeline():
+    """The pipelined dispatch + FFN (mdc_dispatch_layout, then mdc_dispatch_ffn:
+    plan, route placement and the persistent kernel, whose synchronisation
+    words the plan kernel clears without a memset) captured once and replayed
+    three times, every output scrambled in between: each replay equals the
+    eager stream-ordered calls bit for bit."""
+    w = gen.workload("tiny", world=4, bs=128, hidden=256, experts=16, topk=4, index=77)
+    inter = 512
+    say(f"case graph dispatch_ffn W={w.world} BS={w.bs} H={w.hidden} E={w.experts} K={w.topk} N={inter}")
+    wi = gen.world_inputs(w)
+    fw = gen.ffn_weights(w, rank=0, inter=inter)
+    shape = mdc.Shape(w.world, 0, w.bs, w.hidden, w.topk, w.experts, w.capacity)
+    d = G.DEV
+    x = G.to_dev_bf16(wi.x)
+    ids = torch.from_numpy(np.ascontiguousarray(wi.ids)).to(d)
+    wts = [torch.from_numpy(a).to(d) for a in (fw.w1, fw.w1_scale, fw.w2, fw.w2_scale)]
+    A, H, L, W = shape.capacity, shape.hidden, shape.local_experts, shape.world
+
+    def bufs():
+        return dict(q=torch.zeros((A, H), dtype=torch.int8, device=d),
+                    qs=torch.zeros((A,), dtype=torch.float32, device=d),
+                    assist=torch.zeros((A, 3), dtype=torch.int32, device=d),
+                    recv=torch.zeros((L * W,), dtype=torch.int32, device=d),
+                    etn=torch.zeros((L,), dtype=torch.int64, device=d),
+                    row=torch.full((W, w.bs, w.topk), -1, dtype=torch.int32, device=d),
+                    y=torch.zeros((A, H), dtype=torch.bfloat16, device=d),
+                    dws=torch.empty(mdc.mdc_dispatch_workspace(shape), dtype=torch.uint8, device=d),
+                    fws=torch.empty(mdc.mdc_ffn_workspace(shape, inter), dtype=torch.uint8, device=d))
+
+    ref = bufs()
+    mdc.mdc_dispatch_layout(shape, ids, None, ref["dws"])
+    mdc.mdc_dispatch_quant_gather(shape, x, ref["q"], ref["qs"], ref["assist"], ref["recv"], ref["etn"], ref["row"],
+                                  ref["dws"])
+    mdc.mdc_ffn_quant_input(shape, inter, ref["q"], ref["qs"], ref["etn"], *wts, ref["y"], ref["fws"])
+    torch.cuda.synchronize()
+    n = min(int(ref["etn"].sum().item()), A)
+    assert n > 0
+
+    def outputs(b):
+        return (b["q"][:n].cpu(), b["qs"][:n].view(torch.int32).cpu(), b["assist"][:n].cpu(), b["recv"].cpu(),
+                b["etn"].cpu(), b["row"].cpu(), b["y"][:n].view(torch.int16).cpu())
+
+    want = outputs(ref)
+    cs = torch.cuda.Stream()
+    o = bufs()
+    lay = mdc.prepare_dispatch_layout(shape, ids, None, o["dws"], cs)
+    dfn = mdc.prepare_dispatch_ffn(shape, inter, x, o["q"], o["qs"], o["assist"], o["recv"], o["etn"], o["row"],
+                                   *wts, o["y"], o["dws"], o["fws"], cs)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        lay()
+        dfn()
+    torch.cuda.synchronize()
+    L0 = w.experts // w.world
+    sent0 = torch.from_numpy((wi.ids >= 0) & (wi.ids < w.experts) & (wi.ids // L0 == 0)).to(d)
+    for rep in range(3):
+        o["q"].fill_(-1)
+        o["qs"].fill_(float("nan"))
+        o["assist"].fill_(-7)
+        o["recv"].fill_(-3)
+        o["etn"].fill_(-5)
+        o["row"].masked_fill_(sent0, -9)
+        o["y"].view(torch.int16).fill_(0x7F00)
+        o["fws"][:64].fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = outputs(o)
+        for i, (a, b) in enumerate(zip(got, want)):
+            assert torch.equal(a, b), f"replay {rep}: output {i} differs from the eager stream-ordered calls"
+        assert mdc.read_status(o["fws"])["wait_timeouts"] == 0
         say(f"  replay {rep}: bit-exact")
