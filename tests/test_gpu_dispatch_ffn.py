@@ -50,7 +50,8 @@ class Inputs:
             self.wi.ids = ids
         self.cap = w.capacity if capacity is None else capacity
         self.shape = mdc.Shape(w.world, rank, w.bs, w.hidden, w.topk, w.experts, self.cap,
-                               mask_per_route=mask_per_route)
+                               mask_per_route=mask_per_route, zero_experts=w.zero_experts,
+                               copy_experts=w.copy_experts)
         self.fw = gen.ffn_weights(w, rank=rank, inter=inter)
         d = G.DEV
         W, BS, H = w.world, w.bs, w.hidden
@@ -120,7 +121,8 @@ def assert_same_dispatch(a, b, n):
 def check_against_oracle(inp, o, n, check_y=True):
     w, wi = inp.w, inp.wi
     mask = wi.mask
-    ref = O.dispatch(wi.x, wi.ids, mask, inp.rank, w.experts, inp.cap, scales=wi.scales)
+    ref = O.dispatch(wi.x, wi.ids, mask, inp.rank, w.experts, inp.cap, w.zero_experts, w.copy_experts,
+                     scales=wi.scales)
     assert n == ref.assist_info.shape[0]
     assert np.array_equal(o["assist"][:n].cpu().numpy(), ref.assist_info)
     assert np.array_equal(o["recv"].cpu().numpy(), ref.ep_recv_counts)
@@ -146,13 +148,15 @@ def check_against_oracle(inp, o, n, check_y=True):
     dict(world=4, bs=128, hidden=256, experts=32, topk=4, inter=256, inactive_frac=0.25),  # 1D mask
     dict(world=4, bs=128, hidden=256, experts=32, topk=4, inter=256, route_mask_frac=0.2),  # 2D mask
     dict(world=2, bs=1024, hidden=8192, experts=4, topk=2, inter=256),     # the widest quantised row
+    dict(world=4, bs=128, hidden=256, experts=32, topk=4, inter=256, zero_experts=4, copy_experts=4),
 ])
 def test_dispatch_ffn_equals_stream_ordered(variant):
     v = dict(variant)
     inter = v.pop("inter")
     w = gen.workload("tiny", index=60 + v["bs"] % 13 + v["experts"] % 7, **v)
     say(f"dispatch_ffn W={w.world} BS={w.bs} H={w.hidden} E={w.experts} K={w.topk} N={inter} "
-        f"routing={w.routing} mask1d={w.inactive_frac} mask2d={w.route_mask_frac}")
+        f"routing={w.routing} mask1d={w.inactive_frac} mask2d={w.route_mask_frac} "
+        f"Z={w.zero_experts} C={w.copy_experts}")
     inp = Inputs(w, inter, mask_per_route=1 if w.route_mask_frac > 0 else 0)
     a = inp.run_stream_ordered()
     b = inp.run_pipelined()
