@@ -149,6 +149,7 @@ def check_against_oracle(inp, o, n, check_y=True):
     dict(world=4, bs=128, hidden=256, experts=32, topk=4, inter=256, route_mask_frac=0.2),  # 2D mask
     dict(world=2, bs=1024, hidden=8192, experts=4, topk=2, inter=256),     # the widest quantised row
     dict(world=4, bs=128, hidden=256, experts=32, topk=4, inter=256, zero_experts=4, copy_experts=4),
+    dict(world=1, bs=128, hidden=128, experts=2048, topk=16, inter=256),   # max L: 2048 experts of ~1 row
 ])
 def test_dispatch_ffn_equals_stream_ordered(variant):
     v = dict(variant)
@@ -189,6 +190,21 @@ def test_dispatch_ffn_invalid_ids_and_overflow():
     assert n == cap
     assert_same_dispatch(a, b, n)
     assert torch.equal(a["y"][:n].view(torch.int16), b["y"][:n].view(torch.int16))
+    check_against_oracle(inp, b, n)
+
+
+def test_dispatch_ffn_tile_table_in_global_memory():
+    """A capacity of 400000 rows bounds the m-tile table above the 1536 entries
+    the persistent kernel caches in LDS: it reads the table from global memory."""
+    w = gen.workload("tiny", world=2, bs=256, hidden=256, experts=4, topk=2, index=79)
+    inp = Inputs(w, 256, capacity=400_000)
+    a = inp.run_stream_ordered()
+    b = inp.run_pipelined()
+    n = rows_received(a, inp.cap)
+    assert n > 0
+    assert_same_dispatch(a, b, n)
+    assert torch.equal(a["y"][:n].view(torch.int16), b["y"][:n].view(torch.int16))
+    assert mdc.read_status(b["fws"])["wait_timeouts"] == 0
     check_against_oracle(inp, b, n)
 
 
