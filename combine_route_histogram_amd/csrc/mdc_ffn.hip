@@ -413,38 +413,45 @@ __device__ __forceinline__ void ffn_stage_load(const FfnStaging& st, int k0, v4i
   }
 }
 
-// The k loop of one tile (see ffn_tile).  Stage ks + 1 travels global ->
-// registers during stage ks - 1 and registers -> LDS during stage ks, into the
-// buffer nobody reads in stage ks; one barrier ends each stage.  Fragments of
-// k substep q + 1 are read while the MFMAs of substep q run, and the last
-// substep's MFMAs run after the stage barrier, beside the next stage's first
-// fragment reads.  Scheduling groups (sched_group_barrier masks: 0x8 MFMA,
-// 0x100 LDS read, 0x200 LDS write, 0x20 global read) interleave the memory
-// instructions with the MFMAs.
+// The k loop of one tile (see ffn_tile).  The two k stages live in two LDS
+// arrays, l0 (even stages) and l1 (odd stages).  Stage 0 comes through
+// registers (loaded ahead by the persistent walk, or here), every later
+// stage goes global -> LDS directly (buffer loads with the lds bit: no
+// register round trip, no LDS write instructions): stage ks + 1 is loaded
+// into the other array while stage ks is read, each wavefront waits for its
+// own loads (vmcnt 0) before the barrier that ends the stage, and the next
+// load into an array is issued only after that barrier.  Because the arrays
+// are distinct objects, the compiler does not make reads of one wait for
+// loads into the other.  Fragments of k substep q + 1 are read while the
+// MFMAs of substep q run, and the last substep's MFMAs run after the stage
+// barrier, beside the next stage's first fragment reads.  Scheduling groups
+// (sched_group_barrier masks: 0x8 MFMA, 0x100 LDS read) interleave the
+// fragment reads with the MFMAs.
+//
+// A direct load writes lane l's 16 bytes at the block base + 16 l: wavefront
+// w loads 1 KB blocks 4w .. 4w + 3 of the token rows and of the weight rows
+// (8 rows per block), lane l taking row 8 b + l / 8 and LDS slot l % 8, which
+// holds chunk (l % 8) ^ ((row / 2) & 7) of the row: the layout the register
+// path writes.
 //
 // NB = number of the wavefront's 32-row token blocks that hold valid rows:
 // blocks past them stay zero, and their fragment reads and MFMAs are not
 // issued (an expert's short last m-tile is cheap).  NB = 0 still stages and
 // joins the barriers.
 template <bool GLU, int NB, bool COH>
-__device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const FfnStaging& st, int wt, int wn,
-                                          const int (&fr)[4], const FfnStage0& s0, bool pre) {
+__device__ __forceinline__ void ffn_kloop(uint8_t* l0, uint8_t* l1, v16i (&acc)[2][4], const FfnStaging& st, int wt,
+                                          int wn, const int (&fr)[4], const FfnStage0& s0, bool pre) {
   constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;
   constexpr int NR = NB > 0 ? NB + 2 : 0;   // fragment reads per k substep
   constexpr int NM = 2 * NB;                // MFMAs per k substep
+  constexpr int kAux = COH ? 0x10 : 0;      // token rows written in the same launch: agent-coherent loads
+  typedef __attribute__((address_space(3))) void lds_void;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // LDS row of weight block j (32 rows) within the stage's weight tile
   auto wrow = [&](int j) {
     if (GLU) return j == 0 ? wn * 32 : NCOLS + wn * 32;
     return wn * 64 + 32 * j;
-  };
-  v4i sa[4], sw[4];
-  auto gload = [&](int k0) { ffn_stage_load<COH>(st, k0, sa, sw); };
-  auto lwrite = [&](uint8_t* buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<v4i*>(buf + st.lds_off + 64 * i * kFfnBK) = sa[i];
-      *reinterpret_cast<v4i*>(buf + kFfnBM * kFfnBK + st.lds_off + 64 * i * kFfnBK) = sw[i];
-    }
   };
   auto frags = [&](const uint8_t* sb, int q, v4i (&tf)[4], v4i (&wf)[2]) {
     if (NB == 0) return;
@@ -469,52 +476,72 @@ __device__ __forceinline__ void ffn_kloop(uint8_t* lds, v16i (&acc)[2][4], const
     if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto interleave_staging = [&]() {
+  // Direct-load offsets.  Block b = 4 wv + j holds rows 8 b + l / 8; the
+  // lane part (row within the block, swizzled chunk) depends on j only
+  // through j's parity ((row / 2) & 7 = (4 j + l / 16) & 7), and the block's
+  // row offset (with GMM1's gate -> up jump for the weight rows of wavefronts
+  // 4..7, blocks 16..31) is wavefront-uniform: it goes in the scalar offset.
+  unsigned vo[2];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      if (n < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (n < 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      if (n < 8) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      if (n < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  for (int par = 0; par < 2; ++par)
+    vo[par] = (unsigned)((lane >> 3) * st.K) + (unsigned)(((lane & 7) ^ ((4 * par + (lane >> 4)) & 7)) << 4);
+  const unsigned whi_w = (GLU && wv >= 4) ? st.whi : 0u;
+  auto dma = [&](uint8_t* buf, int k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int blk = 4 * wv + j;
+      const unsigned so = (unsigned)k0 + (unsigned)(8 * blk * st.K);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(st.ra, (lds_void*)(buf + blk * 1024), 16, vo[j & 1], so, 0, kAux);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rw, (lds_void*)(buf + kFfnBM * kFfnBK + blk * 1024), 16, vo[j & 1],
+                                               so + whi_w, 0, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   };
 
   const int nk = st.K / kFfnBK;
-  v4i tf[4], wf[2], tg[4], wg[2];
-  if (pre) {   // stage 0 is already in s0
+  {
+    // stage 0 through registers
+    v4i sa[4], sw[4];
+    if (pre) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sa[i] = s0.sa[i];
+        sw[i] = s0.sw[i];
+      }
+    } else {
+      ffn_stage_load<COH>(st, 0, sa, sw);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sa[i] = s0.sa[i];
-      sw[i] = s0.sw[i];
+      *reinterpret_cast<v4i*>(l0 + st.lds_off + 64 * i * kFfnBK) = sa[i];
+      *reinterpret_cast<v4i*>(l0 + kFfnBM * kFfnBK + st.lds_off + 64 * i * kFfnBK) = sw[i];
     }
-  } else {
-    gload(0);
   }
-  lwrite(lds);
+  if (nk > 1) dma(l1, kFfnBK);
   __syncthreads();
-  gload(min(1, nk - 1) * kFfnBK);
-  frags(lds, 0, tf, wf);
-  for (int ks = 0; ks < nk; ++ks) {
-    uint8_t* cur = lds + (ks & 1) * kFfnStage;
-    uint8_t* nxt = lds + ((ks + 1) & 1) * kFfnStage;
+  v4i tf[4], wf[2], tg[4], wg[2];
+  frags(l0, 0, tf, wf);
+  // one stage: substeps 0..2 from cur, then (after the barrier) the load of
+  // stage ks + 2 into cur and substep 3's MFMAs beside stage ks + 1's first reads
+  auto stage = [&](uint8_t* cur, uint8_t* nxt, int ks) {
     frags(cur, 1, tg, wg);
     mfmas(tf, wf);
     interleave_reads();
-    // stage ks + 1: registers -> LDS, then stage ks + 2: global -> registers
-    // (the last iterations repeat the last stage; nobody reads it)
-    lwrite(nxt);
-    gload(min(ks + 2, nk - 1) * kFfnBK);
     frags(cur, 2, tf, wf);
     mfmas(tg, wg);
-    interleave_staging();
+    interleave_reads();
     frags(cur, 3, tg, wg);
     mfmas(tf, wf);
     interleave_reads();
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wavefront's loads into nxt have landed
     __syncthreads();
-    frags(nxt, 0, tf, wf);
+    if (ks + 2 < nk) dma(cur, (ks + 2) * kFfnBK);
+    frags(nxt, 0, tf, wf);   // (after the last stage: read, never used)
     mfmas(tg, wg);
     interleave_reads();
+  };
+  for (int ks = 0; ks < nk; ks += 2) {
+    stage(l0, l1, ks);
+    if (ks + 1 < nk) stage(l1, l0, ks + 1);
   }
 }
 
@@ -568,7 +595,8 @@ struct FfnGemm {
 
 // The kernel's LDS, shared by every tile it runs.
 struct FfnSmem {
-  uint8_t* lds;     // 2 * kFfnStage bytes: k stages, then the output tile
+  uint8_t* l0;      // kFfnStage bytes: even k stages, then output rows 0..127
+  uint8_t* l1;      // kFfnStage bytes: odd k stages, then output rows 128..255
   float* sc_row;    // [kFfnBM] row scales of the tile's token rows
   float* sc_col;    // [kFfnBW] weight-row scales (GMM1: 128 gate, then 128 up)
 };
@@ -661,7 +689,6 @@ __device__ __forceinline__ FfnNext ffn_tile(const FfnGemm& g, int4 ti, int nt, c
   const int row_end = __builtin_amdgcn_readfirstlane(ti.z);
   const int n0 = nt * NCOLS;
   const int rows_here = min(row_end - row0, kFfnBM);
-  uint8_t* lds = sm.lds;
   const FfnStaging st = ffn_staging<GLU>(g, ti, nt);
   const float scv = have ? cur.sc : ffn_scale<GLU, COH>(g, ti, nt);
   __syncthreads();   // the previous tile is done with LDS
@@ -678,11 +705,11 @@ __device__ __forceinline__ FfnNext ffn_tile(const FfnGemm& g, int4 ti, int nt, c
   // 32-row token blocks of this wavefront's half that hold valid rows
   const int nblk = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows_here - wt * 128 + 31) / 32)));
   switch (nblk) {
-    case 4: ffn_kloop<GLU, 4, COH>(lds, acc, st, wt, wn, fr, cur, have); break;
-    case 3: ffn_kloop<GLU, 3, COH>(lds, acc, st, wt, wn, fr, cur, have); break;
-    case 2: ffn_kloop<GLU, 2, COH>(lds, acc, st, wt, wn, fr, cur, have); break;
-    case 1: ffn_kloop<GLU, 1, COH>(lds, acc, st, wt, wn, fr, cur, have); break;
-    default: ffn_kloop<GLU, 0, COH>(lds, acc, st, wt, wn, fr, cur, have); break;
+    case 4: ffn_kloop<GLU, 4, COH>(sm.l0, sm.l1, acc, st, wt, wn, fr, cur, have); break;
+    case 3: ffn_kloop<GLU, 3, COH>(sm.l0, sm.l1, acc, st, wt, wn, fr, cur, have); break;
+    case 2: ffn_kloop<GLU, 2, COH>(sm.l0, sm.l1, acc, st, wt, wn, fr, cur, have); break;
+    case 1: ffn_kloop<GLU, 1, COH>(sm.l0, sm.l1, acc, st, wt, wn, fr, cur, have); break;
+    default: ffn_kloop<GLU, 0, COH>(sm.l0, sm.l1, acc, st, wt, wn, fr, cur, have); break;
   }
 
   // Epilogue.  Lane l holds, for each (j, i) and run q < 4, token
@@ -696,7 +723,7 @@ __device__ __forceinline__ FfnNext ffn_tile(const FfnGemm& g, int4 ti, int nt, c
   for (int i = 0; i < 4; ++i) {
     const int trow = wt * 128 + 32 * i + (lane & 31);
     const float rs = sm.sc_row[trow];
-    uint8_t* orow = lds + trow * (NCOLS * 2);
+    uint8_t* orow = (wt ? sm.l1 : sm.l0) + (trow & 127) * (NCOLS * 2);
     auto put = [&](int c, uint32_t lo, uint32_t hi) {   // c: tile column, multiple of 4
       const int u = (c >> 3) ^ (trow % OU);
       *reinterpret_cast<uint2*>(orow + u * 16 + (c & 4) * 2) = uint2{lo, hi};
@@ -742,7 +769,8 @@ __device__ __forceinline__ FfnNext ffn_tile(const FfnGemm& g, int4 ti, int nt, c
 #pragma unroll 4
   for (int rr = tid / OU; rr < kFfnBM; rr += kFfnThreads / OU) {
     const int row = row0 + rr;
-    const v4u v = *reinterpret_cast<const v4u*>(lds + rr * (NCOLS * 2) + ((u ^ (rr % OU)) * 16));
+    const v4u v = *reinterpret_cast<const v4u*>((rr < 128 ? sm.l0 : sm.l1) + (rr & 127) * (NCOLS * 2) +
+                                                ((u ^ (rr % OU)) * 16));
     if (row < row_end && col < Nout) *reinterpret_cast<v4u*>(g.out + (int64_t)row * Nout + col) = v;
     if (GLU && amax_bits != nullptr) {
       // max |g| over this row's NCOLS columns: the OU threads of a row are
@@ -808,11 +836,12 @@ __device__ __forceinline__ void ffn_cache_tab(const int4* __restrict__ tiles, in
 // Persistent grouped GEMM over the plan's tiles (one workgroup per CU).
 template <bool GLU, bool TAB>
 __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(FfnGemm g, const int4* __restrict__ tiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFfnStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[kFfnStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[kFfnStage];
   __shared__ float sc_row[kFfnBM];
   __shared__ float sc_col[kFfnBW];
   __shared__ int4 tab_s[TAB ? kFfnTabCache : 1];
-  const FfnSmem sm{lds, sc_row, sc_col};
+  const FfnSmem sm{lds0, lds1, sc_row, sc_col};
   constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;
   const int G = gridDim.x;
   const int nn = (g.Nout + NCOLS - 1) / NCOLS;
@@ -1045,12 +1074,13 @@ static_assert(kDfnLead >= kFfnChunkM, "a chunk's m-tiles must be dispatched befo
 template <bool TAB, bool DISPATCH>
 __global__ __launch_bounds__(kFfnThreads) void k_ffn_fused(FfnGemm g1, FfnGemm g2, const int4* __restrict__ tiles,
                                                             FfnSync sync, int spin_limit, FfnDispatchIn din) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFfnStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[kFfnStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[kFfnStage];
   __shared__ float sc_row[kFfnBM];
   __shared__ float sc_col[kFfnBW];
   __shared__ int4 tab_s[TAB ? kFfnTabCache : 1];
   __shared__ int bcast[2];
-  const FfnSmem sm{lds, sc_row, sc_col};
+  const FfnSmem sm{lds0, lds1, sc_row, sc_col};
   const int tid = threadIdx.x;
   const int MT = __builtin_amdgcn_readfirstlane(tiles[0].x);
   ffn_cache_tab<TAB>(tiles, tab_s, MT);
