@@ -272,3 +272,44 @@ def test_dispatch_ffn_wait_timeout_is_reported():
     c = inp.run_pipelined(o=b)
     assert mdc.read_status(c["fws"])["wait_timeouts"] == 0
     assert torch.equal(c["y"][:n].view(torch.int16), a["y"][:n].view(torch.int16))
+
+
+def _random_worlds(n=16, seed=20261203):
+    """Seeded random small worlds for the pipelined path: ragged W/BS/E/K, H a
+    multiple of 128 up to 2048, FFN widths up to 1024, uniform, Zipf, first-K
+    or round-robin routing, 1D or 2D masks, zero/copy experts, full or
+    overflowing capacity."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        W = int(rng.integers(1, 9))
+        L = int(rng.integers(1, 33))
+        Z = int(rng.choice([0, 0, 2]))
+        C = int(rng.choice([0, 0, 2]))
+        E = W * L
+        K = int(rng.integers(1, min(8, E + Z + C) + 1))
+        routing = str(rng.choice(["uniform", "uniform", "zipf", "first_k", "round_robin"]))
+        if Z or C or (routing == "zipf" and K > E):
+            routing = "uniform"   # the other generators draw routed experts only
+        c = dict(world=W, bs=int(rng.integers(1, 513)), hidden=int(rng.choice([128, 256, 384, 1024, 2048])),
+                 experts=E, topk=K, zero_experts=Z, copy_experts=C, routing=routing,
+                 inactive_frac=float(rng.choice([0.0, 0.2])), route_mask_frac=float(rng.choice([0.0, 0.0, 0.3])))
+        inter = int(rng.choice([256, 512, 1024]))
+        cap_scale = float(rng.choice([1.0, 1.0, 0.4]))
+        cases.append(pytest.param(i, c, inter, cap_scale, id=f"world{i}"))
+    return cases
+
+
+@pytest.mark.parametrize("i,cfg,inter,cap_scale", _random_worlds())
+def test_dispatch_ffn_random_worlds(i, cfg, inter, cap_scale):
+    w = gen.workload("tiny", index=300 + i, **cfg)
+    cap = max(1, int(round(w.capacity * cap_scale)))
+    say(f"dispatch_ffn random world {i}: {cfg} N={inter} A={cap}")
+    inp = Inputs(w, inter, capacity=cap, mask_per_route=1 if w.route_mask_frac > 0 else 0)
+    a = inp.run_stream_ordered()
+    b = inp.run_pipelined()
+    n = rows_received(a, inp.cap)
+    assert_same_dispatch(a, b, n)
+    assert mdc.read_status(b["fws"])["wait_timeouts"] == 0
+    assert torch.equal(a["y"][:n].view(torch.int16), b["y"][:n].view(torch.int16))
+    check_against_oracle(inp, b, n)
