@@ -1,8 +1,10 @@
 // libmdc: grouped int8 expert FFN of the MoE hot path for AMD Instinct MI355X
-// (gfx950): mdc_ffn and mdc_ffn_quant_input.
+// (gfx950): mdc_ffn, mdc_ffn_quant_input, and mdc_dispatch_ffn (the quantised
+// dispatch and the FFN as one pipeline).
 //
 // Source: "PTO MegaMoE Dispatch + Combine Fusion Example", GMM1 / SwiGLU /
-// GMM2 stages and the per-token dynamic quantisation between them.
+// GMM2 stages and the per-token dynamic quantisation between them; Overall
+// Architecture and Dispatch Stage for the pipeline.
 
 #include "mdc_route.h"
 
@@ -20,12 +22,14 @@ namespace {
 // The GEMMs use v_mfma_i32_32x32x32_i8 on 256-token x 256-weight-row tiles
 // (GMM1: 128 gate + 128 up weight rows per tile so gate and up land in the
 // same lanes), eight wavefronts (two per SIMD) each holding a 128 x 64 int32
-// accumulator block in registers, k staged through a double-buffered LDS ring
-// 128 bytes deep; the output tile leaves through LDS as whole rows.  By
+// accumulator block in registers, k staged 128 bytes deep through two LDS
+// arrays (a tile's first stage through registers, the others by direct
+// global -> LDS loads); the output tile leaves through LDS as whole rows.  By
 // default GMM1, the quantisation of g and GMM2 run as three stream-ordered
 // kernels, each GEMM persistent and loading its next tile's first k stage
 // before the current tile's output stores; with MDC_FLAG_FFN_PIPELINE they run
-// as one persistent kernel with ready counters between them (k_ffn_fused).
+// as one persistent kernel with ready counters between them (k_ffn_fused), and
+// mdc_dispatch_ffn adds the dispatch of the rows to that kernel's queue.
 // ---------------------------------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
