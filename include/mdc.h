@@ -232,7 +232,7 @@ mdc_status mdc_dispatch(const mdc_shape* shape,
  * static device array of MDC_NOALLOC_SCRATCH_BYTES, one per device, held
  * until the process ends.  Shapes whose mdc_dispatch_workspace exceeds that
  * size return MDC_ERR_UNSUPPORTED (at the share shape the workspace is about
- * 0.53 MB; 8 MiB covers about two million routes).  The call allocates
+ * 0.54 MB; 8 MiB covers about two million routes).  The call allocates
  * nothing; its first call on a device looks up that device's array.  All
  * calls on one device share its array: calls that overlap on one device
  * (other streams, other threads) race and must be ordered by the caller.
