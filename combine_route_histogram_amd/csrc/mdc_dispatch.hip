@@ -16,8 +16,9 @@
 //                     row, writing each row as int8 codes plus a per-row
 //                     fp32 scale.  (mdc_dispatch_quant_gather)
 //   k_dispatch_small  decode-size batches: all of the above in one launch,
-//                     every workgroup re-deriving the histogram and its scan
-//                     from the route list in LDS.  (mdc_dispatch and
+//                     every workgroup counting, over the whole route list,
+//                     the routes placed before each of its token's routes
+//                     (ballots, no histogram).  (mdc_dispatch and
 //                     mdc_dispatch_quant when the route list is small)
 //   k_combine         one wavefront per (token, column tile) of the combining
 //                     rank: reads the token's present expert rows (and the
@@ -470,21 +471,39 @@ __global__ __launch_bounds__(64) void k_dispatch_gather_q(
 
 // ---------------------------------------------------------------------------
 // Small batches: a1 - a5 in one launch.  When the whole route list is small
-// (decode-size batches), every workgroup loads it into LDS, recomputes the
-// per-(le, s) histogram and its scan, ranks its own token's routes (count of
-// earlier routes of the same source with the same expert, [TL] send loop),
-// places them and copies (QUANT: quantises) the token's row.  This replaces
-// the rank kernel and the gather kernel; the outputs are identical.  One
-// 1024-thread workgroup per source token; workgroup 0 also writes
-// epRecvCounts and expertTokenNums.
+// (decode-size batches), every workgroup reads all route ids and counts what
+// it needs instead of building the histogram and its scan.  In the stable
+// expert-major (source, token, k) order, the row of route f with local
+// expert e is the number of routes sent here with a smaller local expert
+// plus the number with expert e that come before f ([TL] GetCumSum and the
+// send loop's ranks, taken together); epRecvCounts[e][s] is the inclusive
+// count of routes with a smaller expert, or expert e from sources <= s, and
+// expertTokenNums[e] the number with expert e.  Each wavefront counts with
+// one ballot per route id it holds and the workgroup sums the wavefronts'
+// counts: no atomics, no scan, two barriers.  Workgroup b places its own
+// token's routes and copies (QUANT: quantises) the token's row, and also
+// writes epRecvCounts entry r G + b and expertTokenNums entry
+// r G + G - 1 - b for rounds r = 0, 1, ... while they exist (G workgroups,
+// one per source token), so that no workgroup counts much more than another;
+// the last epRecvCounts entry is the number of routes sent here, from which
+// its workgroup writes the overflow count, and workgroup 0 counts the
+// dropped ids.  This replaces the rank kernel and the gather kernel; the
+// outputs are identical.
 // ---------------------------------------------------------------------------
-constexpr int kSmallRoutes = 8192;                  // route keys held in LDS
-constexpr int kSmallCounters = 1024;                // L * W counters
+constexpr int kSmallRoutes = 8192;                  // route ids every workgroup reads
+constexpr int kSmallMaxRounds = 16;                 // epRecvCounts entries per workgroup
 constexpr int64_t kSmallRereads = int64_t(1) << 20; // tokens x routes: ids every workgroup rereads
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallRowVec = 1;                     // row vectors per thread kept for the quantiser
 constexpr int kSmallKeyBatch = 2;                   // route ids per thread per batch of kSmallThreads * 2
+// counted values per round: the token's routes, the round's epRecvCounts
+// entry and expert count, and (workgroup 0) the dropped ids
+constexpr int kSmallSlotCnt = MDC_MAX_TOPK;
+constexpr int kSmallSlotExp = kSmallSlotCnt + 1;
+constexpr int kSmallSlotDrop = kSmallSlotExp + 1;
+constexpr int kSmallVals = kSmallSlotDrop + 1;
 static_assert(kSmallRoutes == 4 * kSmallKeyBatch * kSmallThreads, "the small path loads its ids in 1 or 4 batches");
+static_assert(kSmallVals <= kSmallThreads, "one thread sums each counted value");
 
 template <bool QUANT, int NB>
 __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
@@ -494,29 +513,26 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
     int32_t* __restrict__ row_idx, const float* __restrict__ scales_in, float* __restrict__ scales_out,
     mdc_device_status* __restrict__ status, int W, int d, int BS, int K, int E, int L, int64_t A, int nvec,
     int n_ids) {
-  __shared__ int key_s[kSmallRoutes];
-  __shared__ int cnt_s[kSmallCounters];   // histogram, then its exclusive prefix
-  __shared__ int wsum[kSmallThreads / 64];
-  __shared__ int drop_s;
-  __shared__ int rank_s[MDC_MAX_TOPK];
+  __shared__ int part_s[kSmallThreads / 64][kSmallVals];   // per-wavefront counts
+  __shared__ int tkey_s[MDC_MAX_TOPK];   // keys of this token's routes
   __shared__ int row_s[MDC_MAX_TOPK];
   __shared__ float amax_s[kSmallThreads / 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int tok = blockIdx.x;   // s * BS + t
+  const int G = gridDim.x;      // W * BS
   const int s = tok / BS, t = tok - s * BS;
   const int n = W * BS * K;
   const int nc = L * W;
+  const int per_src = BS * K;
 
-  // keys: local expert of an active route sent to d, else -1.  The route
-  // ids are read kSmallKeyBatch per thread at a time, every load issued
-  // before the first is used; the first batch goes out before the token's
-  // row, whose loads then overlap the ranking below.
-  // Route ids and mask flags of all NB batches are loaded first, then the
-  // token's row, then the keys are stored: straight-line code, so the waits
-  // for the ids leave the row loads in flight.  Indices past the end are
-  // clamped, not skipped, and without a mask the mask loads read the first
-  // route id's bytes and are ignored, so that the loads are unconditional.
+  // Route ids and mask flags of all NB batches are loaded first, then this
+  // token's own K ids (lane k of each wavefront loads route k), then the
+  // token's row: straight-line code, so the counting below overlaps the row
+  // loads.
+  // Indices past the end are clamped, not skipped, and without a mask the
+  // mask loads read the first route id's bytes and are ignored, so that the
+  // loads are unconditional.
   constexpr int kB = kSmallKeyBatch * NB;
   int ev[kB];
   uint8_t mv[kB];
@@ -527,6 +543,10 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
   for (int j = 0; j < kB; ++j) ev[j] = ids[min(tid + j * kSmallThreads, n - 1)];
 #pragma unroll
   for (int j = 0; j < kB; ++j) mv[j] = mptr[(min(tid + j * kSmallThreads, n - 1) / mdiv) * mmul];
+  // lane k < K of every wavefront: route k of this token
+  const int ftk = tok * K + min(lane, K - 1);
+  const int tev = ids[ftk];
+  const uint8_t tmv = mptr[(ftk / mdiv) * mmul];
 
   // (clamped as well: vectors past the row's end are never stored, and the
   // quantiser skips them).  The scheduling barriers keep every id and mask
@@ -538,123 +558,118 @@ __global__ __launch_bounds__(kSmallThreads) void k_dispatch_small(
   for (int u = 0; u < kSmallRowVec; ++u) cache[u] = xr[min(tid + u * kSmallThreads, nvec - 1)];
   __builtin_amdgcn_sched_barrier(0);
 
-  // (stored for every f < kB * kSmallThreads <= kSmallRoutes, -1 past n: no
-  // branch for the compiler to sink the loads into)
-  int dropped = 0;   // (workgroup 0 reports the active routes with ids outside [0, n_ids))
+  // key: local expert of an active route sent to d, else -1.  Conditions are
+  // combined with bitwise operators: no branch for the compiler to sink an id
+  // or mask load into (its wait would then also wait for the row loads).
+  auto key_of = [&](int e, uint8_t m) {
+    const int q = e - d * L;
+    const bool ok = ((mask == nullptr) | (m != 0)) & (e >= 0) & (e < E) & (q >= 0) & (q < L);
+    return ok ? q : -1;
+  };
+  // ck: (key, f) of route f as one unsigned number, key * 2^13 + f (f <
+  // kSmallRoutes = 2^13), all ones for routes not sent here; "key below e,
+  // or key e and route before g" is then ck < e * 2^13 + g
+  static_assert(kSmallRoutes <= (1 << 13), "route index must fit 13 bits");
+  unsigned ck[kB];
+  bool drop[kB];   // active routes with ids outside [0, n_ids): dropped, counted by workgroup 0
 #pragma unroll
   for (int j = 0; j < kB; ++j) {
     const int f = tid + j * kSmallThreads;
-    const int q = ev[j] - d * L;
-    const bool active = mask == nullptr || mv[j] != 0;
-    key_s[f] = (f < n && active && ev[j] >= 0 && ev[j] < E && q >= 0 && q < L) ? q : -1;
-    dropped += (f < n && active && (ev[j] < 0 || ev[j] >= n_ids)) ? 1 : 0;
+    const int q = key_of(ev[j], mv[j]);
+    ck[j] = (f < n) & (q >= 0) ? ((unsigned)q << 13) | (unsigned)f : ~0u;
+    drop[j] = (f < n) & ((mask == nullptr) | (mv[j] != 0)) & ((ev[j] < 0) | (ev[j] >= n_ids));
   }
-  for (int i = tid; i < nc; i += kSmallThreads) cnt_s[i] = 0;
-  if (tid < MDC_MAX_TOPK) rank_s[tid] = 0;
-  if (tid == 0) drop_s = 0;
-  __syncthreads();
-  if (tok == 0) {
+  // (lanes >= K hold route K - 1's key and are never read: no select for
+  // the compiler to turn into a branch around the loads)
+  const int tk = key_of(tev, tmv);
+  if (wave == 0 && lane < MDC_MAX_TOPK) tkey_s[lane] = tk;
+  // routes of this wavefront's ids with lo <= ck < hi
+  auto count = [&](unsigned lo, unsigned hi) {
+    int c = 0;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) dropped += __shfl_xor(dropped, o, 64);
-    if (lane == 0 && dropped != 0) atomicAdd(&drop_s, dropped);
-  }
+    for (int j = 0; j < kB; ++j) c += (int)__popcll(__ballot((ck[j] >= lo) & (ck[j] < hi)));
+    return c;
+  };
 
-  // one pass over the keys: histogram cnt[le * W + s'], and the ranks of this
-  // token's routes (earlier routes of source s with the same key).  A rank is
-  // counted per wavefront with one ballot per top-k slot, only in the
-  // wavefronts that hold routes of [f_src, f_tok + K), and added to rank_s by
-  // one lane: at most K LDS atomics per such wavefront instead of one per
-  // matching route.
-  {
-    const int f_tok = tok * K, f_src = s * BS * K, routes_per_src = BS * K;
-    int kk[MDC_MAX_TOPK];
-#pragma unroll
-    for (int k = 0; k < MDC_MAX_TOPK; ++k) kk[k] = k < K ? key_s[f_tok + k] : -1;
-    for (int f0 = 0; f0 < n; f0 += kSmallKeyBatch * kSmallThreads) {
-      int key[kSmallKeyBatch];
-#pragma unroll
-      for (int j = 0; j < kSmallKeyBatch; ++j) {
-        const int f = f0 + tid + j * kSmallThreads;
-        key[j] = f < n ? key_s[f] : -1;
-      }
-#pragma unroll
-      for (int j = 0; j < kSmallKeyBatch; ++j) {
-        const int f = f0 + tid + j * kSmallThreads;
-        if (key[j] >= 0) atomicAdd(&cnt_s[key[j] * W + f / routes_per_src], 1);
-        const bool near = key[j] >= 0 && f >= f_src && f < f_tok + K;
-        if (__ballot(near) != 0) {
-#pragma unroll
-          for (int k = 0; k < MDC_MAX_TOPK; ++k) {
-            if (k >= K) break;
-            const uint64_t m = __ballot(near && key[j] == kk[k] && f < f_tok + k);
-            if (lane == 0 && m != 0) atomicAdd(&rank_s[k], __popcll(m));
-          }
+  const int rounds = (nc + G - 1) / G;
+  for (int r = 0; r < rounds; ++r) {
+    if (r == 0) {
+      // lane k collects the count of route k, then one store per lane
+      int mine = 0;
+#pragma unroll 1
+      for (int k = 0; k < K; ++k) {
+        const int kq = __builtin_amdgcn_readlane(tk, k);
+        if (kq >= 0) {
+          const int c = count(0u, ((unsigned)kq << 13) + (unsigned)(tok * K + k));
+          mine = lane == k ? c : mine;
         }
       }
-    }
-  }
-  __syncthreads();
-
-  // exclusive scan of the counters in (le-major, s-minor) order; thread j
-  // takes counters 4j .. 4j + 3
-  int v[4], sum = 0;
+      if (lane < K) part_s[wave][lane] = mine;
+      if (tok == 0) {
+        int dc = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = 4 * tid + j;
-    v[j] = i < nc ? cnt_s[i] : 0;
-    sum += v[j];
-  }
-  const int incl = wave_inclusive_scan(sum);
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  int run = incl - sum, total = 0;
-#pragma unroll
-  for (int w = 0; w < kSmallThreads / 64; ++w) {
-    run += w < wave ? wsum[w] : 0;
-    total += wsum[w];
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = 4 * tid + j;
-    if (i < nc) {
-      if (tok == 0) ep_recv[i] = run + v[j];   // inclusive ([TL] GetCumSum)
-      cnt_s[i] = run;
-    }
-    run += v[j];
-  }
-  __syncthreads();
-  if (tok == 0) {
-    for (int le = tid; le < L; le += kSmallThreads)
-      expert_nums[le] = (int64_t)((le + 1 < L ? cnt_s[(le + 1) * W] : total) - cnt_s[le * W]);
-    if (tid == 0) {
-      const int64_t over = (int64_t)total - A;
-      status->dropped_ids = drop_s;
-      status->overflow_rows = over > 0 ? (int32_t)over : 0;
-      status->wait_timeouts = 0;
-      status->reserved = 0;
-    }
-  }
-
-  // this token's rows, triplets and inverse-index entries
-  if (tid < K) {
-    const int f = tok * K + tid;
-    const int key = key_s[f];
-    int row = -1;
-    if (key >= 0) {
-      const int64_t r = (int64_t)cnt_s[key * W + s] + rank_s[tid];
-      row = r < A ? (int)r : -1;
-      row_idx[f] = row;
-      if (row >= 0) {
-        int32_t* a = assist + (int64_t)row * 3;
-        a[0] = s;
-        a[1] = t;
-        a[2] = tid;
-        if (scales_out != nullptr) scales_out[row] = scales_in[f];
+        for (int j = 0; j < kB; ++j) dc += (int)__popcll(__ballot(drop[j]));
+        if (lane == 0) part_s[wave][kSmallSlotDrop] = dc;
       }
     }
-    row_s[tid] = row;
+    const int ic = r * G + tok, ie = r * G + G - 1 - tok;
+    if (ic < nc) {
+      const int le = ic / W, lim = (ic - le * W + 1) * per_src;
+      const int c = count(0u, ((unsigned)le << 13) + (unsigned)lim);   // (lim may be 2^13)
+      if (lane == 0) part_s[wave][kSmallSlotCnt] = c;
+    }
+    if (ie < L) {
+      const int c = count((unsigned)ie << 13, (unsigned)(ie + 1) << 13);
+      if (lane == 0) part_s[wave][kSmallSlotExp] = c;
+    }
+    __syncthreads();
+    if (tid < kSmallVals) {
+      const int v = tid;
+      const bool used = v < kSmallSlotCnt ? (r == 0 && v < K)
+                        : v == kSmallSlotCnt ? ic < nc
+                        : v == kSmallSlotExp ? ie < L
+                        : (r == 0 && tok == 0);
+      int sum = 0;
+      if (used)
+#pragma unroll
+        for (int w = 0; w < kSmallThreads / 64; ++w) sum += part_s[w][v];
+      if (v < kSmallSlotCnt) {
+        if (used) {
+          // this token's route k = v
+          const int f = tok * K + v;
+          int row = -1;
+          if (tkey_s[v] >= 0) {
+            row = sum < A ? sum : -1;
+            row_idx[f] = row;
+            if (row >= 0) {
+              int32_t* a = assist + (int64_t)row * 3;
+              a[0] = s;
+              a[1] = t;
+              a[2] = v;
+              if (scales_out != nullptr) scales_out[row] = scales_in[f];
+            }
+          }
+          row_s[v] = row;
+        }
+      } else if (v == kSmallSlotCnt) {
+        if (used) {
+          ep_recv[ic] = sum;   // inclusive ([TL] GetCumSum)
+          if (ic == nc - 1) {
+            // every route sent here
+            const int64_t over = (int64_t)sum - A;
+            status->overflow_rows = over > 0 ? (int32_t)over : 0;
+            status->wait_timeouts = 0;
+            status->reserved = 0;
+          }
+        }
+      } else if (v == kSmallSlotExp) {
+        if (used) expert_nums[ie] = (int64_t)sum;
+      } else if (used) {
+        status->dropped_ids = sum;
+      }
+    }
+    __syncthreads();   // row_s is visible; part_s is free for the next round
   }
-  __syncthreads();
   bool any = false;
   for (int k = 0; k < K; ++k) any |= row_s[k] >= 0;
   if (!any) return;
@@ -1035,7 +1050,8 @@ mdc_status gather_q_impl(const DispatchPlan& p, const void* x, const GatherMeta&
 // see the ids).
 bool small_path(const DispatchPlan& p) {
   const int64_t routes = (int64_t)p.W * p.BS * p.K;
-  return routes > 0 && routes <= kSmallRoutes && (int64_t)p.L * p.W <= kSmallCounters &&
+  return routes > 0 && routes <= kSmallRoutes &&
+         (int64_t)p.L * p.W <= (int64_t)kSmallMaxRounds * p.W * p.BS &&
          (int64_t)p.W * p.BS * routes <= kSmallRereads && p.nvec <= kSmallRowVec * kSmallThreads;
 }
 
