@@ -24,7 +24,10 @@ namespace {
 // same lanes), eight wavefronts (two per SIMD) each holding a 128 x 64 int32
 // accumulator block in registers, k staged 128 bytes deep through two LDS
 // arrays (a tile's first stage through registers, the others by direct
-// global -> LDS loads); the output tile leaves through LDS as whole rows.  By
+// global -> LDS loads); the output tile leaves through LDS as whole rows.  In
+// the stream-ordered GEMMs an expert's tail of at most 32 rows per full m-tile
+// rides along with its full m-tiles as a ninth 32-row token block instead of
+// streaming the expert's weights once more in an m-tile of its own.  By
 // default GMM1, the quantisation of g and GMM2 run as three stream-ordered
 // kernels, each GEMM persistent and loading its next tile's first k stage
 // before the current tile's output stores; with MDC_FLAG_FFN_PIPELINE they run
@@ -40,6 +43,13 @@ constexpr int kFfnBW = 256;        // weight rows per tile (GMM1: 128 gate + 128
 constexpr int kFfnBK = 128;        // k bytes per LDS stage
 constexpr int kFfnThreads = 512;   // 8 wavefronts: 2 along tokens x 4 along weight rows
 constexpr int kFfnStage = (kFfnBM + kFfnBW) * kFfnBK;   // bytes of one LDS stage
+// An expert's tail of at most kFfnExtRows rows per full m-tile rides along
+// with its full m-tiles (the stream-ordered GEMMs only): such an m-tile holds
+// kFfnBM + up to kFfnExtRows token rows, the extra 32-row block of each k
+// stage staged in an LDS array of its own (kFfnExtBytes, one per stage
+// parity).
+constexpr int kFfnExtRows = 32;
+constexpr int kFfnExtBytes = kFfnExtRows * kFfnBK;
 constexpr int kFfnOutAlign = 128;  // GMM output widths (N/2 and H) must be multiples of this
 
 // Tile plan shared by both GEMMs.  Each local expert's rows (contiguous,
@@ -105,7 +115,13 @@ struct FfnSyncLayout {
 // 2t + 1 (thread t; zero past L); with sw.w != NULL it also zeroes the
 // fused kernel's synchronisation words and amax_bits for the rows in use
 // and records each expert's first m-tile and first row.  Zeroes the
-// workspace's status block.
+// workspace's status block.  Table entry 1 + m = {expert, first row, end
+// row, chunk position << 8 | chunk size} of m-tile m.  Without sw.w (the
+// stream-ordered GEMMs) an expert of n rows whose tail t = n % kFfnBM is at
+// most kFfnExtRows per full m-tile has n / kFfnBM m-tiles, the first ones
+// holding kFfnExtRows rows more each until the tail is placed: the tail
+// rows then share their m-tiles' weight stages instead of streaming the
+// expert's weights once more for a nearly empty m-tile.
 __device__ void ffn_plan_body(int64_t c0, int64_t c1, int L, int64_t A, int4* __restrict__ tiles, FfnSyncLayout sw,
                               uint32_t* __restrict__ amax_bits, mdc_device_status* __restrict__ status,
                               int64_t* wsum) {
@@ -116,12 +132,19 @@ __device__ void ffn_plan_body(int64_t c0, int64_t c1, int L, int64_t A, int4* __
   const int64_t x1 = x0 + c0;
   const int lo0 = (int)min(x0, A), hi0 = (int)min(x0 + c0, A);
   const int lo1 = (int)min(x1, A), hi1 = (int)min(x1 + c1, A);
-  const int n0 = (hi0 - lo0 + kFfnBM - 1) / kFfnBM, n1 = (hi1 - lo1 + kFfnBM - 1) / kFfnBM;   // m-tiles
+  const bool ext = sw.w == nullptr;
+  // m-tiles of an expert with n rows (see above)
+  auto mtiles = [&](int n) {
+    const int f = n / kFfnBM, t = n - f * kFfnBM;
+    return ext && f > 0 && t <= kFfnExtRows * f ? f : (n + kFfnBM - 1) / kFfnBM;
+  };
+  const int n0 = mtiles(hi0 - lo0), n1 = mtiles(hi1 - lo1);
   int64_t nm;
   const int p0 = (int)plan_scan_pair(n0, n1, wsum, nm);   // table slot of e0's first m-tile
   for (int h = 0; h < 2; ++h) {
     const int e = h ? e1 : e0, n = h ? n1 : n0, lo = h ? lo1 : lo0, hi = h ? hi1 : hi0;
     const int slot = h ? p0 + n0 : p0;
+    const int tail = hi - lo - n * kFfnBM;   // > 0: rows riding along, kFfnExtRows per m-tile
     // chunks: nch of them, the first `big` with base + 1 m-tiles, the rest with base
     const int nch = (n + kFfnChunkM - 1) / kFfnChunkM;
     const int base = nch ? n / nch : 0, big = nch ? n % nch : 0;
@@ -134,7 +157,9 @@ __device__ void ffn_plan_body(int64_t c0, int64_t c1, int L, int64_t A, int4* __
         pos = (j - big * (base + 1)) % base;
         size = base;
       }
-      tiles[1 + slot + j] = int4{e, lo + j * kFfnBM, hi, (pos << 8) | size};
+      const int r0 = lo + j * kFfnBM + (tail > 0 ? min(tail, kFfnExtRows * j) : 0);
+      const int r1 = tail > 0 ? r0 + kFfnBM + min(kFfnExtRows, max(0, tail - kFfnExtRows * j)) : min(hi, r0 + kFfnBM);
+      tiles[1 + slot + j] = int4{e, r0, r1, (pos << 8) | size};
     }
     if (sw.w != nullptr && e < L) {
       sw.emt()[e] = slot;
@@ -400,6 +425,7 @@ struct FfnStaging {
 struct FfnStage0 {
   v4i sa[4], sw[4];
   float sc;
+  float sc9;   // extended m-tiles: row scale of token row kFfnBM + t (threads t < kFfnExtRows)
 };
 
 // Loads k bytes k0 .. k0 + kFfnBK of this thread's staging rows (4 token
@@ -415,6 +441,22 @@ __device__ __forceinline__ void ffn_stage_load(const FfnStaging& st, int k0, v4i
     sw[i] = __builtin_amdgcn_raw_buffer_load_b128(st.rw, st.vw + (unsigned)(64 * i * st.K) + (i >= 2 ? st.whi : 0u),
                                                   (unsigned)k0, 0);
   }
+}
+
+// The extra token rows kFfnBM .. + 32 of an extended m-tile, k bytes
+// k0 .. k0 + kFfnBK, loaded global -> LDS directly into x (kFfnExtBytes):
+// wavefront w < 4 loads rows kFfnBM + 8 w .. + 8 as one 1 KB block, lane l
+// taking row kFfnBM + 8 w + l / 8 and LDS slot l % 8, which holds chunk
+// (l % 8) ^ ((row / 2) & 7) (the swizzle of every staged row; (row / 2) & 7
+// = (4 w + l / 16) & 7).  Rows past the tile read as zero.
+__device__ __forceinline__ void ffn_stage_dma9(const FfnStaging& st, uint8_t* x, int k0) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wv >= 4) return;
+  const unsigned vo = (unsigned)((lane >> 3) * st.K) + (unsigned)(((lane & 7) ^ ((4 * wv + (lane >> 4)) & 7)) << 4);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(st.ra, (lds_void*)(x + wv * 1024), 16, vo,
+                                           (unsigned)k0 + (unsigned)((kFfnBM + 8 * wv) * st.K), 0, 0);
 }
 
 // The k loop of one tile (see ffn_tile).  The two k stages live in two LDS
@@ -442,12 +484,20 @@ __device__ __forceinline__ void ffn_stage_load(const FfnStaging& st, int k0, v4i
 // blocks past them stay zero, and their fragment reads and MFMAs are not
 // issued (an expert's short last m-tile is cheap).  NB = 0 still stages and
 // joins the barriers.
-template <bool GLU, int NB, bool COH>
-__device__ __forceinline__ void ffn_kloop(uint8_t* l0, uint8_t* l1, v16i (&acc)[2][4], const FfnStaging& st, int wt,
-                                          int wn, const int (&fr)[4], const FfnStage0& s0, bool pre) {
+//
+// X9: the m-tile is extended (NB = 4): the extra 32 token rows of even and
+// odd stages sit in x0 and x1 (ffn_stage_dma9; stage 0's is issued with the
+// stage 0 loads, before them, so it has landed when they have), and
+// wavefront (wt, wn) also multiplies them by its weight block wt into acc9
+// (GLU: wt = 0 gate, wt = 1 up rows of its quarter).
+template <bool GLU, int NB, bool COH, bool X9 = false>
+__device__ __forceinline__ void ffn_kloop(uint8_t* l0, uint8_t* l1, uint8_t* x0, uint8_t* x1, v16i (&acc)[2][4],
+                                          v16i& acc9, const FfnStaging& st, int wt, int wn, const int (&fr)[4],
+                                          const FfnStage0& s0, bool pre) {
+  static_assert(!X9 || NB == 4, "an extended m-tile has all token blocks");
   constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;
-  constexpr int NR = NB > 0 ? NB + 2 : 0;   // fragment reads per k substep
-  constexpr int NM = 2 * NB;                // MFMAs per k substep
+  constexpr int NR = NB > 0 ? NB + 2 + (X9 ? 1 : 0) : 0;   // fragment reads per k substep
+  constexpr int NM = 2 * NB + (X9 ? 1 : 0);                // MFMAs per k substep
   constexpr int kAux = COH ? 0x10 : 0;      // token rows written in the same launch: agent-coherent loads
   typedef __attribute__((address_space(3))) void lds_void;
   const int lane = threadIdx.x & 63;
@@ -457,19 +507,21 @@ __device__ __forceinline__ void ffn_kloop(uint8_t* l0, uint8_t* l1, v16i (&acc)[
     if (GLU) return j == 0 ? wn * 32 : NCOLS + wn * 32;
     return wn * 64 + 32 * j;
   };
-  auto frags = [&](const uint8_t* sb, int q, v4i (&tf)[4], v4i (&wf)[2]) {
+  auto frags = [&](const uint8_t* sb, const uint8_t* sx, int q, v4i (&tf)[4], v4i (&wf)[2], v4i& t9) {
     if (NB == 0) return;
 #pragma unroll
     for (int i = 0; i < NB; ++i) tf[i] = *reinterpret_cast<const v4i*>(sb + (wt * 128 + 32 * i) * kFfnBK + fr[q]);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       wf[j] = *reinterpret_cast<const v4i*>(sb + kFfnBM * kFfnBK + wrow(j) * kFfnBK + fr[q]);
+    if (X9) t9 = *reinterpret_cast<const v4i*>(sx + fr[q]);
   };
-  auto mfmas = [&](const v4i (&tf)[4], const v4i (&wf)[2]) {
+  auto mfmas = [&](const v4i (&tf)[4], const v4i (&wf)[2], const v4i& t9) {
 #pragma unroll
     for (int i = 0; i < NB; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j], tf[i], acc[j][i], 0, 0, 0);
+    if (X9) acc9 = __builtin_amdgcn_mfma_i32_32x32x32_i8(wt ? wf[1] : wf[0], t9, acc9, 0, 0, 0);
   };
   auto interleave_reads = [&]() {
 #pragma unroll
@@ -490,7 +542,7 @@ __device__ __forceinline__ void ffn_kloop(uint8_t* l0, uint8_t* l1, v16i (&acc)[
   for (int par = 0; par < 2; ++par)
     vo[par] = (unsigned)((lane >> 3) * st.K) + (unsigned)(((lane & 7) ^ ((4 * par + (lane >> 4)) & 7)) << 4);
   const unsigned whi_w = (GLU && wv >= 4) ? st.whi : 0u;
-  auto dma = [&](uint8_t* buf, int k0) {
+  auto dma = [&](uint8_t* buf, uint8_t* xbuf, int k0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int blk = 4 * wv + j;
@@ -499,6 +551,10 @@ __device__ __forceinline__ void ffn_kloop(uint8_t* l0, uint8_t* l1, v16i (&acc)[
       __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rw, (lds_void*)(buf + kFfnBM * kFfnBK + blk * 1024), 16, vo[j & 1],
                                                so + whi_w, 0, 0);
     }
+    // extra token rows kFfnBM + 8 wv .. + 8 (block parity wv & 1)
+    if (X9 && wv < 4)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(st.ra, (lds_void*)(xbuf + wv * 1024), 16, vo[wv & 1],
+                                               (unsigned)k0 + (unsigned)((kFfnBM + 8 * wv) * st.K), 0, kAux);
   };
 
   const int nk = st.K / kFfnBK;
@@ -512,6 +568,7 @@ __device__ __forceinline__ void ffn_kloop(uint8_t* l0, uint8_t* l1, v16i (&acc)[
         sw[i] = s0.sw[i];
       }
     } else {
+      if (X9) ffn_stage_dma9(st, x0, 0);
       ffn_stage_load<COH>(st, 0, sa, sw);
     }
 #pragma unroll
@@ -520,32 +577,32 @@ __device__ __forceinline__ void ffn_kloop(uint8_t* l0, uint8_t* l1, v16i (&acc)[
       *reinterpret_cast<v4i*>(l0 + kFfnBM * kFfnBK + st.lds_off + 64 * i * kFfnBK) = sw[i];
     }
   }
-  if (nk > 1) dma(l1, kFfnBK);
+  if (nk > 1) dma(l1, x1, kFfnBK);
   __syncthreads();
-  v4i tf[4], wf[2], tg[4], wg[2];
-  frags(l0, 0, tf, wf);
+  v4i tf[4], wf[2], tg[4], wg[2], tf9, tg9;
+  frags(l0, x0, 0, tf, wf, tf9);
   // one stage: substeps 0..2 from cur, then (after the barrier) the load of
   // stage ks + 2 into cur and substep 3's MFMAs beside stage ks + 1's first reads
-  auto stage = [&](uint8_t* cur, uint8_t* nxt, int ks) {
-    frags(cur, 1, tg, wg);
-    mfmas(tf, wf);
+  auto stage = [&](uint8_t* cur, uint8_t* nxt, uint8_t* ccur, uint8_t* cnxt, int ks) {
+    frags(cur, ccur, 1, tg, wg, tg9);
+    mfmas(tf, wf, tf9);
     interleave_reads();
-    frags(cur, 2, tf, wf);
-    mfmas(tg, wg);
+    frags(cur, ccur, 2, tf, wf, tf9);
+    mfmas(tg, wg, tg9);
     interleave_reads();
-    frags(cur, 3, tg, wg);
-    mfmas(tf, wf);
+    frags(cur, ccur, 3, tg, wg, tg9);
+    mfmas(tf, wf, tf9);
     interleave_reads();
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wavefront's loads into nxt have landed
     __syncthreads();
-    if (ks + 2 < nk) dma(cur, (ks + 2) * kFfnBK);
-    frags(nxt, 0, tf, wf);   // (after the last stage: read, never used)
-    mfmas(tg, wg);
+    if (ks + 2 < nk) dma(cur, ccur, (ks + 2) * kFfnBK);
+    frags(nxt, cnxt, 0, tf, wf, tf9);   // (after the last stage: read, never used)
+    mfmas(tg, wg, tg9);
     interleave_reads();
   };
   for (int ks = 0; ks < nk; ks += 2) {
-    stage(l0, l1, ks);
-    if (ks + 1 < nk) stage(l1, l0, ks + 1);
+    stage(l0, l1, x0, x1, ks);
+    if (ks + 1 < nk) stage(l1, l0, x1, x0, ks + 1);
   }
 }
 
@@ -601,8 +658,10 @@ struct FfnGemm {
 struct FfnSmem {
   uint8_t* l0;      // kFfnStage bytes: even k stages, then output rows 0..127
   uint8_t* l1;      // kFfnStage bytes: odd k stages, then output rows 128..255
-  float* sc_row;    // [kFfnBM] row scales of the tile's token rows
+  float* sc_row;    // [kFfnBM (+ kFfnExtRows)] row scales of the tile's token rows
   float* sc_col;    // [kFfnBW] weight-row scales (GMM1: 128 gate, then 128 up)
+  uint8_t* x0;      // kFfnExtBytes each: the extra rows of even / odd k stages
+  uint8_t* x1;      // (kernels whose plans hold extended m-tiles)
 };
 
 // Buffer descriptors and this thread's staging offsets for tile (ti, nt):
@@ -624,7 +683,7 @@ __device__ __forceinline__ FfnStaging ffn_staging(const FfnGemm& g, int4 ti, int
   const int row0 = __builtin_amdgcn_readfirstlane(ti.y);
   const int row_end = __builtin_amdgcn_readfirstlane(ti.z);
   const int n0 = nt * NCOLS;
-  const int rows_here = min(row_end - row0, kFfnBM);
+  const int rows_here = min(row_end - row0, kFfnBM + kFfnExtRows);   // (only extended m-tiles exceed kFfnBM)
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(g.a_src + (int64_t)row0 * K), (short)0, rows_here * K, 0x00020000);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
@@ -670,7 +729,10 @@ struct FfnNext {
   int nt;
 };
 
-template <bool GLU, bool COH, bool PF, class NextF>
+// EXT: the plan may hold extended m-tiles (up to kFfnBM + kFfnExtRows rows;
+// the LDS stages then hold kFfnExtStage bytes); their extra rows are
+// computed beside the others (ffn_kloop's X9) and leave through registers.
+template <bool GLU, bool COH, bool PF, bool EXT, class NextF>
 __device__ __forceinline__ FfnNext ffn_tile(const FfnGemm& g, int4 ti, int nt, const FfnSmem& sm,
                                             uint32_t* __restrict__ amax_bits, FfnStage0& cur, bool have,
                                             FfnStage0& nxt, NextF&& next) {
@@ -693,27 +755,35 @@ __device__ __forceinline__ FfnNext ffn_tile(const FfnGemm& g, int4 ti, int nt, c
   const int row_end = __builtin_amdgcn_readfirstlane(ti.z);
   const int n0 = nt * NCOLS;
   const int rows_here = min(row_end - row0, kFfnBM);
+  const bool x9 = EXT && row_end - row0 > kFfnBM;   // extended m-tile (uniform)
   const FfnStaging st = ffn_staging<GLU>(g, ti, nt);
   const float scv = have ? cur.sc : ffn_scale<GLU, COH>(g, ti, nt);
+  // row scales of the extra token rows (extended m-tiles; threads < kFfnExtRows)
+  const float sc9 = !x9 ? 0.f : have ? cur.sc9 : g.row_scale[min(row0 + kFfnBM + tid, row_end - 1)];
   __syncthreads();   // the previous tile is done with LDS
   // the epilogue's scales, read from LDS after the k loop's first barrier
   if (tid < kFfnBM) sm.sc_row[tid] = scv;
   else sm.sc_col[tid - kFfnBM] = scv;
+  if (x9 && tid < kFfnExtRows) sm.sc_row[kFfnBM + tid] = sc9;
 
   // acc[j][i]: weight block j (32 rows), token block i (32 rows)
-  v16i acc[2][4];
+  v16i acc[2][4], acc9 = v16i{};
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[j][i] = v16i{};
   // 32-row token blocks of this wavefront's half that hold valid rows
   const int nblk = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows_here - wt * 128 + 31) / 32)));
-  switch (nblk) {
-    case 4: ffn_kloop<GLU, 4, COH>(sm.l0, sm.l1, acc, st, wt, wn, fr, cur, have); break;
-    case 3: ffn_kloop<GLU, 3, COH>(sm.l0, sm.l1, acc, st, wt, wn, fr, cur, have); break;
-    case 2: ffn_kloop<GLU, 2, COH>(sm.l0, sm.l1, acc, st, wt, wn, fr, cur, have); break;
-    case 1: ffn_kloop<GLU, 1, COH>(sm.l0, sm.l1, acc, st, wt, wn, fr, cur, have); break;
-    default: ffn_kloop<GLU, 0, COH>(sm.l0, sm.l1, acc, st, wt, wn, fr, cur, have); break;
+  if (EXT && x9) {
+    ffn_kloop<GLU, 4, COH, EXT>(sm.l0, sm.l1, sm.x0, sm.x1, acc, acc9, st, wt, wn, fr, cur, have);
+  } else {
+    switch (nblk) {
+      case 4: ffn_kloop<GLU, 4, COH>(sm.l0, sm.l1, sm.x0, sm.x1, acc, acc9, st, wt, wn, fr, cur, have); break;
+      case 3: ffn_kloop<GLU, 3, COH>(sm.l0, sm.l1, sm.x0, sm.x1, acc, acc9, st, wt, wn, fr, cur, have); break;
+      case 2: ffn_kloop<GLU, 2, COH>(sm.l0, sm.l1, sm.x0, sm.x1, acc, acc9, st, wt, wn, fr, cur, have); break;
+      case 1: ffn_kloop<GLU, 1, COH>(sm.l0, sm.l1, sm.x0, sm.x1, acc, acc9, st, wt, wn, fr, cur, have); break;
+      default: ffn_kloop<GLU, 0, COH>(sm.l0, sm.l1, sm.x0, sm.x1, acc, acc9, st, wt, wn, fr, cur, have); break;
+    }
   }
 
   // Epilogue.  Lane l holds, for each (j, i) and run q < 4, token
@@ -758,16 +828,65 @@ __device__ __forceinline__ FfnNext ffn_tile(const FfnGemm& g, int4 ti, int nt, c
         }
     }
   }
+  // Extended m-tile: lane l holds token row kFfnBM + (l & 31) and, for run
+  // q, columns cb + 8 q + cq .. + 3 of its weight block.  GLU: the up
+  // values (wt = 1) go to LDS past the staged output rows, [wn][32 rows][36
+  // floats] (padded rows), for the gate wavefront (wt = 0) of the same
+  // quarter; the stream-ordered GEMMs, the only ones with extended m-tiles,
+  // take no amax_bits.
+  float* xup = reinterpret_cast<float*>(sm.l1 + 128 * NCOLS * 2) + wn * (32 * 36) + (lane & 31) * 36;
+  const float rs9 = sm.sc_row[min(kFfnBM + (lane & 31), EXT ? kFfnBM + kFfnExtRows - 1 : kFfnBM - 1)];
+  if (GLU && EXT && x9 && wt == 1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = wn * 32 + 8 * q + cq;
+      float4 hu;
+      hu.x = (float)acc9[4 * q + 0] * rs9 * sm.sc_col[NCOLS + c + 0];
+      hu.y = (float)acc9[4 * q + 1] * rs9 * sm.sc_col[NCOLS + c + 1];
+      hu.z = (float)acc9[4 * q + 2] * rs9 * sm.sc_col[NCOLS + c + 2];
+      hu.w = (float)acc9[4 * q + 3] * rs9 * sm.sc_col[NCOLS + c + 3];
+      *reinterpret_cast<float4*>(xup + 8 * q + cq) = hu;
+    }
+  }
   // the accumulators are spent: load the next tile's stage 0 and scale now,
   // ahead of this tile's output stores
   const FfnNext nx = PF ? next() : FfnNext{false, ti, nt};
   if (PF) {
     const int4 pti = nx.pf ? nx.ti : ti;
     const int pnt = nx.pf ? nx.nt : nt;
-    ffn_stage_load<COH>(ffn_staging<GLU>(g, pti, pnt), 0, nxt.sa, nxt.sw);
+    const FfnStaging pst = ffn_staging<GLU>(g, pti, pnt);
+    // (an extended next tile's extra rows of stage 0 go to x0 first: they
+    // have landed once the stage 0 registers have.  Only for a real next
+    // tile, whose k loop waits for them: no direct load into LDS may be in
+    // flight when the workgroup ends.)
+    const bool px9 = EXT && nx.pf && pti.z - pti.y > kFfnBM;
+    if (px9) ffn_stage_dma9(pst, sm.x0, 0);
+    ffn_stage_load<COH>(pst, 0, nxt.sa, nxt.sw);
     nxt.sc = ffn_scale<GLU, COH>(g, pti, pnt);
+    if (px9) nxt.sc9 = g.row_scale[min(pti.y + kFfnBM + tid, pti.z - 1)];
   }
   __syncthreads();
+  if (EXT && x9 && (!GLU || wt == 0)) {
+    // the extra rows leave from registers, 8 bytes (4 columns) per store
+    const int row = row0 + kFfnBM + (lane & 31);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = GLU ? wn * 32 + 8 * q + cq : wn * 64 + 32 * wt + 8 * q + cq;
+      float v[4];
+      if (GLU) {
+        const float4 hu = *reinterpret_cast<const float4*>(xup + 8 * q + cq);
+        const float hus[4] = {hu.x, hu.y, hu.z, hu.w};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) v[jj] = ffn_silu((float)acc9[4 * q + jj] * rs9 * sm.sc_col[c + jj]) * hus[jj];
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) v[jj] = (float)acc9[4 * q + jj] * rs9 * sm.sc_col[c + jj];
+      }
+      if (row < row_end && n0 + c < Nout)
+        *reinterpret_cast<uint2*>(g.out + (int64_t)row * Nout + n0 + c) =
+            uint2{ffn_pack_bf16(v[0], v[1]), ffn_pack_bf16(v[2], v[3])};
+    }
+  }
   const int u = tid % OU;
   const int col = n0 + u * 8;
 #pragma unroll 4
@@ -818,9 +937,11 @@ __device__ __forceinline__ void ffn_decode_tile(int t, int nn, const Tab& tab, i
 // TAB the kernel copies it into LDS at its start: a global read of a tile's
 // entry would wait behind the previous tile's output stores (loads and
 // stores retire in order), an LDS read does not.  The host takes TAB when
-// the table fits (kFfnTabCache entries); otherwise entries are read from
-// global memory.
+// the table fits (kFfnTabCache entries, kFfnTabCacheExt for the GEMMs whose
+// LDS stages hold extended m-tiles); otherwise entries are read from global
+// memory.
 constexpr int kFfnTabCache = 1536;
+constexpr int kFfnTabCacheExt = 1024;
 
 template <bool TAB>
 struct FfnTab {
@@ -829,23 +950,26 @@ struct FfnTab {
   __device__ __forceinline__ int4 at(int m) const { return TAB ? s[m] : g[1 + m]; }
 };
 
-template <bool TAB>
+template <bool TAB, int CAP = kFfnTabCache>
 __device__ __forceinline__ void ffn_cache_tab(const int4* __restrict__ tiles, int4* tab_s, int MT) {
   if (!TAB) return;
-  const int n = min(MT, kFfnTabCache);   // MT <= kFfnTabCache whenever the host picks TAB
+  const int n = min(MT, CAP);   // MT <= CAP whenever the host picks TAB
   for (int i = threadIdx.x; i < n; i += kFfnThreads) tab_s[i] = tiles[1 + i];
   __syncthreads();
 }
 
-// Persistent grouped GEMM over the plan's tiles (one workgroup per CU).
+// Persistent grouped GEMM over the plan's tiles (one workgroup per CU); the
+// plan may hold extended m-tiles.
 template <bool GLU, bool TAB>
 __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(FfnGemm g, const int4* __restrict__ tiles) {
   __shared__ __attribute__((aligned(16))) uint8_t lds0[kFfnStage];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[kFfnStage];
-  __shared__ float sc_row[kFfnBM];
+  __shared__ __attribute__((aligned(16))) uint8_t ldx0[kFfnExtBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ldx1[kFfnExtBytes];
+  __shared__ float sc_row[kFfnBM + kFfnExtRows];
   __shared__ float sc_col[kFfnBW];
-  __shared__ int4 tab_s[TAB ? kFfnTabCache : 1];
-  const FfnSmem sm{lds0, lds1, sc_row, sc_col};
+  __shared__ int4 tab_s[TAB ? kFfnTabCacheExt : 1];
+  const FfnSmem sm{lds0, lds1, sc_row, sc_col, ldx0, ldx1};
   constexpr int NCOLS = GLU ? kFfnBW / 2 : kFfnBW;
   const int G = gridDim.x;
   const int nn = (g.Nout + NCOLS - 1) / NCOLS;
@@ -853,7 +977,7 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(FfnGemm g, const int4*
   const int T = MT * nn;
   const int b = blockIdx.x;
   const int lin = (b % 8) * (G / 8) + b / 8;   // XCD-contiguous walk (G is a multiple of 8)
-  ffn_cache_tab<TAB>(tiles, tab_s, MT);
+  ffn_cache_tab<TAB, kFfnTabCacheExt>(tiles, tab_s, MT);
   const FfnTab<TAB> tab{tiles, tab_s};
   int t = lin;
   if (t >= T) return;
@@ -861,8 +985,12 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(FfnGemm g, const int4*
   ffn_decode_tile(t, nn, tab, mt, nt);
   int4 ti = tab.at(mt);
   FfnStage0 s0;
-  ffn_stage_load<false>(ffn_staging<GLU>(g, ti, nt), 0, s0.sa, s0.sw);
+  const FfnStaging st0 = ffn_staging<GLU>(g, ti, nt);
+  const bool x9 = ti.z - ti.y > kFfnBM;
+  if (x9) ffn_stage_dma9(st0, ldx0, 0);
+  ffn_stage_load<false>(st0, 0, s0.sa, s0.sw);
   s0.sc = ffn_scale<GLU, false>(g, ti, nt);
+  if (x9) s0.sc9 = g.row_scale[min(ti.y + kFfnBM + (int)threadIdx.x, ti.z - 1)];
   for (;;) {
     // the next tile of this workgroup's walk; its stage 0 is loaded before
     // this tile's output stores
@@ -873,7 +1001,8 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_gemm(FfnGemm g, const int4*
     const int4 te = tab.at(mtn);
     const int4 tin = int4{__builtin_amdgcn_readfirstlane(te.x), __builtin_amdgcn_readfirstlane(te.y),
                           __builtin_amdgcn_readfirstlane(te.z), 0};
-    ffn_tile<GLU, false, true>(g, ti, nt, sm, nullptr, s0, true, s0, [&]() { return FfnNext{has_next, tin, ntn}; });
+    ffn_tile<GLU, false, true, true>(g, ti, nt, sm, nullptr, s0, true, s0,
+                                     [&]() { return FfnNext{has_next, tin, ntn}; });
     if (!has_next) break;
     t = tn;
     mt = mtn;
@@ -1084,7 +1213,7 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_fused(FfnGemm g1, FfnGemm g
   __shared__ float sc_col[kFfnBW];
   __shared__ int4 tab_s[TAB ? kFfnTabCache : 1];
   __shared__ int bcast[2];
-  const FfnSmem sm{lds0, lds1, sc_row, sc_col};
+  const FfnSmem sm{lds0, lds1, sc_row, sc_col, nullptr, nullptr};
   const int tid = threadIdx.x;
   const int MT = __builtin_amdgcn_readfirstlane(tiles[0].x);
   ffn_cache_tab<TAB>(tiles, tab_s, MT);
@@ -1139,7 +1268,7 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_fused(FfnGemm g1, FfnGemm g
         ffn_poison_tile(g1, ti, nt, kFfnBW / 2, sync.amax_bits);
       } else {
         // dispatched rows are read with agent-coherent loads
-        ffn_tile<true, DISPATCH, false>(g1, ti, nt, sm, sync.amax_bits, s0, false, s0, no_next);
+        ffn_tile<true, DISPATCH, false, false>(g1, ti, nt, sm, sync.amax_bits, s0, false, s0, no_next);
       }
       // Publish the g tile (and max |g|) before counting it.
       ffn_publish_begin();
@@ -1166,7 +1295,7 @@ __global__ __launch_bounds__(kFfnThreads) void k_ffn_fused(FfnGemm g1, FfnGemm g
         continue;
       }
       // q2 and s2 are read with agent-coherent loads (no L2 invalidate)
-      ffn_tile<false, true, false>(g2, tab.at(mt), nt, sm, nullptr, s0, false, s0, no_next);
+      ffn_tile<false, true, false, false>(g2, tab.at(mt), nt, sm, nullptr, s0, false, s0, no_next);
     }
   }
 }
@@ -1274,8 +1403,8 @@ mdc_status ffn_impl(const FfnPlan& f, uint32_t flags, const void* expand_x, cons
   const FfnSyncLayout sw = ffn_sync_layout(f, ws, fused);
   hipLaunchKernelGGL(k_ffn_plan, dim3(1), dim3(kPlanThreads), 0, s, expert_token_nums, f.L, f.A, tiles, sw, amax,
                      status);
-  const bool tab = sw.stride <= kFfnTabCache;   // the m-tile table fits in LDS
   if (fused) {
+    const bool tab = sw.stride <= kFfnTabCache;   // the m-tile table fits in LDS
     const FfnSync sync = ffn_sync(sw, amax, status);
     const int spin = ffn_spin_limit(flags);
     const FfnDispatchIn none{nullptr, nullptr, 0, 0};
@@ -1286,6 +1415,7 @@ mdc_status ffn_impl(const FfnPlan& f, uint32_t flags, const void* expand_x, cons
       hipLaunchKernelGGL((k_ffn_fused<false, false>), dim3(g1), dim3(kFfnThreads), 0, s, gemm1, gemm2, tiles, sync,
                          spin, none);
   } else {
+    const bool tab = sw.stride <= kFfnTabCacheExt;
     if (tab)
       hipLaunchKernelGGL((k_ffn_gemm<true, true>), dim3(g1), dim3(kFfnThreads), 0, s, gemm1, tiles);
     else
