@@ -142,6 +142,53 @@ def test_ffn_full_size_then_combine():
     assert err2 <= REL_L2
 
 
+@pytest.mark.parametrize("hidden", [384, 256])
+def test_ffn_tail_rows_ride_along(hidden):
+    """Expert loads chosen around the tail rule of the stream-ordered GEMMs:
+    an expert with n rows whose tail n % 256 is at most 32 per full 256-row
+    m-tile spreads it over its first full m-tiles, 32 rows each; a longer
+    tail keeps an m-tile of its own.  Counts: 0, 1, 33 (no full m-tile),
+    256 (no tail), 288 (tail 32 on one m-tile), 289 (tail 33: own m-tile),
+    544 (tail 32 on two m-tiles), 576 (tail 64: 32 + 32), 577 (tail 65: own
+    m-tile).  H = 384 leaves GMM2's last n-tile half full (the extra rows'
+    column check) and gives GMM1 an odd number of k stages.  The fused
+    pipeline keeps every tail in an m-tile of its own, so its y must be
+    bit-identical; both are checked against the oracle row by row."""
+    counts = [0, 1, 33, 256, 288, 289, 544, 576, 577]
+    L, inter = len(counts), 512
+    w = gen.workload("tiny", world=1, bs=64, hidden=hidden, experts=L, topk=2, index=98)
+    n = sum(counts)
+    cap = n + 64
+    say(f"ffn tail rows H={hidden} N={inter} counts={counts}")
+    x = gen.normal_bf16(gen.rng(w.index, 0, "x"), (cap, hidden))
+    fw = gen.ffn_weights(w, rank=0, inter=inter)
+    w1, s1, w2, s2 = _weights_dev(fw)
+    shape = mdc.Shape(1, 0, w.bs, hidden, 2, L, cap)
+    xd = torch.from_numpy(x.view(np.int16)).to(G.DEV).view(torch.bfloat16)
+    nums = torch.tensor(counts, dtype=torch.int64, device=G.DEV)
+    ws = torch.empty(mdc.mdc_ffn_workspace(shape, inter), dtype=torch.uint8, device=G.DEV)
+    ys = []
+    for flag in (0, mdc.MDC_FLAG_FFN_PIPELINE):
+        y = torch.zeros((cap, hidden), dtype=torch.bfloat16, device=G.DEV)
+        mdc.mdc_ffn(replace(shape, flags=flag), inter, xd, nums, w1, s1, w2, s2, y, ws)
+        torch.cuda.synchronize()
+        assert mdc.read_status(ws)["wait_timeouts"] == 0
+        ys.append(y)
+    a, b = (t[:n].view(torch.int16) for t in ys)
+    assert torch.equal(a, b), f"stream-ordered vs pipeline: {(a != b).sum().item()} values differ"
+    assert not torch.any(ys[0][n:].view(torch.int16) != 0), "rows past the experts' rows were written"
+    row_expert = np.repeat(np.arange(L), counts)
+    want = O.ffn(x[:n], row_expert, fw.w1, fw.w1_scale, fw.w2, fw.w2_scale)
+    got = G.bits(ys[0][:n])
+    af = O.bf16_to_f32(got).astype(np.float64)
+    bf = O.bf16_to_f32(want).astype(np.float64)
+    row_err = np.linalg.norm(af - bf, axis=1) / np.maximum(np.linalg.norm(bf, axis=1), 1e-30)
+    err = rel_l2(got, want)
+    say(f"  bit-identical to the pipeline; rel L2 {err:.3e}, worst row {row_err.max():.3e}")
+    assert err <= REL_L2
+    assert row_err.max() <= 3 * REL_L2
+
+
 @pytest.mark.parametrize("pipeline", [0, 1])
 def test_ffn_tile_table_in_global_memory(pipeline):
     """A capacity of 400000 rows bounds the m-tile table above the 1536 entries
