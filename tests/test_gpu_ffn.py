@@ -189,14 +189,18 @@ def test_ffn_tail_rows_ride_along(hidden):
     assert row_err.max() <= 3 * REL_L2
 
 
+@pytest.mark.parametrize("capacity", [300_000, 400_000])
 @pytest.mark.parametrize("pipeline", [0, 1])
-def test_ffn_tile_table_in_global_memory(pipeline):
-    """A capacity of 400000 rows bounds the m-tile table above the 1536 entries
-    the persistent GEMMs cache in LDS: they read it from global memory."""
+def test_ffn_tile_table_in_global_memory(pipeline, capacity):
+    """A capacity of 400000 rows bounds the m-tile table above the 1536
+    entries the fused kernel caches in LDS and the 1024 the stream-ordered
+    GEMMs cache: both read it from global memory.  At 300000 rows (a bound of
+    1177 entries) the GEMMs read it from global memory and the fused kernel
+    from LDS."""
     w = gen.workload("tiny", world=2, bs=64, hidden=128, experts=4, topk=2, index=90)
-    got, want, *_ = _run_ffn(w, 256, capacity=400_000, flags=mdc.MDC_FLAG_FFN_PIPELINE if pipeline else 0)
+    got, want, *_ = _run_ffn(w, 256, capacity=capacity, flags=mdc.MDC_FLAG_FFN_PIPELINE if pipeline else 0)
     err = rel_l2(got, want)
-    say(f"  pipeline={pipeline} rel L2 {err:.3e} over {got.shape[0]} rows")
+    say(f"  pipeline={pipeline} capacity={capacity} rel L2 {err:.3e} over {got.shape[0]} rows")
     assert err <= REL_L2
 
 
