@@ -487,15 +487,15 @@ __global__ __launch_bounds__(64) void k_dispatch_gather_q(
 // one per source token), so that no workgroup counts much more than another;
 // the last epRecvCounts entry is the number of routes sent here, from which
 // its workgroup writes the overflow count, and workgroup 0 counts the
-// dropped ids.  This replaces the rank kernel and the gather kernel; the
-// outputs are identical.
+// dropped ids.  One 512-thread workgroup per source token.  This replaces
+// the rank kernel and the gather kernel; the outputs are identical.
 // ---------------------------------------------------------------------------
 constexpr int kSmallRoutes = 8192;                  // route ids every workgroup reads
 constexpr int kSmallMaxRounds = 16;                 // epRecvCounts entries per workgroup
 constexpr int64_t kSmallRereads = int64_t(1) << 20; // tokens x routes: ids every workgroup rereads
-constexpr int kSmallThreads = 1024;
-constexpr int kSmallRowVec = 1;                     // row vectors per thread kept for the quantiser
-constexpr int kSmallKeyBatch = 2;                   // route ids per thread per batch of kSmallThreads * 2
+constexpr int kSmallThreads = 512;
+constexpr int kSmallRowVec = 2;                     // row vectors per thread kept for the quantiser
+constexpr int kSmallKeyBatch = 4;                   // route ids per thread per batch of kSmallThreads * 4
 // counted values per round: the token's routes, the round's epRecvCounts
 // entry and expert count, and (workgroup 0) the dropped ids
 constexpr int kSmallSlotCnt = MDC_MAX_TOPK;
