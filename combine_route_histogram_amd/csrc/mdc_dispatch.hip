@@ -63,7 +63,10 @@ namespace {
 // Cache policy per kernel (1 = non-temporal).  Measured on MI355X over whole
 // dispatch+combine steps: non-temporal row loads and stores in both kernels
 // give the shortest step (the two kernels share the Infinity Cache, so each
-// one's policy also moves the other's time).
+// one's policy also moves the other's time).  The quantised gather's int8
+// rows are the exception: they are stored with the default policy, which
+// is faster for its 8-byte stores and leaves the rows cached for the GEMM
+// that reads them next (MDC_GATHER_Q_NT_STORES).
 // Wavefronts per workgroup (each wavefront handles its own row tile).
 #ifndef MDC_GATHER_WAVES
 #define MDC_GATHER_WAVES 1
@@ -76,6 +79,9 @@ namespace {
 #endif
 #ifndef MDC_GATHER_NT_STORES
 #define MDC_GATHER_NT_STORES 1
+#endif
+#ifndef MDC_GATHER_Q_NT_STORES
+#define MDC_GATHER_Q_NT_STORES 0
 #endif
 #ifndef MDC_COMBINE_NT_LOADS
 #define MDC_COMBINE_NT_LOADS 1
@@ -462,7 +468,7 @@ __global__ __launch_bounds__(64) void k_dispatch_gather_q(
     for (int u = 0; u < VPL; ++u) {
       const int idx = lane + u * 64;
       if (idx < nvec) {
-        if (MDC_GATHER_NT_STORES) __builtin_nontemporal_store(qv[u], dst + idx);
+        if (MDC_GATHER_Q_NT_STORES) __builtin_nontemporal_store(qv[u], dst + idx);
         else dst[idx] = qv[u];
       }
     }
