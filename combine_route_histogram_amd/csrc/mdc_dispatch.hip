@@ -61,14 +61,12 @@ namespace {
 #define MDC_COMBINE_VEC 1
 #endif
 // Cache policy per kernel (1 = non-temporal).  Measured on MI355X over whole
-// dispatch+combine steps (the two kernels share the Infinity Cache, so each
-// one's policy also moves the other's time): non-temporal stores in both
-// kernels and non-temporal loads in the combine give the shortest step; the
-// bf16 gather reads its source rows with the default policy (share step
-// 2 us shorter, its gather 3.5 us).  The quantised gather keeps
-// non-temporal source loads, and stores its int8 rows with the default
-// policy, which is faster for its 8-byte stores and leaves the rows cached
-// for the GEMM that reads them next.
+// dispatch+combine steps: non-temporal row loads and stores in both kernels
+// give the shortest step (the two kernels share the Infinity Cache, so each
+// one's policy also moves the other's time).  The quantised gather's int8
+// rows are the exception: they are stored with the default policy, which
+// is faster for its 8-byte stores and leaves the rows cached for the GEMM
+// that reads them next (MDC_GATHER_Q_NT_STORES).
 // Wavefronts per workgroup (each wavefront handles its own row tile).
 #ifndef MDC_GATHER_WAVES
 #define MDC_GATHER_WAVES 1
@@ -77,10 +75,7 @@ namespace {
 #define MDC_COMBINE_WAVES 1
 #endif
 #ifndef MDC_GATHER_NT_LOADS
-#define MDC_GATHER_NT_LOADS 0
-#endif
-#ifndef MDC_GATHER_Q_NT_LOADS
-#define MDC_GATHER_Q_NT_LOADS 1
+#define MDC_GATHER_NT_LOADS 1
 #endif
 #ifndef MDC_GATHER_NT_STORES
 #define MDC_GATHER_NT_STORES 1
@@ -440,7 +435,7 @@ __global__ __launch_bounds__(64) void k_dispatch_gather_q(
 #pragma unroll
     for (int u = 0; u < VPL; ++u) {
       const int idx = lane + u * 64;
-      v[u] = idx < nvec ? load_v4<MDC_GATHER_Q_NT_LOADS != 0>(src + (uint64_t)idx * 16) : v4u{0u, 0u, 0u, 0u};
+      v[u] = idx < nvec ? load_v4<MDC_GATHER_NT_LOADS != 0>(src + (uint64_t)idx * 16) : v4u{0u, 0u, 0u, 0u};
     }
   }
   const int le = p & 0xFFFF;
